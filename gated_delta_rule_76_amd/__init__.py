@@ -5,7 +5,7 @@ package does not load the library -- the first call does, and fails loudly if
 it has not been built.
 """
 
-__all__ = ["prefill", "decode_step", "prefill_workspace_size", "KdaError"]
+__all__ = ["prefill", "decode_step", "prefill_workspace_size", "PrefillCall", "KdaError"]
 
 
 def __getattr__(name):

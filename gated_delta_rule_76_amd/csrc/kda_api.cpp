@@ -1,0 +1,153 @@
+// C ABI of the KDA library: argument validation (host only, before any HIP
+// call) and dispatch to the kernel launchers.  See include/kda.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Shape checks shared by prefill and its workspace query.
+kda_status_t check_prefill_shape(const kda_shape_t *s, bool varlen) {
+  if (s == nullptr) return KDA_ERR_INVALID_ARGUMENT;
+  if (s->num_seqs < 0 || s->total_tokens < 0 || s->num_heads < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (s->d_k < 1 || s->d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (s->qkv_dtype != KDA_F32 && s->qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (!varlen) {
+    if (s->seq_len < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)s->num_seqs * (int64_t)s->seq_len != s->total_tokens) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  if (s->d_k != s->d_v || !supported_dim(s->d_k)) return KDA_ERR_UNSUPPORTED;
+  // Grid limits: one workgroup per (chunk, head) in the chunk-local kernel.
+  if (kda::max_chunks(*s) * (int64_t)s->num_heads >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(kda_status_t status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+kda_status_t kda_prefill_workspace_size(const kda_shape_t *shape, size_t *bytes) {
+  if (bytes == nullptr || shape == nullptr) return KDA_ERR_INVALID_ARGUMENT;
+  // The size does not depend on seq_len, so validate as a varlen shape.
+  kda_status_t st = check_prefill_shape(shape, /*varlen=*/true);
+  if (st != KDA_OK) return st;
+  *bytes = kda::prefill_workspace_bytes(*shape);
+  return KDA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation shared by kda_prefill and its two phases.  `need_*` say which
+// pointers the call reads or writes.
+kda_status_t check_prefill_call(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                                const float *S0, const float *o, const float *S_T,
+                                const void *workspace, size_t workspace_bytes, bool need_v,
+                                bool need_beta, bool need_o) {
+  const bool varlen = cu_seqlens != nullptr;
+  kda_status_t st = check_prefill_shape(shape, varlen);
+  if (st != KDA_OK) return st;
+  const bool has_tokens = shape->total_tokens > 0;
+  if (has_tokens) {
+    if (!q || !k || !alpha || (need_v && !v) || (need_beta && !beta) || (need_o && !o))
+      return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(alpha) || (need_v && !aligned16(v)) ||
+        (need_beta && !aligned4(beta)) || (need_o && !aligned16(o)))
+      return KDA_ERR_INVALID_ARGUMENT;
+  }
+  if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T)) || (cu_seqlens && !aligned16(cu_seqlens)))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (shape->num_seqs == 0) return has_tokens ? KDA_ERR_INVALID_ARGUMENT : KDA_OK;
+  const size_t need = kda::prefill_workspace_bytes(*shape);
+  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kda::kWorkspaceAlign - 1)) != 0)
+    return KDA_ERR_INVALID_ARGUMENT;
+  return KDA_OK;
+}
+
+kda_status_t run_prefill(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                         const float *S0, float *o, float *S_T, void *workspace,
+                         size_t workspace_bytes, void *stream, int phases) {
+  const bool state = (phases & kda::kPhaseState) != 0;
+  const bool local = (phases & kda::kPhaseLocal) != 0;
+  kda_status_t st = check_prefill_call(shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace,
+                                       workspace_bytes, state, local, state);
+  if (st != KDA_OK || shape->num_seqs == 0) return st;
+  hipError_t e = kda::launch_prefill(*shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace,
+                                     static_cast<hipStream_t>(stream), phases);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_prefill(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                         const float *S0, float *o, float *S_T, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  return run_prefill(shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, workspace_bytes,
+                     stream, kda::kPhaseLocal | kda::kPhaseState);
+}
+
+kda_status_t kda_prefill_chunk_local(const kda_shape_t *shape, const void *q, const void *k,
+                                     const float *alpha, const float *beta,
+                                     const int32_t *cu_seqlens, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  return run_prefill(shape, q, k, nullptr, alpha, beta, cu_seqlens, nullptr, nullptr, nullptr,
+                     workspace, workspace_bytes, stream, kda::kPhaseLocal);
+}
+
+kda_status_t kda_prefill_state_pass(const kda_shape_t *shape, const void *q, const void *k,
+                                    const void *v, const float *alpha, const int32_t *cu_seqlens,
+                                    const float *S0, float *o, float *S_T, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  return run_prefill(shape, q, k, v, alpha, nullptr, cu_seqlens, S0, o, S_T, workspace, workspace_bytes,
+                     stream, kda::kPhaseState);
+}
+
+kda_status_t kda_decode_step(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta, float *S, float *o,
+                             void *stream) {
+  if (shape == nullptr) return KDA_ERR_INVALID_ARGUMENT;
+  const kda_shape_t &s = *shape;
+  if (s.num_seqs < 0 || s.num_heads < 1 || s.seq_len != 1 || s.total_tokens != s.num_seqs)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (s.qkv_dtype != KDA_F32 && s.qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (s.d_k < 1 || s.d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (s.d_k != s.d_v || !supported_dim(s.d_k)) return KDA_ERR_UNSUPPORTED;
+  if (s.num_seqs == 0) return KDA_OK;
+  if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned4(beta) ||
+      !aligned16(S) || !aligned16(o))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)s.num_seqs * s.num_heads * (s.d_v / (s.d_v >= 64 ? 64 : s.d_v)) >= ((int64_t)1 << 31))
+    return KDA_ERR_UNSUPPORTED;
+  hipError_t e = kda::launch_decode(s, q, k, v, alpha, beta, S, o, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // extern "C"

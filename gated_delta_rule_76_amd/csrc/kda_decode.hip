@@ -1,0 +1,178 @@
+// Single-token decode step of the KDA layer.
+//
+// For one (sequence, head) and one new token (q, k, v, alpha, beta) the
+// update rule S' = (I - beta k k^T) Diag(alpha) S + beta k v^T (dimsnsums.com
+// "GLM-5.3-FLASH" attention page, section "How can a layer remember without
+// rereading?", update rule) is evaluated column by column of S, in one pass
+// over the state:
+//
+//   x_j = sum_i alpha_i k_i S_ij          (k^T Diag(alpha) S)
+//   y_j = sum_i alpha_i q_i S_ij          (q^T Diag(alpha) S)
+//   w_j = beta (v_j - x_j)
+//   S'_ij = alpha_i S_ij + k_i w_j        (written back in place)
+//   o_j = y_j + (q.k) w_j                 (= sum_i q_i S'_ij, post-update read-out)
+//
+// Value columns never mix, so a workgroup owns a block of up to 64 columns of
+// one head: it reads that 128 x 64 fp32 slab once into registers (float4 per
+// lane, each row's 256 B read by 16 consecutive lanes), reduces x and y over
+// rows with cross-lane shuffles and one LDS round, and writes the slab back.
+// The kernel is bound by HBM: 2 x 64 KiB of state traffic per head and step
+// against ~115 kflop.
+#include <hip/hip_runtime.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+template <int D>
+struct DecodeCfg {
+  static constexpr int CB = D >= 64 ? 64 : D;         // columns per workgroup
+  static constexpr int NCB = D / CB;                   // column blocks per head
+  static constexpr int TPR = CB / 4;                   // lanes per row (float4 each)
+  static constexpr int NT = (TPR * D < 256) ? TPR * D : 256;
+  static constexpr int RPP = NT / TPR;                 // rows per pass
+  static constexpr int PASSES = D / RPP;
+  static constexpr int NW = NT / 64;
+  static_assert(NT % 64 == 0, "workgroup must be whole waves");
+  static_assert(D % RPP == 0, "rows must tile evenly");
+  static_assert(NT >= D, "one staging lane per key channel");
+};
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ S,
+    float *__restrict__ o) {
+  using Cfg = DecodeCfg<D>;
+  constexpr int CB = Cfg::CB, TPR = Cfg::TPR, RPP = Cfg::RPP, PASSES = Cfg::PASSES, NW = Cfg::NW;
+
+  __shared__ float s_al[D];      // alpha_i
+  __shared__ float s_ka[D];      // alpha_i k_i
+  __shared__ float s_qa[D];      // alpha_i q_i
+  __shared__ float s_k[D];       // k_i
+  __shared__ float s_red[NW][2][CB];
+  __shared__ float s_qk[NW];
+  __shared__ float s_w[CB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t nh = (int64_t)(blockIdx.x / Cfg::NCB);  // flattened (sequence, head)
+  const int cb = blockIdx.x % Cfg::NCB;
+
+  const int cq = tid % TPR;  // float4 column within the block
+  const int r0 = tid / TPR;  // first row of this lane
+  float *Sp = S + nh * (int64_t)(D * D) + cb * CB + cq * 4;
+
+  // Issue the state loads first; they are the long-latency part.
+  float4 s[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) s[p] = *reinterpret_cast<const float4 *>(Sp + (int64_t)(r0 + p * RPP) * D);
+
+  float qk_part = 0.0f;
+  if (tid < D) {
+    const float a = alpha[nh * D + tid];
+    const float qi = to_f32(q[nh * D + tid]);
+    const float ki = to_f32(k[nh * D + tid]);
+    s_al[tid] = a;
+    s_ka[tid] = a * ki;
+    s_qa[tid] = a * qi;
+    s_k[tid] = ki;
+    qk_part = qi * ki;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
+  if (lane == 0) s_qk[wave] = qk_part;
+  __syncthreads();
+
+  float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = r0 + p * RPP;
+    const float ka = s_ka[r], qa = s_qa[r];
+    x[0] += ka * s[p].x; x[1] += ka * s[p].y; x[2] += ka * s[p].z; x[3] += ka * s[p].w;
+    y[0] += qa * s[p].x; y[1] += qa * s[p].y; y[2] += qa * s[p].z; y[3] += qa * s[p].w;
+  }
+  // Lanes of one wave that share a column group differ in the bits >= TPR.
+#pragma unroll
+  for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] += __shfl_xor(x[j], off);
+      y[j] += __shfl_xor(y[j], off);
+    }
+  }
+  if (lane < TPR) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s_red[wave][0][cq * 4 + j] = x[j];
+      s_red[wave][1][cq * 4 + j] = y[j];
+    }
+  }
+  __syncthreads();
+
+  if (tid < CB) {
+    float xs = 0.f, ys = 0.f, qk = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      xs += s_red[w][0][tid];
+      ys += s_red[w][1][tid];
+      qk += s_qk[w];
+    }
+    const int col = cb * CB + tid;
+    const float wv = beta[nh] * (to_f32(v[nh * D + col]) - xs);
+    s_w[tid] = wv;
+    o[nh * D + col] = ys + qk * wv;
+  }
+  __syncthreads();
+
+  const float w0 = s_w[cq * 4 + 0], w1 = s_w[cq * 4 + 1], w2 = s_w[cq * 4 + 2], w3 = s_w[cq * 4 + 3];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = r0 + p * RPP;
+    const float a = s_al[r], kr = s_k[r];
+    float4 n;
+    n.x = a * s[p].x + kr * w0;
+    n.y = a * s[p].y + kr * w1;
+    n.z = a * s[p].z + kr * w2;
+    n.w = a * s[p].w + kr * w3;
+    *reinterpret_cast<float4 *>(Sp + (int64_t)r * D) = n;
+  }
+}
+
+template <int D, typename TIn>
+hipError_t launch_decode_t(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta, float *S, float *o,
+                           hipStream_t stream) {
+  using Cfg = DecodeCfg<D>;
+  const int64_t blocks = (int64_t)s.num_seqs * s.num_heads * Cfg::NCB;
+  hipLaunchKernelGGL((decode_kernel<D, TIn>), dim3((unsigned)blocks), dim3(Cfg::NT), 0, stream,
+                     static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                     static_cast<const TIn *>(v), alpha, beta, S, o);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t dispatch_d(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                      const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
+  switch (s.d_k) {
+    case 16: return launch_decode_t<16, TIn>(s, q, k, v, alpha, beta, S, o, st);
+    case 32: return launch_decode_t<32, TIn>(s, q, k, v, alpha, beta, S, o, st);
+    case 64: return launch_decode_t<64, TIn>(s, q, k, v, alpha, beta, S, o, st);
+    case 128: return launch_decode_t<128, TIn>(s, q, k, v, alpha, beta, S, o, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, float *S, float *o,
+                         hipStream_t stream) {
+  if (s.qkv_dtype == KDA_BF16) return dispatch_d<__bf16>(s, q, k, v, alpha, beta, S, o, stream);
+  return dispatch_d<float>(s, q, k, v, alpha, beta, S, o, stream);
+}
+
+}  // namespace kda

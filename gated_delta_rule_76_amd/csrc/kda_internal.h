@@ -1,0 +1,52 @@
+// Internal interface between the C ABI (kda_api.cpp) and the kernel
+// launchers (kda_decode.hip, kda_prefill.hip).  Not installed; not part of
+// the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+constexpr int kChunk = KDA_CHUNK;  // tokens per prefill chunk
+
+// Per chunk and head the prefill keeps two 64x64 fp32 matrices in the
+// workspace (the UT-transformed erase matrix and the decayed q.k^T block).
+constexpr size_t kChunkMatBytes = size_t(2) * kChunk * kChunk * sizeof(float);
+constexpr size_t kWorkspaceAlign = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Upper bound on the number of 64-token chunks of a batch: every sequence
+// contributes at most one partial chunk.
+inline int64_t max_chunks(const kda_shape_t &s) {
+  return s.total_tokens / kChunk + (int64_t)s.num_seqs;
+}
+
+// Workspace layout: [chunk base table: (N+1) int32, padded to 256 B]
+//                   [chunk matrices: max_chunks * H * kChunkMatBytes]
+inline size_t schedule_bytes(const kda_shape_t &s) {
+  return align_up(sizeof(int32_t) * (size_t)(s.num_seqs + 1), kWorkspaceAlign);
+}
+inline size_t prefill_workspace_bytes(const kda_shape_t &s) {
+  return schedule_bytes(s) + (size_t)max_chunks(s) * (size_t)s.num_heads * kChunkMatBytes;
+}
+
+hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, float *S, float *o,
+                         hipStream_t stream);
+
+// Prefill phases (bit mask): the chunk table and chunk-local matrices, then
+// the sequential state pass.
+constexpr int kPhaseLocal = 1;
+constexpr int kPhaseState = 2;
+
+hipError_t launch_prefill(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                          const float *S0, float *o, float *S_T, void *workspace,
+                          hipStream_t stream, int phases);
+
+}  // namespace kda

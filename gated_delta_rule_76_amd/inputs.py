@@ -19,9 +19,8 @@ Distributions (per the workloads the layer is measured on):
   lengths  uniform integers in [lo, hi] inclusive.
 
 Draw order and seeding: every tensor has its own stream id and is drawn in
-blocks of 65,536 tokens, block b of stream s seeded with
-seed * 1_000_003 + 7919 * s + b, so that a prefix of a long input does not
-depend on how long the rest is.  Lengths use a CPU generator; everything
+blocks of 65,536 tokens (bounding the temporaries of very long inputs),
+block b of stream s seeded with seed * 1_000_003 + 7919 * s + b.  Lengths use a CPU generator; everything
 else uses a generator on ``device`` (CPU and GPU generators give different
 numbers, which is fine: the oracle always consumes the exact tensors the GPU
 consumed, copied back).

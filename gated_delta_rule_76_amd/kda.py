@@ -1,0 +1,252 @@
+"""Python binding of the KDA C ABI (include/kda.h): argument marshalling only.
+
+Every step of the layer runs in the HIP library (lib/libkda.so); this module
+checks tensor shapes/dtypes/devices, allocates outputs and the workspace with
+torch on the tensors' device, and passes raw pointers plus the current HIP
+stream.  There is no fallback: if the library is missing or the tensors are
+not on a GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARGUMENT = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_WORKSPACE_TOO_SMALL = 3
+KDA_ERR_LAUNCH = 4
+KDA_F32 = 0
+KDA_BF16 = 1
+CHUNK = 64
+
+_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+class KdaError(RuntimeError):
+    """A KDA library call returned a non-OK status."""
+
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class KdaShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("num_heads", ctypes.c_int32),
+        ("d_k", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("qkv_dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def lib():
+    """Load (once) and return the ctypes handle of libkda.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"KDA library not built ({_LIB_PATH} missing); "
+                           "run `python -m gated_delta_rule_76_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    shp = ctypes.POINTER(KdaShape)
+    L.kda_abi_version.restype = ctypes.c_int
+    L.kda_abi_version.argtypes = []
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_prefill_workspace_size.restype = ctypes.c_int
+    L.kda_prefill_workspace_size.argtypes = [shp, ctypes.POINTER(sz)]
+    L.kda_prefill.restype = ctypes.c_int
+    L.kda_prefill.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kda_prefill_chunk_local.restype = ctypes.c_int
+    L.kda_prefill_chunk_local.argtypes = [shp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kda_prefill_state_pass.restype = ctypes.c_int
+    L.kda_prefill_state_pass.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kda_decode_step.restype = ctypes.c_int
+    L.kda_decode_step.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().kda_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != KDA_OK:
+        raise KdaError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device}); the KDA library has no CPU path")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_shape(num_seqs, seq_len, total_tokens, num_heads, d, dtype):
+    return KdaShape(int(num_seqs), int(seq_len), int(total_tokens), int(num_heads), int(d), int(d),
+                    _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype))
+
+
+def prefill_workspace_size(num_seqs, total_tokens, num_heads, d, dtype=torch.bfloat16):
+    """Workspace bytes kda_prefill needs (depends on N, T, H only)."""
+    shape = make_shape(num_seqs, 0, total_tokens, num_heads, d, dtype)
+    out = ctypes.c_size_t(0)
+    _check(lib().kda_prefill_workspace_size(ctypes.byref(shape), ctypes.byref(out)),
+           "kda_prefill_workspace_size")
+    return int(out.value)
+
+
+class PrefillCall:
+    """A validated prefill problem: tensors, outputs and workspace bound to
+    the three C entry points.  ``run()`` is kda_prefill; ``chunk_local()``
+    and ``state_pass()`` are its two phases (run in that order)."""
+
+    def __init__(self, q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
+                 output_final_state=True, workspace=None, out=None, final_state=None):
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _require_gpu(name, t)
+        if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("q, k, v must share one dtype, float32 or bfloat16")
+        _require_gpu("alpha", alpha, torch.float32)
+        _require_gpu("beta", beta, torch.float32)
+        dev = q.device
+        if q.dim() == 4:
+            if cu_seqlens is not None:
+                raise ValueError("cu_seqlens needs the packed [T, H, D] layout")
+            B, T, H, D = q.shape
+            N, seq_len, total = B, T, B * T
+        elif q.dim() == 3:
+            T, H, D = q.shape
+            total = T
+            if cu_seqlens is None:
+                N, seq_len = 1, T
+            else:
+                _require_gpu("cu_seqlens", cu_seqlens, torch.int32)
+                if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+                    raise ValueError("cu_seqlens must be a 1-D int32 tensor [N+1]")
+                N, seq_len = cu_seqlens.numel() - 1, 0
+        else:
+            raise ValueError("q must be [T, H, D] or [B, T, H, D]")
+        for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("alpha", alpha, q.shape),
+                             ("beta", beta, q.shape[:-1])):
+            if tuple(t.shape) != tuple(shp):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
+        if initial_state is not None:
+            _require_gpu("initial_state", initial_state, torch.float32)
+            if tuple(initial_state.shape) != (N, H, D, D):
+                raise ValueError(f"initial_state must be {(N, H, D, D)}")
+        self.shape = make_shape(N, seq_len, total, H, D, q.dtype)
+        self.o = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=dev)
+        _require_gpu("out", self.o, torch.float32)
+        self.S_T = None
+        if output_final_state:
+            self.S_T = (final_state if final_state is not None
+                        else torch.empty((N, H, D, D), dtype=torch.float32, device=dev))
+            _require_gpu("final_state", self.S_T, torch.float32)
+        need = prefill_workspace_size(N, total, H, D, q.dtype)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        _require_gpu("workspace", workspace)
+        self.workspace = workspace
+        self.device = dev
+        self._t = (q, k, v, alpha, beta, cu_seqlens, initial_state)
+
+    def _ws(self):
+        return _ptr(self.workspace), self.workspace.numel() * self.workspace.element_size()
+
+    def run(self):
+        q, k, v, alpha, beta, cu, S0 = self._t
+        ws, nb = self._ws()
+        _check(lib().kda_prefill(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                 _ptr(beta), _ptr(cu), _ptr(S0), _ptr(self.o), _ptr(self.S_T), ws, nb,
+                                 _stream(self.device)), "kda_prefill")
+        return self.o, self.S_T
+
+    def chunk_local(self):
+        q, k, _, alpha, beta, cu, _ = self._t
+        ws, nb = self._ws()
+        _check(lib().kda_prefill_chunk_local(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(alpha),
+                                             _ptr(beta), _ptr(cu), ws, nb, _stream(self.device)),
+               "kda_prefill_chunk_local")
+
+    def state_pass(self):
+        q, k, v, alpha, _, cu, S0 = self._t
+        ws, nb = self._ws()
+        _check(lib().kda_prefill_state_pass(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(alpha), _ptr(cu), _ptr(S0), _ptr(self.o),
+                                            _ptr(self.S_T), ws, nb, _stream(self.device)),
+               "kda_prefill_state_pass")
+        return self.o, self.S_T
+
+
+def prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
+            output_final_state=True, workspace=None, out=None, final_state=None):
+    """Chunked KDA prefill.  Returns (o, S_T).
+
+    Layouts: q, k, alpha [T, H, D] with v [T, H, D] (one sequence, or a
+    packed varlen batch when ``cu_seqlens`` [N+1] int32 is given), or
+    [B, T, H, D] for a dense batch of B equal-length sequences; beta
+    [T, H] / [B, T, H].  q, k, v are bf16 or fp32; alpha, beta fp32.
+    initial_state [N, H, D, D] fp32 or None (zeros).  o is fp32 with v's
+    shape; S_T is [N, H, D, D] fp32 (None if output_final_state is False).
+    ``final_state`` may be ``initial_state`` for an in-place update.
+    """
+    return PrefillCall(q, k, v, alpha, beta, initial_state, cu_seqlens,
+                       output_final_state=output_final_state, workspace=workspace, out=out,
+                       final_state=final_state).run()
+
+
+def decode_step(q, k, v, alpha, beta, state, out=None):
+    """One decode step for N sequences: q, k, v, alpha [N, H, D]; beta [N, H];
+    state [N, H, D, D] fp32 updated in place.  Returns o [N, H, D] fp32."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_gpu(name, t)
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float32 or bfloat16")
+    _require_gpu("alpha", alpha, torch.float32)
+    _require_gpu("beta", beta, torch.float32)
+    _require_gpu("state", state, torch.float32)
+    if q.dim() != 3:
+        raise ValueError("decode inputs are [N, H, D]")
+    N, H, D = q.shape
+    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("alpha", alpha, q.shape),
+                         ("beta", beta, q.shape[:-1]), ("state", state, (N, H, D, D))):
+        if tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
+    o = out if out is not None else torch.empty((N, H, D), dtype=torch.float32, device=q.device)
+    _require_gpu("out", o, torch.float32)
+    shape = make_shape(N, 1, N, H, D, q.dtype)
+    st = lib().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(state), _ptr(o), _stream(q.device))
+    _check(st, "kda_decode_step")
+    return o

@@ -1,0 +1,177 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * The layer: each head keeps a d_k x d_v state S (rows = key channels) and
+ * every token updates it once with the gated delta rule
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *
+ * (dimsnsums.com "GLM-5.3-FLASH" attention page, section "How can a layer
+ * remember without rereading?": the update rule and the sentence that
+ * defines its symbols; the same section fixes a 128x128 state per head that
+ * each token updates once).  The output of token t is the read-out of the
+ * post-update state, o_t = S_t^T q_t, with no scale (a convention: the page
+ * prints only the update).  alpha_t holds one decay rate per key channel
+ * (Diag(alpha_t) multiplies S from the left), beta_t one scalar per token
+ * and head.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Tensor arguments are DEVICE pointers to contiguous, row-major arrays
+ *    on the current HIP device, aligned to 16 bytes (beta: 4 bytes).
+ *    Layouts are token-major:
+ *        q, k, alpha   [tokens][H][d_k]
+ *        v, o          [tokens][H][d_v]
+ *        beta          [tokens][H]
+ *        state         [N][H][d_k][d_v]        (fp32)
+ *    q, k, v are fp32 or bf16 (shape->qkv_dtype); alpha, beta, state and o
+ *    are always fp32.
+ *  - The caller owns every buffer, including the prefill workspace.  The
+ *    library allocates no device memory, keeps no mutable global state and
+ *    never synchronises: every call only enqueues kernels on `stream` (a
+ *    hipStream_t passed as void*; NULL = the default stream) and returns.
+ *    Calls on different streams may run concurrently.
+ *  - Errors: every call returns a kda_status_t and never throws, aborts or
+ *    prints.  Argument validation happens on the host before any HIP call,
+ *    so an invalid call enqueues nothing.  KDA_ERR_LAUNCH reports a failed
+ *    kernel launch (hipGetLastError); faults inside a kernel surface as HIP
+ *    errors at the caller's next synchronisation, as for any HIP kernel.
+ *  - Supported sizes: d_k == d_v in {16, 32, 64, 128}; H >= 1.
+ *  - Device-side preconditions (not checked, a check would need a sync):
+ *    0 <= alpha <= 1; beta, q, k, v finite; cu_seqlens[0] == 0,
+ *    non-decreasing, cu_seqlens[N] == total_tokens; outputs do not overlap
+ *    inputs except where aliasing is stated below.  Non-finite inputs give
+ *    non-finite outputs; they do not fault.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+#define KDA_CHUNK 64 /* prefill chunk length (tokens); not a semantic parameter */
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned, inconsistent shape */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not built: d_k != d_v, d not in {16,32,64,128} */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERR_LAUNCH = 4            /* a kernel launch failed (HIP error) */
+} kda_status_t;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype_t;
+
+/* Problem shape.  Dense batch: cu_seqlens == NULL, num_seqs sequences of
+ * seq_len tokens each, sequence n owning tokens n*seq_len .. (n+1)*seq_len-1,
+ * and total_tokens == num_seqs * seq_len.  Varlen batch: cu_seqlens != NULL,
+ * seq_len ignored, total_tokens == cu_seqlens[num_seqs]. */
+typedef struct kda_shape {
+    int32_t num_seqs;     /* N >= 0 */
+    int32_t seq_len;      /* tokens per sequence (dense batch only), >= 0 */
+    int64_t total_tokens; /* >= 0 */
+    int32_t num_heads;    /* H >= 1 */
+    int32_t d_k;          /* key channels per head */
+    int32_t d_v;          /* value channels per head (must equal d_k) */
+    int32_t qkv_dtype;    /* kda_dtype_t of q, k, v */
+} kda_shape_t;
+
+/* Version of this ABI (KDA_ABI_VERSION of the built library). */
+int kda_abi_version(void);
+
+/* Human-readable name of a status code; never NULL. */
+const char *kda_status_string(kda_status_t status);
+
+/* Bytes of device workspace kda_prefill needs for `shape` (written to
+ * *bytes).  The size depends on N, H and total_tokens only (an upper bound
+ * on the number of 64-token chunks, floor(total_tokens/64) + N, times
+ * 32 KiB per chunk and head, plus a small schedule table).  Returns
+ * KDA_ERR_INVALID_ARGUMENT / KDA_ERR_UNSUPPORTED for a shape kda_prefill
+ * would reject. */
+kda_status_t kda_prefill_workspace_size(const kda_shape_t *shape, size_t *bytes);
+
+/* Prefill (chunked): run the update over every token of every sequence and
+ * write o for every token and, if S_T != NULL, the final state of every
+ * sequence.
+ *   q, k        [total_tokens][H][d_k]      fp32 or bf16 (qkv_dtype)
+ *   v           [total_tokens][H][d_v]      same dtype
+ *   alpha       [total_tokens][H][d_k]      fp32, per key channel
+ *   beta        [total_tokens][H]           fp32
+ *   cu_seqlens  [N+1] int32 device array, or NULL for a dense batch
+ *   S0          [N][H][d_k][d_v] fp32 initial states, or NULL for zeros
+ *   o           [total_tokens][H][d_v] fp32 output
+ *   S_T         [N][H][d_k][d_v] fp32 final states, or NULL to skip; may be
+ *               the same pointer as S0 (in-place update)
+ *   workspace   device scratch of at least kda_prefill_workspace_size()
+ *               bytes, 256-byte aligned; its contents on entry do not
+ *               matter and are clobbered
+ * A zero-length sequence gets S_T[n] = S0[n] (zeros if S0 == NULL).
+ * Sequences and heads are independent. */
+kda_status_t kda_prefill(const kda_shape_t *shape,
+                         const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta,
+                         const int32_t *cu_seqlens,
+                         const float *S0,
+                         float *o, float *S_T,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* The two phases of kda_prefill, for callers that schedule them separately
+ * (e.g. phase 1 of the next batch on another stream while phase 2 of this
+ * one runs).  kda_prefill(...) is exactly phase 1 followed by phase 2 on the
+ * same stream with the same arguments.
+ *
+ * Phase 1 (fully parallel over chunks and heads): builds the per-sequence
+ * chunk table and, for every 64-token chunk and head, the two 64x64
+ * chunk-local matrices of the chunked form, into `workspace`.  Reads q, k,
+ * alpha, beta and cu_seqlens. */
+kda_status_t kda_prefill_chunk_local(const kda_shape_t *shape,
+                                     const void *q, const void *k,
+                                     const float *alpha, const float *beta,
+                                     const int32_t *cu_seqlens,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* Phase 2 (sequential over the chunks of each sequence, parallel over
+ * sequences, heads and value columns): carries each state across its
+ * sequence's chunks and writes o and S_T.  `workspace` must hold the result
+ * of kda_prefill_chunk_local for the same shape, q, k, alpha, beta and
+ * cu_seqlens, ordered before this call (same stream, or an event).
+ * Arguments as for kda_prefill. */
+kda_status_t kda_prefill_state_pass(const kda_shape_t *shape,
+                                    const void *q, const void *k, const void *v,
+                                    const float *alpha,
+                                    const int32_t *cu_seqlens,
+                                    const float *S0,
+                                    float *o, float *S_T,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* Decode: one new token for each of N sequences; every head state is read
+ * once, advanced one step and written back in place.
+ *   shape       num_seqs = N, seq_len must be 1, total_tokens must be N,
+ *               no cu_seqlens
+ *   q, k        [N][H][d_k]   fp32 or bf16 (qkv_dtype)
+ *   v           [N][H][d_v]
+ *   alpha       [N][H][d_k]   fp32
+ *   beta        [N][H]        fp32
+ *   S           [N][H][d_k][d_v] fp32, updated in place
+ *   o           [N][H][d_v]   fp32 output (must not overlap S) */
+kda_status_t kda_decode_step(const kda_shape_t *shape,
+                             const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta,
+                             float *S, float *o,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

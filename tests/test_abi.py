@@ -1,0 +1,146 @@
+"""C ABI of libkda.so, exercised without a GPU.
+
+The library must load on a machine without a GPU, export every function
+include/kda.h declares, and reject every invalid call with the documented
+status before it touches HIP (so these calls use fake, aligned device
+addresses: nothing is dereferenced).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from gated_delta_rule_76_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, LAUNCH = 0, 1, 2, 3, 4
+FAKE = 1 << 20          # a 256-byte aligned non-null address (never dereferenced)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return kda.lib()
+
+
+def shape(N=1, T=64, H=2, d=16, dtype=0, total=None):
+    return kda.KdaShape(N, T, N * T if total is None else total, H, d, d, dtype)
+
+
+def prefill(L, s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, cu=None, S0=None, o=FAKE, ST=FAKE,
+            ws=FAKE, ws_bytes=1 << 40, stream=None):
+    p = ctypes.byref(s) if s is not None else None
+    return L.kda_prefill(p, q, k, v, a, b, cu, S0, o, ST, ws, ws_bytes, stream)
+
+
+def decode(L, s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, o=FAKE):
+    p = ctypes.byref(s) if s is not None else None
+    return L.kda_decode_step(p, q, k, v, a, b, S, o, None)
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["kda_abi_version", "kda_decode_step", "kda_prefill",
+                                    "kda_prefill_chunk_local", "kda_prefill_state_pass",
+                                    "kda_prefill_workspace_size", "kda_status_string"]
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.kda_abi_version() == 1
+    names = [L.kda_status_string(i).decode() for i in range(5)]
+    assert names == ["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
+                     "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_LAUNCH"]
+    assert L.kda_status_string(99).decode() == "KDA_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("N,T,H,d", [(1, 64, 2, 16), (1, 4096, 32, 128), (8, 0, 32, 128), (3, 65, 4, 64)])
+def test_workspace_size_formula(N, T, H, d):
+    need = kda.prefill_workspace_size(N, N * T, H, d)
+    sched = ((4 * (N + 1) + 255) // 256) * 256
+    chunks = (N * T) // 64 + N
+    assert need == sched + chunks * H * 2 * 64 * 64 * 4
+
+
+def test_workspace_size_rejects(L):
+    out = ctypes.c_size_t(0)
+    assert L.kda_prefill_workspace_size(None, ctypes.byref(out)) == INVALID
+    assert L.kda_prefill_workspace_size(ctypes.byref(shape()), None) == INVALID
+    assert L.kda_prefill_workspace_size(ctypes.byref(shape(d=48)), ctypes.byref(out)) == UNSUPPORTED
+
+
+def test_prefill_validation(L):
+    need = kda.prefill_workspace_size(1, 64, 2, 16, torch.float32)
+    assert prefill(L, None) == INVALID
+    assert prefill(L, shape(N=-1)) == INVALID
+    assert prefill(L, shape(H=0)) == INVALID
+    assert prefill(L, shape(dtype=7)) == INVALID
+    assert prefill(L, shape(total=63)) == INVALID                 # dense: N*T != total
+    assert prefill(L, shape(d=48)) == UNSUPPORTED
+    s = kda.KdaShape(1, 64, 64, 2, 16, 32, 0)
+    assert prefill(L, s) == UNSUPPORTED                           # d_k != d_v
+    for field in ("q", "k", "v", "a", "b", "o"):
+        assert prefill(L, shape(), **{field: None}) == INVALID, field
+        assert prefill(L, shape(), **{field: FAKE + 2}) == INVALID, field   # misaligned
+    for field in ("q", "k", "v", "a", "o"):
+        assert prefill(L, shape(), **{field: FAKE + 4}) == INVALID, field   # needs 16 B
+    assert prefill(L, shape(), S0=FAKE + 8) == INVALID
+    assert prefill(L, shape(), ST=FAKE + 8) == INVALID
+    assert prefill(L, shape(), ws=None) == WS_SMALL
+    assert prefill(L, shape(), ws_bytes=need - 1) == WS_SMALL
+    assert prefill(L, shape(), ws=FAKE + 16, ws_bytes=need) == INVALID  # workspace not 256-aligned
+    assert prefill(L, shape(N=0, T=0)) == OK                      # nothing to do, nothing launched
+    assert prefill(L, kda.KdaShape(0, 0, 5, 2, 16, 16, 0), cu=FAKE) == INVALID   # tokens, no sequences
+
+
+def test_prefill_phase_validation(L):
+    need = kda.prefill_workspace_size(1, 64, 2, 16, torch.float32)
+    s = ctypes.byref(shape())
+    # phase 1 reads q, k, alpha, beta; it does not need v, o
+    assert L.kda_prefill_chunk_local(s, FAKE, FAKE, FAKE, None, None, FAKE, need, None) == INVALID
+    assert L.kda_prefill_chunk_local(s, None, FAKE, FAKE, FAKE, None, FAKE, need, None) == INVALID
+    assert L.kda_prefill_chunk_local(s, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == WS_SMALL
+    # phase 2 needs v and o but not beta
+    assert L.kda_prefill_state_pass(s, FAKE, FAKE, None, FAKE, None, None, FAKE, None, FAKE, need,
+                                    None) == INVALID
+    assert L.kda_prefill_state_pass(s, FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, need,
+                                    None) == INVALID
+    assert L.kda_prefill_state_pass(s, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None, need,
+                                    None) == WS_SMALL
+
+
+def test_decode_validation(L):
+    good = kda.KdaShape(4, 1, 4, 2, 128, 128, 1)
+    assert decode(L, None) == INVALID
+    assert decode(L, kda.KdaShape(4, 2, 8, 2, 128, 128, 1)) == INVALID       # seq_len must be 1
+    assert decode(L, kda.KdaShape(4, 1, 5, 2, 128, 128, 1)) == INVALID       # total != N
+    assert decode(L, kda.KdaShape(4, 1, 4, 0, 128, 128, 1)) == INVALID
+    assert decode(L, kda.KdaShape(4, 1, 4, 2, 96, 96, 1)) == UNSUPPORTED
+    assert decode(L, kda.KdaShape(4, 1, 4, 2, 128, 64, 1)) == UNSUPPORTED
+    for field in ("q", "k", "v", "a", "b", "S", "o"):
+        assert decode(L, good, **{field: None}) == INVALID, field
+        assert decode(L, good, **{field: FAKE + 2}) == INVALID, field
+    for field in ("q", "k", "v", "a", "S", "o"):
+        assert decode(L, good, **{field: FAKE + 4}) == INVALID, field
+    assert decode(L, kda.KdaShape(0, 1, 0, 2, 128, 128, 1)) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(4, 2, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.prefill(x, x, x, x, torch.zeros(4, 2))
+    with pytest.raises(ValueError, match="GPU"):
+        kda.decode_step(x, x, x, x, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))
