@@ -14,6 +14,63 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 
+// Eight consecutive q/k/v elements as loaded from memory (one 16-byte load
+// for bf16, two for fp32), kept packed in registers until converted.
+template <typename T>
+struct Raw8;
+
+template <>
+struct Raw8<__bf16> {
+  uint4 u;
+  __device__ __forceinline__ void load(const __bf16 *p) { u = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void to_f32(float (&x)[8]) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *reinterpret_cast<const float4 *>(p);
+    b = *reinterpret_cast<const float4 *>(p + 4);
+  }
+  __device__ __forceinline__ void to_f32(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
+// Four consecutive elements (8 bytes for bf16, 16 for fp32).
+template <typename T>
+struct Raw4;
+
+template <>
+struct Raw4<__bf16> {
+  uint2 u;
+  __device__ __forceinline__ void load(const __bf16 *p) { u = *reinterpret_cast<const uint2 *>(p); }
+  __device__ __forceinline__ void to_f32(float (&x)[4]) const {
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xffff0000u);
+  }
+};
+
+template <>
+struct Raw4<float> {
+  float4 a;
+  __device__ __forceinline__ void load(const float *p) { a = *reinterpret_cast<const float4 *>(p); }
+  __device__ __forceinline__ void to_f32(float (&x)[4]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // 16x16 output tiles on the matrix cores.
 //

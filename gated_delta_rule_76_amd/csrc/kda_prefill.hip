@@ -80,6 +80,16 @@ struct alignas(16) Plane<SplitBF16, ROWS, COLS> {
     *reinterpret_cast<bf16x4 *>(&hi[r * PITCH + c]) = h;
     *reinterpret_cast<bf16x4 *>(&lo[r * PITCH + c]) = l;
   }
+  __device__ __forceinline__ void store8(int r, int c, const float (&x)[8]) {
+    bf16x8 h, l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      h[i] = (__bf16)x[i];
+      l[i] = (__bf16)(x[i] - (float)h[i]);
+    }
+    *reinterpret_cast<bf16x8 *>(&hi[r * PITCH + c]) = h;
+    *reinterpret_cast<bf16x8 *>(&lo[r * PITCH + c]) = l;
+  }
   __device__ __forceinline__ SplitBF16::Frag load8(int r, int c) const {
     SplitBF16::Frag f;
     f.hi = *reinterpret_cast<const bf16x8 *>(&hi[r * PITCH + c]);
@@ -95,6 +105,16 @@ struct alignas(16) Plane<F32, ROWS, COLS> {
   __device__ __forceinline__ void store(int r, int c, float x) { f[r * PITCH + c] = x; }
   __device__ __forceinline__ void store4(int r, int c, const f32x4 &x) {
     *reinterpret_cast<f32x4 *>(&f[r * PITCH + c]) = x;
+  }
+  __device__ __forceinline__ void store8(int r, int c, const float (&x)[8]) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = x[i];
+      b[i] = x[4 + i];
+    }
+    *reinterpret_cast<f32x4 *>(&f[r * PITCH + c]) = a;
+    *reinterpret_cast<f32x4 *>(&f[r * PITCH + c + 4]) = b;
   }
   __device__ __forceinline__ F32::Frag load8(int r, int c) const {
     F32::Frag fr;
@@ -139,6 +159,16 @@ __device__ __forceinline__ ChunkTok chunk_tokens(int64_t start, int64_t len, int
   v = v < room ? v : room;
   ct.valid = (v > 0 && ct.t0 >= 0) ? (int)v : 0;
   return ct;
+}
+
+// Token read for chunk row r: rows past the valid ones re-read the last valid
+// row (their values are then replaced by the padding), and every index is
+// clamped into [0, total_tokens) so a load can never leave the tensors.
+__device__ __forceinline__ int64_t load_token(int64_t t0, int r, int valid, int64_t total_tokens) {
+  const int rr = r < valid ? r : (valid > 0 ? valid - 1 : 0);
+  int64_t t = t0 + rr;
+  t = t < total_tokens ? t : total_tokens - 1;
+  return t > 0 ? t : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -209,10 +239,10 @@ struct LocalCfg {
   static constexpr int MP = C + 1;             // 64x64 matrix pitch
 };
 
-// Tiles per wave: waves 0/1 take block-row 3 plus tile (0,0) of A / M,
-// waves 2/3 take block-rows 2 and 1 of A / M (5 tiles each).
-__constant__ int kTileR[2][5] = {{3, 3, 3, 3, 0}, {2, 2, 2, 1, 1}};
-__constant__ int kTileJ[2][5] = {{0, 1, 2, 3, 0}, {0, 1, 2, 0, 1}};
+// Tiles per wave (5 each): waves 0/1 take block-row 3 plus tile (0,0) of
+// A / M, waves 2/3 take block-rows 2 and 1 of A / M.
+__device__ __forceinline__ int tile_R(int tsel, int t) { return tsel == 0 ? (t < 4 ? 3 : 0) : (t < 3 ? 2 : 1); }
+__device__ __forceinline__ int tile_J(int tsel, int t) { return tsel == 0 ? (t < 4 ? t : 0) : (t < 3 ? t : t - 3); }
 
 template <int D, typename TIn, typename P>
 __global__ __launch_bounds__(NT) void chunk_local_kernel(
@@ -257,16 +287,55 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
 #pragma unroll
   for (int t = 0; t < 5; ++t) acc[t] = zero4();
 
+  // All of the chunk's q, k and alpha are loaded up front with unconditional
+  // vector loads (rows past the valid ones re-read a valid row and are
+  // replaced by the padding when written to LDS): per 32-channel slice a
+  // thread holds 8 channels of q and k of one row and 2 x 4 channels of
+  // alpha of two rows.
+  const int kr = tid >> 2, kc = 8 * (tid & 3);       // q/k: row, first channel in slice
+  Raw8<TIn> rk[L::NSL], rq[L::NSL];
+  float4 ra[L::NSL][2];
+  {
+    const int64_t tk = load_token(t0, kr, nvalid, total_tokens);
+#pragma unroll
+    for (int sl = 0; sl < L::NSL; ++sl) {
+      const int ch = sl * KS + kc < D - 8 ? sl * KS + kc : D - 8;
+      rk[sl].load(k + (tk * H + h) * D + ch);
+      rq[sl].load(q + (tk * H + h) * D + ch);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + NT * u, ar = e >> 3, ac = 4 * (e & 7);
+        const int cha = sl * KS + ac < D - 4 ? sl * KS + ac : D - 4;
+        ra[sl][u] = *reinterpret_cast<const float4 *>(
+            alpha + (load_token(t0, ar, nvalid, total_tokens) * H + h) * D + cha);
+      }
+    }
+  }
+
+#pragma unroll
   for (int sl = 0; sl < L::NSL; ++sl) {
-    const int c0 = sl * KS;
     __syncthreads();  // previous slice fully consumed
-    for (int e = tid; e < C * KS; e += NT) {
-      const int r = e / KS, cc = e % KS, ch = c0 + cc;
-      const bool ok = (r < nvalid) && (ch < D);
-      const int64_t off = ((t0 + r) * H + h) * D + ch;
-      s_k[r * SP + cc] = ok ? to_f32(k[off]) : 0.f;
-      s_q[r * SP + cc] = ok ? to_f32(q[off]) : 0.f;
-      s_bp[r * SP + cc] = ok ? alpha[off] : 1.f;
+    {
+      const bool okr = kr < nvalid;
+      float xk[8], xq[8];
+      rk[sl].to_f32(xk);
+      rq[sl].to_f32(xq);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = okr && (sl * KS + kc + j < D);
+        s_k[kr * SP + kc + j] = ok ? xk[j] : 0.f;
+        s_q[kr * SP + kc + j] = ok ? xq[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + NT * u, ar = e >> 3, ac = 4 * (e & 7);
+        const float av[4] = {ra[sl][u].x, ra[sl][u].y, ra[sl][u].z, ra[sl][u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = (ar < nvalid) && (sl * KS + ac + j < D);
+          s_bp[ar * SP + ac + j] = ok ? av[j] : 1.f;
+        }
+      }
     }
     __syncthreads();
     if (tid < 4 * KS) {
@@ -298,7 +367,7 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 5; ++t) {
-      const int R = kTileR[tsel][t], J = kTileJ[tsel][t];
+      const int R = tile_R(tsel, t), J = tile_J(tsel, t);
       const int r = 16 * R + m, jr = 16 * J + m;
       const float *X = isM ? s_q : s_k;
       float xa[8], xb[8];
@@ -325,7 +394,7 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     float *dst = isM ? s_M : s_A;
 #pragma unroll
     for (int t = 0; t < 5; ++t) {
-      const int R = kTileR[tsel][t], J = kTileJ[tsel][t];
+      const int R = tile_R(tsel, t), J = tile_J(tsel, t);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * R + 4 * g + i, j = 16 * J + m;
@@ -430,16 +499,64 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
 // W = T (V - E), and state row tiles w, w+4 (16 key channels each) for the
 // update S <- Diag(Gamma_C) S + Ktil^T W.  S is kept in fp32 accumulators;
 // a copy in operand form (S^T, split for the matrix cores) lives in LDS so
-// that every wave can use all key rows.  Per chunk, all 256 threads first
-// stage the decay factors and the operands Khat, Qhat, Ktil^T (one key
-// channel and 64/(256/D) tokens per thread, alpha products run along the
-// tokens).
+// that every wave can use all key rows.
+//
+// Per chunk, every thread stages 8 key channels of TPG consecutive tokens:
+// q, k, alpha arrive as 16-byte vector loads issued one chunk ahead (the
+// next chunk's loads are in flight while this chunk computes), the decay
+// factors are running products of alpha along the tokens (a two-level scan:
+// inside the thread's tokens, then across token groups through LDS), and
+// the operands Khat, Qhat (rows = tokens) and Ktil^T (rows = channels) are
+// written to LDS already split for the matrix cores.
 //
 // blockIdx -> work: consecutive workgroups are dealt round-robin to the 8
 // XCDs, so the D/16 workgroups of one (sequence, head) are mapped to block
 // indices congruent mod 8: they share an XCD and its L2, and the chunk
 // inputs and T/M they all read are fetched from HBM once.
 // ---------------------------------------------------------------------------
+template <int D>
+struct StateCfg {
+  static constexpr int G = D / 16;                            // value-column groups per head
+  static constexpr int DK = D < 32 ? 32 : D;                  // key width of operand planes
+  static constexpr int NKB = DK / 32;                         // 32-wide k-blocks over key channels
+  static constexpr int NTILE = D / 16;                        // 16-row tiles of the state
+  static constexpr int TPW = (NTILE + 3) / 4;                 // state tiles per wave (max)
+  static constexpr int CGR = D / 8;                           // 8-channel groups per token row
+  static constexpr int NTG = (NT / CGR) < C ? NT / CGR : C;   // token groups
+  static constexpr int TPG = C / NTG;                         // tokens per staging thread
+  static constexpr int ACTIVE = CGR * NTG;                    // staging threads
+  static_assert(ACTIVE <= NT && C % NTG == 0, "staging layout");
+};
+
+template <int D, typename TIn>
+struct StateRaw {
+  static constexpr int TPG = StateCfg<D>::TPG;
+  Raw8<TIn> k[TPG], q[TPG];
+  float4 a0[TPG], a1[TPG];
+  Raw4<TIn> v;
+};
+
+template <int D, typename TIn>
+__device__ __forceinline__ void load_state_raw(StateRaw<D, TIn> &R, const TIn *__restrict__ q,
+                                               const TIn *__restrict__ k, const TIn *__restrict__ v,
+                                               const float *__restrict__ alpha, int64_t t0, int valid,
+                                               int64_t total, int h, int H, int col0, int tid) {
+  using Cf = StateCfg<D>;
+  if (tid < Cf::ACTIVE) {
+    const int cg8 = tid % Cf::CGR, tg = tid / Cf::CGR;
+#pragma unroll
+    for (int i = 0; i < Cf::TPG; ++i) {
+      const int64_t off = (load_token(t0, tg * Cf::TPG + i, valid, total) * H + h) * D + 8 * cg8;
+      R.k[i].load(k + off);
+      R.q[i].load(q + off);
+      R.a0[i] = *reinterpret_cast<const float4 *>(alpha + off);
+      R.a1[i] = *reinterpret_cast<const float4 *>(alpha + off + 4);
+    }
+  }
+  const int64_t voff = (load_token(t0, tid >> 2, valid, total) * H + h) * D + col0 + 4 * (tid & 3);
+  R.v.load(v + voff);
+}
+
 template <int D, typename TIn, typename P>
 __global__ __launch_bounds__(NT) void chunk_state_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
@@ -447,14 +564,9 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
     int64_t total_tokens, int64_t max_chunks, const int32_t *__restrict__ base,
     const float *__restrict__ mats, const float *__restrict__ S0, float *__restrict__ o,
     float *__restrict__ S_T) {
-  constexpr int G = D / 16;              // value-column groups per head
-  constexpr int DK = D < 32 ? 32 : D;    // key width of the operand planes (zero padded)
-  constexpr int NKB = DK / 32;           // 32-wide k-blocks over key channels
-  constexpr int NTILE = D / 16;          // 16-row tiles of the state
-  constexpr int TPW = (NTILE + 3) / 4;   // state tiles per wave (max)
-  constexpr int NTG = NT / D;            // token groups in the staging pass
-  constexpr int TPG = C / NTG;           // tokens per staging thread
-  static_assert(NT % D == 0 && C % NTG == 0, "staging layout");
+  using Cf = StateCfg<D>;
+  constexpr int G = Cf::G, DK = Cf::DK, NKB = Cf::NKB, NTILE = Cf::NTILE, TPW = Cf::TPW;
+  constexpr int CGR = Cf::CGR, NTG = Cf::NTG, TPG = Cf::TPG;
 
   __shared__ Plane<P, C, DK> Khat;
   __shared__ Plane<P, C, DK> Qhat;
@@ -464,7 +576,8 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
   __shared__ Plane<P, 16, C> Wop;
   __shared__ float s_v[C * 17];
   __shared__ float s_gam[D];
-  __shared__ float s_tot[NTG * D];
+  __shared__ __attribute__((aligned(16))) float s_pre[NTG * D];  // group totals, then exclusive prefix
+  __shared__ __attribute__((aligned(16))) float s_suf[NTG * D];  // exclusive suffix over groups
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
@@ -506,64 +619,132 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
 
   int64_t sstart, slen;
   seq_range(cu, seq_len, n, sstart, slen);
-  int64_t cbeg = base[n], cend = base[n + 1];
+  const int64_t cbeg = base[n];
+  int64_t cend = base[n + 1];
   if (cend > max_chunks) cend = max_chunks;
+  if (total_tokens <= 0) cend = cbeg;
 
-  const int ch = tid % D, grp = tid / D;
+  const int cg8 = tid % CGR, tg = tid / CGR;
+  const int rbase = 16 * wave;
+  const int nkb = (wave >> 1) + 1;  // T and M are lower triangular
+
+  // Loads run one chunk ahead and land in the registers they are consumed
+  // from: the raw inputs of chunk c+1 are issued right after chunk c is
+  // staged, its T/M rows right after chunk c's last use of T/M.
+  StateRaw<D, TIn> cur;
+  float4 tq[4], mq[4];
+  auto load_tm = [&](int64_t cc) {
+    const float *src = mats + ((size_t)cc * H + h) * (size_t)(2 * C * C) + (rbase + m) * C + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {  // both k-blocks; above the diagonal T and M are 0
+      tq[2 * kb] = *reinterpret_cast<const float4 *>(src + kb * 32);
+      tq[2 * kb + 1] = *reinterpret_cast<const float4 *>(src + kb * 32 + 4);
+      mq[2 * kb] = *reinterpret_cast<const float4 *>(src + C * C + kb * 32);
+      mq[2 * kb + 1] = *reinterpret_cast<const float4 *>(src + C * C + kb * 32 + 4);
+    }
+  };
+  if (cbeg < cend) {
+    const ChunkTok ct = chunk_tokens(sstart, slen, 0, total_tokens);
+    load_state_raw<D, TIn>(cur, q, k, v, alpha, ct.t0, ct.valid, total_tokens, h, H, col0, tid);
+    load_tm(cbeg);
+  }
+
   for (int64_t c = cbeg; c < cend; ++c) {
     const ChunkTok ct = chunk_tokens(sstart, slen, c - cbeg, total_tokens);
     const int64_t t0 = ct.t0;
     const int nvalid = ct.valid;
+    const bool more = c + 1 < cend;
+    if (c != cbeg) load_tm(c);
     __syncthreads();  // previous chunk's operands fully consumed
 
-    // ---- stage decay factors and operands --------------------------------
-    float av[TPG];
-    float prod = 1.f;
+    // ---- stage: decay factors and operands --------------------------------
+    float av[TPG][8], kv[TPG][8], qv[TPG][8];
+    if (tid < Cf::ACTIVE) {
+      float tot[8];
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      const int r = grp * TPG + i;
-      av[i] = r < nvalid ? alpha[((t0 + r) * H + h) * D + ch] : 1.f;
-      prod *= av[i];
-    }
-    s_tot[grp * D + ch] = prod;
-    for (int e = tid; e < C * 16; e += NT) {
-      const int r = e >> 4, cc = e & 15;
-      s_v[r * 17 + cc] = r < nvalid ? to_f32(v[((t0 + r) * H + h) * D + col0 + cc]) : 0.f;
-    }
-    __syncthreads();
-    float pre = 1.f, suf = 1.f;
-#pragma unroll
-    for (int gg = 0; gg < NTG; ++gg) {
-      const float tv = s_tot[gg * D + ch];
-      if (gg < grp) pre *= tv;
-      if (gg > grp) suf *= tv;
-    }
-    if (grp == NTG - 1) s_gam[ch] = pre * prod;  // Gamma_C
-    {
-      float kv[TPG];
-      float ep = pre;
+      for (int j = 0; j < 8; ++j) tot[j] = 1.f;
 #pragma unroll
       for (int i = 0; i < TPG; ++i) {
-        const int r = grp * TPG + i;
-        const int64_t off = ((t0 + r) * H + h) * D + ch;
-        const float kk = r < nvalid ? to_f32(k[off]) : 0.f;
-        const float qq = r < nvalid ? to_f32(q[off]) : 0.f;
-        kv[i] = kk;
-        ep *= av[i];
-        Khat.store(r, ch, ep * kk);
-        Qhat.store(r, ch, ep * qq);
+        const bool ok = tg * TPG + i < nvalid;
+        cur.k[i].to_f32(kv[i]);
+        cur.q[i].to_f32(qv[i]);
+        const float a[8] = {cur.a0[i].x, cur.a0[i].y, cur.a0[i].z, cur.a0[i].w,
+                            cur.a1[i].x, cur.a1[i].y, cur.a1[i].z, cur.a1[i].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          av[i][j] = ok ? a[j] : 1.f;
+          kv[i][j] = ok ? kv[i][j] : 0.f;
+          qv[i][j] = ok ? qv[i][j] : 0.f;
+          tot[j] *= av[i][j];
+        }
       }
-      float es = suf;
+      *reinterpret_cast<float4 *>(&s_pre[tg * D + 8 * cg8]) = make_float4(tot[0], tot[1], tot[2], tot[3]);
+      *reinterpret_cast<float4 *>(&s_pre[tg * D + 8 * cg8 + 4]) = make_float4(tot[4], tot[5], tot[6], tot[7]);
+    }
+    {
+      float vv[4];
+      cur.v.to_f32(vv);
+      const int r = tid >> 2;
+      const bool ok = r < nvalid;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_v[r * 17 + 4 * (tid & 3) + j] = ok ? vv[j] : 0.f;
+    }
+    __syncthreads();
+    if (tid < D) {  // exclusive suffix, then exclusive prefix (in place), over token groups
+      float sfx = 1.f;
+      for (int gg = NTG - 1; gg >= 0; --gg) {
+        s_suf[gg * D + tid] = sfx;
+        sfx *= s_pre[gg * D + tid];
+      }
+      float pfx = 1.f;
+      for (int gg = 0; gg < NTG; ++gg) {
+        const float tv = s_pre[gg * D + tid];
+        s_pre[gg * D + tid] = pfx;
+        pfx *= tv;
+      }
+      s_gam[tid] = pfx;  // Gamma_C
+    }
+    __syncthreads();
+    if (tid < Cf::ACTIVE) {
+      float ep[8], es[8];
+      {
+        const float4 p0 = *reinterpret_cast<const float4 *>(&s_pre[tg * D + 8 * cg8]);
+        const float4 p1 = *reinterpret_cast<const float4 *>(&s_pre[tg * D + 8 * cg8 + 4]);
+        const float4 s0 = *reinterpret_cast<const float4 *>(&s_suf[tg * D + 8 * cg8]);
+        const float4 s1 = *reinterpret_cast<const float4 *>(&s_suf[tg * D + 8 * cg8 + 4]);
+        ep[0] = p0.x; ep[1] = p0.y; ep[2] = p0.z; ep[3] = p0.w;
+        ep[4] = p1.x; ep[5] = p1.y; ep[6] = p1.z; ep[7] = p1.w;
+        es[0] = s0.x; es[1] = s0.y; es[2] = s0.z; es[3] = s0.w;
+        es[4] = s1.x; es[5] = s1.y; es[6] = s1.z; es[7] = s1.w;
+      }
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        float xk[8], xq[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          ep[j] *= av[i][j];  // Gamma_r (inclusive)
+          xk[j] = ep[j] * kv[i][j];
+          xq[j] = ep[j] * qv[i][j];
+        }
+        Khat.store8(tg * TPG + i, 8 * cg8, xk);
+        Qhat.store8(tg * TPG + i, 8 * cg8, xq);
+      }
 #pragma unroll
       for (int i = TPG - 1; i >= 0; --i) {
-        KtilT.store(ch, grp * TPG + i, es * kv[i]);
-        es *= av[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          KtilT.store(8 * cg8 + j, tg * TPG + i, es[j] * kv[i][j]);  // Gamma_C / Gamma_r
+          es[j] *= av[i][j];
+        }
       }
+    }
+    {  // unconditional (the last chunk re-reads itself) so wait counts stay exact
+      const ChunkTok cn = chunk_tokens(sstart, slen, (more ? c + 1 : c) - cbeg, total_tokens);
+      load_state_raw<D, TIn>(cur, q, k, v, alpha, cn.t0, cn.valid, total_tokens, h, H, col0, tid);
     }
     __syncthreads();
 
     // ---- E = Khat S, O = Qhat S (chunk rows of this wave) ------------------
-    const int rbase = 16 * wave;
     f32x4 E = zero4(), O = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -580,31 +761,26 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
     __syncthreads();
 
     // ---- W = T (V - E) ------------------------------------------------------
-    const float *Tm = mats + ((size_t)c * H + h) * (size_t)(2 * C * C);
-    const float *Mm = Tm + C * C;
     f32x4 W = zero4();
-    const int nkb = (wave >> 1) + 1;  // T and M are lower triangular
-    for (int kb = 0; kb < nkb; ++kb) {
-      float x[8];
-      const float *src = Tm + (rbase + m) * C + kb * 32 + 8 * g;
-      const float4 a0 = *reinterpret_cast<const float4 *>(src);
-      const float4 a1 = *reinterpret_cast<const float4 *>(src + 4);
-      x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
-      x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
-      P::mma(W, P::make(x), Vme.load8(m, kb * 32 + 8 * g));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb < nkb) {
+        const float x[8] = {tq[2 * kb].x, tq[2 * kb].y, tq[2 * kb].z, tq[2 * kb].w,
+                            tq[2 * kb + 1].x, tq[2 * kb + 1].y, tq[2 * kb + 1].z, tq[2 * kb + 1].w};
+        P::mma(W, P::make(x), Vme.load8(m, kb * 32 + 8 * g));
+      }
     }
     Wop.store4(m, rbase + 4 * g, W);
     __syncthreads();
 
     // ---- O += M W; store o ----------------------------------------------------
-    for (int kb = 0; kb < nkb; ++kb) {
-      float x[8];
-      const float *src = Mm + (rbase + m) * C + kb * 32 + 8 * g;
-      const float4 a0 = *reinterpret_cast<const float4 *>(src);
-      const float4 a1 = *reinterpret_cast<const float4 *>(src + 4);
-      x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
-      x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
-      P::mma(O, P::make(x), Wop.load8(m, kb * 32 + 8 * g));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb < nkb) {
+        const float x[8] = {mq[2 * kb].x, mq[2 * kb].y, mq[2 * kb].z, mq[2 * kb].w,
+                            mq[2 * kb + 1].x, mq[2 * kb + 1].y, mq[2 * kb + 1].z, mq[2 * kb + 1].w};
+        P::mma(O, P::make(x), Wop.load8(m, kb * 32 + 8 * g));
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -169,8 +169,8 @@ def test_prefill_4k_workload():
 def test_prefill_varlen_8seq_workload():
     """8 sequences, lengths uniform in [1024, 16384], H=32, d=128, bf16,
     S0 ~ 0.02 N(0,1).  For a seeded sample of 4 heads: the first 1024 tokens
-    of every sequence from its S0, and its last 1024 tokens (o and S_T) from
-    zero, against the oracle."""
+    of every sequence from its S0, and (o of the last 512 tokens, S_T) from a
+    run of the last 1024 tokens from zero, against the oracle."""
     dev = device()
     spec = inputs.WORKLOADS["varlen_8seq"]
     lens = inputs.workload_lengths(spec, seed=0)
@@ -187,7 +187,10 @@ def test_prefill_varlen_8seq_workload():
         assert rel_l2(np64(o[s:s + W, heads]), ro) < 2e-3, n
         win = {key: d[key][e - W:e] for key in ("q", "k", "v", "alpha", "beta")}
         ro, rST = _oracle(win, heads=heads)
-        _check(o[e - W:e, heads], ST[n:n + 1, heads], ro, rST, 2e-3, f"varlen seq {n} tail")
+        # The window's first tokens still see the dropped history; from its
+        # second half on, that history weighs < 1e-300.
+        _check(o[e - W // 2:e, heads], ST[n:n + 1, heads], ro[W // 2:], rST, 2e-3,
+               f"varlen seq {n} tail")
 
 
 def test_two_phase_calls_equal_prefill():
