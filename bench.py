@@ -47,6 +47,9 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-batch", type=int, default=256)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 256 MiB device copy (a known-size kernel for "
+                        "scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -155,6 +158,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
     pf = bench_prefill(args.workload, args.steps, args.warmup, dev)

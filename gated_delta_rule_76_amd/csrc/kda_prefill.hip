@@ -628,12 +628,13 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
   const int rbase = 16 * wave;
   const int nkb = (wave >> 1) + 1;  // T and M are lower triangular
 
-  // Loads run one chunk ahead and land in the registers they are consumed
-  // from: the raw inputs of chunk c+1 are issued right after chunk c is
-  // staged, its T/M rows right after chunk c's last use of T/M.
-  StateRaw<D, TIn> cur;
-  float4 tq[4], mq[4];
-  auto load_tm = [&](int64_t cc) {
+  // Two register sets for the per-chunk loads (raw inputs and this wave's
+  // T/M rows), used alternately: while chunk c is processed from one set,
+  // chunk c+1 is loading into the other (the loop is unrolled by two so that
+  // no register copy sits between a load and its use).
+  StateRaw<D, TIn> bufA, bufB;
+  float4 tA[4], mA[4], tB[4], mB[4];
+  auto load_tm = [&](int64_t cc, float4 (&tq)[4], float4 (&mq)[4]) {
     const float *src = mats + ((size_t)cc * H + h) * (size_t)(2 * C * C) + (rbase + m) * C + 8 * g;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {  // both k-blocks; above the diagonal T and M are 0
@@ -643,18 +644,17 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
       mq[2 * kb + 1] = *reinterpret_cast<const float4 *>(src + C * C + kb * 32 + 4);
     }
   };
-  if (cbeg < cend) {
-    const ChunkTok ct = chunk_tokens(sstart, slen, 0, total_tokens);
-    load_state_raw<D, TIn>(cur, q, k, v, alpha, ct.t0, ct.valid, total_tokens, h, H, col0, tid);
-    load_tm(cbeg);
-  }
+  auto prefetch = [&](int64_t cc, StateRaw<D, TIn> &R, float4 (&tq)[4], float4 (&mq)[4]) {
+    const ChunkTok cn = chunk_tokens(sstart, slen, cc - cbeg, total_tokens);
+    load_state_raw<D, TIn>(R, q, k, v, alpha, cn.t0, cn.valid, total_tokens, h, H, col0, tid);
+    load_tm(cc, tq, mq);
+  };
 
-  for (int64_t c = cbeg; c < cend; ++c) {
+  auto process = [&](int64_t c, const StateRaw<D, TIn> &use, const float4 (&tu)[4], const float4 (&mu)[4],
+                     int64_t cn, StateRaw<D, TIn> &nb, float4 (&tn)[4], float4 (&mn)[4]) {
     const ChunkTok ct = chunk_tokens(sstart, slen, c - cbeg, total_tokens);
     const int64_t t0 = ct.t0;
     const int nvalid = ct.valid;
-    const bool more = c + 1 < cend;
-    if (c != cbeg) load_tm(c);
     __syncthreads();  // previous chunk's operands fully consumed
 
     // ---- stage: decay factors and operands --------------------------------
@@ -666,10 +666,10 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
 #pragma unroll
       for (int i = 0; i < TPG; ++i) {
         const bool ok = tg * TPG + i < nvalid;
-        cur.k[i].to_f32(kv[i]);
-        cur.q[i].to_f32(qv[i]);
-        const float a[8] = {cur.a0[i].x, cur.a0[i].y, cur.a0[i].z, cur.a0[i].w,
-                            cur.a1[i].x, cur.a1[i].y, cur.a1[i].z, cur.a1[i].w};
+        use.k[i].to_f32(kv[i]);
+        use.q[i].to_f32(qv[i]);
+        const float a[8] = {use.a0[i].x, use.a0[i].y, use.a0[i].z, use.a0[i].w,
+                            use.a1[i].x, use.a1[i].y, use.a1[i].z, use.a1[i].w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           av[i][j] = ok ? a[j] : 1.f;
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
     }
     {
       float vv[4];
-      cur.v.to_f32(vv);
+      use.v.to_f32(vv);
       const int r = tid >> 2;
       const bool ok = r < nvalid;
 #pragma unroll
@@ -738,10 +738,7 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
         }
       }
     }
-    {  // unconditional (the last chunk re-reads itself) so wait counts stay exact
-      const ChunkTok cn = chunk_tokens(sstart, slen, (more ? c + 1 : c) - cbeg, total_tokens);
-      load_state_raw<D, TIn>(cur, q, k, v, alpha, cn.t0, cn.valid, total_tokens, h, H, col0, tid);
-    }
+    prefetch(cn, nb, tn, mn);  // next chunk, into the other register set
     __syncthreads();
 
     // ---- E = Khat S, O = Qhat S (chunk rows of this wave) ------------------
@@ -765,8 +762,8 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (kb < nkb) {
-        const float x[8] = {tq[2 * kb].x, tq[2 * kb].y, tq[2 * kb].z, tq[2 * kb].w,
-                            tq[2 * kb + 1].x, tq[2 * kb + 1].y, tq[2 * kb + 1].z, tq[2 * kb + 1].w};
+        const float x[8] = {tu[2 * kb].x, tu[2 * kb].y, tu[2 * kb].z, tu[2 * kb].w,
+                            tu[2 * kb + 1].x, tu[2 * kb + 1].y, tu[2 * kb + 1].z, tu[2 * kb + 1].w};
         P::mma(W, P::make(x), Vme.load8(m, kb * 32 + 8 * g));
       }
     }
@@ -777,8 +774,8 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (kb < nkb) {
-        const float x[8] = {mq[2 * kb].x, mq[2 * kb].y, mq[2 * kb].z, mq[2 * kb].w,
-                            mq[2 * kb + 1].x, mq[2 * kb + 1].y, mq[2 * kb + 1].z, mq[2 * kb + 1].w};
+        const float x[8] = {mu[2 * kb].x, mu[2 * kb].y, mu[2 * kb].z, mu[2 * kb].w,
+                            mu[2 * kb + 1].x, mu[2 * kb + 1].y, mu[2 * kb + 1].z, mu[2 * kb + 1].w};
         P::mma(O, P::make(x), Wop.load8(m, kb * 32 + 8 * g));
       }
     }
@@ -803,6 +800,15 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
         Sop.store4(m, 16 * t + 4 * g, acc);
       }
     }
+  };
+
+  if (cbeg < cend) prefetch(cbeg, bufA, tA, mA);
+  for (int64_t c = cbeg; c < cend; c += 2) {
+    // The prefetch is unconditional (the last chunk re-reads itself) so
+    // that every wait count stays exact.
+    process(c, bufA, tA, mA, c + 1 < cend ? c + 1 : c, bufB, tB, mB);
+    if (c + 1 >= cend) break;
+    process(c + 1, bufB, tB, mB, c + 2 < cend ? c + 2 : c + 1, bufA, tA, mA);
   }
 
   if (S_T != nullptr) {
