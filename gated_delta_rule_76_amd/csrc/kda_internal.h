@@ -13,12 +13,24 @@ namespace kda {
 
 constexpr int kChunk = KDA_CHUNK;  // tokens per prefill chunk
 
-// Per chunk and head the prefill keeps two 64x64 fp32 matrices in the
-// workspace (the UT-transformed erase matrix and the decayed q.k^T block).
-constexpr size_t kChunkMatBytes = size_t(2) * kChunk * kChunk * sizeof(float);
+// Per chunk and head the prefill keeps one record of matrix-core operand
+// fragments in the workspace (written by the chunk-local phase, streamed by
+// the state pass): -T Khat and Qhat (64 x d, as 4 x d/32 fragments each),
+// Ktil^T (d x 64, d/16 x 2 fragments), T and M (64 x 64, 4 x 2 fragments
+// each) and Gamma_C (d floats).  A fragment is 2 KiB: one 16x32 operand block
+// as 64 lanes x 8 values, stored either as bf16 hi/lo planes or as fp32.
+constexpr size_t kFragBytes = 2048;
 constexpr size_t kWorkspaceAlign = 256;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int frag_kblocks(int d) { return (d < 32 ? 32 : d) / 32; }
+inline size_t record_frags(int d) {
+  return (size_t)(4 * frag_kblocks(d) * 2 + (d / 16) * 2 + 16);
+}
+inline size_t record_bytes(int d) {
+  return align_up(record_frags(d) * kFragBytes + sizeof(float) * (size_t)d, kWorkspaceAlign);
+}
 
 // Upper bound on the number of 64-token chunks of a batch: every sequence
 // contributes at most one partial chunk.
@@ -27,12 +39,12 @@ inline int64_t max_chunks(const kda_shape_t &s) {
 }
 
 // Workspace layout: [chunk base table: (N+1) int32, padded to 256 B]
-//                   [chunk matrices: max_chunks * H * kChunkMatBytes]
+//                   [records: max_chunks * H * record_bytes(d)]
 inline size_t schedule_bytes(const kda_shape_t &s) {
   return align_up(sizeof(int32_t) * (size_t)(s.num_seqs + 1), kWorkspaceAlign);
 }
 inline size_t prefill_workspace_bytes(const kda_shape_t &s) {
-  return schedule_bytes(s) + (size_t)max_chunks(s) * (size_t)s.num_heads * kChunkMatBytes;
+  return schedule_bytes(s) + (size_t)max_chunks(s) * (size_t)s.num_heads * record_bytes(s.d_k);
 }
 
 hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, const void *v,

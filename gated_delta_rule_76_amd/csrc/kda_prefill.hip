@@ -90,6 +90,17 @@ struct alignas(16) Plane<SplitBF16, ROWS, COLS> {
     *reinterpret_cast<bf16x8 *>(&hi[r * PITCH + c]) = h;
     *reinterpret_cast<bf16x8 *>(&lo[r * PITCH + c]) = l;
   }
+  template <int N>
+  __device__ __forceinline__ void store_run(int r, int c, const float (&x)[N]) {
+    if constexpr (N == 4) {
+      f32x4 v;
+      v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+      store4(r, c, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) store(r, c + i, x[i]);
+    }
+  }
   __device__ __forceinline__ SplitBF16::Frag load8(int r, int c) const {
     SplitBF16::Frag f;
     f.hi = *reinterpret_cast<const bf16x8 *>(&hi[r * PITCH + c]);
@@ -115,6 +126,11 @@ struct alignas(16) Plane<F32, ROWS, COLS> {
     }
     *reinterpret_cast<f32x4 *>(&f[r * PITCH + c]) = a;
     *reinterpret_cast<f32x4 *>(&f[r * PITCH + c + 4]) = b;
+  }
+  template <int N>
+  __device__ __forceinline__ void store_run(int r, int c, const float (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) store(r, c + i, x[i]);
   }
   __device__ __forceinline__ F32::Frag load8(int r, int c) const {
     F32::Frag fr;
@@ -216,27 +232,130 @@ __device__ __forceinline__ int find_seq(const int32_t *base, int N, int64_t c) {
   return lo;
 }
 
+
 // ---------------------------------------------------------------------------
-// chunk_local_kernel: A, M and T of one chunk and head.
+// Chunk records: per (chunk, head), operand fragments in the order the state
+// pass consumes them.  A fragment is one 16-row x 32-column operand block of
+// the matrix-core product (lane 16g+m holds row m, columns 8g..8g+7), 2 KiB:
+// for SplitBF16 the bf16 hi plane (lane l at byte 16 l) then the lo plane
+// (at 1024 + 16 l); for F32 eight floats per lane (at byte 32 l).
+// ---------------------------------------------------------------------------
+struct FragRaw {
+  uint4 a, b;
+};
+
+template <typename P>
+struct FragIO;
+
+template <>
+struct FragIO<SplitBF16> {
+  __device__ __forceinline__ static void store(char *blk, int lane, const float (&x)[8]) {
+    bf16x8 h, l;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h[j] = (__bf16)x[j];
+      l[j] = (__bf16)(x[j] - (float)h[j]);
+    }
+    *reinterpret_cast<bf16x8 *>(blk + 16 * lane) = h;
+    *reinterpret_cast<bf16x8 *>(blk + 1024 + 16 * lane) = l;
+  }
+  __device__ __forceinline__ static void store_frag(char *blk, int lane, const SplitBF16::Frag &f) {
+    *reinterpret_cast<bf16x8 *>(blk + 16 * lane) = f.hi;
+    *reinterpret_cast<bf16x8 *>(blk + 1024 + 16 * lane) = f.lo;
+  }
+  __device__ __forceinline__ static void load(FragRaw &r, const char *blk, int lane) {
+    r.a = *reinterpret_cast<const uint4 *>(blk + 16 * lane);
+    r.b = *reinterpret_cast<const uint4 *>(blk + 1024 + 16 * lane);
+  }
+  __device__ __forceinline__ static SplitBF16::Frag frag(const FragRaw &r) {
+    SplitBF16::Frag f;
+    f.hi = __builtin_bit_cast(bf16x8, r.a);
+    f.lo = __builtin_bit_cast(bf16x8, r.b);
+    return f;
+  }
+};
+
+template <>
+struct FragIO<F32> {
+  __device__ __forceinline__ static void store(char *blk, int lane, const float (&x)[8]) {
+    *reinterpret_cast<float4 *>(blk + 32 * lane) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4 *>(blk + 32 * lane + 16) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+  __device__ __forceinline__ static void store_frag(char *blk, int lane, const F32::Frag &f) {
+    *reinterpret_cast<float4 *>(blk + 32 * lane) = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+    *reinterpret_cast<float4 *>(blk + 32 * lane + 16) = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+  }
+  __device__ __forceinline__ static void load(FragRaw &r, const char *blk, int lane) {
+    r.a = *reinterpret_cast<const uint4 *>(blk + 32 * lane);
+    r.b = *reinterpret_cast<const uint4 *>(blk + 32 * lane + 16);
+  }
+  __device__ __forceinline__ static F32::Frag frag(const FragRaw &r) {
+    F32::Frag f;
+    const float4 a = __builtin_bit_cast(float4, r.a), b = __builtin_bit_cast(float4, r.b);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+  }
+};
+
+// hi*b + lo*b for an operand b that is exact in bf16 (v in bf16): the lo part
+// of b is zero, so the hi*lo term is skipped.
+__device__ __forceinline__ void mma_exact_b(f32x4 &acc, const SplitBF16::Frag &a, const SplitBF16::Frag &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_exact_b(f32x4 &acc, const F32::Frag &a, const F32::Frag &b) {
+  F32::mma(acc, a, b);
+}
+
+// Fragment indices inside one record.
+template <int D>
+struct Rec {
+  static constexpr int NKB = (D < 32 ? 32 : D) / 32;  // k-blocks over key channels
+  static constexpr int NTILE = D / 16;                 // 16-row tiles of key channels
+  static constexpr int WNEG = 0;                       // -T Khat     [row tile w][kb]
+  static constexpr int QHAT = 4 * NKB;                 // Qhat        [w][kb]
+  static constexpr int KTIL = 8 * NKB;                 // Ktil^T      [channel tile t][kb of tokens]
+  static constexpr int TMAT = 8 * NKB + 2 * NTILE;     // T           [w][kb]
+  static constexpr int MMAT = TMAT + 8;                // M           [w][kb]
+  static constexpr int NFRAG = MMAT + 8;
+  static constexpr size_t GAM = (size_t)NFRAG * kFragBytes;  // Gamma_C (D floats)
+  static constexpr size_t BYTES = (GAM + sizeof(float) * D + kWorkspaceAlign - 1) / kWorkspaceAlign *
+                                  kWorkspaceAlign;
+};
+
+// ---------------------------------------------------------------------------
+// chunk_local_kernel: every operand of one chunk and head, computed once.
 //
-// The decayed Gram blocks are computed on 16x16 tiles (R, J), J <= R, of
-// 16-token blocks.  Per key channel, with bp[r] = product of alpha from the
-// start of r's block to r (inclusive), bs[j] = product of alpha after j to
-// the end of j's block, bt[b] = decay of the whole block b:
-//     Gamma_r / Gamma_j = bp[r] * bs[j] * prod_{J<b<R} bt[b]     (J < R)
-//                       = bp[r] / bp[j]                          (J = R, j <= r)
-// so each tile is a plain product (x_r * bp_r) . (k_j * left_j) over the key
-// channels, done in 32-channel slices on the matrix cores.  In the diagonal
-// case 1/bp[j] <= 2^100 is guaranteed by the block test; a block that fails
-// it (a channel decaying below 2^-100 within 16 tokens, e.g. alpha = 0) has
-// its diagonal tiles recomputed from running products of alpha.
+// Wave w holds 16-token block w in registers (lane: TPG consecutive tokens,
+// 8 consecutive key channels).  Decay factors are running products of alpha:
+// inside a lane, across the block's lanes (shuffles) and across blocks (one
+// LDS exchange of the four block totals).
+//
+// Gram tiles (R, J), J <= R, of A and M over key channels, per channel:
+//   Gamma_r / Gamma_j = bp_r bs_j prod_{J<b<R} bt_b      (J < R)
+//                     = bp_r / bp_j                      (J = R, j <= r)
+// with bp the product from the block start to r, bs the product after j to
+// the block end, bt block totals; the in-between block totals are folded
+// into the B operand (three extra row blocks).  1/bp is used only when every
+// channel's block total is >= 2^-100; otherwise the block's diagonal tiles
+// are recomputed directly from running products of alpha.
+//
+// Then L = I + Diag(beta) A, X = L^-1 (blocked forward substitution in fp32),
+// T = X Diag(beta), -T Khat on the matrix cores, and every operand is written
+// to the record as fragments.
 // ---------------------------------------------------------------------------
 template <int D>
-struct LocalCfg {
-  static constexpr int KS = 32;                // channels per slice
-  static constexpr int NSL = (D + KS - 1) / KS;
-  static constexpr int SP = KS + 4;            // slice pitch (floats)
-  static constexpr int MP = C + 1;             // 64x64 matrix pitch
+struct PrepCfg {
+  static constexpr int CGR = D / 8;                               // 8-channel groups per token
+  static constexpr int LPB = (64 / CGR) < 16 ? 64 / CGR : 16;     // token lanes per block
+  static constexpr int TPG = 16 / LPB;                            // tokens per lane
+  static constexpr int ACT = CGR * LPB;                           // active lanes per wave
+  static constexpr int DK = D < 32 ? 32 : D;
+  static constexpr int PW = DK < 64 ? DK : 64;                    // channels per Gram pass
+  static constexpr int NPASS = DK / PW;
+  static constexpr int MP = C + 1;
+  static_assert(ACT <= 64 && LPB * TPG == 16, "lane layout");
 };
 
 // Tiles per wave (5 each): waves 0/1 take block-row 3 plus tile (0,0) of
@@ -244,169 +363,263 @@ struct LocalCfg {
 __device__ __forceinline__ int tile_R(int tsel, int t) { return tsel == 0 ? (t < 4 ? 3 : 0) : (t < 3 ? 2 : 1); }
 __device__ __forceinline__ int tile_J(int tsel, int t) { return tsel == 0 ? (t < 4 ? t : 0) : (t < 3 ? t : t - 3); }
 
+template <int D, typename P>
+struct PrepLds {
+  using Cf = PrepCfg<D>;
+  // Gram pass (region G) and output staging (region O) share one buffer.
+  struct Gram {
+    Plane<P, C, Cf::PW> ka, qa, kb, ki;           // k bp, q bp, k bs, k / bp  (rows = tokens)
+    Plane<P, 16, Cf::PW> e0a, e0b, e1;             // block 0 rows x bt1, x bt1 bt2; block 1 x bt2
+  };
+  struct Out {
+    float qn[C * (Cf::DK + 4)];                    // token-major fp32: Qhat, then -T Khat
+    Plane<P, D, C> kt;                             // Khat^T, then Ktil^T (rows = channels)
+  };
+  static constexpr size_t U = sizeof(Gram) > sizeof(Out) ? sizeof(Gram) : sizeof(Out);
+};
+
 template <int D, typename TIn, typename P>
 __global__ __launch_bounds__(NT) void chunk_local_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ alpha,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
-    int64_t total_tokens, int64_t max_chunks, const int32_t *__restrict__ base,
-    float *__restrict__ mats) {
-  using L = LocalCfg<D>;
-  constexpr int KS = L::KS, SP = L::SP, MP = L::MP;
+    int64_t total_tokens, int64_t max_chunks, const int32_t *__restrict__ base, char *__restrict__ recs) {
+  using Cf = PrepCfg<D>;
+  using Rc = Rec<D>;
+  using L = PrepLds<D, P>;
+  using IO = FragIO<P>;
+  constexpr int CGR = Cf::CGR, LPB = Cf::LPB, TPG = Cf::TPG, DK = Cf::DK, PW = Cf::PW, MP = Cf::MP;
+  constexpr int QP = DK + 4;  // pitch of qn
 
-  __shared__ float s_k[C * SP], s_q[C * SP], s_bp[C * SP], s_bs[C * SP], s_ibp[C * SP];
-  __shared__ float s_bt[4 * KS];
-  __shared__ float s_A[C * MP], s_M[C * MP], s_X[C * MP];
+  __shared__ __attribute__((aligned(16))) char s_u[L::U];
+  __shared__ float s_L[C * MP], s_M[C * MP], s_X[C * MP];
   __shared__ float s_Y[3 * 16 * 17];
   __shared__ float s_beta[C];
+  __shared__ __attribute__((aligned(16))) float s_bt[4 * D];
   __shared__ int s_flag[4];
+  auto &G = *reinterpret_cast<typename L::Gram *>(s_u);
+  auto &O = *reinterpret_cast<typename L::Out *>(s_u);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int64_t c = (int64_t)(blockIdx.x / H);
   const int h = blockIdx.x % H;
   const int64_t nchunks = base[N] < max_chunks ? (int64_t)base[N] : max_chunks;
-  if (c >= nchunks) return;
+  if (c >= nchunks || total_tokens <= 0) return;
   const int n = find_seq(base, N, c);
   int64_t sstart, slen;
   seq_range(cu, seq_len, n, sstart, slen);
   const ChunkTok ct = chunk_tokens(sstart, slen, c - base[n], total_tokens);
   const int64_t t0 = ct.t0;
   const int nvalid = ct.valid;
+  char *rec = recs + ((size_t)c * H + h) * Rc::BYTES;
 
+  // ---- P1: loads (unconditional 16-byte vector loads, clamped rows) ----------
+  const int cgl = lane % CGR, tgl = lane / CGR;
+  const bool act = lane < Cf::ACT;
+  const int r0 = 16 * wave + TPG * tgl;  // first token row of this lane
+  Raw8<TIn> kr[TPG], qr[TPG];
+  float4 ar0[TPG], ar1[TPG];
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+      const int64_t off = (load_token(t0, r0 + i, nvalid, total_tokens) * H + h) * D + 8 * cgl;
+      kr[i].load(k + off);
+      qr[i].load(q + off);
+      ar0[i] = *reinterpret_cast<const float4 *>(alpha + off);
+      ar1[i] = *reinterpret_cast<const float4 *>(alpha + off + 4);
+    }
+  }
+  if (tid < C) {
+    const float bv = beta[load_token(t0, tid, nvalid, total_tokens) * H + h];
+    s_beta[tid] = tid < nvalid ? bv : 0.f;
+  }
   for (int e = tid; e < C * MP; e += NT) {
-    s_A[e] = 0.f;
+    s_L[e] = 0.f;
     s_M[e] = 0.f;
     s_X[e] = 0.f;
   }
-  if (tid < C) s_beta[tid] = tid < nvalid ? beta[(t0 + tid) * H + h] : 0.f;
   if (tid < 4) s_flag[tid] = 0;
 
+  // ---- P2: block-local decay products ----------------------------------------
+  float kv[TPG][8], qv[TPG][8], bp[TPG][8], bs[TPG][8], bt[8];
+  bool tiny = false;
+  if (act) {
+    float av[TPG][8], lt[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lt[j] = 1.f;
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+      const bool ok = r0 + i < nvalid;
+      kr[i].to_f32(kv[i]);
+      qr[i].to_f32(qv[i]);
+      const float a[8] = {ar0[i].x, ar0[i].y, ar0[i].z, ar0[i].w, ar1[i].x, ar1[i].y, ar1[i].z, ar1[i].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        av[i][j] = ok ? a[j] : 1.f;
+        kv[i][j] = ok ? kv[i][j] : 0.f;
+        qv[i][j] = ok ? qv[i][j] : 0.f;
+        lt[j] *= av[i][j];
+        bp[i][j] = lt[j];  // prefix inside the lane, completed below
+      }
+    }
+    float y[8], z[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = z[j] = lt[j];
+#pragma unroll
+    for (int st = 1; st < LPB; st <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float u = __shfl_up(y[j], CGR * st);
+        const float d = __shfl_down(z[j], CGR * st);
+        if (tgl >= st) y[j] *= u;
+        if (tgl + st < LPB) z[j] *= d;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float u = __shfl_up(y[j], CGR);
+      const float d = __shfl_down(z[j], CGR);
+      const float ex = tgl >= 1 ? u : 1.f;       // earlier lanes of the block
+      const float sx = tgl + 1 < LPB ? d : 1.f;  // later lanes of the block
+      bt[j] = __shfl(y[j], (LPB - 1) * CGR + cgl);
+      float suf = sx;
+#pragma unroll
+      for (int i = TPG - 1; i >= 0; --i) {
+        bs[i][j] = suf;  // product after token i to the block end
+        suf *= av[i][j];
+        bp[i][j] *= ex;  // product from the block start to token i
+      }
+      tiny = tiny || !(bt[j] >= kTinyBlock);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bt[j] = 1.f;
+  }
+  const bool block_tiny = __ballot(tiny) != 0;
+  if (lane == 0 && block_tiny) s_flag[wave] = 1;
+  if (act && tgl == 0) {
+    *reinterpret_cast<float4 *>(&s_bt[wave * D + 8 * cgl]) = make_float4(bt[0], bt[1], bt[2], bt[3]);
+    *reinterpret_cast<float4 *>(&s_bt[wave * D + 8 * cgl + 4]) = make_float4(bt[4], bt[5], bt[6], bt[7]);
+  }
+  __syncthreads();
+
+  // ---- P3: factors from the other blocks ---------------------------------------
+  float before[8], after[8], bt1[8], bt2[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) before[j] = after[j] = bt1[j] = bt2[j] = 1.f;
+  if (act) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float4 u0 = *reinterpret_cast<const float4 *>(&s_bt[b * D + 8 * cgl]);
+      const float4 u1 = *reinterpret_cast<const float4 *>(&s_bt[b * D + 8 * cgl + 4]);
+      const float tv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (b < wave) before[j] *= tv[j];
+        if (b > wave) after[j] *= tv[j];
+        if (b == 1) bt1[j] = tv[j];
+        if (b == 2) bt2[j] = tv[j];
+      }
+    }
+  }
+
+  // ---- P4: decayed Gram tiles on the matrix cores ----------------------------
   const int tsel = wave >> 1;
   const bool isM = (wave & 1) != 0;
   f32x4 acc[5];
 #pragma unroll
   for (int t = 0; t < 5; ++t) acc[t] = zero4();
-
-  // All of the chunk's q, k and alpha are loaded up front with unconditional
-  // vector loads (rows past the valid ones re-read a valid row and are
-  // replaced by the padding when written to LDS): per 32-channel slice a
-  // thread holds 8 channels of q and k of one row and 2 x 4 channels of
-  // alpha of two rows.
-  const int kr = tid >> 2, kc = 8 * (tid & 3);       // q/k: row, first channel in slice
-  Raw8<TIn> rk[L::NSL], rq[L::NSL];
-  float4 ra[L::NSL][2];
-  {
-    const int64_t tk = load_token(t0, kr, nvalid, total_tokens);
 #pragma unroll
-    for (int sl = 0; sl < L::NSL; ++sl) {
-      const int ch = sl * KS + kc < D - 8 ? sl * KS + kc : D - 8;
-      rk[sl].load(k + (tk * H + h) * D + ch);
-      rq[sl].load(q + (tk * H + h) * D + ch);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + NT * u, ar = e >> 3, ac = 4 * (e & 7);
-        const int cha = sl * KS + ac < D - 4 ? sl * KS + ac : D - 4;
-        ra[sl][u] = *reinterpret_cast<const float4 *>(
-            alpha + (load_token(t0, ar, nvalid, total_tokens) * H + h) * D + cha);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int sl = 0; sl < L::NSL; ++sl) {
-    __syncthreads();  // previous slice fully consumed
-    {
-      const bool okr = kr < nvalid;
-      float xk[8], xq[8];
-      rk[sl].to_f32(xk);
-      rq[sl].to_f32(xq);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool ok = okr && (sl * KS + kc + j < D);
-        s_k[kr * SP + kc + j] = ok ? xk[j] : 0.f;
-        s_q[kr * SP + kc + j] = ok ? xq[j] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + NT * u, ar = e >> 3, ac = 4 * (e & 7);
-        const float av[4] = {ra[sl][u].x, ra[sl][u].y, ra[sl][u].z, ra[sl][u].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool ok = (ar < nvalid) && (sl * KS + ac + j < D);
-          s_bp[ar * SP + ac + j] = ok ? av[j] : 1.f;
+  for (int p = 0; p < Cf::NPASS; ++p) {
+    if constexpr (DK > D) {  // channels past D are zero in every operand
+      for (int e = tid; e < C * (DK - D); e += NT) {
+        const int r = e / (DK - D), cc = D + e % (DK - D);
+        G.ka.store(r, cc, 0.f);
+        G.qa.store(r, cc, 0.f);
+        G.kb.store(r, cc, 0.f);
+        G.ki.store(r, cc, 0.f);
+        if (r < 16) {
+          G.e0a.store(r, cc, 0.f);
+          G.e0b.store(r, cc, 0.f);
+          G.e1.store(r, cc, 0.f);
         }
       }
     }
-    __syncthreads();
-    if (tid < 4 * KS) {
-      const int b = tid / KS, cc = tid % KS;
-      float a[16];
+    const int c8 = 8 * cgl - p * PW;
+    if (act && c8 >= 0 && c8 < PW) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a[i] = s_bp[(16 * b + i) * SP + cc];
-      float p = 1.f;
+      for (int i = 0; i < TPG; ++i) {
+        float xa[8], xq[8], xb[8], xi[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p *= a[i];
-        s_bp[(16 * b + i) * SP + cc] = p;
+        for (int j = 0; j < 8; ++j) {
+          xa[j] = kv[i][j] * bp[i][j];
+          xq[j] = qv[i][j] * bp[i][j];
+          xb[j] = kv[i][j] * bs[i][j];
+          xi[j] = block_tiny ? 0.f : kv[i][j] * __builtin_amdgcn_rcpf(bp[i][j]);
+        }
+        const int r = r0 + i;
+        G.ka.store8(r, c8, xa);
+        G.qa.store8(r, c8, xq);
+        G.kb.store8(r, c8, xb);
+        G.ki.store8(r, c8, xi);
+        if (wave == 0) {
+          float x1[8], x2[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            x1[j] = xb[j] * bt1[j];
+            x2[j] = x1[j] * bt2[j];
+          }
+          G.e0a.store8(r, c8, x1);
+          G.e0b.store8(r, c8, x2);
+        } else if (wave == 1) {
+          float x1[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x1[j] = xb[j] * bt2[j];
+          G.e1.store8(r - 16, c8, x1);
+        }
       }
-      const bool tiny = !(p >= kTinyBlock);
-      float sfx = 1.f;
-#pragma unroll
-      for (int i = 15; i >= 0; --i) {
-        s_bs[(16 * b + i) * SP + cc] = sfx;
-        sfx *= a[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float bpv = s_bp[(16 * b + i) * SP + cc];
-        s_ibp[(16 * b + i) * SP + cc] = tiny ? 0.f : 1.0f / bpv;
-      }
-      s_bt[b * KS + cc] = p;
-      if (tiny) atomicOr(&s_flag[b], 1);
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 5; ++t) {
       const int R = tile_R(tsel, t), J = tile_J(tsel, t);
-      const int r = 16 * R + m, jr = 16 * J + m;
-      const float *X = isM ? s_q : s_k;
-      float xa[8], xb[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int cc = 8 * g + j;
-        xa[j] = X[r * SP + cc] * s_bp[r * SP + cc];
-        float left;
-        if (J == R) {
-          left = s_ibp[jr * SP + cc];
-        } else {
-          left = s_bs[jr * SP + cc];
-          for (int b = J + 1; b < R; ++b) left *= s_bt[b * KS + cc];
-        }
-        xb[j] = s_k[jr * SP + cc] * left;
+      for (int kb = 0; kb < PW / 32; ++kb) {
+        const int col = kb * 32 + 8 * g;
+        const auto A = isM ? G.qa.load8(16 * R + m, col) : G.ka.load8(16 * R + m, col);
+        typename P::Frag B;
+        if (J == R)
+          B = G.ki.load8(16 * J + m, col);
+        else if (J == R - 1)
+          B = G.kb.load8(16 * J + m, col);
+        else if (J == R - 2)
+          B = J == 0 ? G.e0a.load8(m, col) : G.e1.load8(m, col);
+        else
+          B = G.e0b.load8(m, col);
+        P::mma(acc[t], A, B);
       }
-      P::mma(acc[t], P::make(xa), P::make(xb));
     }
+    __syncthreads();
   }
 
-  // Scatter the tiles (accumulator layout: row 4g+i, column m of the tile),
-  // keeping j < r for A and j <= r for M.
-  {
-    float *dst = isM ? s_M : s_A;
+  // ---- P5: L = I + Diag(beta) A (strictly lower part) and M ----------------------
 #pragma unroll
-    for (int t = 0; t < 5; ++t) {
-      const int R = tile_R(tsel, t), J = tile_J(tsel, t);
+  for (int t = 0; t < 5; ++t) {
+    const int R = tile_R(tsel, t), J = tile_J(tsel, t);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * R + 4 * g + i, j = 16 * J + m;
-        const bool keep = isM ? (j <= r) : (j < r);
-        dst[r * MP + j] = keep ? acc[t][i] : 0.f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * R + 4 * g + i, j = 16 * J + m;
+      if (isM)
+        s_M[r * MP + j] = (j <= r) ? acc[t][i] : 0.f;
+      else
+        s_L[r * MP + j] = (j < r) ? acc[t][i] * s_beta[r] : 0.f;
     }
   }
   __syncthreads();
 
   // Rare path: a 16-token block whose decay underflows 2^-100 in some
-  // channel.  Recompute its diagonal tiles of A and M directly:
+  // channel.  Its diagonal tiles of A and M, directly:
   //   sum_c x_rc k_jc prod_{j<s<=r} alpha_sc.
   for (int b = 0; b < 4; ++b) {
     if (s_flag[b] == 0) continue;  // uniform across the workgroup
@@ -429,21 +642,15 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
           m_acc += to_f32(q[orr]) * kj;
         }
       }
-      s_A[rr * MP + jj] = (j < r) ? a_acc : 0.f;
+      s_L[rr * MP + jj] = (j < r) ? a_acc * s_beta[rr] : 0.f;
       s_M[rr * MP + jj] = m_acc;
     }
     __syncthreads();
   }
 
-  // L = I + Diag(beta) A (strictly lower part kept in s_A, unit diagonal implied).
-  for (int e = tid; e < C * C; e += NT) {
-    const int r = e / C, j = e % C;
-    if (j < r) s_A[r * MP + j] *= s_beta[r];
-  }
-  __syncthreads();
-
-  // X = L^-1, blocked by 16.  Diagonal blocks: forward substitution, one
-  // column per lane (wave b inverts block b).
+  // ---- P6: X = L^-1, blocked by 16 ---------------------------------------------
+  // Diagonal blocks: forward substitution, one column per lane (wave b
+  // inverts block b).
   if (lane < 16) {
     const int b = wave, jj = lane;
     float x[16];
@@ -451,7 +658,7 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     for (int i = 0; i < 16; ++i) {
       float s = (i == jj) ? 1.f : 0.f;
 #pragma unroll
-      for (int t = 0; t < i; ++t) s -= s_A[(16 * b + i) * MP + 16 * b + t] * x[t];
+      for (int t = 0; t < i; ++t) s -= s_L[(16 * b + i) * MP + 16 * b + t] * x[t];
       x[i] = s;
     }
 #pragma unroll
@@ -466,7 +673,7 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
       float s = 0.f;
       for (int K = J; K < I; ++K) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) s += s_A[(16 * I + rr) * MP + 16 * K + t] * s_X[(16 * K + t) * MP + 16 * J + cc];
+        for (int t = 0; t < 16; ++t) s += s_L[(16 * I + rr) * MP + 16 * K + t] * s_X[(16 * K + t) * MP + 16 * J + cc];
       }
       s_Y[(J * 16 + rr) * 17 + cc] = s;
     }
@@ -481,105 +688,188 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     __syncthreads();
   }
 
-  // T = X Diag(beta); write T then M (64x64 fp32 each, row-major).
-  float *outT = mats + ((size_t)c * H + h) * (size_t)(2 * C * C);
-  float *outM = outT + C * C;
-  for (int e = tid; e < C * C; e += NT) {
-    const int r = e / C, j = e % C;
-    outT[e] = s_X[r * MP + j] * s_beta[j];
-    outM[e] = s_M[r * MP + j];
+  // ---- P7: records ------------------------------------------------------------------
+  // T = X Diag(beta) and M fragments (row tile = wave).
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float xt[8], xm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = kb * 32 + 8 * g + j;
+      xt[j] = s_X[(16 * wave + m) * MP + col] * s_beta[col];
+      xm[j] = s_M[(16 * wave + m) * MP + col];
+    }
+    IO::store(rec + (size_t)(Rc::TMAT + 2 * wave + kb) * kFragBytes, lane, xt);
+    IO::store(rec + (size_t)(Rc::MMAT + 2 * wave + kb) * kFragBytes, lane, xm);
+  }
+  // Qhat (token-major, fp32) and Khat^T (channel-major, operand form) to LDS.
+  if constexpr (DK > D) {
+    for (int e = tid; e < C * (DK - D); e += NT) O.qn[(e / (DK - D)) * QP + D + e % (DK - D)] = 0.f;
+  }
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+      float xq[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xq[j] = before[j] * bp[i][j] * qv[i][j];
+      *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl]) = make_float4(xq[0], xq[1], xq[2], xq[3]);
+      *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl + 4]) = make_float4(xq[4], xq[5], xq[6], xq[7]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float xk[TPG];
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) xk[i] = before[j] * bp[i][j] * kv[i][j];  // Gamma_r k_r
+      O.kt.template store_run<TPG>(8 * cgl + j, r0, xk);
+    }
+  }
+  __syncthreads();
+  // Qhat fragments.
+#pragma unroll
+  for (int kb = 0; kb < Rc::NKB; ++kb) {
+    float x[8];
+    const float4 u0 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g]);
+    const float4 u1 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g + 4]);
+    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+    IO::store(rec + (size_t)(Rc::QHAT + Rc::NKB * wave + kb) * kFragBytes, lane, x);
+  }
+  // -T Khat for row tile = wave: A = T rows (from s_X, beta applied), B = Khat^T.
+  f32x4 wn[Rc::NTILE];
+#pragma unroll
+  for (int t = 0; t < Rc::NTILE; ++t) wn[t] = zero4();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if (kb <= (wave >> 1)) {  // T is lower triangular
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = kb * 32 + 8 * g + j;
+        x[j] = -s_X[(16 * wave + m) * MP + col] * s_beta[col];
+      }
+      const auto A = P::make(x);
+#pragma unroll
+      for (int t = 0; t < Rc::NTILE; ++t) P::mma(wn[t], A, O.kt.load8(16 * t + m, kb * 32 + 8 * g));
+    }
+  }
+  __syncthreads();  // Qhat fragments read, Khat^T consumed
+#pragma unroll
+  for (int t = 0; t < Rc::NTILE; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) O.qn[(16 * wave + 4 * g + i) * QP + 16 * t + m] = wn[t][i];
+  }
+  if (act) {  // Ktil^T into the channel-major plane
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float xk[TPG];
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) xk[i] = bs[i][j] * after[j] * kv[i][j];  // (Gamma_C / Gamma_r) k_r
+      O.kt.template store_run<TPG>(8 * cgl + j, r0, xk);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int kb = 0; kb < Rc::NKB; ++kb) {
+    float x[8];
+    const float4 u0 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g]);
+    const float4 u1 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g + 4]);
+    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+    IO::store(rec + (size_t)(Rc::WNEG + Rc::NKB * wave + kb) * kFragBytes, lane, x);
+  }
+#pragma unroll
+  for (int tt = 0; tt < (Rc::NTILE + 3) / 4; ++tt) {
+    const int t = wave + 4 * tt;
+    if (t < Rc::NTILE) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        IO::store_frag(rec + (size_t)(Rc::KTIL + 2 * t + kb) * kFragBytes, lane, O.kt.load8(16 * t + m, kb * 32 + 8 * g));
+    }
+  }
+  if (wave == 0 && act && tgl == 0) {
+    float *gam = reinterpret_cast<float *>(rec + Rc::GAM);
+    *reinterpret_cast<float4 *>(gam + 8 * cgl) =
+        make_float4(bt[0] * after[0], bt[1] * after[1], bt[2] * after[2], bt[3] * after[3]);
+    *reinterpret_cast<float4 *>(gam + 8 * cgl + 4) =
+        make_float4(bt[4] * after[4], bt[5] * after[5], bt[6] * after[6], bt[7] * after[7]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// chunk_state_kernel: the sequential pass over the chunks of one sequence
-// for one head and 16 value columns.
+// chunk_state_kernel: the sequential pass over the chunks of one sequence for
+// one head and 16 value columns, streaming the chunk records.
 //
-// Wave w owns chunk rows 16w..16w+15 for E = Khat S, O = Qhat S + M W and
-// W = T (V - E), and state row tiles w, w+4 (16 key channels each) for the
-// update S <- Diag(Gamma_C) S + Ktil^T W.  S is kept in fp32 accumulators;
-// a copy in operand form (S^T, split for the matrix cores) lives in LDS so
-// that every wave can use all key rows.
-//
-// Per chunk, every thread stages 8 key channels of TPG consecutive tokens:
-// q, k, alpha arrive as 16-byte vector loads issued one chunk ahead (the
-// next chunk's loads are in flight while this chunk computes), the decay
-// factors are running products of alpha along the tokens (a two-level scan:
-// inside the thread's tokens, then across token groups through LDS), and
-// the operands Khat, Qhat (rows = tokens) and Ktil^T (rows = channels) are
-// written to LDS already split for the matrix cores.
+// Per chunk, with S the 128x16 state slice (fp32 accumulators across chunks)
+// and wave w owning chunk rows 16w..16w+15 and state row tiles w, w+4:
+//   W = T V + (-T Khat) S               (rows of this wave)
+//   O = Qhat S                          (rows of this wave)
+//   --- W of every wave to LDS; barrier ---
+//   O += M W;  o <- O
+//   S <- Diag(Gamma_C) S + Ktil^T W     (this wave's state tiles; to LDS)
+//   --- barrier ---
+// The record fragments of chunk c+1 are loaded into the other register set
+// while chunk c computes (the loop is unrolled by two so no copy sits between
+// a load and its use).  V is staged into LDS transposed, one chunk ahead.
 //
 // blockIdx -> work: consecutive workgroups are dealt round-robin to the 8
-// XCDs, so the D/16 workgroups of one (sequence, head) are mapped to block
-// indices congruent mod 8: they share an XCD and its L2, and the chunk
-// inputs and T/M they all read are fetched from HBM once.
+// XCDs, so the D/16 workgroups of one (sequence, head) get block indices
+// congruent mod 8: they share an XCD and its L2, and every record is fetched
+// from HBM once for all of them.
 // ---------------------------------------------------------------------------
-template <int D>
-struct StateCfg {
-  static constexpr int G = D / 16;                            // value-column groups per head
-  static constexpr int DK = D < 32 ? 32 : D;                  // key width of operand planes
-  static constexpr int NKB = DK / 32;                         // 32-wide k-blocks over key channels
-  static constexpr int NTILE = D / 16;                        // 16-row tiles of the state
-  static constexpr int TPW = (NTILE + 3) / 4;                 // state tiles per wave (max)
-  static constexpr int CGR = D / 8;                           // 8-channel groups per token row
-  static constexpr int NTG = (NT / CGR) < C ? NT / CGR : C;   // token groups
-  static constexpr int TPG = C / NTG;                         // tokens per staging thread
-  static constexpr int ACTIVE = CGR * NTG;                    // staging threads
-  static_assert(ACTIVE <= NT && C % NTG == 0, "staging layout");
-};
-
 template <int D, typename TIn>
-struct StateRaw {
-  static constexpr int TPG = StateCfg<D>::TPG;
-  Raw8<TIn> k[TPG], q[TPG];
-  float4 a0[TPG], a1[TPG];
+struct ScanBuf {
+  static constexpr int NKB = Rec<D>::NKB;
+  static constexpr int TPW = (Rec<D>::NTILE + 3) / 4;
   Raw4<TIn> v;
+  FragRaw wneg[NKB], qhat[NKB], ktil[TPW][2], tm[2], mm[2];
+  float4 gam[TPW];
 };
 
-template <int D, typename TIn>
-__device__ __forceinline__ void load_state_raw(StateRaw<D, TIn> &R, const TIn *__restrict__ q,
-                                               const TIn *__restrict__ k, const TIn *__restrict__ v,
-                                               const float *__restrict__ alpha, int64_t t0, int valid,
-                                               int64_t total, int h, int H, int col0, int tid) {
-  using Cf = StateCfg<D>;
-  if (tid < Cf::ACTIVE) {
-    const int cg8 = tid % Cf::CGR, tg = tid / Cf::CGR;
+template <int D, typename TIn, typename P>
+__device__ __forceinline__ void load_scan_buf(ScanBuf<D, TIn> &B, const char *rec, const TIn *v,
+                                              int64_t vt0, int valid, int64_t total, int h, int H,
+                                              int col0, int tid, int wave, int lane) {
+  using Rc = Rec<D>;
+  using IO = FragIO<P>;
+  B.v.load(v + (load_token(vt0, tid >> 2, valid, total) * H + h) * D + col0 + 4 * (tid & 3));
 #pragma unroll
-    for (int i = 0; i < Cf::TPG; ++i) {
-      const int64_t off = (load_token(t0, tg * Cf::TPG + i, valid, total) * H + h) * D + 8 * cg8;
-      R.k[i].load(k + off);
-      R.q[i].load(q + off);
-      R.a0[i] = *reinterpret_cast<const float4 *>(alpha + off);
-      R.a1[i] = *reinterpret_cast<const float4 *>(alpha + off + 4);
-    }
+  for (int kb = 0; kb < Rc::NKB; ++kb) {
+    IO::load(B.wneg[kb], rec + (size_t)(Rc::WNEG + Rc::NKB * wave + kb) * kFragBytes, lane);
+    IO::load(B.qhat[kb], rec + (size_t)(Rc::QHAT + Rc::NKB * wave + kb) * kFragBytes, lane);
   }
-  const int64_t voff = (load_token(t0, tid >> 2, valid, total) * H + h) * D + col0 + 4 * (tid & 3);
-  R.v.load(v + voff);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    IO::load(B.tm[kb], rec + (size_t)(Rc::TMAT + 2 * wave + kb) * kFragBytes, lane);
+    IO::load(B.mm[kb], rec + (size_t)(Rc::MMAT + 2 * wave + kb) * kFragBytes, lane);
+  }
+  const int g = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < ScanBuf<D, TIn>::TPW; ++u) {
+    const int t0 = wave + 4 * u, t = t0 < Rc::NTILE ? t0 : Rc::NTILE - 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      IO::load(B.ktil[u][kb], rec + (size_t)(Rc::KTIL + 2 * t + kb) * kFragBytes, lane);
+    B.gam[u] = *reinterpret_cast<const float4 *>(rec + Rc::GAM + sizeof(float) * (16 * t + 4 * g));
+  }
 }
 
 template <int D, typename TIn, typename P>
 __global__ __launch_bounds__(NT) void chunk_state_kernel(
-    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-    const float *__restrict__ alpha, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
+    const TIn *__restrict__ v, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
     int64_t total_tokens, int64_t max_chunks, const int32_t *__restrict__ base,
-    const float *__restrict__ mats, const float *__restrict__ S0, float *__restrict__ o,
+    const char *__restrict__ recs, const float *__restrict__ S0, float *__restrict__ o,
     float *__restrict__ S_T) {
-  using Cf = StateCfg<D>;
-  constexpr int G = Cf::G, DK = Cf::DK, NKB = Cf::NKB, NTILE = Cf::NTILE, TPW = Cf::TPW;
-  constexpr int CGR = Cf::CGR, NTG = Cf::NTG, TPG = Cf::TPG;
+  using Rc = Rec<D>;
+  using IO = FragIO<P>;
+  using Buf = ScanBuf<D, TIn>;
+  constexpr int G = D / 16, DK = D < 32 ? 32 : D, NKB = Rc::NKB, NTILE = Rc::NTILE, TPW = Buf::TPW;
 
-  __shared__ Plane<P, C, DK> Khat;
-  __shared__ Plane<P, C, DK> Qhat;
-  __shared__ Plane<P, D, C> KtilT;
-  __shared__ Plane<P, 16, DK> Sop;
-  __shared__ Plane<P, 16, C> Vme;
-  __shared__ Plane<P, 16, C> Wop;
-  __shared__ float s_v[C * 17];
-  __shared__ float s_gam[D];
-  __shared__ __attribute__((aligned(16))) float s_pre[NTG * D];  // group totals, then exclusive prefix
-  __shared__ __attribute__((aligned(16))) float s_suf[NTG * D];  // exclusive suffix over groups
+  __shared__ Plane<P, 16, DK> Sop;     // S^T in operand form (rows = value columns)
+  __shared__ Plane<P, 16, C> Wop;      // W^T in operand form
+  __shared__ Plane<P, 16, C> Vt[2];    // V^T of this chunk / the next
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
 
   const int id = blockIdx.x;
@@ -589,18 +879,11 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
   if (pair >= (int64_t)N * H) return;
   const int n = (int)(pair / H), h = (int)(pair % H);
   const int col0 = 16 * cg;
+  const int rbase = 16 * wave;
 
-  // Zero the padded key channels of the channel-indexed planes once.
   if constexpr (DK > D) {
-    for (int e = tid; e < C * (DK - D); e += NT) {
-      const int r = e / (DK - D), cc = D + e % (DK - D);
-      Khat.store(r, cc, 0.f);
-      Qhat.store(r, cc, 0.f);
-      if (r < 16) Sop.store(r, cc, 0.f);
-    }
+    for (int e = tid; e < 16 * (DK - D); e += NT) Sop.store(e / (DK - D), D + e % (DK - D), 0.f);
   }
-
-  // Initial state: rows 16t + 4g + i, column col0 + m.
   f32x4 sreg[TPW];
   const float *S0p = S0 ? S0 + (size_t)pair * D * D : nullptr;
 #pragma unroll
@@ -609,10 +892,7 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
     sreg[u] = zero4();
     if (t < NTILE) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * t + 4 * g + i;
-        sreg[u][i] = S0p ? S0p[(size_t)row * D + col0 + m] : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) sreg[u][i] = S0p ? S0p[(size_t)(16 * t + 4 * g + i) * D + col0 + m] : 0.f;
       Sop.store4(m, 16 * t + 4 * g, sreg[u]);
     }
   }
@@ -624,191 +904,85 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
   if (cend > max_chunks) cend = max_chunks;
   if (total_tokens <= 0) cend = cbeg;
 
-  const int cg8 = tid % CGR, tg = tid / CGR;
-  const int rbase = 16 * wave;
-  const int nkb = (wave >> 1) + 1;  // T and M are lower triangular
-
-  // Two register sets for the per-chunk loads (raw inputs and this wave's
-  // T/M rows), used alternately: while chunk c is processed from one set,
-  // chunk c+1 is loading into the other (the loop is unrolled by two so that
-  // no register copy sits between a load and its use).
-  StateRaw<D, TIn> bufA, bufB;
-  float4 tA[4], mA[4], tB[4], mB[4];
-  auto load_tm = [&](int64_t cc, float4 (&tq)[4], float4 (&mq)[4]) {
-    const float *src = mats + ((size_t)cc * H + h) * (size_t)(2 * C * C) + (rbase + m) * C + 8 * g;
+  auto rec_of = [&](int64_t cc) { return recs + ((size_t)cc * H + h) * Rc::BYTES; };
+  auto stage_v = [&](const Buf &B, int slot, int valid) {
+    float vv[4];
+    B.v.to_f32(vv);
+    const int r = tid >> 2;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {  // both k-blocks; above the diagonal T and M are 0
-      tq[2 * kb] = *reinterpret_cast<const float4 *>(src + kb * 32);
-      tq[2 * kb + 1] = *reinterpret_cast<const float4 *>(src + kb * 32 + 4);
-      mq[2 * kb] = *reinterpret_cast<const float4 *>(src + C * C + kb * 32);
-      mq[2 * kb + 1] = *reinterpret_cast<const float4 *>(src + C * C + kb * 32 + 4);
-    }
+    for (int j = 0; j < 4; ++j) Vt[slot].store(4 * (tid & 3) + j, r, r < valid ? vv[j] : 0.f);
   };
-  auto prefetch = [&](int64_t cc, StateRaw<D, TIn> &R, float4 (&tq)[4], float4 (&mq)[4]) {
+
+  Buf bufA, bufB;
+  auto prefetch = [&](int64_t cc, Buf &B) {
     const ChunkTok cn = chunk_tokens(sstart, slen, cc - cbeg, total_tokens);
-    load_state_raw<D, TIn>(R, q, k, v, alpha, cn.t0, cn.valid, total_tokens, h, H, col0, tid);
-    load_tm(cc, tq, mq);
+    load_scan_buf<D, TIn, P>(B, rec_of(cc), v, cn.t0, cn.valid, total_tokens, h, H, col0, tid, wave, lane);
   };
 
-  auto process = [&](int64_t c, const StateRaw<D, TIn> &use, const float4 (&tu)[4], const float4 (&mu)[4],
-                     int64_t cn, StateRaw<D, TIn> &nb, float4 (&tn)[4], float4 (&mn)[4]) {
+  auto process = [&](int64_t c, const Buf &U, Buf &Nx, int64_t cn) {
     const ChunkTok ct = chunk_tokens(sstart, slen, c - cbeg, total_tokens);
-    const int64_t t0 = ct.t0;
-    const int nvalid = ct.valid;
-    __syncthreads();  // previous chunk's operands fully consumed
+    const int slot = (int)((c - cbeg) & 1);
+    prefetch(cn, Nx);  // unconditional (the last chunk re-reads itself)
 
-    // ---- stage: decay factors and operands --------------------------------
-    float av[TPG][8], kv[TPG][8], qv[TPG][8];
-    if (tid < Cf::ACTIVE) {
-      float tot[8];
+    // W = T V + (-T Khat) S;  O = Qhat S
+    f32x4 wv = zero4(), ws = zero4(), ov = zero4();
 #pragma unroll
-      for (int j = 0; j < 8; ++j) tot[j] = 1.f;
-#pragma unroll
-      for (int i = 0; i < TPG; ++i) {
-        const bool ok = tg * TPG + i < nvalid;
-        use.k[i].to_f32(kv[i]);
-        use.q[i].to_f32(qv[i]);
-        const float a[8] = {use.a0[i].x, use.a0[i].y, use.a0[i].z, use.a0[i].w,
-                            use.a1[i].x, use.a1[i].y, use.a1[i].z, use.a1[i].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          av[i][j] = ok ? a[j] : 1.f;
-          kv[i][j] = ok ? kv[i][j] : 0.f;
-          qv[i][j] = ok ? qv[i][j] : 0.f;
-          tot[j] *= av[i][j];
-        }
-      }
-      *reinterpret_cast<float4 *>(&s_pre[tg * D + 8 * cg8]) = make_float4(tot[0], tot[1], tot[2], tot[3]);
-      *reinterpret_cast<float4 *>(&s_pre[tg * D + 8 * cg8 + 4]) = make_float4(tot[4], tot[5], tot[6], tot[7]);
-    }
-    {
-      float vv[4];
-      use.v.to_f32(vv);
-      const int r = tid >> 2;
-      const bool ok = r < nvalid;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s_v[r * 17 + 4 * (tid & 3) + j] = ok ? vv[j] : 0.f;
-    }
-    __syncthreads();
-    if (tid < D) {  // exclusive suffix, then exclusive prefix (in place), over token groups
-      float sfx = 1.f;
-      for (int gg = NTG - 1; gg >= 0; --gg) {
-        s_suf[gg * D + tid] = sfx;
-        sfx *= s_pre[gg * D + tid];
-      }
-      float pfx = 1.f;
-      for (int gg = 0; gg < NTG; ++gg) {
-        const float tv = s_pre[gg * D + tid];
-        s_pre[gg * D + tid] = pfx;
-        pfx *= tv;
-      }
-      s_gam[tid] = pfx;  // Gamma_C
-    }
-    __syncthreads();
-    if (tid < Cf::ACTIVE) {
-      float ep[8], es[8];
-      {
-        const float4 p0 = *reinterpret_cast<const float4 *>(&s_pre[tg * D + 8 * cg8]);
-        const float4 p1 = *reinterpret_cast<const float4 *>(&s_pre[tg * D + 8 * cg8 + 4]);
-        const float4 s0 = *reinterpret_cast<const float4 *>(&s_suf[tg * D + 8 * cg8]);
-        const float4 s1 = *reinterpret_cast<const float4 *>(&s_suf[tg * D + 8 * cg8 + 4]);
-        ep[0] = p0.x; ep[1] = p0.y; ep[2] = p0.z; ep[3] = p0.w;
-        ep[4] = p1.x; ep[5] = p1.y; ep[6] = p1.z; ep[7] = p1.w;
-        es[0] = s0.x; es[1] = s0.y; es[2] = s0.z; es[3] = s0.w;
-        es[4] = s1.x; es[5] = s1.y; es[6] = s1.z; es[7] = s1.w;
-      }
-#pragma unroll
-      for (int i = 0; i < TPG; ++i) {
-        float xk[8], xq[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          ep[j] *= av[i][j];  // Gamma_r (inclusive)
-          xk[j] = ep[j] * kv[i][j];
-          xq[j] = ep[j] * qv[i][j];
-        }
-        Khat.store8(tg * TPG + i, 8 * cg8, xk);
-        Qhat.store8(tg * TPG + i, 8 * cg8, xq);
-      }
-#pragma unroll
-      for (int i = TPG - 1; i >= 0; --i) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          KtilT.store(8 * cg8 + j, tg * TPG + i, es[j] * kv[i][j]);  // Gamma_C / Gamma_r
-          es[j] *= av[i][j];
-        }
-      }
-    }
-    prefetch(cn, nb, tn, mn);  // next chunk, into the other register set
-    __syncthreads();
-
-    // ---- E = Khat S, O = Qhat S (chunk rows of this wave) ------------------
-    f32x4 E = zero4(), O = zero4();
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb <= (wave >> 1)) mma_exact_b(wv, IO::frag(U.tm[kb]), Vt[slot].load8(m, kb * 32 + 8 * g));
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const auto B = Sop.load8(m, kb * 32 + 8 * g);
-      P::mma(E, Khat.load8(rbase + m, kb * 32 + 8 * g), B);
-      P::mma(O, Qhat.load8(rbase + m, kb * 32 + 8 * g), B);
+      const auto Bs = Sop.load8(m, kb * 32 + 8 * g);
+      P::mma(ws, IO::frag(U.wneg[kb]), Bs);
+      P::mma(ov, IO::frag(U.qhat[kb]), Bs);
     }
-    {
-      f32x4 vme;
+    f32x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vme[i] = s_v[(rbase + 4 * g + i) * 17 + m] - E[i];
-      Vme.store4(m, rbase + 4 * g, vme);
-    }
+    for (int i = 0; i < 4; ++i) w[i] = wv[i] + ws[i];
+    Wop.store4(m, rbase + 4 * g, w);
     __syncthreads();
 
-    // ---- W = T (V - E) ------------------------------------------------------
-    f32x4 W = zero4();
+    // O += M W
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb < nkb) {
-        const float x[8] = {tu[2 * kb].x, tu[2 * kb].y, tu[2 * kb].z, tu[2 * kb].w,
-                            tu[2 * kb + 1].x, tu[2 * kb + 1].y, tu[2 * kb + 1].z, tu[2 * kb + 1].w};
-        P::mma(W, P::make(x), Vme.load8(m, kb * 32 + 8 * g));
-      }
-    }
-    Wop.store4(m, rbase + 4 * g, W);
-    __syncthreads();
-
-    // ---- O += M W; store o ----------------------------------------------------
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb < nkb) {
-        const float x[8] = {mu[2 * kb].x, mu[2 * kb].y, mu[2 * kb].z, mu[2 * kb].w,
-                            mu[2 * kb + 1].x, mu[2 * kb + 1].y, mu[2 * kb + 1].z, mu[2 * kb + 1].w};
-        P::mma(O, P::make(x), Wop.load8(m, kb * 32 + 8 * g));
-      }
-    }
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb <= (wave >> 1)) P::mma(ov, IO::frag(U.mm[kb]), Wop.load8(m, kb * 32 + 8 * g));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rbase + 4 * g + i;
-      if (r < nvalid) o[((t0 + r) * H + h) * D + col0 + m] = O[i];
+      if (r < ct.valid) o[((ct.t0 + r) * H + h) * D + col0 + m] = ov[i];
     }
-
-    // ---- S <- Diag(Gamma_C) S + Ktil^T W (this wave's state tiles) ------------
+    // S <- Diag(Gamma_C) S + Ktil^T W
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int t = wave + 4 * u;
       if (t < NTILE) {
         f32x4 acc;
+        const float gm[4] = {U.gam[u].x, U.gam[u].y, U.gam[u].z, U.gam[u].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = s_gam[16 * t + 4 * g + i] * sreg[u][i];
+        for (int i = 0; i < 4; ++i) acc[i] = gm[i] * sreg[u][i];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          P::mma(acc, KtilT.load8(16 * t + m, kb * 32 + 8 * g), Wop.load8(m, kb * 32 + 8 * g));
+          P::mma(acc, IO::frag(U.ktil[u][kb]), Wop.load8(m, kb * 32 + 8 * g));
         sreg[u] = acc;
         Sop.store4(m, 16 * t + 4 * g, acc);
       }
     }
+    {  // V of the next chunk into the other slot
+      const ChunkTok cnt = chunk_tokens(sstart, slen, cn - cbeg, total_tokens);
+      stage_v(Nx, slot ^ 1, cn == c ? 0 : cnt.valid);
+    }
+    __syncthreads();
   };
 
-  if (cbeg < cend) prefetch(cbeg, bufA, tA, mA);
+  if (cbeg < cend) {
+    prefetch(cbeg, bufA);
+    const ChunkTok c0 = chunk_tokens(sstart, slen, 0, total_tokens);
+    stage_v(bufA, 0, c0.valid);
+  }
+  __syncthreads();
   for (int64_t c = cbeg; c < cend; c += 2) {
-    // The prefetch is unconditional (the last chunk re-reads itself) so
-    // that every wait count stays exact.
-    process(c, bufA, tA, mA, c + 1 < cend ? c + 1 : c, bufB, tB, mB);
+    process(c, bufA, bufB, c + 1 < cend ? c + 1 : c);
     if (c + 1 >= cend) break;
-    process(c + 1, bufB, tB, mB, c + 2 < cend ? c + 2 : c + 1, bufA, tA, mA);
+    process(c + 1, bufB, bufA, c + 2 < cend ? c + 2 : c + 1);
   }
 
   if (S_T != nullptr) {
@@ -829,9 +1003,10 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
                             const float *alpha, const float *beta, const int32_t *cu,
                             const float *S0, float *o, float *S_T, void *workspace,
                             hipStream_t stream, int phases) {
+  static_assert(Rec<D>::BYTES == 0 || true, "");
   char *ws = static_cast<char *>(workspace);
   int32_t *base = reinterpret_cast<int32_t *>(ws);
-  float *mats = reinterpret_cast<float *>(ws + schedule_bytes(s));
+  char *recs = ws + schedule_bytes(s);
   const int N = s.num_seqs, H = s.num_heads;
   const int64_t mc = max_chunks(s);
   const TIn *qp = static_cast<const TIn *>(q), *kp = static_cast<const TIn *>(k),
@@ -843,7 +1018,7 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
     if (e != hipSuccess) return e;
     if (mc > 0) {
       hipLaunchKernelGGL((chunk_local_kernel<D, TIn, P>), dim3((unsigned)(mc * H)), dim3(NT), 0, stream,
-                         qp, kp, alpha, beta, cu, s.seq_len, N, H, s.total_tokens, mc, base, mats);
+                         qp, kp, alpha, beta, cu, s.seq_len, N, H, s.total_tokens, mc, base, recs);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -851,8 +1026,8 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   if (phases & kPhaseState) {
     const int64_t pairs = (int64_t)N * H;
     const int64_t blocks = (pairs + 7) / 8 * 8 * (D / 16);
-    hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P>), dim3((unsigned)blocks), dim3(NT), 0, stream, qp,
-                       kp, vp, alpha, cu, s.seq_len, N, H, s.total_tokens, mc, base, mats, S0, o, S_T);
+    hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P>), dim3((unsigned)blocks), dim3(NT), 0, stream, vp, cu,
+                       s.seq_len, N, H, s.total_tokens, mc, base, recs, S0, o, S_T);
     e = hipGetLastError();
   }
   return e;

@@ -90,11 +90,11 @@ int kda_abi_version(void);
 const char *kda_status_string(kda_status_t status);
 
 /* Bytes of device workspace kda_prefill needs for `shape` (written to
- * *bytes).  The size depends on N, H and total_tokens only (an upper bound
- * on the number of 64-token chunks, floor(total_tokens/64) + N, times
- * 32 KiB per chunk and head, plus a small schedule table).  Returns
- * KDA_ERR_INVALID_ARGUMENT / KDA_ERR_UNSUPPORTED for a shape kda_prefill
- * would reject. */
+ * *bytes).  The size depends on N, H, d and total_tokens only: an upper bound
+ * on the number of 64-token chunks, floor(total_tokens/64) + N, times one
+ * record of chunk operands per chunk and head (128.5 KiB at d = 128), plus a
+ * small schedule table.  Returns KDA_ERR_INVALID_ARGUMENT /
+ * KDA_ERR_UNSUPPORTED for a shape kda_prefill would reject. */
 kda_status_t kda_prefill_workspace_size(const kda_shape_t *shape, size_t *bytes);
 
 /* Prefill (chunked): run the update over every token of every sequence and
@@ -129,9 +129,9 @@ kda_status_t kda_prefill(const kda_shape_t *shape,
  * same stream with the same arguments.
  *
  * Phase 1 (fully parallel over chunks and heads): builds the per-sequence
- * chunk table and, for every 64-token chunk and head, the two 64x64
- * chunk-local matrices of the chunked form, into `workspace`.  Reads q, k,
- * alpha, beta and cu_seqlens. */
+ * chunk table and, for every 64-token chunk and head, the chunk-local
+ * operands of the chunked form, into `workspace`.  Reads q, k, alpha, beta
+ * and cu_seqlens. */
 kda_status_t kda_prefill_chunk_local(const kda_shape_t *shape,
                                      const void *q, const void *k,
                                      const float *alpha, const float *beta,

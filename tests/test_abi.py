@@ -72,7 +72,12 @@ def test_workspace_size_formula(N, T, H, d):
     need = kda.prefill_workspace_size(N, N * T, H, d)
     sched = ((4 * (N + 1) + 255) // 256) * 256
     chunks = (N * T) // 64 + N
-    assert need == sched + chunks * H * 2 * 64 * 64 * 4
+    nkb = max(d, 32) // 32
+    frags = 4 * nkb * 2 + (d // 16) * 2 + 16          # -T Khat, Qhat, Ktil^T, T, M
+    record = -(-(frags * 2048 + 4 * d) // 256) * 256   # + Gamma_C, 256-byte aligned
+    assert need == sched + chunks * H * record
+    if d == 128:
+        assert record == 131584                          # 128.5 KiB per chunk and head
 
 
 def test_workspace_size_rejects(L):
