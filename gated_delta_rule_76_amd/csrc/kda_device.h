@@ -71,6 +71,29 @@ struct Raw4<float> {
   }
 };
 
+// Two consecutive elements (4 bytes for bf16, 8 for fp32).
+template <typename T>
+struct Raw2;
+
+template <>
+struct Raw2<__bf16> {
+  uint32_t u;
+  __device__ __forceinline__ void load(const __bf16 *p) { u = *reinterpret_cast<const uint32_t *>(p); }
+  __device__ __forceinline__ void to_f32(float (&x)[2]) const {
+    x[0] = __uint_as_float(u << 16);
+    x[1] = __uint_as_float(u & 0xffff0000u);
+  }
+};
+
+template <>
+struct Raw2<float> {
+  float2 a;
+  __device__ __forceinline__ void load(const float *p) { a = *reinterpret_cast<const float2 *>(p); }
+  __device__ __forceinline__ void to_f32(float (&x)[2]) const {
+    x[0] = a.x; x[1] = a.y;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // 16x16 output tiles on the matrix cores.
 //

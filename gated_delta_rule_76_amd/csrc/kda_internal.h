@@ -15,10 +15,11 @@ constexpr int kChunk = KDA_CHUNK;  // tokens per prefill chunk
 
 // Per chunk and head the prefill keeps one record of matrix-core operand
 // fragments in the workspace (written by the chunk-local phase, streamed by
-// the state pass): -T Khat and Qhat (64 x d, as 4 x d/32 fragments each),
-// Ktil^T (d x 64, d/16 x 2 fragments), T and M (64 x 64, 4 x 2 fragments
-// each) and Gamma_C (d floats).  A fragment is 2 KiB: one 16x32 operand block
-// as 64 lanes x 8 values, stored either as bf16 hi/lo planes or as fp32.
+// the state pass): Khat and Qhat (64 x d, as 4 x d/32 fragments each),
+// Ktil^T T (d x 64, d/16 x 2 fragments), the six non-zero fragments of the
+// lower-triangular M T (64 x 64) and Gamma_C (d floats).  A fragment is
+// 2 KiB: one 16x32 operand block as 64 lanes x 8 values, stored either as
+// bf16 hi/lo planes or as fp32.
 constexpr size_t kFragBytes = 2048;
 constexpr size_t kWorkspaceAlign = 256;
 
@@ -26,7 +27,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline int frag_kblocks(int d) { return (d < 32 ? 32 : d) / 32; }
 inline size_t record_frags(int d) {
-  return (size_t)(4 * frag_kblocks(d) * 2 + (d / 16) * 2 + 16);
+  return (size_t)(4 * frag_kblocks(d) * 2 + (d / 16) * 2 + 6);
 }
 inline size_t record_bytes(int d) {
   return align_up(record_frags(d) * kFragBytes + sizeof(float) * (size_t)d, kWorkspaceAlign);

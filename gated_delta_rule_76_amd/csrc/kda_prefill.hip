@@ -235,7 +235,8 @@ __device__ __forceinline__ int find_seq(const int32_t *base, int N, int64_t c) {
 
 // ---------------------------------------------------------------------------
 // Chunk records: per (chunk, head), operand fragments in the order the state
-// pass consumes them.  A fragment is one 16-row x 32-column operand block of
+// pass consumes them.  Records are head-major (record h * max_chunks + c), so
+// the chunks one state-pass workgroup walks through are contiguous in memory.  A fragment is one 16-row x 32-column operand block of
 // the matrix-core product (lane 16g+m holds row m, columns 8g..8g+7), 2 KiB:
 // for SplitBF16 the bf16 hi plane (lane l at byte 16 l) then the lo plane
 // (at 1024 + 16 l); for F32 eight floats per lane (at byte 32 l).
@@ -313,15 +314,16 @@ template <int D>
 struct Rec {
   static constexpr int NKB = (D < 32 ? 32 : D) / 32;  // k-blocks over key channels
   static constexpr int NTILE = D / 16;                 // 16-row tiles of key channels
-  static constexpr int WNEG = 0;                       // -T Khat     [row tile w][kb]
-  static constexpr int QHAT = 4 * NKB;                 // Qhat        [w][kb]
-  static constexpr int KTIL = 8 * NKB;                 // Ktil^T      [channel tile t][kb of tokens]
-  static constexpr int TMAT = 8 * NKB + 2 * NTILE;     // T           [w][kb]
-  static constexpr int MMAT = TMAT + 8;                // M           [w][kb]
-  static constexpr int NFRAG = MMAT + 8;
+  static constexpr int KHAT = 0;                       // Khat        [row tile][kb]
+  static constexpr int QHAT = 4 * NKB;                 // Qhat        [row tile][kb]
+  static constexpr int PMAT = 8 * NKB;                 // Ktil^T T    [channel tile][kb of tokens]
+  static constexpr int MTM = 8 * NKB + 2 * NTILE;      // M T         non-zero [row tile][kb], 6 blocks
+  static constexpr int NFRAG = MTM + 6;
   static constexpr size_t GAM = (size_t)NFRAG * kFragBytes;  // Gamma_C (D floats)
   static constexpr size_t BYTES = (GAM + sizeof(float) * D + kWorkspaceAlign - 1) / kWorkspaceAlign *
                                   kWorkspaceAlign;
+  // M T is lower triangular: row tiles 0 and 1 have k-block 0 only.
+  __device__ __forceinline__ static int mt_frag(int rt, int kb) { return rt < 2 ? rt : 2 * rt - 2 + kb; }
 };
 
 // ---------------------------------------------------------------------------
@@ -372,9 +374,10 @@ struct PrepLds {
     Plane<P, 16, Cf::PW> e0a, e0b, e1;             // block 0 rows x bt1, x bt1 bt2; block 1 x bt2
   };
   struct Out {
-    float qn[C * (Cf::DK + 4)];                    // token-major fp32: Qhat, then -T Khat
-    Plane<P, D, C> kt;                             // Khat^T, then Ktil^T (rows = channels)
+    float qn[C * (Cf::DK + 4)];                    // token-major fp32: Qhat, then Khat
+    Plane<P, D, C> kt;                             // Ktil^T (rows = channels), then Ktil^T T in fp32
   };
+  static_assert(sizeof(Plane<P, D, C>) >= sizeof(float) * D * (C + 4), "Ktil^T T staging");
   static constexpr size_t U = sizeof(Gram) > sizeof(Out) ? sizeof(Gram) : sizeof(Out);
 };
 
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
   const ChunkTok ct = chunk_tokens(sstart, slen, c - base[n], total_tokens);
   const int64_t t0 = ct.t0;
   const int nvalid = ct.valid;
-  char *rec = recs + ((size_t)c * H + h) * Rc::BYTES;
+  char *rec = recs + ((size_t)h * max_chunks + c) * Rc::BYTES;
 
   // ---- P1: loads (unconditional 16-byte vector loads, clamped rows) ----------
   const int cgl = lane % CGR, tgl = lane / CGR;
@@ -689,20 +692,10 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
   }
 
   // ---- P7: records ------------------------------------------------------------------
-  // T = X Diag(beta) and M fragments (row tile = wave).
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    float xt[8], xm[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = kb * 32 + 8 * g + j;
-      xt[j] = s_X[(16 * wave + m) * MP + col] * s_beta[col];
-      xm[j] = s_M[(16 * wave + m) * MP + col];
-    }
-    IO::store(rec + (size_t)(Rc::TMAT + 2 * wave + kb) * kFragBytes, lane, xt);
-    IO::store(rec + (size_t)(Rc::MMAT + 2 * wave + kb) * kFragBytes, lane, xm);
-  }
-  // Qhat (token-major, fp32) and Khat^T (channel-major, operand form) to LDS.
+  // T = X Diag(beta) is lower triangular; the products Ktil^T T and M T use
+  // its column tile ct against token k-block kb only where that block meets
+  // rows >= 16 ct: (ct, kb) in {(0,0), (0,1), (1,0), (1,1), (2,1), (3,1)}.
+  // Qhat (token-major, fp32) and Ktil^T (channel-major, operand form) to LDS.
   if constexpr (DK > D) {
     for (int e = tid; e < C * (DK - D); e += NT) O.qn[(e / (DK - D)) * QP + D + e % (DK - D)] = 0.f;
   }
@@ -711,7 +704,7 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     for (int i = 0; i < TPG; ++i) {
       float xq[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) xq[j] = before[j] * bp[i][j] * qv[i][j];
+      for (int j = 0; j < 8; ++j) xq[j] = before[j] * bp[i][j] * qv[i][j];  // Gamma_r q_r
       *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl]) = make_float4(xq[0], xq[1], xq[2], xq[3]);
       *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl + 4]) = make_float4(xq[4], xq[5], xq[6], xq[7]);
     }
@@ -719,7 +712,7 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     for (int j = 0; j < 8; ++j) {
       float xk[TPG];
 #pragma unroll
-      for (int i = 0; i < TPG; ++i) xk[i] = before[j] * bp[i][j] * kv[i][j];  // Gamma_r k_r
+      for (int i = 0; i < TPG; ++i) xk[i] = bs[i][j] * after[j] * kv[i][j];  // (Gamma_C / Gamma_r) k_r
       O.kt.template store_run<TPG>(8 * cgl + j, r0, xk);
     }
   }
@@ -734,40 +727,90 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
     IO::store(rec + (size_t)(Rc::QHAT + Rc::NKB * wave + kb) * kFragBytes, lane, x);
   }
-  // -T Khat for row tile = wave: A = T rows (from s_X, beta applied), B = Khat^T.
-  f32x4 wn[Rc::NTILE];
+  // T as a B operand for the six (ct, kb) blocks: rows kb*32 + 8g + j, column 16 ct + m.
+  typename P::Frag tb[6];
 #pragma unroll
-  for (int t = 0; t < Rc::NTILE; ++t) wn[t] = zero4();
+  for (int u = 0; u < 6; ++u) {
+    const int ct = u < 4 ? u >> 1 : u - 2, kb = u < 4 ? u & 1 : 1;
+    const float bc = s_beta[16 * ct + m];
+    float x[8];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    if (kb <= (wave >> 1)) {  // T is lower triangular
-      float x[8];
+    for (int j = 0; j < 8; ++j) x[j] = s_X[(kb * 32 + 8 * g + j) * MP + 16 * ct + m] * bc;
+    tb[u] = P::make(x);
+  }
+  // Ktil^T T for channel tiles wave, wave + 4 (all four column tiles).
+  constexpr int PT = (Rc::NTILE + 3) / 4;
+  f32x4 pacc[PT][4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = kb * 32 + 8 * g + j;
-        x[j] = -s_X[(16 * wave + m) * MP + col] * s_beta[col];
+  for (int tt = 0; tt < PT; ++tt) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) pacc[tt][ct] = zero4();
+    const int t = wave + 4 * tt;
+    if (t < Rc::NTILE) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const auto A = O.kt.load8(16 * t + m, kb * 32 + 8 * g);
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          const int ct = u < 4 ? u >> 1 : u - 2, ukb = u < 4 ? u & 1 : 1;
+          if (ukb == kb) P::mma(pacc[tt][ct], A, tb[u]);
+        }
       }
-      const auto A = P::make(x);
-#pragma unroll
-      for (int t = 0; t < Rc::NTILE; ++t) P::mma(wn[t], A, O.kt.load8(16 * t + m, kb * 32 + 8 * g));
     }
   }
-  __syncthreads();  // Qhat fragments read, Khat^T consumed
+  // M T for row tile wave: column tiles ct <= wave, k-blocks ct/2 .. wave/2.
+  f32x4 macc[4];
 #pragma unroll
-  for (int t = 0; t < Rc::NTILE; ++t) {
+  for (int ct = 0; ct < 4; ++ct) macc[ct] = zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) O.qn[(16 * wave + 4 * g + i) * QP + 16 * t + m] = wn[t][i];
+  for (int kb = 0; kb < 2; ++kb) {
+    if (kb <= (wave >> 1)) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = s_M[(16 * wave + m) * MP + kb * 32 + 8 * g + j];
+      const auto A = P::make(x);
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        const int ct = u < 4 ? u >> 1 : u - 2, ukb = u < 4 ? u & 1 : 1;
+        if (ukb == kb && ct <= wave) P::mma(macc[ct], A, tb[u]);
+      }
+    }
   }
-  if (act) {  // Ktil^T into the channel-major plane
+  __syncthreads();  // Qhat and Ktil^T consumed
+  // Khat (token-major) into qn; Ktil^T T (channel-major fp32) over the kt
+  // plane; M T into s_L (its strictly upper blocks stay zero from the start).
+  float *pm = reinterpret_cast<float *>(&O.kt);
+  constexpr int PP = C + 4;
+  if (act) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float xk[TPG];
+    for (int i = 0; i < TPG; ++i) {
+      float xk[8];
 #pragma unroll
-      for (int i = 0; i < TPG; ++i) xk[i] = bs[i][j] * after[j] * kv[i][j];  // (Gamma_C / Gamma_r) k_r
-      O.kt.template store_run<TPG>(8 * cgl + j, r0, xk);
+      for (int j = 0; j < 8; ++j) xk[j] = before[j] * bp[i][j] * kv[i][j];  // Gamma_r k_r
+      *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl]) = make_float4(xk[0], xk[1], xk[2], xk[3]);
+      *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl + 4]) = make_float4(xk[4], xk[5], xk[6], xk[7]);
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < PT; ++tt) {
+    const int t = wave + 4 * tt;
+    if (t < Rc::NTILE) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm[(16 * t + 4 * g + i) * PP + 16 * ct + m] = pacc[tt][ct][i];
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    if (ct <= wave) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_L[(16 * wave + 4 * g + i) * MP + 16 * ct + m] = macc[ct][i];
     }
   }
   __syncthreads();
+  // Khat, Ktil^T T and M T fragments; Gamma_C.
 #pragma unroll
   for (int kb = 0; kb < Rc::NKB; ++kb) {
     float x[8];
@@ -775,15 +818,30 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     const float4 u1 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g + 4]);
     x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
     x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-    IO::store(rec + (size_t)(Rc::WNEG + Rc::NKB * wave + kb) * kFragBytes, lane, x);
+    IO::store(rec + (size_t)(Rc::KHAT + Rc::NKB * wave + kb) * kFragBytes, lane, x);
   }
 #pragma unroll
-  for (int tt = 0; tt < (Rc::NTILE + 3) / 4; ++tt) {
+  for (int tt = 0; tt < PT; ++tt) {
     const int t = wave + 4 * tt;
     if (t < Rc::NTILE) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        IO::store_frag(rec + (size_t)(Rc::KTIL + 2 * t + kb) * kFragBytes, lane, O.kt.load8(16 * t + m, kb * 32 + 8 * g));
+      for (int kb = 0; kb < 2; ++kb) {
+        float x[8];
+        const float4 u0 = *reinterpret_cast<const float4 *>(&pm[(16 * t + m) * PP + kb * 32 + 8 * g]);
+        const float4 u1 = *reinterpret_cast<const float4 *>(&pm[(16 * t + m) * PP + kb * 32 + 8 * g + 4]);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+        IO::store(rec + (size_t)(Rc::PMAT + 2 * t + kb) * kFragBytes, lane, x);
+      }
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if (kb <= (wave >> 1)) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = s_L[(16 * wave + m) * MP + kb * 32 + 8 * g + j];
+      IO::store(rec + (size_t)(Rc::MTM + Rc::mt_frag(wave, kb)) * kFragBytes, lane, x);
     }
   }
   if (wave == 0 && act && tgl == 0) {
@@ -797,79 +855,104 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
 
 // ---------------------------------------------------------------------------
 // chunk_state_kernel: the sequential pass over the chunks of one sequence for
-// one head and 16 value columns, streaming the chunk records.
+// one head and 16 value columns, streaming the records.
 //
-// Per chunk, with S the 128x16 state slice (fp32 accumulators across chunks)
-// and wave w owning chunk rows 16w..16w+15 and state row tiles w, w+4:
-//   W = T V + (-T Khat) S               (rows of this wave)
-//   O = Qhat S                          (rows of this wave)
-//   --- W of every wave to LDS; barrier ---
-//   O += M W;  o <- O
-//   S <- Diag(Gamma_C) S + Ktil^T W     (this wave's state tiles; to LDS)
+// Eight waves; wave w has row tile rt = w mod 4 (chunk rows 16 rt..+15) and
+// owns state row tile w.  Waves 0-3 ("U waves") and 4-7 ("O waves") split
+// the two products with S.  Per chunk, with S the d x 16 state slice (fp32
+// accumulators, kept across chunks):
+//   U waves:  U = V - Khat S       (their row tile; to LDS in operand form)
+//   O waves:  O = Qhat S
 //   --- barrier ---
-// The record fragments of chunk c+1 are loaded into the other register set
-// while chunk c computes (the loop is unrolled by two so no copy sits between
-// a load and its use).  V is staged into LDS transposed, one chunk ahead.
+//   all:      S <- Diag(Gamma_C) S + (Ktil^T T) U     (state tile w; to LDS)
+//   O waves:  o = O + (M T) U
+//   --- barrier ---
+// Each record fragment is read by one wave of the workgroup.  The record of
+// chunk c+1 is loaded into the other register set while chunk c computes
+// (the loop is unrolled by two so no copy sits between a load and its use).
 //
 // blockIdx -> work: consecutive workgroups are dealt round-robin to the 8
-// XCDs, so the D/16 workgroups of one (sequence, head) get block indices
+// XCDs, so the d/16 workgroups of one (sequence, head) get block indices
 // congruent mod 8: they share an XCD and its L2, and every record is fetched
 // from HBM once for all of them.
 // ---------------------------------------------------------------------------
+template <int D>
+struct ScanCfg {
+  static constexpr int NW = 8;                   // waves per workgroup
+  static constexpr int NTH = 64 * NW;
+  static constexpr int VW = 16;                  // value columns per workgroup
+  static constexpr int G = D / VW;               // workgroups per (sequence, head)
+  static constexpr int NKB = Rec<D>::NKB;
+  static constexpr int NTILE = Rec<D>::NTILE;    // state row tiles
+  static_assert(NTILE <= NW, "shape");
+};
+
 template <int D, typename TIn>
 struct ScanBuf {
-  static constexpr int NKB = Rec<D>::NKB;
-  static constexpr int TPW = (Rec<D>::NTILE + 3) / 4;
-  Raw4<TIn> v;
-  FragRaw wneg[NKB], qhat[NKB], ktil[TPW][2], tm[2], mm[2];
-  float4 gam[TPW];
+  using Cf = ScanCfg<D>;
+  TIn v[4];                 // U waves: V rows 16 rt + 4 g + i, column m
+  FragRaw mt[2];            // O waves: M T, row tile rt
+  FragRaw a[Cf::NKB];       // Khat (U waves) or Qhat (O waves), row tile rt
+  FragRaw p[2];             // Ktil^T T, state tile = wave
+  float4 gam;               // Gamma_C, rows of state tile = wave
+  uint32_t tch;             // one word of a record two chunks ahead
 };
 
 template <int D, typename TIn, typename P>
 __device__ __forceinline__ void load_scan_buf(ScanBuf<D, TIn> &B, const char *rec, const TIn *v,
                                               int64_t vt0, int valid, int64_t total, int h, int H,
-                                              int col0, int tid, int wave, int lane) {
+                                              int col0, int wave, int lane, int rot) {
+  using Cf = ScanCfg<D>;
   using Rc = Rec<D>;
   using IO = FragIO<P>;
-  B.v.load(v + (load_token(vt0, tid >> 2, valid, total) * H + h) * D + col0 + 4 * (tid & 3));
+  const int rt = wave & 3, g = lane >> 4, m = lane & 15;
+  if (wave < 4) {
 #pragma unroll
-  for (int kb = 0; kb < Rc::NKB; ++kb) {
-    IO::load(B.wneg[kb], rec + (size_t)(Rc::WNEG + Rc::NKB * wave + kb) * kFragBytes, lane);
-    IO::load(B.qhat[kb], rec + (size_t)(Rc::QHAT + Rc::NKB * wave + kb) * kFragBytes, lane);
+    for (int i = 0; i < 4; ++i) B.v[i] = v[(load_token(vt0, 16 * rt + 4 * g + i, valid, total) * H + h) * D + col0 + m];
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int f = Rc::mt_frag(rt, rt < 2 ? 0 : kb);  // row tiles 0, 1: the k-block 0 block twice
+      IO::load(B.mt[kb], rec + (size_t)(Rc::MTM + f) * kFragBytes, lane);
+    }
   }
+  // The workgroups of one head read the same record at the same time; each
+  // starts at a different k-block (register slot kk holds k-block
+  // (kk + rot) mod NKB).
+  const int abase = wave < 4 ? Rc::KHAT : Rc::QHAT;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    IO::load(B.tm[kb], rec + (size_t)(Rc::TMAT + 2 * wave + kb) * kFragBytes, lane);
-    IO::load(B.mm[kb], rec + (size_t)(Rc::MMAT + 2 * wave + kb) * kFragBytes, lane);
+  for (int kk = 0; kk < Cf::NKB; ++kk) {
+    const int kb = (kk + rot) % Cf::NKB;
+    IO::load(B.a[kk], rec + (size_t)(abase + Cf::NKB * rt + kb) * kFragBytes, lane);
   }
-  const int g = lane >> 4;
+  const int t = wave < Cf::NTILE ? wave : Cf::NTILE - 1;
 #pragma unroll
-  for (int u = 0; u < ScanBuf<D, TIn>::TPW; ++u) {
-    const int t0 = wave + 4 * u, t = t0 < Rc::NTILE ? t0 : Rc::NTILE - 1;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      IO::load(B.ktil[u][kb], rec + (size_t)(Rc::KTIL + 2 * t + kb) * kFragBytes, lane);
-    B.gam[u] = *reinterpret_cast<const float4 *>(rec + Rc::GAM + sizeof(float) * (16 * t + 4 * g));
-  }
+  for (int kb = 0; kb < 2; ++kb) IO::load(B.p[kb], rec + (size_t)(Rc::PMAT + 2 * t + kb) * kFragBytes, lane);
+  B.gam = *reinterpret_cast<const float4 *>(rec + Rc::GAM + sizeof(float) * (16 * t + 4 * g));
 }
 
+// Two waves per SIMD: the two register sets of record fragments take about
+// half of each wave's 256 registers.
 template <int D, typename TIn, typename P>
-__global__ __launch_bounds__(NT) void chunk_state_kernel(
+__global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_state_kernel(
     const TIn *__restrict__ v, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
     int64_t total_tokens, int64_t max_chunks, const int32_t *__restrict__ base,
     const char *__restrict__ recs, const float *__restrict__ S0, float *__restrict__ o,
     float *__restrict__ S_T) {
+  using Cf = ScanCfg<D>;
   using Rc = Rec<D>;
   using IO = FragIO<P>;
   using Buf = ScanBuf<D, TIn>;
-  constexpr int G = D / 16, DK = D < 32 ? 32 : D, NKB = Rc::NKB, NTILE = Rc::NTILE, TPW = Buf::TPW;
+  constexpr int VW = Cf::VW, G = Cf::G, NKB = Cf::NKB, NTILE = Cf::NTILE, NTH = Cf::NTH;
+  constexpr int DK = D < 32 ? 32 : D;
 
-  __shared__ Plane<P, 16, DK> Sop;     // S^T in operand form (rows = value columns)
-  __shared__ Plane<P, 16, C> Wop;      // W^T in operand form
-  __shared__ Plane<P, 16, C> Vt[2];    // V^T of this chunk / the next
+  __shared__ Plane<P, VW, DK> Sop;     // S^T in operand form (rows = value columns)
+  __shared__ Plane<P, VW, C> Uop;      // U^T in operand form
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = wave & 3;
+  const bool uwave = wave < 4;
   const int m = lane & 15, g = lane >> 4;
 
   const int id = blockIdx.x;
@@ -878,23 +961,17 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
   const int cg = within % G;
   if (pair >= (int64_t)N * H) return;
   const int n = (int)(pair / H), h = (int)(pair % H);
-  const int col0 = 16 * cg;
-  const int rbase = 16 * wave;
+  const int col0 = VW * cg;
 
   if constexpr (DK > D) {
-    for (int e = tid; e < 16 * (DK - D); e += NT) Sop.store(e / (DK - D), D + e % (DK - D), 0.f);
+    for (int e = tid; e < VW * (DK - D); e += NTH) Sop.store(e / (DK - D), D + e % (DK - D), 0.f);
   }
-  f32x4 sreg[TPW];
+  f32x4 sreg = zero4();
   const float *S0p = S0 ? S0 + (size_t)pair * D * D : nullptr;
+  if (wave < NTILE) {
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = wave + 4 * u;
-    sreg[u] = zero4();
-    if (t < NTILE) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sreg[u][i] = S0p ? S0p[(size_t)(16 * t + 4 * g + i) * D + col0 + m] : 0.f;
-      Sop.store4(m, 16 * t + 4 * g, sreg[u]);
-    }
+    for (int i = 0; i < 4; ++i) sreg[i] = S0p ? S0p[(size_t)(16 * wave + 4 * g + i) * D + col0 + m] : 0.f;
+    Sop.store4(m, 16 * wave + 4 * g, sreg);
   }
 
   int64_t sstart, slen;
@@ -904,79 +981,82 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
   if (cend > max_chunks) cend = max_chunks;
   if (total_tokens <= 0) cend = cbeg;
 
-  auto rec_of = [&](int64_t cc) { return recs + ((size_t)cc * H + h) * Rc::BYTES; };
-  auto stage_v = [&](const Buf &B, int slot, int valid) {
-    float vv[4];
-    B.v.to_f32(vv);
-    const int r = tid >> 2;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Vt[slot].store(4 * (tid & 3) + j, r, r < valid ? vv[j] : 0.f);
+  auto rec_of = [&](int64_t cc) __attribute__((always_inline)) { return recs + ((size_t)h * max_chunks + cc) * Rc::BYTES; };
+  // The workgroups of a head split the cache lines of the record two chunks
+  // ahead and each reads one word per line, so that the record is in L2 by
+  // the time all of them load it in full.
+  constexpr int NLINE = (int)(Rc::BYTES / 128);
+  constexpr int LPG = (NLINE + G - 1) / G;
+  auto touch = [&](int64_t cc) __attribute__((always_inline)) {
+    const int li = cg * LPG + tid % LPG;
+    return *reinterpret_cast<const uint32_t *>(rec_of(cc) + 128 * (li < NLINE ? li : NLINE - 1));
   };
+  uint32_t sink = 0;
 
   Buf bufA, bufB;
-  auto prefetch = [&](int64_t cc, Buf &B) {
+  auto prefetch = [&](int64_t cc, Buf &B) __attribute__((always_inline)) {
     const ChunkTok cn = chunk_tokens(sstart, slen, cc - cbeg, total_tokens);
-    load_scan_buf<D, TIn, P>(B, rec_of(cc), v, cn.t0, cn.valid, total_tokens, h, H, col0, tid, wave, lane);
+    load_scan_buf<D, TIn, P>(B, rec_of(cc), v, cn.t0, cn.valid, total_tokens, h, H, col0, wave, lane, cg);
   };
 
-  auto process = [&](int64_t c, const Buf &U, Buf &Nx, int64_t cn) {
+  auto process = [&](int64_t c, const Buf &U, Buf &Nx, int64_t cn) __attribute__((always_inline)) {
     const ChunkTok ct = chunk_tokens(sstart, slen, c - cbeg, total_tokens);
-    const int slot = (int)((c - cbeg) & 1);
     prefetch(cn, Nx);  // unconditional (the last chunk re-reads itself)
+    Nx.tch = touch(cn + 1 < cend ? cn + 1 : cn);
 
-    // W = T V + (-T Khat) S;  O = Qhat S
-    f32x4 wv = zero4(), ws = zero4(), ov = zero4();
+    // Khat S (U waves) or Qhat S (O waves) for row tile rt.
+    f32x4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (kb <= (wave >> 1)) mma_exact_b(wv, IO::frag(U.tm[kb]), Vt[slot].load8(m, kb * 32 + 8 * g));
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kk = 0; kk < NKB; ++kk) {
+      const int kb = (kk + cg) % NKB;  // the k-block held in register slot kk
       const auto Bs = Sop.load8(m, kb * 32 + 8 * g);
-      P::mma(ws, IO::frag(U.wneg[kb]), Bs);
-      P::mma(ov, IO::frag(U.qhat[kb]), Bs);
+      P::mma((kk & 1) ? acc1 : acc0, IO::frag(U.a[kk]), Bs);
     }
-    f32x4 w;
+    f32x4 ov;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = wv[i] + ws[i];
-    Wop.store4(m, rbase + 4 * g, w);
+    for (int i = 0; i < 4; ++i) ov[i] = acc0[i] + acc1[i];
+    if (uwave) {
+      f32x4 u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        u[i] = (r < ct.valid ? to_f32(U.v[i]) : 0.f) - ov[i];
+      }
+      Uop.store4(m, 16 * rt + 4 * g, u);
+    }
     __syncthreads();
 
-    // O += M W
+    // U as an operand: rows kb*32 + 8g .. +7 of column m.
+    const auto u0 = Uop.load8(m, 8 * g);
+    const auto u1 = Uop.load8(m, 32 + 8 * g);
+    // S <- Diag(Gamma_C) S + (Ktil^T T) U
+    if (wave < NTILE) {
+      const float gm[4] = {U.gam.x, U.gam.y, U.gam.z, U.gam.w};
+      f32x4 acc;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (kb <= (wave >> 1)) P::mma(ov, IO::frag(U.mm[kb]), Wop.load8(m, kb * 32 + 8 * g));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rbase + 4 * g + i;
-      if (r < ct.valid) o[((ct.t0 + r) * H + h) * D + col0 + m] = ov[i];
+      for (int i = 0; i < 4; ++i) acc[i] = gm[i] * sreg[i];
+      P::mma(acc, IO::frag(U.p[0]), u0);
+      P::mma(acc, IO::frag(U.p[1]), u1);
+      sreg = acc;
+      Sop.store4(m, 16 * wave + 4 * g, acc);
     }
-    // S <- Diag(Gamma_C) S + Ktil^T W
+    // o = Qhat S + (M T) U
+    if (!uwave) {
+      P::mma(ov, IO::frag(U.mt[0]), u0);
+      if (rt >= 2) P::mma(ov, IO::frag(U.mt[1]), u1);
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = wave + 4 * u;
-      if (t < NTILE) {
-        f32x4 acc;
-        const float gm[4] = {U.gam[u].x, U.gam[u].y, U.gam[u].z, U.gam[u].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = gm[i] * sreg[u][i];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          P::mma(acc, IO::frag(U.ktil[u][kb]), Wop.load8(m, kb * 32 + 8 * g));
-        sreg[u] = acc;
-        Sop.store4(m, 16 * t + 4 * g, acc);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        if (r < ct.valid) o[((ct.t0 + r) * H + h) * D + col0 + m] = ov[i];
       }
     }
-    {  // V of the next chunk into the other slot
-      const ChunkTok cnt = chunk_tokens(sstart, slen, cn - cbeg, total_tokens);
-      stage_v(Nx, slot ^ 1, cn == c ? 0 : cnt.valid);
-    }
+    sink += U.tch;
     __syncthreads();
   };
 
   if (cbeg < cend) {
     prefetch(cbeg, bufA);
-    const ChunkTok c0 = chunk_tokens(sstart, slen, 0, total_tokens);
-    stage_v(bufA, 0, c0.valid);
+    bufA.tch = touch(cbeg);
   }
   __syncthreads();
   for (int64_t c = cbeg; c < cend; c += 2) {
@@ -984,17 +1064,12 @@ __global__ __launch_bounds__(NT) void chunk_state_kernel(
     if (c + 1 >= cend) break;
     process(c + 1, bufB, bufA, c + 2 < cend ? c + 2 : c + 1);
   }
+  if (N < 0) o[sink & 1] = 0.f;  // never taken (N >= 0): keeps the touches alive
 
-  if (S_T != nullptr) {
+  if (S_T != nullptr && wave < NTILE) {
     float *STp = S_T + (size_t)pair * D * D;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = wave + 4 * u;
-      if (t < NTILE) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) STp[(size_t)(16 * t + 4 * g + i) * D + col0 + m] = sreg[u][i];
-      }
-    }
+    for (int i = 0; i < 4; ++i) STp[(size_t)(16 * wave + 4 * g + i) * D + col0 + m] = sreg[i];
   }
 }
 
@@ -1003,7 +1078,6 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
                             const float *alpha, const float *beta, const int32_t *cu,
                             const float *S0, float *o, float *S_T, void *workspace,
                             hipStream_t stream, int phases) {
-  static_assert(Rec<D>::BYTES == 0 || true, "");
   char *ws = static_cast<char *>(workspace);
   int32_t *base = reinterpret_cast<int32_t *>(ws);
   char *recs = ws + schedule_bytes(s);
@@ -1025,8 +1099,9 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   }
   if (phases & kPhaseState) {
     const int64_t pairs = (int64_t)N * H;
-    const int64_t blocks = (pairs + 7) / 8 * 8 * (D / 16);
-    hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P>), dim3((unsigned)blocks), dim3(NT), 0, stream, vp, cu,
+    const int64_t blocks = (pairs + 7) / 8 * 8 * ScanCfg<D>::G;
+    hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P>), dim3((unsigned)blocks), dim3(ScanCfg<D>::NTH), 0, stream,
+                       vp, cu,
                        s.seq_len, N, H, s.total_tokens, mc, base, recs, S0, o, S_T);
     e = hipGetLastError();
   }

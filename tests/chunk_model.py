@@ -111,8 +111,37 @@ def chunk_state_step(S, k, q, v, alpha, T, M, round_operand=_ident):
     return O, S_new
 
 
-def chunked_prefill(q, k, v, alpha, beta, S0=None, round_operand=_ident):
-    """One head, one sequence: q, k, alpha [T, d], v [T, dv], beta [T]."""
+def chunk_products(k, alpha, T, M, round_operand=_ident):
+    """The chunk-local products of the re-associated state step:
+    P = Ktil^T T (d x 64) and MT = M T (64 x 64, lower triangular), each
+    formed from rounded operands and rounded once more as stored."""
+    suf = np.ones_like(alpha)
+    for r in range(C - 2, -1, -1):
+        suf[r] = suf[r + 1] * alpha[r + 1]
+    Tr = round_operand(T)
+    P = round_operand(round_operand(suf * k).T @ Tr)
+    MT = round_operand(round_operand(M) @ Tr)
+    return P, MT
+
+
+def chunk_state_step_reassociated(S, k, q, v, alpha, P, MT, round_operand=_ident):
+    """One chunk of the state pass in the re-associated form the kernels use:
+    U = V - Khat S, O = Qhat S + (M T) U, S_new = Diag(Gamma_C) S + (Ktil^T T) U
+    (W = T U is never formed)."""
+    gam = np.cumprod(alpha, axis=0)
+    Khat = round_operand(gam * k)
+    Qhat = round_operand(gam * q)
+    Sr = round_operand(S)
+    U = round_operand(v - Khat @ Sr)
+    O = Qhat @ Sr + MT @ U
+    S_new = gam[-1][:, None] * S + P @ U
+    return O, S_new
+
+
+def chunked_prefill(q, k, v, alpha, beta, S0=None, round_operand=_ident, form="wy"):
+    """One head, one sequence: q, k, alpha [T, d], v [T, dv], beta [T].
+    ``form`` picks the state step: "wy" (W = T (V - Khat S)) or
+    "reassociated" (U = V - Khat S with the products Ktil^T T and M T)."""
     T_len, d = k.shape
     dv = v.shape[1]
     S = np.zeros((d, dv)) if S0 is None else np.array(S0, dtype=np.float64)
@@ -123,6 +152,10 @@ def chunked_prefill(q, k, v, alpha, beta, S0=None, round_operand=_ident):
         kc, qc, vc = pad(k, 0.0), pad(q, 0.0), pad(v, 0.0)
         ac, bc = pad(alpha, 1.0), pad(beta, 0.0)
         T, M, _ = chunk_local(kc, qc, ac, bc, round_operand)
-        O, S = chunk_state_step(S, kc, qc, vc, ac, T, M, round_operand)
+        if form == "wy":
+            O, S = chunk_state_step(S, kc, qc, vc, ac, T, M, round_operand)
+        else:
+            P, MT = chunk_products(kc, ac, T, M, round_operand)
+            O, S = chunk_state_step_reassociated(S, kc, qc, vc, ac, P, MT, round_operand)
         o[c0:c0 + n] = O[:n]
     return o, S

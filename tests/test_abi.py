@@ -73,11 +73,11 @@ def test_workspace_size_formula(N, T, H, d):
     sched = ((4 * (N + 1) + 255) // 256) * 256
     chunks = (N * T) // 64 + N
     nkb = max(d, 32) // 32
-    frags = 4 * nkb * 2 + (d // 16) * 2 + 16          # -T Khat, Qhat, Ktil^T, T, M
+    frags = 4 * nkb * 2 + (d // 16) * 2 + 6           # Khat, Qhat, Ktil^T T, M T
     record = -(-(frags * 2048 + 4 * d) // 256) * 256   # + Gamma_C, 256-byte aligned
     assert need == sched + chunks * H * record
     if d == 128:
-        assert record == 131584                          # 128.5 KiB per chunk and head
+        assert record == 111104                          # 108.5 KiB per chunk and head
 
 
 def test_workspace_size_rejects(L):
