@@ -898,32 +898,39 @@ struct ScanBuf {
   uint32_t tch;             // one word of a record two chunks ahead
 };
 
+// Loads of one record, in two groups issued in the two phases of the
+// previous chunk: the row-tile operands (group 0) and the rest (group 1).
 template <int D, typename TIn, typename P>
-__device__ __forceinline__ void load_scan_buf(ScanBuf<D, TIn> &B, const char *rec, const TIn *v,
-                                              int64_t vt0, int valid, int64_t total, int h, int H,
-                                              int col0, int wave, int lane, int rot) {
+__device__ __forceinline__ void load_scan_a(ScanBuf<D, TIn> &B, int kk, const char *rec, int wave, int lane,
+                                            int rot) {
   using Cf = ScanCfg<D>;
   using Rc = Rec<D>;
-  using IO = FragIO<P>;
-  const int rt = wave & 3, g = lane >> 4, m = lane & 15;
-  if (wave < 4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) B.v[i] = v[(load_token(vt0, 16 * rt + 4 * g + i, valid, total) * H + h) * D + col0 + m];
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int f = Rc::mt_frag(rt, rt < 2 ? 0 : kb);  // row tiles 0, 1: the k-block 0 block twice
-      IO::load(B.mt[kb], rec + (size_t)(Rc::MTM + f) * kFragBytes, lane);
-    }
-  }
   // The workgroups of one head read the same record at the same time; each
   // starts at a different k-block (register slot kk holds k-block
   // (kk + rot) mod NKB).
+  const int rt = wave & 3;
   const int abase = wave < 4 ? Rc::KHAT : Rc::QHAT;
+  const int kb = (kk + rot) % Cf::NKB;
+  FragIO<P>::load(B.a[kk], rec + (size_t)(abase + Cf::NKB * rt + kb) * kFragBytes, lane);
+}
+
+template <int D, typename TIn, typename P>
+__device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec, const TIn *v,
+                                            int64_t vt0, int valid, int64_t total, int h, int H,
+                                            int col0, int wave, int lane) {
+  using Cf = ScanCfg<D>;
+  using Rc = Rec<D>;
+  using IO = FragIO<P>;
+  // Both roles issue the same loads (V is used by the U waves, M T by the
+  // O waves; the partner wave of the same row tile reads the same M T lines):
+  // no branch separates the loads, so none of them has to be waited for early.
+  const int rt = wave & 3, g = lane >> 4, m = lane & 15;
 #pragma unroll
-  for (int kk = 0; kk < Cf::NKB; ++kk) {
-    const int kb = (kk + rot) % Cf::NKB;
-    IO::load(B.a[kk], rec + (size_t)(abase + Cf::NKB * rt + kb) * kFragBytes, lane);
+  for (int i = 0; i < 4; ++i) B.v[i] = v[(load_token(vt0, 16 * rt + 4 * g + i, valid, total) * H + h) * D + col0 + m];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int f = Rc::mt_frag(rt, rt < 2 ? 0 : kb);  // row tiles 0, 1: the k-block 0 block twice
+    IO::load(B.mt[kb], rec + (size_t)(Rc::MTM + f) * kFragBytes, lane);
   }
   const int t = wave < Cf::NTILE ? wave : Cf::NTILE - 1;
 #pragma unroll
@@ -987,22 +994,26 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   // the time all of them load it in full.
   constexpr int NLINE = (int)(Rc::BYTES / 128);
   constexpr int LPG = (NLINE + G - 1) / G;
+  // (threads past the workgroup's share repeat its first line, so each line
+  // costs one request)
   auto touch = [&](int64_t cc) __attribute__((always_inline)) {
-    const int li = cg * LPG + tid % LPG;
+    const int li = cg * LPG + (tid < LPG ? tid : 0);
     return *reinterpret_cast<const uint32_t *>(rec_of(cc) + 128 * (li < NLINE ? li : NLINE - 1));
   };
   uint32_t sink = 0;
 
   Buf bufA, bufB;
-  auto prefetch = [&](int64_t cc, Buf &B) __attribute__((always_inline)) {
+  auto prefetch_b = [&](int64_t cc, Buf &B) __attribute__((always_inline)) {
     const ChunkTok cn = chunk_tokens(sstart, slen, cc - cbeg, total_tokens);
-    load_scan_buf<D, TIn, P>(B, rec_of(cc), v, cn.t0, cn.valid, total_tokens, h, H, col0, wave, lane, cg);
+    load_scan_b<D, TIn, P>(B, rec_of(cc), v, cn.t0, cn.valid, total_tokens, h, H, col0, wave, lane);
   };
 
+  // The loads of the next record are spread over this chunk's two phases,
+  // between its matrix-core products, so that each wave keeps computing
+  // while its loads queue.
   auto process = [&](int64_t c, const Buf &U, Buf &Nx, int64_t cn) __attribute__((always_inline)) {
     const ChunkTok ct = chunk_tokens(sstart, slen, c - cbeg, total_tokens);
-    prefetch(cn, Nx);  // unconditional (the last chunk re-reads itself)
-    Nx.tch = touch(cn + 1 < cend ? cn + 1 : cn);
+    const char *rn = rec_of(cn);  // unconditional (the last chunk re-reads itself)
 
     // Khat S (U waves) or Qhat S (O waves) for row tile rt.
     f32x4 acc0 = zero4(), acc1 = zero4();
@@ -1011,7 +1022,11 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
       const int kb = (kk + cg) % NKB;  // the k-block held in register slot kk
       const auto Bs = Sop.load8(m, kb * 32 + 8 * g);
       P::mma((kk & 1) ? acc1 : acc0, IO::frag(U.a[kk]), Bs);
+      __builtin_amdgcn_sched_barrier(0);
+      load_scan_a<D, TIn, P>(Nx, kk, rn, wave, lane, cg);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    Nx.tch = touch(cn + 1 < cend ? cn + 1 : cn);
     f32x4 ov;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = acc0[i] + acc1[i];
@@ -1044,6 +1059,11 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     if (!uwave) {
       P::mma(ov, IO::frag(U.mt[0]), u0);
       if (rt >= 2) P::mma(ov, IO::frag(U.mt[1]), u1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch_b(cn, Nx);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!uwave) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
@@ -1055,7 +1075,9 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   };
 
   if (cbeg < cend) {
-    prefetch(cbeg, bufA);
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) load_scan_a<D, TIn, P>(bufA, kk, rec_of(cbeg), wave, lane, cg);
+    prefetch_b(cbeg, bufA);
     bufA.tch = touch(cbeg);
   }
   __syncthreads();
