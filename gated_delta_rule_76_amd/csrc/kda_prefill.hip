@@ -107,6 +107,18 @@ struct alignas(16) Plane<SplitBF16, ROWS, COLS> {
     f.lo = *reinterpret_cast<const bf16x8 *>(&lo[r * PITCH + c]);
     return f;
   }
+  // Columns c0 + 4g .. +3 and c0 + 16 + 4g .. +3 of row r: the k-order of
+  // fragments written from matrix-core accumulators.
+  __device__ __forceinline__ SplitBF16::Frag load_acc_order(int r, int c0, int g) const {
+    const bf16x4 h0 = *reinterpret_cast<const bf16x4 *>(&hi[r * PITCH + c0 + 4 * g]);
+    const bf16x4 h1 = *reinterpret_cast<const bf16x4 *>(&hi[r * PITCH + c0 + 16 + 4 * g]);
+    const bf16x4 l0 = *reinterpret_cast<const bf16x4 *>(&lo[r * PITCH + c0 + 4 * g]);
+    const bf16x4 l1 = *reinterpret_cast<const bf16x4 *>(&lo[r * PITCH + c0 + 16 + 4 * g]);
+    SplitBF16::Frag f;
+    f.hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+  }
 };
 
 template <int ROWS, int COLS>
@@ -136,6 +148,17 @@ struct alignas(16) Plane<F32, ROWS, COLS> {
     F32::Frag fr;
     const f32x4 a = *reinterpret_cast<const f32x4 *>(&f[r * PITCH + c]);
     const f32x4 b = *reinterpret_cast<const f32x4 *>(&f[r * PITCH + c + 4]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      fr.v[j] = a[j];
+      fr.v[4 + j] = b[j];
+    }
+    return fr;
+  }
+  __device__ __forceinline__ F32::Frag load_acc_order(int r, int c0, int g) const {
+    F32::Frag fr;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(&f[r * PITCH + c0 + 4 * g]);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(&f[r * PITCH + c0 + 16 + 4 * g]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       fr.v[j] = a[j];
@@ -329,82 +352,138 @@ struct Rec {
 // ---------------------------------------------------------------------------
 // chunk_local_kernel: every operand of one chunk and head, computed once.
 //
-// Wave w holds 16-token block w in registers (lane: TPG consecutive tokens,
-// 8 consecutive key channels).  Decay factors are running products of alpha:
-// inside a lane, across the block's lanes (shuffles) and across blocks (one
-// LDS exchange of the four block totals).
+// Lane layout: wave w holds token block w (16 tokens) in the matrix-core
+// operand layout, lane 16 g + m holding token 16 w + m and channels
+// kb*32 + 8g .. +7 of every k-block kb (32 channels at d = 128).  The Gram
+// operands of the wave's own block and the Khat and Qhat fragments of the
+// record are therefore formed in registers and written without passing
+// through LDS.
 //
-// Gram tiles (R, J), J <= R, of A and M over key channels, per channel:
-//   Gamma_r / Gamma_j = bp_r bs_j prod_{J<b<R} bt_b      (J < R)
-//                     = bp_r / bp_j                      (J = R, j <= r)
-// with bp the product from the block start to r, bs the product after j to
-// the block end, bt block totals; the in-between block totals are folded
-// into the B operand (three extra row blocks).  1/bp is used only when every
-// channel's block total is >= 2^-100; otherwise the block's diagonal tiles
-// are recomputed directly from running products of alpha.
+// Decay factors, per channel, as running products of alpha:
+//   bp_r   product over the block up to and including token r
+//   bs_r   product over the block after token r
+//   bt_b   block totals; before / after = products of the totals of the
+//          blocks before / after w
+//   Gamma_r = before bp_r,   Gamma_C / Gamma_r = bs_r after.
+// The in-block products are scans across the 16 lanes m of a row (DPP).
 //
-// Then L = I + Diag(beta) A, X = L^-1 (blocked forward substitution in fp32),
-// T = X Diag(beta), -T Khat on the matrix cores, and every operand is written
-// to the record as fragments.
+// Gram tiles (R, J <= R) of A (k against k) and M (q against k):
+//   Gamma_r / Gamma_j = bp_r bs_j prod_{J<b<R} bt_b   (J < R)
+//                     = bp_r / bp_j                   (J = R, j <= r)
+// Wave R forms row block R from its A operands k bp and q bp and the B
+// operands of block J: its own k / bp for J = R, else k bs times the
+// in-between block totals, written to LDS by wave J.  1/bp is used only when
+// every channel's block total is >= 2^-100; otherwise the block's diagonal
+// tiles are recomputed directly.
+//
+// Then L = I + Diag(beta) A and X = L^-1 (diagonal blocks by forward
+// substitution, the others by 16 x 16 block products on the fp32 matrix
+// cores), T = X Diag(beta), and (Ktil^T T)^T = T^T Ktil and (M T)^T = T^T M^T
+// on the matrix cores.  Their accumulators are written as operand fragments
+// directly: lane (g, m) of output tiles 2kb and 2kb+1 holds row m at token
+// columns 32kb + 4g + i and 32kb + 16 + 4g + i, which is the k-order the
+// state pass uses for U.
 // ---------------------------------------------------------------------------
+
+// In-place products within 16-lane rows: x_m <- x_{m -/+ s} x_m.  Lanes whose
+// source falls outside the row are disabled by the DPP operation and keep x.
+// (The s_nop covers the wait states a DPP read needs after a VALU write.)
+#define KDA_DPP_MUL4(CTRL, a, b, c, d)            \
+  asm volatile("s_nop 1\n"                        \
+               "v_mul_f32_dpp %0, %0, %0 " CTRL "\n" \
+               "v_mul_f32_dpp %1, %1, %1 " CTRL "\n" \
+               "v_mul_f32_dpp %2, %2, %2 " CTRL "\n" \
+               "v_mul_f32_dpp %3, %3, %3 " CTRL "\n" \
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d))
+
+// Inclusive prefix (y) and suffix (z) products across the 16 lanes of a row,
+// for eight channels.
+__device__ __forceinline__ void row_scans8(float (&y)[8], float (&z)[8]) {
+  KDA_DPP_MUL4("row_shr:1", y[0], y[1], y[2], y[3]);
+  KDA_DPP_MUL4("row_shr:1", y[4], y[5], y[6], y[7]);
+  KDA_DPP_MUL4("row_shl:1", z[0], z[1], z[2], z[3]);
+  KDA_DPP_MUL4("row_shl:1", z[4], z[5], z[6], z[7]);
+  KDA_DPP_MUL4("row_shr:2", y[0], y[1], y[2], y[3]);
+  KDA_DPP_MUL4("row_shr:2", y[4], y[5], y[6], y[7]);
+  KDA_DPP_MUL4("row_shl:2", z[0], z[1], z[2], z[3]);
+  KDA_DPP_MUL4("row_shl:2", z[4], z[5], z[6], z[7]);
+  KDA_DPP_MUL4("row_shr:4", y[0], y[1], y[2], y[3]);
+  KDA_DPP_MUL4("row_shr:4", y[4], y[5], y[6], y[7]);
+  KDA_DPP_MUL4("row_shl:4", z[0], z[1], z[2], z[3]);
+  KDA_DPP_MUL4("row_shl:4", z[4], z[5], z[6], z[7]);
+  KDA_DPP_MUL4("row_shr:8", y[0], y[1], y[2], y[3]);
+  KDA_DPP_MUL4("row_shr:8", y[4], y[5], y[6], y[7]);
+  KDA_DPP_MUL4("row_shl:8", z[0], z[1], z[2], z[3]);
+  KDA_DPP_MUL4("row_shl:8", z[4], z[5], z[6], z[7]);
+}
+
+// x_m <- z_{m+1} within each row, 1 for the last lane (exclusive suffix).
+__device__ __forceinline__ void row_next8(float (&x)[8], const float (&z)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 1.f;
+  asm volatile("s_nop 1\n"
+               "v_mov_b32_dpp %0, %8 row_shl:1\n"
+               "v_mov_b32_dpp %1, %9 row_shl:1\n"
+               "v_mov_b32_dpp %2, %10 row_shl:1\n"
+               "v_mov_b32_dpp %3, %11 row_shl:1\n"
+               "v_mov_b32_dpp %4, %12 row_shl:1\n"
+               "v_mov_b32_dpp %5, %13 row_shl:1\n"
+               "v_mov_b32_dpp %6, %14 row_shl:1\n"
+               "v_mov_b32_dpp %7, %15 row_shl:1\n"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
+               : "v"(z[0]), "v"(z[1]), "v"(z[2]), "v"(z[3]), "v"(z[4]), "v"(z[5]), "v"(z[6]), "v"(z[7]));
+}
+
 template <int D>
-struct PrepCfg {
-  static constexpr int CGR = D / 8;                               // 8-channel groups per token
-  static constexpr int LPB = (64 / CGR) < 16 ? 64 / CGR : 16;     // token lanes per block
-  static constexpr int TPG = 16 / LPB;                            // tokens per lane
-  static constexpr int ACT = CGR * LPB;                           // active lanes per wave
+struct LocCfg {
   static constexpr int DK = D < 32 ? 32 : D;
-  static constexpr int PW = DK < 64 ? DK : 64;                    // channels per Gram pass
-  static constexpr int NPASS = DK / PW;
-  static constexpr int MP = C + 1;
-  static_assert(ACT <= 64 && LPB * TPG == 16, "lane layout");
+  static constexpr int NKB = DK / 32;
+  static constexpr int MP = C + 1;   // pitch of s_X (fp32)
+  static constexpr int LP = C + 4;   // pitch of s_L and s_M (fp32, 16-byte rows)
+  static constexpr int KP = DK + 4;  // pitch of the token-major Ktil staging (fp32)
+  // B-operand planes: k bs of blocks 0, 1, 2; block 0 times bt1 and times
+  // bt1 bt2; block 1 times bt2.
+  static constexpr int NPLANE = 6;
+  static constexpr size_t GRAM = (size_t)2 * NPLANE * kFragBytes;  // one k-block, double-buffered
+  static constexpr size_t LM = sizeof(float) * (2 * C * LP + 4 * 256);  // s_L, s_M, per-wave Y
+  static constexpr size_t KT = sizeof(float) * C * KP;
+  static constexpr size_t U = GRAM > LM ? (GRAM > KT ? GRAM : KT) : (LM > KT ? LM : KT);
 };
 
-// Tiles per wave (5 each): waves 0/1 take block-row 3 plus tile (0,0) of
-// A / M, waves 2/3 take block-rows 2 and 1 of A / M.
-__device__ __forceinline__ int tile_R(int tsel, int t) { return tsel == 0 ? (t < 4 ? 3 : 0) : (t < 3 ? 2 : 1); }
-__device__ __forceinline__ int tile_J(int tsel, int t) { return tsel == 0 ? (t < 4 ? t : 0) : (t < 3 ? t : t - 3); }
+// Plane holding the B operand of Gram tile (R, J < R).
+__device__ __forceinline__ int gram_plane(int R, int J) {
+  return R - J == 1 ? J : (R - J == 2 ? (J == 0 ? 3 : 5) : 4);
+}
 
-template <int D, typename P>
-struct PrepLds {
-  using Cf = PrepCfg<D>;
-  // Gram pass (region G) and output staging (region O) share one buffer.
-  struct Gram {
-    Plane<P, C, Cf::PW> ka, qa, kb, ki;           // k bp, q bp, k bs, k / bp  (rows = tokens)
-    Plane<P, 16, Cf::PW> e0a, e0b, e1;             // block 0 rows x bt1, x bt1 bt2; block 1 x bt2
-  };
-  struct Out {
-    float qn[C * (Cf::DK + 4)];                    // token-major fp32: Qhat, then Khat
-    Plane<P, D, C> kt;                             // Ktil^T (rows = channels), then Ktil^T T in fp32
-  };
-  static_assert(sizeof(Plane<P, D, C>) >= sizeof(float) * D * (C + 4), "Ktil^T T staging");
-  static constexpr size_t U = sizeof(Gram) > sizeof(Out) ? sizeof(Gram) : sizeof(Out);
-};
+// T^T as an A operand for column tile ct and token k-block kb, for the six
+// (ct, kb) blocks where T (lower triangular) can be non-zero.
+__device__ __forceinline__ int tb_ct(int u) { return u < 4 ? u >> 1 : u - 2; }
+__device__ __forceinline__ int tb_kb(int u) { return u < 4 ? u & 1 : 1; }
 
 template <int D, typename TIn, typename P>
-__global__ __launch_bounds__(NT) void chunk_local_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void chunk_local_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ alpha,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
     int64_t total_tokens, int64_t max_chunks, const int32_t *__restrict__ base, char *__restrict__ recs) {
-  using Cf = PrepCfg<D>;
+  using Cf = LocCfg<D>;
   using Rc = Rec<D>;
-  using L = PrepLds<D, P>;
   using IO = FragIO<P>;
-  constexpr int CGR = Cf::CGR, LPB = Cf::LPB, TPG = Cf::TPG, DK = Cf::DK, PW = Cf::PW, MP = Cf::MP;
-  constexpr int QP = DK + 4;  // pitch of qn
+  using Frag = typename P::Frag;
+  constexpr int DK = Cf::DK, NKB = Cf::NKB, MP = Cf::MP, LP = Cf::LP, KP = Cf::KP;
 
-  __shared__ __attribute__((aligned(16))) char s_u[L::U];
-  __shared__ float s_L[C * MP], s_M[C * MP], s_X[C * MP];
-  __shared__ float s_Y[3 * 16 * 17];
+  __shared__ __attribute__((aligned(16))) char s_u[Cf::U];  // Gram planes; then L, M, Y; then Ktil
+  __shared__ float s_X[C * MP];
+  __shared__ __attribute__((aligned(16))) float s_bt[4 * DK];
   __shared__ float s_beta[C];
-  __shared__ __attribute__((aligned(16))) float s_bt[4 * D];
   __shared__ int s_flag[4];
-  auto &G = *reinterpret_cast<typename L::Gram *>(s_u);
-  auto &O = *reinterpret_cast<typename L::Out *>(s_u);
+  float *s_L = reinterpret_cast<float *>(s_u);
+  float *s_M = s_L + C * LP;
+  float *s_kt = reinterpret_cast<float *>(s_u);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
+  float *s_Yw = s_M + C * LP + 256 * wave;
   const int64_t c = (int64_t)(blockIdx.x / H);
   const int h = blockIdx.x % H;
   const int64_t nchunks = base[N] < max_chunks ? (int64_t)base[N] : max_chunks;
@@ -417,206 +496,158 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
   const int nvalid = ct.valid;
   char *rec = recs + ((size_t)h * max_chunks + c) * Rc::BYTES;
 
-  // ---- P1: loads (unconditional 16-byte vector loads, clamped rows) ----------
-  const int cgl = lane % CGR, tgl = lane / CGR;
-  const bool act = lane < Cf::ACT;
-  const int r0 = 16 * wave + TPG * tgl;  // first token row of this lane
-  Raw8<TIn> kr[TPG], qr[TPG];
-  float4 ar0[TPG], ar1[TPG];
-  if (act) {
+  // ---- loads: token 16 w + m, channels kb*32 + 8g .. +7 (rows past the
+  // chunk and channels past d are padding: k = q = 0, alpha = 1) ------------
+  const int r = 16 * wave + m;
+  const bool rv = r < nvalid;
+  const int64_t tok = load_token(t0, r, nvalid, total_tokens);
+  Raw8<TIn> kr[NKB], qr[NKB];
+  float4 ar0[NKB], ar1[NKB];
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      const int64_t off = (load_token(t0, r0 + i, nvalid, total_tokens) * H + h) * D + 8 * cgl;
-      kr[i].load(k + off);
-      qr[i].load(q + off);
-      ar0[i] = *reinterpret_cast<const float4 *>(alpha + off);
-      ar1[i] = *reinterpret_cast<const float4 *>(alpha + off + 4);
-    }
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int ch = kb * 32 + 8 * g;
+    const int64_t off = (tok * H + h) * D + (ch < D ? ch : 0);
+    kr[kb].load(k + off);
+    qr[kb].load(q + off);
+    ar0[kb] = *reinterpret_cast<const float4 *>(alpha + off);
+    ar1[kb] = *reinterpret_cast<const float4 *>(alpha + off + 4);
   }
+  for (int e = tid; e < C * MP; e += NT) s_X[e] = 0.f;
   if (tid < C) {
     const float bv = beta[load_token(t0, tid, nvalid, total_tokens) * H + h];
     s_beta[tid] = tid < nvalid ? bv : 0.f;
   }
-  for (int e = tid; e < C * MP; e += NT) {
-    s_L[e] = 0.f;
-    s_M[e] = 0.f;
-    s_X[e] = 0.f;
-  }
-  if (tid < 4) s_flag[tid] = 0;
 
-  // ---- P2: block-local decay products ----------------------------------------
-  float kv[TPG][8], qv[TPG][8], bp[TPG][8], bs[TPG][8], bt[8];
+  // ---- in-block decay products -------------------------------------------------
+  float bp[NKB][8], bs[NKB][8];
   bool tiny = false;
-  if (act) {
-    float av[TPG][8], lt[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lt[j] = 1.f;
+  for (int kb = 0; kb < NKB; ++kb) {
+    const bool ok = rv && kb * 32 + 8 * g < D;
+    const float a[8] = {ar0[kb].x, ar0[kb].y, ar0[kb].z, ar0[kb].w, ar1[kb].x, ar1[kb].y, ar1[kb].z, ar1[kb].w};
+    float z[8];
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      const bool ok = r0 + i < nvalid;
-      kr[i].to_f32(kv[i]);
-      qr[i].to_f32(qv[i]);
-      const float a[8] = {ar0[i].x, ar0[i].y, ar0[i].z, ar0[i].w, ar1[i].x, ar1[i].y, ar1[i].z, ar1[i].w};
+    for (int j = 0; j < 8; ++j) bp[kb][j] = z[j] = ok ? a[j] : 1.f;
+    row_scans8(bp[kb], z);
+    row_next8(bs[kb], z);
+    if (m == 15) {
+      *reinterpret_cast<float4 *>(&s_bt[wave * DK + kb * 32 + 8 * g]) =
+          make_float4(bp[kb][0], bp[kb][1], bp[kb][2], bp[kb][3]);
+      *reinterpret_cast<float4 *>(&s_bt[wave * DK + kb * 32 + 8 * g + 4]) =
+          make_float4(bp[kb][4], bp[kb][5], bp[kb][6], bp[kb][7]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        av[i][j] = ok ? a[j] : 1.f;
-        kv[i][j] = ok ? kv[i][j] : 0.f;
-        qv[i][j] = ok ? qv[i][j] : 0.f;
-        lt[j] *= av[i][j];
-        bp[i][j] = lt[j];  // prefix inside the lane, completed below
-      }
+      for (int j = 0; j < 8; ++j) tiny = tiny || !(bp[kb][j] >= kTinyBlock);
     }
-    float y[8], z[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = z[j] = lt[j];
-#pragma unroll
-    for (int st = 1; st < LPB; st <<= 1) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float u = __shfl_up(y[j], CGR * st);
-        const float d = __shfl_down(z[j], CGR * st);
-        if (tgl >= st) y[j] *= u;
-        if (tgl + st < LPB) z[j] *= d;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float u = __shfl_up(y[j], CGR);
-      const float d = __shfl_down(z[j], CGR);
-      const float ex = tgl >= 1 ? u : 1.f;       // earlier lanes of the block
-      const float sx = tgl + 1 < LPB ? d : 1.f;  // later lanes of the block
-      bt[j] = __shfl(y[j], (LPB - 1) * CGR + cgl);
-      float suf = sx;
-#pragma unroll
-      for (int i = TPG - 1; i >= 0; --i) {
-        bs[i][j] = suf;  // product after token i to the block end
-        suf *= av[i][j];
-        bp[i][j] *= ex;  // product from the block start to token i
-      }
-      tiny = tiny || !(bt[j] >= kTinyBlock);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bt[j] = 1.f;
   }
   const bool block_tiny = __ballot(tiny) != 0;
-  if (lane == 0 && block_tiny) s_flag[wave] = 1;
-  if (act && tgl == 0) {
-    *reinterpret_cast<float4 *>(&s_bt[wave * D + 8 * cgl]) = make_float4(bt[0], bt[1], bt[2], bt[3]);
-    *reinterpret_cast<float4 *>(&s_bt[wave * D + 8 * cgl + 4]) = make_float4(bt[4], bt[5], bt[6], bt[7]);
-  }
+  if (lane == 0) s_flag[wave] = block_tiny ? 1 : 0;
   __syncthreads();
 
-  // ---- P3: factors from the other blocks ---------------------------------------
-  float before[8], after[8], bt1[8], bt2[8];
+  // ---- operands and Gram tiles, one k-block at a time --------------------------------
+  // Registers: the A operands k bp and q bp and the diagonal B operand k / bp
+  // of this block; Khat, Qhat to the record; k bs (times block totals) to the
+  // Gram planes of the k-block (double-buffered); Ktil kept for the last step.
+  // Wave R accumulates row block R of A and M.
+  f32x4 aacc[4], macc[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) before[j] = after[j] = bt1[j] = bt2[j] = 1.f;
-  if (act) {
+  for (int J = 0; J < 4; ++J) aacc[J] = macc[J] = zero4();
+  float ktl[NKB][8];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    char *pl = s_u + (size_t)(kb & 1) * Cf::NPLANE * kFragBytes;
+    const int cb = kb * 32 + 8 * g;
+    float tv[4][8];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float4 u0 = *reinterpret_cast<const float4 *>(&s_bt[b * D + 8 * cgl]);
-      const float4 u1 = *reinterpret_cast<const float4 *>(&s_bt[b * D + 8 * cgl + 4]);
-      const float tv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      const float4 u0 = *reinterpret_cast<const float4 *>(&s_bt[b * DK + cb]);
+      const float4 u1 = *reinterpret_cast<const float4 *>(&s_bt[b * DK + cb + 4]);
+      tv[b][0] = u0.x; tv[b][1] = u0.y; tv[b][2] = u0.z; tv[b][3] = u0.w;
+      tv[b][4] = u1.x; tv[b][5] = u1.y; tv[b][6] = u1.z; tv[b][7] = u1.w;
+    }
+    float bef[8], aft[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (b < wave) before[j] *= tv[j];
-        if (b > wave) after[j] *= tv[j];
-        if (b == 1) bt1[j] = tv[j];
-        if (b == 2) bt2[j] = tv[j];
+    for (int j = 0; j < 8; ++j) {
+      bef[j] = aft[j] = 1.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b < wave) bef[j] *= tv[b][j];
+        if (b > wave) aft[j] *= tv[b][j];
+      }
+    }
+    const bool ok = rv && cb < D;
+    float kf[8], qf[8];
+    kr[kb].to_f32(kf);
+    qr[kb].to_f32(qf);
+    float xa[8], xq[8], x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      kf[j] = ok ? kf[j] : 0.f;
+      qf[j] = ok ? qf[j] : 0.f;
+      xa[j] = kf[j] * bp[kb][j];
+      xq[j] = qf[j] * bp[kb][j];
+    }
+    const Frag ka = P::make(xa);
+    const Frag qa = P::make(xq);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = xa[j] * bef[j];  // Gamma_r k_r
+    IO::store(rec + (size_t)(Rc::KHAT + NKB * wave + kb) * kFragBytes, lane, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = xq[j] * bef[j];  // Gamma_r q_r
+    IO::store(rec + (size_t)(Rc::QHAT + NKB * wave + kb) * kFragBytes, lane, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = block_tiny ? 0.f : kf[j] * __builtin_amdgcn_rcpf(bp[kb][j]);
+    const Frag ki = P::make(x);
+    float xb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xb[j] = kf[j] * bs[kb][j];
+      ktl[kb][j] = xb[j] * aft[j];  // (Gamma_C / Gamma_r) k_r
+    }
+    if (wave <= 2) IO::store_frag(pl + (size_t)wave * kFragBytes, lane, P::make(xb));
+    if (wave == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = xb[j] * tv[1][j];
+      IO::store_frag(pl + (size_t)3 * kFragBytes, lane, P::make(x));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] *= tv[2][j];
+      IO::store_frag(pl + (size_t)4 * kFragBytes, lane, P::make(x));
+      if (m == 0 && cb < D) {  // Gamma_C
+        float *gam = reinterpret_cast<float *>(rec + Rc::GAM);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = tv[0][j] * tv[1][j] * tv[2][j] * tv[3][j];
+        *reinterpret_cast<float4 *>(gam + cb) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4 *>(gam + cb + 4) = make_float4(x[4], x[5], x[6], x[7]);
+      }
+    } else if (wave == 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = xb[j] * tv[2][j];
+      IO::store_frag(pl + (size_t)5 * kFragBytes, lane, P::make(x));
+    }
+    __syncthreads();  // this k-block's planes are written (and the other buffer is free)
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J < wave) {
+        FragRaw raw;
+        IO::load(raw, pl + (size_t)gram_plane(wave, J) * kFragBytes, lane);
+        const Frag B = IO::frag(raw);
+        P::mma(aacc[J], ka, B);
+        P::mma(macc[J], qa, B);
+      } else if (J == wave) {
+        P::mma(aacc[J], ka, ki);
+        P::mma(macc[J], qa, ki);
       }
     }
   }
+  __syncthreads();  // Gram planes consumed: the region now holds L, M, Y
 
-  // ---- P4: decayed Gram tiles on the matrix cores ----------------------------
-  const int tsel = wave >> 1;
-  const bool isM = (wave & 1) != 0;
-  f32x4 acc[5];
+  // L = I + Diag(beta) A (strictly lower part) and M (lower), row block wave.
 #pragma unroll
-  for (int t = 0; t < 5; ++t) acc[t] = zero4();
-#pragma unroll
-  for (int p = 0; p < Cf::NPASS; ++p) {
-    if constexpr (DK > D) {  // channels past D are zero in every operand
-      for (int e = tid; e < C * (DK - D); e += NT) {
-        const int r = e / (DK - D), cc = D + e % (DK - D);
-        G.ka.store(r, cc, 0.f);
-        G.qa.store(r, cc, 0.f);
-        G.kb.store(r, cc, 0.f);
-        G.ki.store(r, cc, 0.f);
-        if (r < 16) {
-          G.e0a.store(r, cc, 0.f);
-          G.e0b.store(r, cc, 0.f);
-          G.e1.store(r, cc, 0.f);
-        }
-      }
-    }
-    const int c8 = 8 * cgl - p * PW;
-    if (act && c8 >= 0 && c8 < PW) {
-#pragma unroll
-      for (int i = 0; i < TPG; ++i) {
-        float xa[8], xq[8], xb[8], xi[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xa[j] = kv[i][j] * bp[i][j];
-          xq[j] = qv[i][j] * bp[i][j];
-          xb[j] = kv[i][j] * bs[i][j];
-          xi[j] = block_tiny ? 0.f : kv[i][j] * __builtin_amdgcn_rcpf(bp[i][j]);
-        }
-        const int r = r0 + i;
-        G.ka.store8(r, c8, xa);
-        G.qa.store8(r, c8, xq);
-        G.kb.store8(r, c8, xb);
-        G.ki.store8(r, c8, xi);
-        if (wave == 0) {
-          float x1[8], x2[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            x1[j] = xb[j] * bt1[j];
-            x2[j] = x1[j] * bt2[j];
-          }
-          G.e0a.store8(r, c8, x1);
-          G.e0b.store8(r, c8, x2);
-        } else if (wave == 1) {
-          float x1[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x1[j] = xb[j] * bt2[j];
-          G.e1.store8(r - 16, c8, x1);
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 5; ++t) {
-      const int R = tile_R(tsel, t), J = tile_J(tsel, t);
-#pragma unroll
-      for (int kb = 0; kb < PW / 32; ++kb) {
-        const int col = kb * 32 + 8 * g;
-        const auto A = isM ? G.qa.load8(16 * R + m, col) : G.ka.load8(16 * R + m, col);
-        typename P::Frag B;
-        if (J == R)
-          B = G.ki.load8(16 * J + m, col);
-        else if (J == R - 1)
-          B = G.kb.load8(16 * J + m, col);
-        else if (J == R - 2)
-          B = J == 0 ? G.e0a.load8(m, col) : G.e1.load8(m, col);
-        else
-          B = G.e0b.load8(m, col);
-        P::mma(acc[t], A, B);
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- P5: L = I + Diag(beta) A (strictly lower part) and M ----------------------
-#pragma unroll
-  for (int t = 0; t < 5; ++t) {
-    const int R = tile_R(tsel, t), J = tile_J(tsel, t);
+  for (int J = 0; J < 4; ++J) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * R + 4 * g + i, j = 16 * J + m;
-      if (isM)
-        s_M[r * MP + j] = (j <= r) ? acc[t][i] : 0.f;
-      else
-        s_L[r * MP + j] = (j < r) ? acc[t][i] * s_beta[r] : 0.f;
+      const int rr = 16 * wave + 4 * g + i, jj = 16 * J + m;
+      s_L[rr * LP + jj] = (J <= wave && jj < rr) ? aacc[J][i] * s_beta[rr] : 0.f;
+      s_M[rr * LP + jj] = (J <= wave && jj <= rr) ? macc[J][i] : 0.f;
     }
   }
   __syncthreads();
@@ -627,13 +658,13 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
   for (int b = 0; b < 4; ++b) {
     if (s_flag[b] == 0) continue;  // uniform across the workgroup
     if (tid < 136) {
-      int r = 0, rem = tid;
-      while (rem > r) {  // pair index -> (r, j), j <= r, within the block
-        rem -= r + 1;
-        ++r;
+      int rl = 0, rem = tid;
+      while (rem > rl) {  // pair index -> (r, j), j <= r, within the block
+        rem -= rl + 1;
+        ++rl;
       }
-      const int j = rem;
-      const int rr = 16 * b + r, jj = 16 * b + j;
+      const int jl = rem;
+      const int rr = 16 * b + rl, jj = 16 * b + jl;
       float a_acc = 0.f, m_acc = 0.f;
       if (rr < nvalid && jj < nvalid) {
         for (int ch = 0; ch < D; ++ch) {
@@ -645,13 +676,13 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
           m_acc += to_f32(q[orr]) * kj;
         }
       }
-      s_L[rr * MP + jj] = (j < r) ? a_acc * s_beta[rr] : 0.f;
-      s_M[rr * MP + jj] = m_acc;
+      s_L[rr * LP + jj] = (jl < rl) ? a_acc * s_beta[rr] : 0.f;
+      s_M[rr * LP + jj] = m_acc;
     }
     __syncthreads();
   }
 
-  // ---- P6: X = L^-1, blocked by 16 ---------------------------------------------
+  // ---- X = L^-1, blocked by 16 ---------------------------------------------------
   // Diagonal blocks: forward substitution, one column per lane (wave b
   // inverts block b).
   if (lane < 16) {
@@ -661,195 +692,123 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(
     for (int i = 0; i < 16; ++i) {
       float s = (i == jj) ? 1.f : 0.f;
 #pragma unroll
-      for (int t = 0; t < i; ++t) s -= s_L[(16 * b + i) * MP + 16 * b + t] * x[t];
+      for (int t = 0; t < i; ++t) s -= s_L[(16 * b + i) * LP + 16 * b + t] * x[t];
       x[i] = s;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) s_X[(16 * b + i) * MP + 16 * b + jj] = x[i];
   }
   __syncthreads();
-  // Off-diagonal blocks by distance d: X_IJ = -X_II sum_{K=J}^{I-1} L_IK X_KJ.
+  // Off-diagonal blocks by distance d, block (I, I - d) on wave I:
+  //   X_IJ = -X_II sum_{K=J}^{I-1} L_IK X_KJ      (fp32 matrix cores, k = 4s + g)
+#pragma unroll
   for (int d = 1; d < 4; ++d) {
-    const int nblk = 4 - d;
-    for (int e = tid; e < nblk * 256; e += NT) {
-      const int J = e >> 8, rr = (e >> 4) & 15, cc = e & 15, I = J + d;
-      float s = 0.f;
+    if (wave >= d) {
+      const int I = wave, J = wave - d;
+      f32x4 y = zero4();
       for (int K = J; K < I; ++K) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) s += s_L[(16 * I + rr) * MP + 16 * K + t] * s_X[(16 * K + t) * MP + 16 * J + cc];
+        for (int s = 0; s < 4; ++s)
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(s_L[(16 * I + m) * LP + 16 * K + 4 * s + g],
+                                                   s_X[(16 * K + 4 * s + g) * MP + 16 * J + m], y, 0, 0, 0);
       }
-      s_Y[(J * 16 + rr) * 17 + cc] = s;
-    }
-    __syncthreads();
-    for (int e = tid; e < nblk * 256; e += NT) {
-      const int J = e >> 8, rr = (e >> 4) & 15, cc = e & 15, I = J + d;
-      float s = 0.f;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) s += s_X[(16 * I + rr) * MP + 16 * I + t] * s_Y[(J * 16 + t) * 17 + cc];
-      s_X[(16 * I + rr) * MP + 16 * J + cc] = -s;
+      for (int i = 0; i < 4; ++i) s_Yw[(4 * g + i) * 16 + m] = y[i];
+      f32x4 xv = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        xv = __builtin_amdgcn_mfma_f32_16x16x4f32(s_X[(16 * I + m) * MP + 16 * I + 4 * s + g],
+                                                  s_Yw[(4 * s + g) * 16 + m], xv, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_X[(16 * I + 4 * g + i) * MP + 16 * J + m] = -xv[i];
     }
     __syncthreads();
   }
 
-  // ---- P7: records ------------------------------------------------------------------
-  // T = X Diag(beta) is lower triangular; the products Ktil^T T and M T use
-  // its column tile ct against token k-block kb only where that block meets
-  // rows >= 16 ct: (ct, kb) in {(0,0), (0,1), (1,0), (1,1), (2,1), (3,1)}.
-  // Qhat (token-major, fp32) and Ktil^T (channel-major, operand form) to LDS.
-  if constexpr (DK > D) {
-    for (int e = tid; e < C * (DK - D); e += NT) O.qn[(e / (DK - D)) * QP + D + e % (DK - D)] = 0.f;
-  }
-  if (act) {
-#pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      float xq[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xq[j] = before[j] * bp[i][j] * qv[i][j];  // Gamma_r q_r
-      *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl]) = make_float4(xq[0], xq[1], xq[2], xq[3]);
-      *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl + 4]) = make_float4(xq[4], xq[5], xq[6], xq[7]);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float xk[TPG];
-#pragma unroll
-      for (int i = 0; i < TPG; ++i) xk[i] = bs[i][j] * after[j] * kv[i][j];  // (Gamma_C / Gamma_r) k_r
-      O.kt.template store_run<TPG>(8 * cgl + j, r0, xk);
-    }
-  }
-  __syncthreads();
-  // Qhat fragments.
-#pragma unroll
-  for (int kb = 0; kb < Rc::NKB; ++kb) {
-    float x[8];
-    const float4 u0 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g]);
-    const float4 u1 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g + 4]);
-    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-    IO::store(rec + (size_t)(Rc::QHAT + Rc::NKB * wave + kb) * kFragBytes, lane, x);
-  }
-  // T as a B operand for the six (ct, kb) blocks: rows kb*32 + 8g + j, column 16 ct + m.
-  typename P::Frag tb[6];
+  // ---- records: (M T)^T and (Ktil^T T)^T -------------------------------------------
+  Frag tb[6];  // T^T: lane (g, m) holds T[kb*32 + 8g + j][16 ct + m]
 #pragma unroll
   for (int u = 0; u < 6; ++u) {
-    const int ct = u < 4 ? u >> 1 : u - 2, kb = u < 4 ? u & 1 : 1;
-    const float bc = s_beta[16 * ct + m];
+    const int cc = tb_ct(u), kb = tb_kb(u);
+    const float bc = s_beta[16 * cc + m];
     float x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = s_X[(kb * 32 + 8 * g + j) * MP + 16 * ct + m] * bc;
+    for (int j = 0; j < 8; ++j) x[j] = s_X[(kb * 32 + 8 * g + j) * MP + 16 * cc + m] * bc;
     tb[u] = P::make(x);
   }
-  // Ktil^T T for channel tiles wave, wave + 4 (all four column tiles).
-  constexpr int PT = (Rc::NTILE + 3) / 4;
-  f32x4 pacc[PT][4];
+  // (M T)^T for row tile wave: B = M^T, lane (g, m) holds M[16 w + m][kb*32 + 8g + j].
+  {
+    f32x4 acc[4];
 #pragma unroll
-  for (int tt = 0; tt < PT; ++tt) {
+    for (int cc = 0; cc < 4; ++cc) acc[cc] = zero4();
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) pacc[tt][ct] = zero4();
-    const int t = wave + 4 * tt;
-    if (t < Rc::NTILE) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const auto A = O.kt.load8(16 * t + m, kb * 32 + 8 * g);
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb <= (wave >> 1)) {
+        float x[8];
+        const float4 u0 = *reinterpret_cast<const float4 *>(&s_M[(16 * wave + m) * LP + kb * 32 + 8 * g]);
+        const float4 u1 = *reinterpret_cast<const float4 *>(&s_M[(16 * wave + m) * LP + kb * 32 + 8 * g + 4]);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+        const Frag Bm = P::make(x);
 #pragma unroll
         for (int u = 0; u < 6; ++u) {
-          const int ct = u < 4 ? u >> 1 : u - 2, ukb = u < 4 ? u & 1 : 1;
-          if (ukb == kb) P::mma(pacc[tt][ct], A, tb[u]);
+          if (tb_kb(u) == kb && tb_ct(u) <= wave) P::mma(acc[tb_ct(u)], tb[u], Bm);
         }
       }
     }
-  }
-  // M T for row tile wave: column tiles ct <= wave, k-blocks ct/2 .. wave/2.
-  f32x4 macc[4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) macc[ct] = zero4();
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb <= (wave >> 1)) {
+        float x[8];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    if (kb <= (wave >> 1)) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = s_M[(16 * wave + m) * MP + kb * 32 + 8 * g + j];
-      const auto A = P::make(x);
-#pragma unroll
-      for (int u = 0; u < 6; ++u) {
-        const int ct = u < 4 ? u >> 1 : u - 2, ukb = u < 4 ? u & 1 : 1;
-        if (ukb == kb && ct <= wave) P::mma(macc[ct], A, tb[u]);
+        for (int i = 0; i < 4; ++i) {
+          x[i] = acc[2 * kb][i];
+          x[4 + i] = acc[2 * kb + 1][i];
+        }
+        IO::store(rec + (size_t)(Rc::MTM + Rc::mt_frag(wave, kb)) * kFragBytes, lane, x);
       }
     }
   }
-  __syncthreads();  // Qhat and Ktil^T consumed
-  // Khat (token-major) into qn; Ktil^T T (channel-major fp32) over the kt
-  // plane; M T into s_L (its strictly upper blocks stay zero from the start).
-  float *pm = reinterpret_cast<float *>(&O.kt);
-  constexpr int PP = C + 4;
-  if (act) {
+  __syncthreads();  // L, M consumed: the region now holds Ktil (token-major)
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      float xk[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xk[j] = before[j] * bp[i][j] * kv[i][j];  // Gamma_r k_r
-      *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl]) = make_float4(xk[0], xk[1], xk[2], xk[3]);
-      *reinterpret_cast<float4 *>(&O.qn[(r0 + i) * QP + 8 * cgl + 4]) = make_float4(xk[4], xk[5], xk[6], xk[7]);
-    }
-  }
-#pragma unroll
-  for (int tt = 0; tt < PT; ++tt) {
-    const int t = wave + 4 * tt;
-    if (t < Rc::NTILE) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pm[(16 * t + 4 * g + i) * PP + 16 * ct + m] = pacc[tt][ct][i];
-      }
-    }
-  }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    if (ct <= wave) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_L[(16 * wave + 4 * g + i) * MP + 16 * ct + m] = macc[ct][i];
-    }
+  for (int kb = 0; kb < NKB; ++kb) {
+    *reinterpret_cast<float4 *>(&s_kt[r * KP + kb * 32 + 8 * g]) =
+        make_float4(ktl[kb][0], ktl[kb][1], ktl[kb][2], ktl[kb][3]);
+    *reinterpret_cast<float4 *>(&s_kt[r * KP + kb * 32 + 8 * g + 4]) =
+        make_float4(ktl[kb][4], ktl[kb][5], ktl[kb][6], ktl[kb][7]);
   }
   __syncthreads();
-  // Khat, Ktil^T T and M T fragments; Gamma_C.
-#pragma unroll
-  for (int kb = 0; kb < Rc::NKB; ++kb) {
-    float x[8];
-    const float4 u0 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g]);
-    const float4 u1 = *reinterpret_cast<const float4 *>(&O.qn[(16 * wave + m) * QP + kb * 32 + 8 * g + 4]);
-    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-    IO::store(rec + (size_t)(Rc::KHAT + Rc::NKB * wave + kb) * kFragBytes, lane, x);
-  }
+  // (Ktil^T T)^T for channel tiles wave, wave + 4: B = Ktil, lane (g, m)
+  // holds Ktil[kb*32 + 8g + j][16 t + m].
+  constexpr int PT = (Rc::NTILE + 3) / 4;
 #pragma unroll
   for (int tt = 0; tt < PT; ++tt) {
     const int t = wave + 4 * tt;
     if (t < Rc::NTILE) {
+      Frag Bk[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float x[8];
-        const float4 u0 = *reinterpret_cast<const float4 *>(&pm[(16 * t + m) * PP + kb * 32 + 8 * g]);
-        const float4 u1 = *reinterpret_cast<const float4 *>(&pm[(16 * t + m) * PP + kb * 32 + 8 * g + 4]);
-        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = s_kt[(kb * 32 + 8 * g + j) * KP + 16 * t + m];
+        Bk[kb] = P::make(x);
+      }
+      f32x4 acc[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) acc[cc] = zero4();
+#pragma unroll
+      for (int u = 0; u < 6; ++u) P::mma(acc[tb_ct(u)], tb[u], Bk[tb_kb(u)]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = acc[2 * kb][i];
+          x[4 + i] = acc[2 * kb + 1][i];
+        }
         IO::store(rec + (size_t)(Rc::PMAT + 2 * t + kb) * kFragBytes, lane, x);
       }
     }
-  }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    if (kb <= (wave >> 1)) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = s_L[(16 * wave + m) * MP + kb * 32 + 8 * g + j];
-      IO::store(rec + (size_t)(Rc::MTM + Rc::mt_frag(wave, kb)) * kFragBytes, lane, x);
-    }
-  }
-  if (wave == 0 && act && tgl == 0) {
-    float *gam = reinterpret_cast<float *>(rec + Rc::GAM);
-    *reinterpret_cast<float4 *>(gam + 8 * cgl) =
-        make_float4(bt[0] * after[0], bt[1] * after[1], bt[2] * after[2], bt[3] * after[3]);
-    *reinterpret_cast<float4 *>(gam + 8 * cgl + 4) =
-        make_float4(bt[4] * after[4], bt[5] * after[5], bt[6] * after[6], bt[7] * after[7]);
   }
 }
 
@@ -1041,9 +1000,10 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     }
     __syncthreads();
 
-    // U as an operand: rows kb*32 + 8g .. +7 of column m.
-    const auto u0 = Uop.load8(m, 8 * g);
-    const auto u1 = Uop.load8(m, 32 + 8 * g);
+    // U as an operand, in the k-order of the Ktil^T T and M T fragments:
+    // rows 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3 of column m.
+    const auto u0 = Uop.load_acc_order(m, 0, g);
+    const auto u1 = Uop.load_acc_order(m, 32, g);
     // S <- Diag(Gamma_C) S + (Ktil^T T) U
     if (wave < NTILE) {
       const float gm[4] = {U.gam.x, U.gam.y, U.gam.z, U.gam.w};
