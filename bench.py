@@ -3,38 +3,46 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-decode]
 
-A step is one kda_prefill call (schedule, chunk-local matrices, state pass)
-over one batch of the prefill workload (default prefill_4k: B=1, H=32,
-T=4096, d=128, bf16 q/k/v, fp32 alpha/beta/state/o, seeded synthetic
-inputs resident in HBM).  Three input sets are rotated so that consecutive
-steps do not find their ~235 MB working set in the 256 MB Infinity Cache.
-Prints one JSON line with the prefill rate as ``value``, the roofline of the
-dominant kernel, the decode rate of the decode workload (B=256, H=32,
-d=128, 100 in-place steps), and the fp64 CPU oracle timed on a bounded sample.
+A step is one kda_prefill call (varlen schedule, chunk-local kernel, state
+pass) over one batch of the prefill workload; by default prefill_4k: B=1,
+H=32, T=4096, d=128, bf16 q/k/v, fp32 alpha/beta/state/o, seeded synthetic
+inputs resident in HBM.  Five input sets (each with its own outputs and
+workspace) are rotated so that consecutive steps do not find their working
+set in the 256 MB Infinity Cache.  W untimed steps, then K steps between
+two synchronisations timed with HIP events on the launch stream.
+
+Prints one JSON line: the prefill rate as ``value``; per-call median and
+p10/p90; the roofline of the dominant kernel (algorithmic bytes per launch
+over its event-timed duration; ``traffic`` from the committed hardware
+counter summary when it was taken on the current kernel source); the decode
+rate (B=256, H=32, d=128, 100 in-place steps) with its own roofline; and the
+fp64 CPU oracle timed on the host over the whole prefill_4k workload.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
 
+import numpy as np
 import torch
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+N_SETS = 5                     # input sets rotated between timed calls
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_prefill_4k.json")
+KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_prefill.hip")
+COPY_BYTES = 256 << 20         # --calibrate-copy: bytes read (and written) by the copy
 
-# Algorithmic bytes per token and head (d = 128).
-#  whole prefill: q,k,v bf16 (768) + alpha fp32 (512) + beta (4) + o fp32 (512)
-#  state pass:    q,k,v (768) + alpha (512) + T,M chunk matrices (512) + o (512)
-#  chunk-local:   q,k (512) + alpha (512) + beta (4) + T,M written (512)
-BYTES_PREFILL = 768 + 512 + 4 + 512
-BYTES_STATE_PASS = 768 + 512 + 512 + 512
-BYTES_CHUNK_LOCAL = 512 + 512 + 4 + 512
-# Decode per (sequence, head) and step: state read + write, q,k,v, alpha, beta, o.
-BYTES_DECODE = 2 * 128 * 128 * 4 + 768 + 512 + 4 + 512
+WORKLOAD_TEXT = {
+    "prefill_4k": "B=1 H=32 T=4096 d=128",
+    "varlen_8seq": "8 seqs, lengths U[1024,16384], H=32 d=128, S0~0.02N",
+    "long_1m": "B=1 H=32 T=1048576 d=128",
+}
 
 
 def _parse():
@@ -42,15 +50,38 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill_4k",
-                   choices=["prefill_4k", "varlen_8seq", "long_1m"])
+    p.add_argument("--workload", default="prefill_4k", choices=sorted(WORKLOAD_TEXT))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-batch", type=int, default=256)
     p.add_argument("--calibrate-copy", action="store_true",
-                   help="also run a plain 256 MiB device copy (a known-size kernel for "
-                        "scaling hardware byte counters)")
+                   help="first run a plain elementwise float64 copy of 256 MiB (a kernel of "
+                        "known size for scaling hardware byte counters)")
     return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes per token and head (d = 128, bf16 q/k/v, fp32 rest).
+#   layer:        q, k, v (768) + alpha (512) + beta (4) + o (512)
+#   chunk-local:  q, k (512) + alpha (512) + beta (4) read; record written
+#   state pass:   record read; v (256) read; o (512) written
+# The record is the chunk-local kernel's output per 64 tokens and head,
+# read once by the state pass (its d/16 workgroups per head share it in L2).
+# ---------------------------------------------------------------------------
+BYTES_LAYER = 768 + 512 + 4 + 512
+BYTES_DECODE = 2 * 128 * 128 * 4 + 768 + 512 + 4 + 512   # per (sequence, head) and step
+
+
+def record_bytes_per_token(d):
+    from gated_delta_rule_76_amd import kda
+    # one sequence of 64 tokens, one head: schedule table (256 B) + 2 records
+    rec = (kda.prefill_workspace_size(1, 64, 1, d) - 256) // 2
+    return rec / 64.0
+
+
+def kernel_bytes(d):
+    rb = record_bytes_per_token(d)
+    return {"chunk_local_kernel": 512 + 512 + 4 + rb, "chunk_state_kernel": rb + 256 + 512}
 
 
 def _events():
@@ -62,7 +93,7 @@ def bench_prefill(name, steps, warmup, dev):
     spec = inputs.WORKLOADS[name]
     lens = inputs.workload_lengths(spec, seed=0)
     H, D = spec["H"], spec["D"]
-    n_sets = 3 if sum(lens) <= 65536 else 1
+    n_sets = N_SETS if sum(lens) <= 65536 else 1
     calls = []
     for s in range(n_sets):
         d = inputs.prefill_inputs(lens, H, D, torch.bfloat16, spec["decay"], spec["s0_std"],
@@ -82,8 +113,8 @@ def bench_prefill(name, steps, warmup, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    # Per-phase timing with events on the launch stream (the current stream).
-    ph = {"chunk_local": 0.0, "state_pass": 0.0}
+    # Per-call and per-phase timing (events on the launch stream, which is
+    # the current stream), in a second pass of the same K calls.
     evs = []
     for i in range(steps):
         a, b = _events()
@@ -96,23 +127,25 @@ def bench_prefill(name, steps, warmup, dev):
         c.record()
         evs.append((a, b, c))
     torch.cuda.synchronize()
-    for a, b, c in evs:
-        ph["chunk_local"] += a.elapsed_time(b) / steps
-        ph["state_pass"] += b.elapsed_time(c) / steps
-    return {"total_tokens": total, "H": H, "D": D, "ms": ms, "wall_s": wall, "phases_ms": ph,
-            "lengths": lens}
+    cl = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    sp = np.array([b.elapsed_time(c) for _, b, c in evs])
+    per_call = cl + sp
+    return {"total_tokens": total, "H": H, "D": D, "ms": ms, "wall_s": wall, "lengths": lens,
+            "phases_ms": {"chunk_local": float(cl.mean()), "state_pass": float(sp.mean())},
+            "call_ms": {"median": float(np.median(per_call)), "p10": float(np.percentile(per_call, 10)),
+                        "p90": float(np.percentile(per_call, 90))}}
 
 
-def bench_decode(B, steps, warmup, dev):
+def bench_decode(B, dev):
     from gated_delta_rule_76_amd import inputs, kda
     spec = inputs.WORKLOADS["decode_b256"]
     H, D = spec["H"], spec["D"]
-    d = inputs.decode_inputs(B, H, D, spec["steps"], torch.bfloat16, spec["decay"], spec["s_std"],
+    n = spec["steps"]
+    d = inputs.decode_inputs(B, H, D, n, torch.bfloat16, spec["decay"], spec["s_std"],
                              seed=0, device=dev)
     S = d["S"].clone()
     o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    n = spec["steps"]
-    for s in range(warmup):
+    for s in range(10):
         kda.decode_step(d["q"][s % n], d["k"][s % n], d["v"][s % n], d["alpha"][s % n],
                         d["beta"][s % n], S, out=o)
     torch.cuda.synchronize()
@@ -122,47 +155,88 @@ def bench_decode(B, steps, warmup, dev):
         kda.decode_step(d["q"][s], d["k"][s], d["v"][s], d["alpha"][s], d["beta"][s], S, out=o)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
-    return {"B": B, "H": H, "D": D, "steps": n, "ms_per_step": ms}
+    return {"B": B, "H": H, "D": D, "steps": n, "ms_per_step": e0.elapsed_time(e1) / n}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands, over the whole prefill_4k
+# workload, one process per group of heads on the host cores.  Runs before
+# anything touches the GPU (the worker processes are forked).
+# ---------------------------------------------------------------------------
+_CPU_INPUTS = {}
+
+
+def _cpu_worker(heads):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kda_recurrent
+    a = _CPU_INPUTS
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kda_recurrent(a["q"][:, heads], a["k"][:, heads], a["v"][:, heads], a["alpha"][:, heads],
+                      a["beta"][:, heads])
+        return time.perf_counter() - t0
 
 
 def cpu_baseline():
-    """The fp64 oracle on the host, single-threaded, on a bounded sample of
-    the prefill_4k workload: all 32 heads, the first 1024 tokens."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+    import multiprocessing as mp
 
     from gated_delta_rule_76_amd import inputs
-    from oracle import kda_recurrent
     spec = inputs.WORKLOADS["prefill_4k"]
-    T = 1024
-    d = inputs.token_inputs(T, spec["H"], spec["D"], torch.bfloat16, spec["decay"], seed=0, device="cpu")
-    a = {k: v.double().numpy() for k, v in d.items()}
-    with threadpool_limits(limits=1):
+    T, H, D = spec["lengths"][0], spec["H"], spec["D"]
+    d = inputs.token_inputs(T, H, D, torch.bfloat16, spec["decay"], seed=0, device="cpu")
+    _CPU_INPUTS.update({k: v.double().numpy() for k, v in d.items()})
+    workers = max(1, min(16, os.cpu_count() or 1, H))
+    groups = [g for g in np.array_split(np.arange(H), workers) if len(g)]
+    with mp.get_context("fork").Pool(len(groups)) as pool:
         t0 = time.perf_counter()
-        kda_recurrent(a["q"], a["k"], a["v"], a["alpha"], a["beta"])
-        dt = time.perf_counter() - t0
-    return {"value": T / dt, "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
-            "sample": f"prefill_4k inputs, all {spec['H']} heads, first {T} tokens, numpy fp64, "
-                      f"one thread ({dt:.2f} s)"}
+        busy = pool.map(_cpu_worker, groups)
+        wall = time.perf_counter() - t0
+    _CPU_INPUTS.clear()
+    return {"value": T / wall, "unit": "tokens/s/layer", "cores": len(groups), "kind": "oracle",
+            "sample": f"the whole prefill_4k workload ({T} tokens x {H} heads, d={D}), numpy fp64 "
+                      f"token-by-token recurrence, {len(groups)} processes over head groups "
+                      f"({wall:.2f} s wall, {sum(busy):.1f} s CPU)"}
+
+
+def _traffic(kernel, workload):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary,
+    or None when it is missing or was taken on other kernel source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            t = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if t.get("source_sha256") != sha or t.get("workload") != workload or k is None:
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
 
 
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the layer shards by head/sequence with no communication; see the design notes)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer shards by "
+              "(sequence, head) with no communication between GPUs, so one GPU's rate is the unit)",
               file=sys.stderr)
         sys.exit(2)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
+        # float64, which nothing else in this program uses, so the copy's
+        # dispatches are easy to pick out of a counter trace
+        src = torch.ones(COPY_BYTES // 8, dtype=torch.float64, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.add(src, 0.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
     print(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
@@ -170,11 +244,12 @@ def main():
     pf = bench_prefill(args.workload, args.steps, args.warmup, dev)
     th = pf["total_tokens"] * pf["H"]
     tok_s = pf["total_tokens"] / (pf["ms"] * 1e-3)
-    sp_ms = pf["phases_ms"]["state_pass"]
-    cl_ms = pf["phases_ms"]["chunk_local"]
-    dom, dom_ms, dom_bytes = (("chunk_state_kernel", sp_ms, BYTES_STATE_PASS) if sp_ms >= cl_ms
-                              else ("chunk_local_kernel", cl_ms, BYTES_CHUNK_LOCAL))
-    achieved = th * dom_bytes / (dom_ms * 1e-3) / 1e9
+    kb = kernel_bytes(pf["D"])
+    times = {"chunk_local_kernel": pf["phases_ms"]["chunk_local"],
+             "chunk_state_kernel": pf["phases_ms"]["state_pass"]}
+    dom = max(times, key=times.get)
+    achieved = th * kb[dom] / (times[dom] * 1e-3) / 1e9
+    traffic = _traffic(dom, args.workload)
     out = {
         "metric": "KDA prefill tokens/s/layer (H=32, d=128)",
         "value": tok_s,
@@ -188,23 +263,23 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: " + (
-            "B=1 H=32 T=4096 d=128" if args.workload == "prefill_4k" else
-            "8 seqs, lengths U[1024,16384], H=32 d=128, S0~0.02N" if args.workload == "varlen_8seq" else
-            "B=1 H=32 T=1048576 d=128") + ", bf16 q/k/v, fp32 alpha/beta/state/o, chunk 64",
-            "total_tokens": pf["total_tokens"], "heads": pf["H"], "head_dim": pf["D"]},
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}, bf16 q/k/v, "
+                               "fp32 alpha/beta/state/o, chunk 64",
+                   "total_tokens": pf["total_tokens"], "heads": pf["H"], "head_dim": pf["D"]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "launch_ms": dom_ms},
-        "layer_roofline": {"bound": "hbm", "bytes_per_token_head": BYTES_PREFILL,
-                           "achieved": th * BYTES_PREFILL / (pf["ms"] * 1e-3) / 1e9,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "launch_ms": times[dom], "bytes_per_token_head": kb[dom]},
+        "kernels": {k: {"ms": times[k], "bytes_per_token_head": kb[k],
+                        "achieved_gbs": th * kb[k] / (times[k] * 1e-3) / 1e9} for k in times},
+        "layer_roofline": {"bound": "hbm", "bytes_per_token_head": BYTES_LAYER,
+                           "achieved": th * BYTES_LAYER / (pf["ms"] * 1e-3) / 1e9,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": th * BYTES_PREFILL / (pf["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "phases_ms": pf["phases_ms"],
+                           "frac": th * BYTES_LAYER / (pf["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "call_ms": pf["call_ms"],
     }
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
-        dc = bench_decode(args.decode_batch, 100, 10, dev)
+        dc = bench_decode(args.decode_batch, dev)
         gbs = dc["B"] * dc["H"] * BYTES_DECODE / (dc["ms_per_step"] * 1e-3) / 1e9
         out["decode"] = {"metric": "KDA decode steps/s (B=%d, H=32, d=128)" % dc["B"],
                          "value": 1e3 / dc["ms_per_step"], "unit": "steps/s",
@@ -212,9 +287,8 @@ def main():
                          "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": gbs,
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -16,8 +16,13 @@
 //
 // (unrolling the recurrence: S_r = Diag(Gamma_r) S0 + sum_{j<=r}
 // Diag(Gamma_r/Gamma_j) k_j w_j^T with w_r = beta_r (v_r - k_r^T Diag(alpha_r)
-// S_{r-1}); collecting the w_r gives the triangular system above).  A tail
-// chunk is padded with alpha = 1, beta = 0, q = k = v = 0, which is an
+// S_{r-1}); collecting the w_r gives the triangular system above).  The
+// kernels use it re-associated, never forming W:
+//
+//   U = V - Khat S0,   O = Qhat S0 + (M T) U,   S_C = Diag(Gamma_C) S0 + (Ktil^T T) U
+//
+// so all that does not depend on S0 is computed once per chunk in parallel.
+// A tail chunk is padded with alpha = 1, beta = 0, q = k = v = 0, which is an
 // exact identity step.
 //
 // Three kernels:
@@ -25,13 +30,14 @@
 //                       of first-chunk indices (exclusive scan).
 //   chunk_local_kernel  one workgroup per (chunk, head), fully parallel:
 //                       A and M on the matrix cores, T by a blocked
-//                       triangular inverse in fp32; T and M go to the
-//                       workspace.
+//                       triangular inverse, Ktil^T T and M T on the matrix
+//                       cores; writes the chunk's record (Khat, Qhat,
+//                       Ktil^T T, M T, Gamma_C as operand fragments).
 //   chunk_state_kernel  one workgroup per (sequence, head, 16 value
 //                       columns), sequential over the chunks of its
 //                       sequence: the state slice stays in registers (fp32)
-//                       across chunks; every product with S, W and T runs on
-//                       the matrix cores.
+//                       across chunks; every product runs on the matrix
+//                       cores with operands streamed from the records.
 //
 // Decay factors are formed as running products of alpha (never as exp of
 // differences of cumulative logs), so no factor exceeds 1 except 1/Gamma

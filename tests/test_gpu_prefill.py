@@ -203,3 +203,35 @@ def test_two_phase_calls_equal_prefill():
     call.chunk_local()
     o, S = call.state_pass()
     assert torch.equal(o, ref_o) and torch.equal(S, ref_S)
+
+
+def test_prefill_long_1m_workload():
+    """B=1, H=32, T=2^20, d=128, bf16, strong decay, S0 = 0 (a 1M-token
+    context; ~130 GB of device memory with the workspace).  For a seeded
+    sample of 2 heads: o of the first 65,536 tokens against the oracle, and
+    (o of the last 512 tokens, S_T) from a run of the last 1024 tokens from
+    zero.  On all heads: the run split in halves at a chunk boundary (the
+    second half from the first half's S_T) is bit-identical to one call."""
+    dev = device()
+    spec = inputs.WORKLOADS["long_1m"]
+    T, H, D = spec["lengths"][0], spec["H"], spec["D"]
+    d = inputs.prefill_inputs([T], H, D, torch.bfloat16, "strong", None, seed=0, device=dev)
+    ws = torch.empty(kda.prefill_workspace_size(1, T, H, D), dtype=torch.uint8, device=dev)
+    o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], workspace=ws)
+    heads = seeded_sample(H, 2, seed=3)
+    P, W = 65536, 1024
+    ro, _ = _oracle({key: d[key][:P] for key in ("q", "k", "v", "alpha", "beta")}, heads=heads)
+    eo = rel_l2(np64(o[:P, heads]), ro)
+    assert eo < 2e-3, f"long_1m prefix: o {eo:.3e}"
+    ro, rST = _oracle({key: d[key][T - W:] for key in ("q", "k", "v", "alpha", "beta")}, heads=heads)
+    _check(o[T - W // 2:, heads], ST[:, heads], ro[W // 2:], rST, 2e-3, "long_1m tail")
+    half = T // 2
+    o2 = torch.empty_like(o)
+    S1 = torch.empty_like(ST)
+    first = {key: d[key][:half] for key in ("q", "k", "v", "alpha", "beta")}
+    second = {key: d[key][half:] for key in ("q", "k", "v", "alpha", "beta")}
+    kda.prefill(first["q"], first["k"], first["v"], first["alpha"], first["beta"], workspace=ws,
+                out=o2[:half], final_state=S1)
+    _, S2 = kda.prefill(second["q"], second["k"], second["v"], second["alpha"], second["beta"], S1,
+                        workspace=ws, out=o2[half:])
+    assert torch.equal(o2, o) and torch.equal(S2, ST)
