@@ -12,12 +12,13 @@
 //   S'_ij = alpha_i S_ij + k_i w_j        (written back in place)
 //   o_j = y_j + (q.k) w_j                 (= sum_i q_i S'_ij, post-update read-out)
 //
-// Value columns never mix, so a workgroup owns a block of up to 64 columns of
-// one head: it reads that 128 x 64 fp32 slab once into registers (float4 per
-// lane, each row's 256 B read by 16 consecutive lanes), reduces x and y over
-// rows with cross-lane shuffles and one LDS round, and writes the slab back.
-// The kernel is bound by HBM: 2 x 64 KiB of state traffic per head and step
-// against ~115 kflop.
+// A workgroup owns one head (up to 512 threads): it reads the d x d fp32 state
+// once into registers (float4 per lane, each row read by d/4 consecutive
+// lanes), reduces x and y over rows with cross-lane shuffles and one LDS
+// round, and writes the state back.  Every lane loads alpha_i, k_i, q_i of
+// its own rows, and the v_j, beta it needs, before the state, so no load
+// waits on another after the state arrives.  The kernel is bound by HBM:
+// 2 x 64 KiB of state traffic per head and step against ~115 kflop.
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -28,16 +29,14 @@ namespace {
 
 template <int D>
 struct DecodeCfg {
-  static constexpr int CB = D >= 64 ? 64 : D;         // columns per workgroup
-  static constexpr int NCB = D / CB;                   // column blocks per head
-  static constexpr int TPR = CB / 4;                   // lanes per row (float4 each)
-  static constexpr int NT = (TPR * D < 256) ? TPR * D : 256;
-  static constexpr int RPP = NT / TPR;                 // rows per pass
+  static constexpr int TPR = D / 4;                                // lanes per row (float4 each)
+  static constexpr int NT = TPR * D < 512 ? TPR * D : 512;         // threads per workgroup
+  static constexpr int RPP = NT / TPR;                             // rows per pass
   static constexpr int PASSES = D / RPP;
   static constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0, "workgroup must be whole waves");
   static_assert(D % RPP == 0, "rows must tile evenly");
-  static_assert(NT >= D, "one staging lane per key channel");
+  static_assert(NT >= D, "one lane per key channel for q.k");
 };
 
 template <int D, typename TIn>
@@ -46,52 +45,44 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
     const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ S,
     float *__restrict__ o) {
   using Cfg = DecodeCfg<D>;
-  constexpr int CB = Cfg::CB, TPR = Cfg::TPR, RPP = Cfg::RPP, PASSES = Cfg::PASSES, NW = Cfg::NW;
+  constexpr int TPR = Cfg::TPR, RPP = Cfg::RPP, PASSES = Cfg::PASSES, NW = Cfg::NW;
 
-  __shared__ float s_al[D];      // alpha_i
-  __shared__ float s_ka[D];      // alpha_i k_i
-  __shared__ float s_qa[D];      // alpha_i q_i
-  __shared__ float s_k[D];       // k_i
-  __shared__ float s_red[NW][2][CB];
+  __shared__ float s_red[NW][2][D];
   __shared__ float s_qk[NW];
-  __shared__ float s_w[CB];
+  __shared__ float s_w[D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t nh = (int64_t)(blockIdx.x / Cfg::NCB);  // flattened (sequence, head)
-  const int cb = blockIdx.x % Cfg::NCB;
+  const int64_t nh = (int64_t)blockIdx.x;  // flattened (sequence, head)
+  const int cq = tid % TPR;                // float4 column
+  const int r0 = tid / TPR;                // first row of this lane
+  float *Sp = S + nh * (int64_t)(D * D) + cq * 4;
 
-  const int cq = tid % TPR;  // float4 column within the block
-  const int r0 = tid / TPR;  // first row of this lane
-  float *Sp = S + nh * (int64_t)(D * D) + cb * CB + cq * 4;
-
-  // Issue the state loads first; they are the long-latency part.
+  // Small inputs first (alpha, k, q of this lane's rows; v, beta of the
+  // column it finalises; q_i k_i of channel tid), then the state.
+  float a[PASSES], kk[PASSES], qq[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = r0 + p * RPP;
+    a[p] = alpha[nh * D + r];
+    kk[p] = to_f32(k[nh * D + r]);
+    qq[p] = to_f32(q[nh * D + r]);
+  }
+  const int cj = tid < D ? tid : 0;
+  const float vj = to_f32(v[nh * D + cj]);
+  const float bt = beta[nh];
+  float qk_part = tid < D ? to_f32(q[nh * D + cj]) * to_f32(k[nh * D + cj]) : 0.f;
   float4 s[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) s[p] = *reinterpret_cast<const float4 *>(Sp + (int64_t)(r0 + p * RPP) * D);
 
-  float qk_part = 0.0f;
-  if (tid < D) {
-    const float a = alpha[nh * D + tid];
-    const float qi = to_f32(q[nh * D + tid]);
-    const float ki = to_f32(k[nh * D + tid]);
-    s_al[tid] = a;
-    s_ka[tid] = a * ki;
-    s_qa[tid] = a * qi;
-    s_k[tid] = ki;
-    qk_part = qi * ki;
-  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
-  if (lane == 0) s_qk[wave] = qk_part;
-  __syncthreads();
-
   float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const int r = r0 + p * RPP;
-    const float ka = s_ka[r], qa = s_qa[r];
+    const float ka = a[p] * kk[p], qa = a[p] * qq[p];
     x[0] += ka * s[p].x; x[1] += ka * s[p].y; x[2] += ka * s[p].z; x[3] += ka * s[p].w;
     y[0] += qa * s[p].x; y[1] += qa * s[p].y; y[2] += qa * s[p].z; y[3] += qa * s[p].w;
   }
@@ -111,9 +102,10 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
       s_red[wave][1][cq * 4 + j] = y[j];
     }
   }
+  if (lane == 0) s_qk[wave] = qk_part;
   __syncthreads();
 
-  if (tid < CB) {
+  if (tid < D) {
     float xs = 0.f, ys = 0.f, qk = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -121,10 +113,9 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
       ys += s_red[w][1][tid];
       qk += s_qk[w];
     }
-    const int col = cb * CB + tid;
-    const float wv = beta[nh] * (to_f32(v[nh * D + col]) - xs);
+    const float wv = bt * (vj - xs);
     s_w[tid] = wv;
-    o[nh * D + col] = ys + qk * wv;
+    o[nh * D + tid] = ys + qk * wv;
   }
   __syncthreads();
 
@@ -132,12 +123,11 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int r = r0 + p * RPP;
-    const float a = s_al[r], kr = s_k[r];
     float4 n;
-    n.x = a * s[p].x + kr * w0;
-    n.y = a * s[p].y + kr * w1;
-    n.z = a * s[p].z + kr * w2;
-    n.w = a * s[p].w + kr * w3;
+    n.x = a[p] * s[p].x + kk[p] * w0;
+    n.y = a[p] * s[p].y + kk[p] * w1;
+    n.z = a[p] * s[p].z + kk[p] * w2;
+    n.w = a[p] * s[p].w + kk[p] * w3;
     *reinterpret_cast<float4 *>(Sp + (int64_t)r * D) = n;
   }
 }
@@ -147,7 +137,7 @@ hipError_t launch_decode_t(const kda_shape_t &s, const void *q, const void *k, c
                            const float *alpha, const float *beta, float *S, float *o,
                            hipStream_t stream) {
   using Cfg = DecodeCfg<D>;
-  const int64_t blocks = (int64_t)s.num_seqs * s.num_heads * Cfg::NCB;
+  const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
   hipLaunchKernelGGL((decode_kernel<D, TIn>), dim3((unsigned)blocks), dim3(Cfg::NT), 0, stream,
                      static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                      static_cast<const TIn *>(v), alpha, beta, S, o);
