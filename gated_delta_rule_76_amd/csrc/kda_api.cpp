@@ -26,6 +26,8 @@ kda_status_t check_prefill_shape(const kda_shape_t *s, bool varlen) {
   if (s->d_k != s->d_v || !supported_dim(s->d_k)) return KDA_ERR_UNSUPPORTED;
   // Grid limits: one workgroup per (chunk, head) in the chunk-local kernel.
   if (kda::max_chunks(*s) * (int64_t)s->num_heads >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  // The state pass addresses one chunk's rows of v and o with 32-bit offsets.
+  if ((int64_t)kda::kChunk * s->num_heads * s->d_v * 4 >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 

@@ -57,6 +57,9 @@ namespace {
 constexpr int C = kChunk;          // 64 tokens per chunk
 constexpr int NT = 256;            // threads per workgroup (4 waves)
 constexpr float kTinyBlock = 7.888609052210118e-31f;  // 2^-100
+// Word 3 of a raw (stride 0) buffer descriptor: 32-bit data format; with it
+// an access at an offset past num_records is dropped (stores) or reads 0.
+constexpr int kBufferWord3 = 0x00020000;
 
 // ---------------------------------------------------------------------------
 // LDS operand planes: a ROWS x COLS fp32 matrix stored either as a bf16
@@ -890,8 +893,24 @@ __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec,
   // O waves; the partner wave of the same row tile reads the same M T lines):
   // no branch separates the loads, so none of them has to be waited for early.
   const int rt = wave & 3, g = lane >> 4, m = lane & 15;
+  // V through a buffer descriptor spanning the chunk's valid rows: padding
+  // rows read 0.  (Offsets are 32-bit: the host requires 64 H d 4 < 2^31.)
+  {
+    const uint64_t addr = reinterpret_cast<uint64_t>(v + (vt0 * H + h) * D + col0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const int nbytes = __builtin_amdgcn_readfirstlane(valid * H * D * (int)sizeof(TIn));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, nbytes, kBufferWord3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) B.v[i] = v[(load_token(vt0, 16 * rt + 4 * g + i, valid, total) * H + h) * D + col0 + m];
+    for (int i = 0; i < 4; ++i) {
+      const int off = ((16 * rt + 4 * g + i) * H * D + m) * (int)sizeof(TIn);
+      if constexpr (sizeof(TIn) == 2)
+        B.v[i] = __builtin_bit_cast(TIn, __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+      else
+        B.v[i] = __builtin_bit_cast(TIn, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    }
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int f = Rc::mt_frag(rt, rt < 2 ? 0 : kb);  // row tiles 0, 1: the k-block 0 block twice
@@ -973,6 +992,34 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     load_scan_b<D, TIn, P>(B, rec_of(cc), v, cn.t0, cn.valid, total_tokens, h, H, col0, wave, lane);
   };
 
+  // o of a chunk is stored during the next chunk's first phase by the O
+  // waves, through a buffer descriptor spanning exactly the chunk's valid
+  // rows: the hardware drops the stores of padding rows (and all stores of
+  // the U waves, whose descriptor is empty), so no branch guards them and
+  // both roles issue the same memory instructions.  (Offsets are 32-bit:
+  // the host requires 64 H d 4 < 2^31.)
+  f32x4 opend = zero4();
+  int64_t pend_t0 = 0;
+  int pend_valid = 0;
+  auto store_o = [&]() __attribute__((always_inline)) {
+    // (the base and size are wave-uniform; readfirstlane lets the compiler
+    // keep the descriptor in scalar registers)
+    const uint64_t addr = reinterpret_cast<uint64_t>(o + (pend_t0 * H + h) * D + col0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const int nbytes = __builtin_amdgcn_readfirstlane(pend_valid * H * D * (int)sizeof(float));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<float *>(((uint64_t)hi << 32) | lo), 0, nbytes, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * g + i;
+      // (__float_as_uint, not __builtin_bit_cast: the latter applied to an
+      // element of a vector type reads element 0 with this compiler)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(opend[i]), rs,
+                                            (r * H * D + m) * (int)sizeof(float), 0, 0);
+    }
+  };
+
   // The loads of the next record are spread over this chunk's two phases,
   // between its matrix-core products, so that each wave keeps computing
   // while its loads queue.
@@ -980,18 +1027,21 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     const ChunkTok ct = chunk_tokens(sstart, slen, c - cbeg, total_tokens);
     const char *rn = rec_of(cn);  // unconditional (the last chunk re-reads itself)
 
-    // Khat S (U waves) or Qhat S (O waves) for row tile rt.
+    // Khat S (U waves) or Qhat S (O waves) for row tile rt.  All S operand
+    // fragments are read first, so their LDS latency is paid once.
+    typename P::Frag Bs[NKB];
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) Bs[kk] = Sop.load8(m, ((kk + cg) % NKB) * 32 + 8 * g);
     f32x4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) {
-      const int kb = (kk + cg) % NKB;  // the k-block held in register slot kk
-      const auto Bs = Sop.load8(m, kb * 32 + 8 * g);
-      P::mma((kk & 1) ? acc1 : acc0, IO::frag(U.a[kk]), Bs);
+    for (int kk = 0; kk < NKB; ++kk) {  // register slot kk holds k-block (kk + cg) mod NKB
+      P::mma((kk & 1) ? acc1 : acc0, IO::frag(U.a[kk]), Bs[kk]);
       __builtin_amdgcn_sched_barrier(0);
       load_scan_a<D, TIn, P>(Nx, kk, rn, wave, lane, cg);
       __builtin_amdgcn_sched_barrier(0);
     }
     Nx.tch = touch(cn + 1 < cend ? cn + 1 : cn);
+    store_o();  // the previous chunk's o (O waves), while the U waves form U
     f32x4 ov;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = acc0[i] + acc1[i];
@@ -1029,13 +1079,9 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     __builtin_amdgcn_sched_barrier(0);
     prefetch_b(cn, Nx);
     __builtin_amdgcn_sched_barrier(0);
-    if (!uwave) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        if (r < ct.valid) o[((ct.t0 + r) * H + h) * D + col0 + m] = ov[i];
-      }
-    }
+    opend = ov;
+    pend_t0 = ct.t0;
+    pend_valid = uwave ? 0 : ct.valid;
     sink += U.tch;
     __syncthreads();
   };
@@ -1047,11 +1093,15 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     bufA.tch = touch(cbeg);
   }
   __syncthreads();
-  for (int64_t c = cbeg; c < cend; c += 2) {
-    process(c, bufA, bufB, c + 1 < cend ? c + 1 : c);
-    if (c + 1 >= cend) break;
+  // Pairs of chunks (no exit between the two halves, so each half's loads
+  // stay where they are issued), then an odd last chunk.
+  int64_t c = cbeg;
+  for (; c + 1 < cend; c += 2) {
+    process(c, bufA, bufB, c + 1);
     process(c + 1, bufB, bufA, c + 2 < cend ? c + 2 : c + 1);
   }
+  if (c < cend) process(c, bufA, bufB, c);
+  store_o();
   if (N < 0) o[sink & 1] = 0.f;  // never taken (N >= 0): keeps the touches alive
 
   if (S_T != nullptr && wave < NTILE) {

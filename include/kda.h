@@ -59,7 +59,8 @@ extern "C" {
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned, inconsistent shape */
-    KDA_ERR_UNSUPPORTED = 2,      /* valid but not built: d_k != d_v, d not in {16,32,64,128} */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not built: d_k != d_v, d not in {16,32,64,128},
+                                     prefill with 64 * H * d * 4 >= 2^31 (H > 65535 at d = 128) */
     KDA_ERR_WORKSPACE_TOO_SMALL = 3,
     KDA_ERR_LAUNCH = 4            /* a kernel launch failed (HIP error) */
 } kda_status_t;

@@ -97,6 +97,11 @@ def test_prefill_validation(L):
     assert prefill(L, shape(d=48)) == UNSUPPORTED
     s = kda.KdaShape(1, 64, 64, 2, 16, 32, 0)
     assert prefill(L, s) == UNSUPPORTED                           # d_k != d_v
+    out = ctypes.c_size_t(0)
+    big = kda.KdaShape(1, 64, 64, 65536, 128, 128, 1)             # 64 * H * d * 4 = 2^31
+    assert L.kda_prefill_workspace_size(ctypes.byref(big), ctypes.byref(out)) == UNSUPPORTED
+    ok = kda.KdaShape(1, 64, 64, 65535, 128, 128, 1)
+    assert L.kda_prefill_workspace_size(ctypes.byref(ok), ctypes.byref(out)) == OK
     for field in ("q", "k", "v", "a", "b", "o"):
         assert prefill(L, shape(), **{field: None}) == INVALID, field
         assert prefill(L, shape(), **{field: FAKE + 2}) == INVALID, field   # misaligned
