@@ -510,22 +510,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
   const int r = 16 * wave + m;
   const bool rv = r < nvalid;
   const int64_t tok = load_token(t0, r, nvalid, total_tokens);
+  // In the order of first use: beta (stored to LDS below, so waiting for it
+  // must not wait for the rest), alpha (the scans), then k and q.
+  const float bv = beta[load_token(t0, tid & (C - 1), nvalid, total_tokens) * H + h];
   Raw8<TIn> kr[NKB], qr[NKB];
   float4 ar0[NKB], ar1[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const int ch = kb * 32 + 8 * g;
     const int64_t off = (tok * H + h) * D + (ch < D ? ch : 0);
-    kr[kb].load(k + off);
-    qr[kb].load(q + off);
     ar0[kb] = *reinterpret_cast<const float4 *>(alpha + off);
     ar1[kb] = *reinterpret_cast<const float4 *>(alpha + off + 4);
   }
-  for (int e = tid; e < C * MP; e += NT) s_X[e] = 0.f;
-  if (tid < C) {
-    const float bv = beta[load_token(t0, tid, nvalid, total_tokens) * H + h];
-    s_beta[tid] = tid < nvalid ? bv : 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int ch = kb * 32 + 8 * g;
+    const int64_t off = (tok * H + h) * D + (ch < D ? ch : 0);
+    kr[kb].load(k + off);
+    qr[kb].load(q + off);
   }
+  for (int e = tid; e < C * MP; e += NT) s_X[e] = 0.f;
+  if (tid < C) s_beta[tid] = tid < nvalid ? bv : 0.f;
 
   // ---- in-block decay products -------------------------------------------------
   float bp[NKB][8], bs[NKB][8];
