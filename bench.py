@@ -17,6 +17,9 @@ over its event-timed duration; ``traffic`` from the committed hardware
 counter summary when it was taken on the current kernel source); the decode
 rate (B=256, H=32, d=128, 100 in-place steps) with its own roofline; and the
 fp64 CPU oracle timed on the host over the whole prefill_4k workload.
+
+``--oracle-rates`` times only the CPU oracle, on every workload, and prints
+those rates as one JSON line.
 """
 
 from __future__ import annotations
@@ -54,6 +57,8 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-batch", type=int, default=256)
+    p.add_argument("--oracle-rates", action="store_true",
+                   help="only time the fp64 CPU oracle on every workload (no GPU)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a plain elementwise float64 copy of 256 MiB (a kernel of "
                         "known size for scaling hardware byte counters)")
@@ -159,44 +164,114 @@ def bench_decode(B, dev):
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the fp64 oracle as it stands, over the whole prefill_4k
-# workload, one process per group of heads on the host cores.  Runs before
+# CPU baseline: the fp64 oracle as it stands, one process per group of heads
+# (or of (sequence, head) pairs for decode) on the host cores.  Runs before
 # anything touches the GPU (the worker processes are forked).
 # ---------------------------------------------------------------------------
 _CPU_INPUTS = {}
 
 
-def _cpu_worker(heads):
+def _cpu_prefill_worker(heads):
     from threadpoolctl import threadpool_limits
 
     from oracle import kda_recurrent
     a = _CPU_INPUTS
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        kda_recurrent(a["q"][:, heads], a["k"][:, heads], a["v"][:, heads], a["alpha"][:, heads],
-                      a["beta"][:, heads])
+        for _ in range(a["passes"]):
+            kda_recurrent(a["q"][:, heads], a["k"][:, heads], a["v"][:, heads], a["alpha"][:, heads],
+                          a["beta"][:, heads], None if a["S0"] is None else a["S0"][:, heads],
+                          cu_seqlens=a["cu"])
         return time.perf_counter() - t0
 
 
-def cpu_baseline():
-    import multiprocessing as mp
+def _cpu_decode_worker(pairs):
+    from threadpoolctl import threadpool_limits
 
-    from gated_delta_rule_76_amd import inputs
-    spec = inputs.WORKLOADS["prefill_4k"]
-    T, H, D = spec["lengths"][0], spec["H"], spec["D"]
-    d = inputs.token_inputs(T, H, D, torch.bfloat16, spec["decay"], seed=0, device="cpu")
-    _CPU_INPUTS.update({k: v.double().numpy() for k, v in d.items()})
-    workers = max(1, min(16, os.cpu_count() or 1, H))
-    groups = [g for g in np.array_split(np.arange(H), workers) if len(g)]
+    from oracle import kda_decode_step
+    a = _CPU_INPUTS
+    with threadpool_limits(limits=1):
+        S = a["S"][pairs]
+        t0 = time.perf_counter()
+        for s in range(a["steps"]):
+            _, S = kda_decode_step(a["q"][s][pairs], a["k"][s][pairs], a["v"][s][pairs],
+                                   a["alpha"][s][pairs], a["beta"][s][pairs], S)
+        return time.perf_counter() - t0
+
+
+def _pool_map(fn, n_items):
+    import multiprocessing as mp
+    workers = max(1, min(16, os.cpu_count() or 1, n_items))
+    groups = [g for g in np.array_split(np.arange(n_items), workers) if len(g)]
     with mp.get_context("fork").Pool(len(groups)) as pool:
         t0 = time.perf_counter()
-        busy = pool.map(_cpu_worker, groups)
+        busy = pool.map(fn, groups)
         wall = time.perf_counter() - t0
+    return wall, sum(busy), len(groups)
+
+
+def oracle_prefill_rate(workload, max_tokens=None, passes=1):
+    """Oracle tokens/s/layer over ``workload`` (or its first ``max_tokens``
+    tokens when the sequence is longer), all heads, ``passes`` repetitions."""
+    from gated_delta_rule_76_amd import inputs
+    spec = inputs.WORKLOADS[workload]
+    lengths = inputs.workload_lengths(spec, seed=0)
+    prefix = max_tokens is not None and sum(lengths) > max_tokens
+    if prefix:
+        lengths = [max_tokens]
+    d = inputs.prefill_inputs(lengths, spec["H"], spec["D"], torch.bfloat16, spec["decay"],
+                              None if prefix else spec["s0_std"], seed=0, device="cpu")
+    _CPU_INPUTS.update({k: d[k].double().numpy() for k in ("q", "k", "v", "alpha", "beta")})
+    _CPU_INPUTS["S0"] = None if d["S0"] is None else d["S0"].double().numpy()
+    _CPU_INPUTS["cu"] = d["cu_seqlens"].numpy()
+    _CPU_INPUTS["passes"] = passes
+    T = sum(lengths)
+    wall, busy, cores = _pool_map(_cpu_prefill_worker, spec["H"])
     _CPU_INPUTS.clear()
-    return {"value": T / wall, "unit": "tokens/s/layer", "cores": len(groups), "kind": "oracle",
-            "sample": f"the whole prefill_4k workload ({T} tokens x {H} heads, d={D}), numpy fp64 "
-                      f"token-by-token recurrence, {len(groups)} processes over head groups "
-                      f"({wall:.2f} s wall, {sum(busy):.1f} s CPU)"}
+    what = (f"the first {T} tokens of {workload}" if prefix else f"the whole {workload} workload")
+    return {"value": passes * T / wall, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
+            "sample": f"{what} ({T} tokens x {spec['H']} heads, d={spec['D']}"
+                      f"{', x%d passes' % passes if passes > 1 else ''}), numpy fp64 token-by-token "
+                      f"recurrence, {cores} processes over head groups ({wall:.2f} s wall, "
+                      f"{busy:.1f} s CPU)"}
+
+
+def oracle_decode_rate(B=256, steps=100):
+    """Oracle steps/s: ``steps`` decode steps of B sequences x 32 heads, d=128."""
+    from gated_delta_rule_76_amd import inputs
+    spec = inputs.WORKLOADS["decode_b256"]
+    H, D = spec["H"], spec["D"]
+    d = inputs.decode_inputs(B, H, D, steps, torch.bfloat16, spec["decay"], spec["s_std"], seed=0,
+                             device="cpu")
+    n = B * H
+    _CPU_INPUTS["S"] = d["S"].double().numpy().reshape(n, 1, D, D)
+    for k in ("q", "k", "v", "alpha"):
+        _CPU_INPUTS[k] = d[k].double().numpy().reshape(steps, n, 1, D)
+    _CPU_INPUTS["beta"] = d["beta"].double().numpy().reshape(steps, n, 1)
+    _CPU_INPUTS["steps"] = steps
+    wall, busy, cores = _pool_map(_cpu_decode_worker, n)
+    _CPU_INPUTS.clear()
+    return {"value": steps / wall, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} decode steps, B={B} H={H} d={D}, numpy fp64, {cores} processes "
+                      f"over (sequence, head) groups ({wall:.2f} s wall, {busy:.1f} s CPU)"}
+
+
+def cpu_baseline():
+    return oracle_prefill_rate("prefill_4k", passes=3)
+
+
+def oracle_rates():
+    """Every workload's oracle rate; the 2^20-token sequence is timed on its
+    first 65,536 tokens and extrapolated linearly (the per-token cost of the
+    recurrence does not depend on the position)."""
+    out = {"host_cpus": os.cpu_count(),
+           "prefill_4k": oracle_prefill_rate("prefill_4k", passes=3),
+           "varlen_8seq": oracle_prefill_rate("varlen_8seq"),
+           "decode_b256": oracle_decode_rate(256, 100)}
+    lg = oracle_prefill_rate("long_1m", max_tokens=65536)
+    lg["extrapolated_seconds_for_2^20_tokens"] = (1 << 20) / lg["value"]
+    out["long_1m"] = lg
+    return out
 
 
 def _traffic(kernel, workload):
@@ -222,6 +297,9 @@ def main():
               "(sequence, head) with no communication between GPUs, so one GPU's rate is the unit)",
               file=sys.stderr)
         sys.exit(2)
+    if args.oracle_rates:
+        print(json.dumps(oracle_rates()), flush=True)
+        return
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
