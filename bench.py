@@ -264,7 +264,13 @@ def oracle_rates():
     """Every workload's oracle rate; the 2^20-token sequence is timed on its
     first 65,536 tokens and extrapolated linearly (the per-token cost of the
     recurrence does not depend on the position)."""
-    out = {"host_cpus": os.cpu_count(),
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    out = {"host_cpus": os.cpu_count(), "cpu_model": model,
            "prefill_4k": oracle_prefill_rate("prefill_4k", passes=3),
            "varlen_8seq": oracle_prefill_rate("varlen_8seq"),
            "decode_b256": oracle_decode_rate(256, 100)}
