@@ -17,10 +17,12 @@ Modules
 recurrence   token-by-token recurrence, fp64 numpy (the oracle proper)
 bruteforce   the printed matrix product formed literally, fp64, tiny sizes
 exact        the printed matrix product in exact rational arithmetic
+scalar_gate  the scalar-gate (Gated DeltaNet) form: one decay rate per token
+             and head instead of one per key channel
 
-Pins (every function is pinned by tests/test_oracle_pins.py against closed
-forms, invariants, a library routine and a hand-worked golden example; see
-the module docstrings).  No function here is "parity unpinned".
+Pins (every function is pinned by tests/test_oracle_pins.py and
+tests/test_oracle_scalar_gate.py against closed forms, invariants, a library
+routine and a hand-worked golden example; see the module docstrings).  No function here is "parity unpinned".
 """
 
 from .recurrence import (  # noqa: F401
@@ -31,3 +33,4 @@ from .recurrence import (  # noqa: F401
 )
 from .bruteforce import kda_bruteforce  # noqa: F401
 from .exact import kda_exact  # noqa: F401
+from .scalar_gate import gdn_decode_step, gdn_recurrent, gdn_step  # noqa: F401
