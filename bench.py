@@ -160,7 +160,18 @@ def bench_decode(B, dev):
         kda.decode_step(d["q"][s], d["k"][s], d["v"][s], d["alpha"][s], d["beta"][s], S, out=o)
     e1.record()
     torch.cuda.synchronize()
-    return {"B": B, "H": H, "D": D, "steps": n, "ms_per_step": e0.elapsed_time(e1) / n}
+    ms = e0.elapsed_time(e1) / n
+    # Context for the decode roofline: torch's in-place elementwise scaling of
+    # the same fp32 state (one read and one write of every byte, nothing else).
+    for _ in range(3):
+        S.mul_(0.5)
+    e0.record()
+    for _ in range(20):
+        S.mul_(0.5)
+    e1.record()
+    torch.cuda.synchronize()
+    rmw_gbs = 2 * S.numel() * 4 / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e9
+    return {"B": B, "H": H, "D": D, "steps": n, "ms_per_step": ms, "state_rmw_gbs": rmw_gbs}
 
 
 # ---------------------------------------------------------------------------
@@ -370,7 +381,8 @@ def main():
                          "ms_per_step": dc["ms_per_step"],
                          "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": gbs,
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+                                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                         "state_rmw_gbs": dc["state_rmw_gbs"]}
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -13,17 +13,33 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// Gate kind and input form: unknown values are invalid, reserved ones unsupported.
+kda_status_t check_kinds(const kda_shape_t *s) {
+  if (s->gate != KDA_GATE_CHANNEL && s->gate != KDA_GATE_HEAD) return KDA_ERR_INVALID_ARGUMENT;
+  if (s->input_form != KDA_INPUT_FINAL && s->input_form != KDA_INPUT_PREACT) return KDA_ERR_INVALID_ARGUMENT;
+  if (s->input_form != KDA_INPUT_FINAL) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+// alpha holds d_k floats per (token, head) rows of 16 bytes, or one float.
+bool alpha_aligned(const kda_shape_t *s, const void *alpha) {
+  return s->gate == KDA_GATE_HEAD ? aligned4(alpha) : aligned16(alpha);
+}
+
 // Shape checks shared by prefill and its workspace query.
 kda_status_t check_prefill_shape(const kda_shape_t *s, bool varlen) {
   if (s == nullptr) return KDA_ERR_INVALID_ARGUMENT;
   if (s->num_seqs < 0 || s->total_tokens < 0 || s->num_heads < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (s->d_k < 1 || s->d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (s->qkv_dtype != KDA_F32 && s->qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARGUMENT;
+  if (s->gate != KDA_GATE_CHANNEL && s->gate != KDA_GATE_HEAD) return KDA_ERR_INVALID_ARGUMENT;
+  if (s->input_form != KDA_INPUT_FINAL && s->input_form != KDA_INPUT_PREACT) return KDA_ERR_INVALID_ARGUMENT;
   if (!varlen) {
     if (s->seq_len < 0) return KDA_ERR_INVALID_ARGUMENT;
     if ((int64_t)s->num_seqs * (int64_t)s->seq_len != s->total_tokens) return KDA_ERR_INVALID_ARGUMENT;
   }
   if (s->d_k != s->d_v || !supported_dim(s->d_k)) return KDA_ERR_UNSUPPORTED;
+  if (check_kinds(s) != KDA_OK) return check_kinds(s);
   // Grid limits: one workgroup per (chunk, head) in the chunk-local kernel.
   if (kda::max_chunks(*s) * (int64_t)s->num_heads >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
   // The state pass addresses one chunk's rows of v and o with 32-bit offsets.
@@ -75,7 +91,7 @@ kda_status_t check_prefill_call(const kda_shape_t *shape, const void *q, const v
   if (has_tokens) {
     if (!q || !k || !alpha || (need_v && !v) || (need_beta && !beta) || (need_o && !o))
       return KDA_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(alpha) || (need_v && !aligned16(v)) ||
+    if (!aligned16(q) || !aligned16(k) || !alpha_aligned(shape, alpha) || (need_v && !aligned16(v)) ||
         (need_beta && !aligned4(beta)) || (need_o && !aligned16(o)))
       return KDA_ERR_INVALID_ARGUMENT;
   }
@@ -140,10 +156,13 @@ kda_status_t kda_decode_step(const kda_shape_t *shape, const void *q, const void
     return KDA_ERR_INVALID_ARGUMENT;
   if (s.qkv_dtype != KDA_F32 && s.qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARGUMENT;
   if (s.d_k < 1 || s.d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (s.gate != KDA_GATE_CHANNEL && s.gate != KDA_GATE_HEAD) return KDA_ERR_INVALID_ARGUMENT;
+  if (s.input_form != KDA_INPUT_FINAL && s.input_form != KDA_INPUT_PREACT) return KDA_ERR_INVALID_ARGUMENT;
   if (s.d_k != s.d_v || !supported_dim(s.d_k)) return KDA_ERR_UNSUPPORTED;
+  if (check_kinds(shape) != KDA_OK) return check_kinds(shape);
   if (s.num_seqs == 0) return KDA_OK;
   if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned4(beta) ||
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !alpha_aligned(shape, alpha) || !aligned4(beta) ||
       !aligned16(S) || !aligned16(o))
     return KDA_ERR_INVALID_ARGUMENT;
   if ((int64_t)s.num_seqs * s.num_heads * (s.d_v / (s.d_v >= 64 ? 64 : s.d_v)) >= ((int64_t)1 << 31))

@@ -1,4 +1,5 @@
-// Single-token decode step of the KDA layer.
+// Single-token decode step of the KDA layer (and of its scalar-gate form,
+// where every alpha_i of a head is the same one rate).
 //
 // For one (sequence, head) and one new token (q, k, v, alpha, beta) the
 // update rule S' = (I - beta k k^T) Diag(alpha) S + beta k v^T (dimsnsums.com
@@ -39,7 +40,7 @@ struct DecodeCfg {
   static_assert(NT >= D, "one lane per key channel for q.k");
 };
 
-template <int D, typename TIn>
+template <int D, typename TIn, int GATE>
 __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ S,
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int r = r0 + p * RPP;
-    a[p] = alpha[nh * D + r];
+    a[p] = GATE == KDA_GATE_HEAD ? alpha[nh] : alpha[nh * D + r];
     kk[p] = to_f32(k[nh * D + r]);
     qq[p] = to_f32(q[nh * D + r]);
   }
@@ -132,28 +133,35 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
   }
 }
 
-template <int D, typename TIn>
+template <int D, typename TIn, int GATE>
 hipError_t launch_decode_t(const kda_shape_t &s, const void *q, const void *k, const void *v,
                            const float *alpha, const float *beta, float *S, float *o,
                            hipStream_t stream) {
   using Cfg = DecodeCfg<D>;
   const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
-  hipLaunchKernelGGL((decode_kernel<D, TIn>), dim3((unsigned)blocks), dim3(Cfg::NT), 0, stream,
+  hipLaunchKernelGGL((decode_kernel<D, TIn, GATE>), dim3((unsigned)blocks), dim3(Cfg::NT), 0, stream,
                      static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                      static_cast<const TIn *>(v), alpha, beta, S, o);
   return hipGetLastError();
 }
 
-template <typename TIn>
+template <typename TIn, int GATE>
 hipError_t dispatch_d(const kda_shape_t &s, const void *q, const void *k, const void *v,
                       const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
   switch (s.d_k) {
-    case 16: return launch_decode_t<16, TIn>(s, q, k, v, alpha, beta, S, o, st);
-    case 32: return launch_decode_t<32, TIn>(s, q, k, v, alpha, beta, S, o, st);
-    case 64: return launch_decode_t<64, TIn>(s, q, k, v, alpha, beta, S, o, st);
-    case 128: return launch_decode_t<128, TIn>(s, q, k, v, alpha, beta, S, o, st);
+    case 16: return launch_decode_t<16, TIn, GATE>(s, q, k, v, alpha, beta, S, o, st);
+    case 32: return launch_decode_t<32, TIn, GATE>(s, q, k, v, alpha, beta, S, o, st);
+    case 64: return launch_decode_t<64, TIn, GATE>(s, q, k, v, alpha, beta, S, o, st);
+    case 128: return launch_decode_t<128, TIn, GATE>(s, q, k, v, alpha, beta, S, o, st);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename TIn>
+hipError_t dispatch_gate(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
+  if (s.gate == KDA_GATE_HEAD) return dispatch_d<TIn, KDA_GATE_HEAD>(s, q, k, v, alpha, beta, S, o, st);
+  return dispatch_d<TIn, KDA_GATE_CHANNEL>(s, q, k, v, alpha, beta, S, o, st);
 }
 
 }  // namespace
@@ -161,8 +169,8 @@ hipError_t dispatch_d(const kda_shape_t &s, const void *q, const void *k, const 
 hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, float *S, float *o,
                          hipStream_t stream) {
-  if (s.qkv_dtype == KDA_BF16) return dispatch_d<__bf16>(s, q, k, v, alpha, beta, S, o, stream);
-  return dispatch_d<float>(s, q, k, v, alpha, beta, S, o, stream);
+  if (s.qkv_dtype == KDA_BF16) return dispatch_gate<__bf16>(s, q, k, v, alpha, beta, S, o, stream);
+  return dispatch_gate<float>(s, q, k, v, alpha, beta, S, o, stream);
 }
 
 }  // namespace kda

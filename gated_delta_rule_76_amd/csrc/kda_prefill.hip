@@ -443,6 +443,33 @@ __device__ __forceinline__ void row_next8(float (&x)[8], const float (&z)[8]) {
                : "v"(z[0]), "v"(z[1]), "v"(z[2]), "v"(z[3]), "v"(z[4]), "v"(z[5]), "v"(z[6]), "v"(z[7]));
 }
 
+// The same two scans and the exclusive suffix for one value per lane (a
+// decay rate shared by every channel of the token).
+__device__ __forceinline__ void row_scans1(float &y, float &z) {
+  asm volatile("s_nop 1\n"
+               "v_mul_f32_dpp %0, %0, %0 row_shr:1\n"
+               "v_mul_f32_dpp %1, %1, %1 row_shl:1\n"
+               "s_nop 1\n"
+               "v_mul_f32_dpp %0, %0, %0 row_shr:2\n"
+               "v_mul_f32_dpp %1, %1, %1 row_shl:2\n"
+               "s_nop 1\n"
+               "v_mul_f32_dpp %0, %0, %0 row_shr:4\n"
+               "v_mul_f32_dpp %1, %1, %1 row_shl:4\n"
+               "s_nop 1\n"
+               "v_mul_f32_dpp %0, %0, %0 row_shr:8\n"
+               "v_mul_f32_dpp %1, %1, %1 row_shl:8\n"
+               : "+v"(y), "+v"(z));
+}
+
+__device__ __forceinline__ float row_next1(float z) {
+  float x = 1.f;
+  asm volatile("s_nop 1\n"
+               "v_mov_b32_dpp %0, %1 row_shl:1\n"
+               : "+v"(x)
+               : "v"(z));
+  return x;
+}
+
 template <int D>
 struct LocCfg {
   static constexpr int DK = D < 32 ? 32 : D;
@@ -469,7 +496,7 @@ __device__ __forceinline__ int gram_plane(int R, int J) {
 __device__ __forceinline__ int tb_ct(int u) { return u < 4 ? u >> 1 : u - 2; }
 __device__ __forceinline__ int tb_kb(int u) { return u < 4 ? u & 1 : 1; }
 
-template <int D, typename TIn, typename P>
+template <int D, typename TIn, typename P, int GATE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void chunk_local_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ alpha,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
@@ -515,12 +542,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
   const float bv = beta[load_token(t0, tid & (C - 1), nvalid, total_tokens) * H + h];
   Raw8<TIn> kr[NKB], qr[NKB];
   float4 ar0[NKB], ar1[NKB];
+  float ah = 1.f;  // KDA_GATE_HEAD: the token's one rate
+  if constexpr (GATE == KDA_GATE_HEAD) {
+    ah = alpha[tok * H + h];
+  } else {
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    const int ch = kb * 32 + 8 * g;
-    const int64_t off = (tok * H + h) * D + (ch < D ? ch : 0);
-    ar0[kb] = *reinterpret_cast<const float4 *>(alpha + off);
-    ar1[kb] = *reinterpret_cast<const float4 *>(alpha + off + 4);
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int ch = kb * 32 + 8 * g;
+      const int64_t off = (tok * H + h) * D + (ch < D ? ch : 0);
+      ar0[kb] = *reinterpret_cast<const float4 *>(alpha + off);
+      ar1[kb] = *reinterpret_cast<const float4 *>(alpha + off + 4);
+    }
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -535,15 +567,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
   // ---- in-block decay products -------------------------------------------------
   float bp[NKB][8], bs[NKB][8];
   bool tiny = false;
+  float hy = rv ? ah : 1.f, hz = hy;  // KDA_GATE_HEAD: one scan, shared by every channel
+  if constexpr (GATE == KDA_GATE_HEAD) row_scans1(hy, hz);
+  const float hs = GATE == KDA_GATE_HEAD ? row_next1(hz) : 1.f;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    const bool ok = rv && kb * 32 + 8 * g < D;
-    const float a[8] = {ar0[kb].x, ar0[kb].y, ar0[kb].z, ar0[kb].w, ar1[kb].x, ar1[kb].y, ar1[kb].z, ar1[kb].w};
-    float z[8];
+    if constexpr (GATE == KDA_GATE_HEAD) {
+      // Padding channels (d = 16) keep the token's products: their k and q
+      // are zero and Gamma_C is stored for real channels only.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bp[kb][j] = z[j] = ok ? a[j] : 1.f;
-    row_scans8(bp[kb], z);
-    row_next8(bs[kb], z);
+      for (int j = 0; j < 8; ++j) {
+        bp[kb][j] = hy;
+        bs[kb][j] = hs;
+      }
+    } else {
+      const bool ok = rv && kb * 32 + 8 * g < D;
+      const float a[8] = {ar0[kb].x, ar0[kb].y, ar0[kb].z, ar0[kb].w, ar1[kb].x, ar1[kb].y, ar1[kb].z, ar1[kb].w};
+      float z[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bp[kb][j] = z[j] = ok ? a[j] : 1.f;
+      row_scans8(bp[kb], z);
+      row_next8(bs[kb], z);
+    }
     if (m == 15) {
       *reinterpret_cast<float4 *>(&s_bt[wave * DK + kb * 32 + 8 * g]) =
           make_float4(bp[kb][0], bp[kb][1], bp[kb][2], bp[kb][3]);
@@ -683,7 +728,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
       if (rr < nvalid && jj < nvalid) {
         for (int ch = 0; ch < D; ++ch) {
           float f = 1.f;
-          for (int s = jj + 1; s <= rr; ++s) f *= alpha[((t0 + s) * H + h) * D + ch];
+          for (int s = jj + 1; s <= rr; ++s)
+            f *= GATE == KDA_GATE_HEAD ? alpha[(t0 + s) * H + h] : alpha[((t0 + s) * H + h) * D + ch];
           const int64_t orr = ((t0 + rr) * H + h) * D + ch, ojj = ((t0 + jj) * H + h) * D + ch;
           const float kj = to_f32(k[ojj]) * f;
           a_acc += to_f32(k[orr]) * kj;
@@ -1116,7 +1162,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   }
 }
 
-template <int D, typename TIn, typename P>
+template <int D, typename TIn, typename P, int GATE>
 hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, const int32_t *cu,
                             const float *S0, float *o, float *S_T, void *workspace,
@@ -1134,7 +1180,7 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (mc > 0) {
-      hipLaunchKernelGGL((chunk_local_kernel<D, TIn, P>), dim3((unsigned)(mc * H)), dim3(NT), 0, stream,
+      hipLaunchKernelGGL((chunk_local_kernel<D, TIn, P, GATE>), dim3((unsigned)(mc * H)), dim3(NT), 0, stream,
                          qp, kp, alpha, beta, cu, s.seq_len, N, H, s.total_tokens, mc, base, recs);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1151,7 +1197,7 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   return e;
 }
 
-template <typename TIn>
+template <typename TIn, int GATE>
 hipError_t dispatch_prefill(const kda_shape_t &s, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, const int32_t *cu,
                             const float *S0, float *o, float *S_T, void *ws, hipStream_t st,
@@ -1160,12 +1206,21 @@ hipError_t dispatch_prefill(const kda_shape_t &s, const void *q, const void *k, 
   // 16-wide heads) the fp32 matrix-core path.
   using PB = typename std::conditional<std::is_same<TIn, __bf16>::value, SplitBF16, F32>::type;
   switch (s.d_k) {
-    case 16: return launch_prefill_t<16, TIn, F32>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 32: return launch_prefill_t<32, TIn, PB>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 64: return launch_prefill_t<64, TIn, PB>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 128: return launch_prefill_t<128, TIn, PB>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 16: return launch_prefill_t<16, TIn, F32, GATE>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 32: return launch_prefill_t<32, TIn, PB, GATE>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 64: return launch_prefill_t<64, TIn, PB, GATE>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 128: return launch_prefill_t<128, TIn, PB, GATE>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename TIn>
+hipError_t dispatch_gate(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, const int32_t *cu, const float *S0,
+                         float *o, float *S_T, void *ws, hipStream_t st, int ph) {
+  if (s.gate == KDA_GATE_HEAD)
+    return dispatch_prefill<TIn, KDA_GATE_HEAD>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+  return dispatch_prefill<TIn, KDA_GATE_CHANNEL>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
 }
 
 }  // namespace
@@ -1175,10 +1230,10 @@ hipError_t launch_prefill(const kda_shape_t &s, const void *q, const void *k, co
                           const float *S0, float *o, float *S_T, void *workspace,
                           hipStream_t stream, int phases) {
   if (s.qkv_dtype == KDA_BF16)
-    return dispatch_prefill<__bf16>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
-                                    phases);
-  return dispatch_prefill<float>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
+    return dispatch_gate<__bf16>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
                                  phases);
+  return dispatch_gate<float>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
+                              phases);
 }
 
 }  // namespace kda

@@ -15,6 +15,8 @@ Distributions (per the workloads the layer is measured on):
   alpha    exp(-softplus(N(0,1) + shift)) per (token, head, key channel),
            fp32; shift 0 ("medium", mean ~0.5), +2 ("strong", mean
            ~0.14, the prefill/decode workloads), -4 ("weak", mean ~0.97);
+           with gate="head" the same law with one draw per (token, head)
+           (the scalar-gate form);
   state    std * N(0,1) fp32 (std 0.02 for the varlen and decode workloads);
   lengths  uniform integers in [lo, hi] inclusive.
 
@@ -63,18 +65,21 @@ def varlen_lengths(n, lo, hi, seed=0):
     return [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=g)]
 
 
-def token_inputs(T, H, D, dtype=torch.bfloat16, decay="strong", seed=0, device="cpu", dv=None):
+def token_inputs(T, H, D, dtype=torch.bfloat16, decay="strong", seed=0, device="cpu", dv=None,
+                 gate="channel"):
     """q, k, v, alpha, beta for T tokens x H heads (token-major layout).
 
     Returns a dict: q, k [T,H,D] and v [T,H,dv] in ``dtype``; alpha [T,H,D]
-    and beta [T,H] fp32.
+    (gate="channel") or [T,H] (gate="head") and beta [T,H] fp32.
     """
+    if gate not in ("channel", "head"):
+        raise ValueError("gate is 'channel' or 'head'")
     dv = D if dv is None else dv
     shift = DECAY_SHIFT[decay]
     q = _unit(_randn_tokens((T, H, D), seed, _STREAM["q"], device)).to(dtype)
     k = _unit(_randn_tokens((T, H, D), seed, _STREAM["k"], device)).to(dtype)
     v = _randn_tokens((T, H, dv), seed, _STREAM["v"], device).to(dtype)
-    a = _randn_tokens((T, H, D), seed, _STREAM["alpha"], device)
+    a = _randn_tokens((T, H, D) if gate == "channel" else (T, H), seed, _STREAM["alpha"], device)
     alpha = torch.exp(-torch.nn.functional.softplus(a + shift))
     del a
     beta = torch.sigmoid(_randn_tokens((T, H), seed, _STREAM["beta"], device))
@@ -89,7 +94,7 @@ def state(N, H, D, std=0.02, seed=0, device="cpu", dv=None, stream_offset=0):
 
 
 def prefill_inputs(lengths, H, D, dtype=torch.bfloat16, decay="strong", s0_std=None,
-                   seed=0, device="cpu"):
+                   seed=0, device="cpu", gate="channel"):
     """Packed prefill batch for sequences of the given lengths.
 
     Returns token_inputs(...) plus ``cu_seqlens`` (int32 [N+1], on device),
@@ -98,7 +103,7 @@ def prefill_inputs(lengths, H, D, dtype=torch.bfloat16, decay="strong", s0_std=N
     """
     lengths = [int(x) for x in lengths]
     T = sum(lengths)
-    d = token_inputs(T, H, D, dtype, decay, seed, device)
+    d = token_inputs(T, H, D, dtype, decay, seed, device, gate=gate)
     cu = [0]
     for L in lengths:
         cu.append(cu[-1] + L)
@@ -109,14 +114,14 @@ def prefill_inputs(lengths, H, D, dtype=torch.bfloat16, decay="strong", s0_std=N
 
 
 def decode_inputs(B, H, D, steps, dtype=torch.bfloat16, decay="strong", s_std=0.02,
-                  seed=0, device="cpu"):
+                  seed=0, device="cpu", gate="channel"):
     """State [B,H,D,D] plus ``steps`` per-step token sets stacked on axis 0.
 
-    Returns dict: S fp32 [B,H,D,D]; q, k, v [steps,B,H,D]; alpha [steps,B,H,D];
-    beta [steps,B,H].  Step s uses token row s*B .. s*B+B-1 of one draw of
+    Returns dict: S fp32 [B,H,D,D]; q, k, v [steps,B,H,D]; alpha [steps,B,H,D]
+    (or [steps,B,H] with gate="head"); beta [steps,B,H].  Step s uses token row s*B .. s*B+B-1 of one draw of
     steps*B tokens.
     """
-    t = token_inputs(steps * B, H, D, dtype, decay, seed, device)
+    t = token_inputs(steps * B, H, D, dtype, decay, seed, device, gate=gate)
     out = {name: x.reshape((steps, B) + tuple(x.shape[1:])) for name, x in t.items()}
     out["S"] = state(B, H, D, s_std, seed, device)
     return out

@@ -23,6 +23,11 @@ KDA_ERR_WORKSPACE_TOO_SMALL = 3
 KDA_ERR_LAUNCH = 4
 KDA_F32 = 0
 KDA_BF16 = 1
+KDA_GATE_CHANNEL = 0
+KDA_GATE_HEAD = 1
+KDA_INPUT_FINAL = 0
+KDA_INPUT_PREACT = 1
+ABI_VERSION = 2
 CHUNK = 64
 
 _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
@@ -45,6 +50,8 @@ class KdaShape(ctypes.Structure):
         ("d_k", ctypes.c_int32),
         ("d_v", ctypes.c_int32),
         ("qkv_dtype", ctypes.c_int32),
+        ("gate", ctypes.c_int32),
+        ("input_form", ctypes.c_int32),
     ]
 
 
@@ -80,6 +87,9 @@ def lib():
     L.kda_prefill_state_pass.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
+    if L.kda_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{_LIB_PATH} has ABI version {L.kda_abi_version()}, this binding "
+                           f"needs {ABI_VERSION}; rebuild with `python -m gated_delta_rule_76_amd.build`")
     _lib = L
     return L
 
@@ -112,9 +122,22 @@ def _require_gpu(name, t, dtype=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def make_shape(num_seqs, seq_len, total_tokens, num_heads, d, dtype):
+def make_shape(num_seqs, seq_len, total_tokens, num_heads, d, dtype, gate=KDA_GATE_CHANNEL,
+               input_form=KDA_INPUT_FINAL):
     return KdaShape(int(num_seqs), int(seq_len), int(total_tokens), int(num_heads), int(d), int(d),
-                    _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype))
+                    _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype), int(gate),
+                    int(input_form))
+
+
+def _gate_of(alpha, q):
+    """KDA_GATE_CHANNEL when alpha has q's shape, KDA_GATE_HEAD when it has
+    q's shape without the channel axis (one rate per token and head)."""
+    if tuple(alpha.shape) == tuple(q.shape):
+        return KDA_GATE_CHANNEL
+    if tuple(alpha.shape) == tuple(q.shape[:-1]):
+        return KDA_GATE_HEAD
+    raise ValueError(f"alpha has shape {tuple(alpha.shape)}, expected {tuple(q.shape)} (a rate per "
+                     f"key channel) or {tuple(q.shape[:-1])} (a rate per head)")
 
 
 def prefill_workspace_size(num_seqs, total_tokens, num_heads, d, dtype=torch.bfloat16):
@@ -157,15 +180,15 @@ class PrefillCall:
                 N, seq_len = cu_seqlens.numel() - 1, 0
         else:
             raise ValueError("q must be [T, H, D] or [B, T, H, D]")
-        for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("alpha", alpha, q.shape),
-                             ("beta", beta, q.shape[:-1])):
+        gate = _gate_of(alpha, q)
+        for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("beta", beta, q.shape[:-1])):
             if tuple(t.shape) != tuple(shp):
                 raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
         if initial_state is not None:
             _require_gpu("initial_state", initial_state, torch.float32)
             if tuple(initial_state.shape) != (N, H, D, D):
                 raise ValueError(f"initial_state must be {(N, H, D, D)}")
-        self.shape = make_shape(N, seq_len, total, H, D, q.dtype)
+        self.shape = make_shape(N, seq_len, total, H, D, q.dtype, gate)
         self.o = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=dev)
         _require_gpu("out", self.o, torch.float32)
         self.S_T = None
@@ -217,6 +240,8 @@ def prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
     packed varlen batch when ``cu_seqlens`` [N+1] int32 is given), or
     [B, T, H, D] for a dense batch of B equal-length sequences; beta
     [T, H] / [B, T, H].  q, k, v are bf16 or fp32; alpha, beta fp32.
+    alpha of beta's shape (one rate per token and head) selects the
+    scalar-gate form.
     initial_state [N, H, D, D] fp32 or None (zeros).  o is fp32 with v's
     shape; S_T is [N, H, D, D] fp32 (None if output_final_state is False).
     ``final_state`` may be ``initial_state`` for an in-place update.
@@ -228,7 +253,8 @@ def prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
 
 def decode_step(q, k, v, alpha, beta, state, out=None):
     """One decode step for N sequences: q, k, v, alpha [N, H, D]; beta [N, H];
-    state [N, H, D, D] fp32 updated in place.  Returns o [N, H, D] fp32."""
+    state [N, H, D, D] fp32 updated in place.  Returns o [N, H, D] fp32.
+    alpha [N, H] (one rate per head) selects the scalar-gate form."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require_gpu(name, t)
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -239,13 +265,14 @@ def decode_step(q, k, v, alpha, beta, state, out=None):
     if q.dim() != 3:
         raise ValueError("decode inputs are [N, H, D]")
     N, H, D = q.shape
-    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("alpha", alpha, q.shape),
+    gate = _gate_of(alpha, q)
+    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape),
                          ("beta", beta, q.shape[:-1]), ("state", state, (N, H, D, D))):
         if tuple(t.shape) != tuple(shp):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
     o = out if out is not None else torch.empty((N, H, D), dtype=torch.float32, device=q.device)
     _require_gpu("out", o, torch.float32)
-    shape = make_shape(N, 1, N, H, D, q.dtype)
+    shape = make_shape(N, 1, N, H, D, q.dtype, gate)
     st = lib().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(state), _ptr(o), _stream(q.device))
     _check(st, "kda_decode_step")

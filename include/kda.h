@@ -15,12 +15,22 @@
  * (Diag(alpha_t) multiplies S from the left), beta_t one scalar per token
  * and head.
  *
+ * Gate kinds (shape->gate):
+ *  - KDA_GATE_CHANNEL: the KDA rule above, alpha [tokens][H][d_k].
+ *  - KDA_GATE_HEAD: one decay rate per token and head, alpha [tokens][H]:
+ *    Diag(alpha_t) = alpha_t I, the scalar-gated delta rule of the Gated
+ *    DeltaNet layers that the ainewsfeed.tech page on the GLM-5.3-Flash
+ *    configuration names (the pages print no formula for it; a scalar
+ *    decay per head is the reading taken).
+ *
  * Conventions shared by every entry point
  * ----------------------------------------
  *  - Tensor arguments are DEVICE pointers to contiguous, row-major arrays
  *    on the current HIP device, aligned to 16 bytes (beta: 4 bytes).
  *    Layouts are token-major:
- *        q, k, alpha   [tokens][H][d_k]
+ *        q, k          [tokens][H][d_k]
+ *        alpha         [tokens][H][d_k]  (KDA_GATE_CHANNEL)
+ *                      [tokens][H]       (KDA_GATE_HEAD; 4-byte aligned)
  *        v, o          [tokens][H][d_v]
  *        beta          [tokens][H]
  *        state         [N][H][d_k][d_v]        (fp32)
@@ -53,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 #define KDA_CHUNK 64 /* prefill chunk length (tokens); not a semantic parameter */
 
 typedef enum kda_status {
@@ -70,6 +80,19 @@ typedef enum kda_dtype {
     KDA_BF16 = 1
 } kda_dtype_t;
 
+/* Layout of alpha: one decay rate per key channel (KDA) or per head. */
+typedef enum kda_gate {
+    KDA_GATE_CHANNEL = 0, /* alpha [tokens][H][d_k] */
+    KDA_GATE_HEAD = 1     /* alpha [tokens][H] */
+} kda_gate_t;
+
+/* What q, k, alpha and beta hold.  KDA_INPUT_FINAL: the values the update
+ * rule uses.  KDA_INPUT_PREACT is reserved (rejected as unsupported). */
+typedef enum kda_input_form {
+    KDA_INPUT_FINAL = 0,
+    KDA_INPUT_PREACT = 1
+} kda_input_form_t;
+
 /* Problem shape.  Dense batch: cu_seqlens == NULL, num_seqs sequences of
  * seq_len tokens each, sequence n owning tokens n*seq_len .. (n+1)*seq_len-1,
  * and total_tokens == num_seqs * seq_len.  Varlen batch: cu_seqlens != NULL,
@@ -82,6 +105,8 @@ typedef struct kda_shape {
     int32_t d_k;          /* key channels per head */
     int32_t d_v;          /* value channels per head (must equal d_k) */
     int32_t qkv_dtype;    /* kda_dtype_t of q, k, v */
+    int32_t gate;         /* kda_gate_t: layout of alpha */
+    int32_t input_form;   /* kda_input_form_t */
 } kda_shape_t;
 
 /* Version of this ABI (KDA_ABI_VERSION of the built library). */
@@ -93,7 +118,7 @@ const char *kda_status_string(kda_status_t status);
 /* Bytes of device workspace kda_prefill needs for `shape` (written to
  * *bytes).  The size depends on N, H, d and total_tokens only: an upper bound
  * on the number of 64-token chunks, floor(total_tokens/64) + N, times one
- * record of chunk operands per chunk and head (128.5 KiB at d = 128), plus a
+ * record of chunk operands per chunk and head (108.5 KiB at d = 128), plus a
  * small schedule table.  Returns KDA_ERR_INVALID_ARGUMENT /
  * KDA_ERR_UNSUPPORTED for a shape kda_prefill would reject. */
 kda_status_t kda_prefill_workspace_size(const kda_shape_t *shape, size_t *bytes);
@@ -103,7 +128,8 @@ kda_status_t kda_prefill_workspace_size(const kda_shape_t *shape, size_t *bytes)
  * sequence.
  *   q, k        [total_tokens][H][d_k]      fp32 or bf16 (qkv_dtype)
  *   v           [total_tokens][H][d_v]      same dtype
- *   alpha       [total_tokens][H][d_k]      fp32, per key channel
+ *   alpha       [total_tokens][H][d_k]      fp32, per key channel, or
+ *               [total_tokens][H]           per head (shape->gate)
  *   beta        [total_tokens][H]           fp32
  *   cu_seqlens  [N+1] int32 device array, or NULL for a dense batch
  *   S0          [N][H][d_k][d_v] fp32 initial states, or NULL for zeros
@@ -161,7 +187,7 @@ kda_status_t kda_prefill_state_pass(const kda_shape_t *shape,
  *               no cu_seqlens
  *   q, k        [N][H][d_k]   fp32 or bf16 (qkv_dtype)
  *   v           [N][H][d_v]
- *   alpha       [N][H][d_k]   fp32
+ *   alpha       [N][H][d_k]   fp32 ([N][H] with KDA_GATE_HEAD)
  *   beta        [N][H]        fp32
  *   S           [N][H][d_k][d_v] fp32, updated in place
  *   o           [N][H][d_v]   fp32 output (must not overlap S) */

@@ -33,8 +33,8 @@ def L():
     return kda.lib()
 
 
-def shape(N=1, T=64, H=2, d=16, dtype=0, total=None):
-    return kda.KdaShape(N, T, N * T if total is None else total, H, d, d, dtype)
+def shape(N=1, T=64, H=2, d=16, dtype=0, total=None, gate=0, form=0):
+    return kda.KdaShape(N, T, N * T if total is None else total, H, d, d, dtype, gate, form)
 
 
 def prefill(L, s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, cu=None, S0=None, o=FAKE, ST=FAKE,
@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.kda_abi_version() == 1
+    assert L.kda_abi_version() == 2
     names = [L.kda_status_string(i).decode() for i in range(5)]
     assert names == ["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                      "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_LAUNCH"]
@@ -116,6 +116,30 @@ def test_prefill_validation(L):
     assert prefill(L, kda.KdaShape(0, 0, 5, 2, 16, 16, 0), cu=FAKE) == INVALID   # tokens, no sequences
 
 
+def test_gate_and_input_form_validation(L):
+    need = kda.prefill_workspace_size(1, 64, 2, 16, torch.float32)
+    out = ctypes.c_size_t(0)
+    assert prefill(L, shape(gate=2)) == INVALID
+    assert prefill(L, shape(gate=-1)) == INVALID
+    assert prefill(L, shape(form=2)) == INVALID
+    assert prefill(L, shape(form=1)) == UNSUPPORTED
+    assert L.kda_prefill_workspace_size(ctypes.byref(shape(gate=3)), ctypes.byref(out)) == INVALID
+    # the workspace size does not depend on the gate kind
+    assert L.kda_prefill_workspace_size(ctypes.byref(shape(gate=1)), ctypes.byref(out)) == OK
+    assert out.value == need
+    # a per-head alpha needs 4-byte alignment only: FAKE + 4 passes the
+    # alignment checks (and the call stops at the workspace check)
+    assert prefill(L, shape(gate=1), a=FAKE + 2) == INVALID
+    assert prefill(L, shape(gate=1), a=FAKE + 4, ws_bytes=need - 1) == WS_SMALL
+    assert prefill(L, shape(gate=0), a=FAKE + 4, ws_bytes=need - 1) == INVALID
+    d = lambda **kw: kda.KdaShape(4, 1, 4, 2, 128, 128, 1, kw.get("gate", 0), kw.get("form", 0))
+    assert decode(L, d(gate=2)) == INVALID
+    assert decode(L, d(form=2)) == INVALID
+    assert decode(L, d(form=1)) == UNSUPPORTED
+    assert decode(L, d(gate=1), a=FAKE + 2) == INVALID
+    assert decode(L, kda.KdaShape(0, 1, 0, 2, 128, 128, 1, 1, 0)) == OK
+
+
 def test_prefill_phase_validation(L):
     need = kda.prefill_workspace_size(1, 64, 2, 16, torch.float32)
     s = ctypes.byref(shape())
@@ -146,6 +170,14 @@ def test_decode_validation(L):
     for field in ("q", "k", "v", "a", "S", "o"):
         assert decode(L, good, **{field: FAKE + 4}) == INVALID, field
     assert decode(L, kda.KdaShape(0, 1, 0, 2, 128, 128, 1)) == OK
+
+
+def test_binding_takes_the_gate_kind_from_alpha():
+    q = torch.zeros(4, 2, 16)
+    assert kda._gate_of(torch.zeros(4, 2, 16), q) == kda.KDA_GATE_CHANNEL
+    assert kda._gate_of(torch.zeros(4, 2), q) == kda.KDA_GATE_HEAD
+    with pytest.raises(ValueError, match="alpha"):
+        kda._gate_of(torch.zeros(4, 16), q)
 
 
 def test_binding_refuses_cpu_tensors():

@@ -49,3 +49,13 @@ def test_workloads_table():
     assert w["long_1m"]["lengths"] == [1 << 20]
     assert sum(inputs.workload_lengths(w["varlen_8seq"])) > 8 * 1024
     assert math.prod([w["decode_b256"]["B"], w["decode_b256"]["H"]]) == 8192
+
+
+def test_scalar_gate_inputs():
+    x = inputs.token_inputs(4096, 4, 64, torch.float32, "strong", seed=0, gate="head")
+    assert x["alpha"].shape == (4096, 4)
+    assert 0.10 < x["alpha"].mean().item() < 0.18
+    c = inputs.token_inputs(4096, 4, 64, torch.float32, "strong", seed=0)
+    assert torch.equal(x["q"], c["q"]) and torch.equal(x["v"], c["v"])   # only alpha differs
+    d = inputs.decode_inputs(4, 2, 16, steps=3, seed=2, gate="head")
+    assert d["alpha"].shape == (3, 4, 2)
