@@ -18,8 +18,10 @@ counter summary when it was taken on the current kernel source); the decode
 rate (B=256, H=32, d=128, 100 in-place steps) with its own roofline; and the
 fp64 CPU oracle timed on the host over the whole prefill_4k workload.
 
-``--oracle-rates`` times only the CPU oracle, on every workload, and prints
-those rates as one JSON line.
+The line also carries the scalar-gate form (one alpha per token and head) on
+the same prefill and decode shapes, under ``scalar_gate`` (``--no-variants``
+skips it).  ``--oracle-rates`` times only the CPU oracle, on every workload,
+and prints those rates as one JSON line.
 """
 
 from __future__ import annotations
@@ -56,6 +58,8 @@ def _parse():
     p.add_argument("--workload", default="prefill_4k", choices=sorted(WORKLOAD_TEXT))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the scalar-gate measurements")
     p.add_argument("--decode-batch", type=int, default=256)
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
@@ -73,8 +77,17 @@ def _parse():
 # The record is the chunk-local kernel's output per 64 tokens and head,
 # read once by the state pass (its d/16 workgroups per head share it in L2).
 # ---------------------------------------------------------------------------
-BYTES_LAYER = 768 + 512 + 4 + 512
-BYTES_DECODE = 2 * 128 * 128 * 4 + 768 + 512 + 4 + 512   # per (sequence, head) and step
+# Decode: state read + write, q, k, v, alpha, beta, o per (sequence, head) and step.
+# Scalar gate (one alpha per token and head): alpha is 4 bytes instead of 512.
+ALPHA_BYTES = {"channel": 512, "head": 4}
+
+
+def layer_bytes(gate):
+    return 768 + ALPHA_BYTES[gate] + 4 + 512
+
+
+def decode_bytes(gate):
+    return 2 * 128 * 128 * 4 + 768 + ALPHA_BYTES[gate] + 4 + 512
 
 
 def record_bytes_per_token(d):
@@ -84,16 +97,16 @@ def record_bytes_per_token(d):
     return rec / 64.0
 
 
-def kernel_bytes(d):
+def kernel_bytes(d, gate="channel"):
     rb = record_bytes_per_token(d)
-    return {"chunk_local_kernel": 512 + 512 + 4 + rb, "chunk_state_kernel": rb + 256 + 512}
+    return {"chunk_local_kernel": 512 + ALPHA_BYTES[gate] + 4 + rb, "chunk_state_kernel": rb + 256 + 512}
 
 
 def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(name, steps, warmup, dev):
+def bench_prefill(name, steps, warmup, dev, gate="channel"):
     from gated_delta_rule_76_amd import inputs, kda
     spec = inputs.WORKLOADS[name]
     lens = inputs.workload_lengths(spec, seed=0)
@@ -102,7 +115,7 @@ def bench_prefill(name, steps, warmup, dev):
     calls = []
     for s in range(n_sets):
         d = inputs.prefill_inputs(lens, H, D, torch.bfloat16, spec["decay"], spec["s0_std"],
-                                  seed=s, device=dev)
+                                  seed=s, device=dev, gate=gate)
         cu = d["cu_seqlens"] if len(lens) > 1 else None
         calls.append(kda.PrefillCall(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], cu))
     total = sum(lens)
@@ -141,13 +154,13 @@ def bench_prefill(name, steps, warmup, dev):
                         "p90": float(np.percentile(per_call, 90))}}
 
 
-def bench_decode(B, dev):
+def bench_decode(B, dev, gate="channel"):
     from gated_delta_rule_76_amd import inputs, kda
     spec = inputs.WORKLOADS["decode_b256"]
     H, D = spec["H"], spec["D"]
     n = spec["steps"]
     d = inputs.decode_inputs(B, H, D, n, torch.bfloat16, spec["decay"], spec["s_std"],
-                             seed=0, device=dev)
+                             seed=0, device=dev, gate=gate)
     S = d["S"].clone()
     o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     for s in range(10):
@@ -185,12 +198,13 @@ _CPU_INPUTS = {}
 def _cpu_prefill_worker(heads):
     from threadpoolctl import threadpool_limits
 
-    from oracle import kda_recurrent
+    from oracle import gdn_recurrent, kda_recurrent
     a = _CPU_INPUTS
+    run = gdn_recurrent if a["gate"] == "head" else kda_recurrent
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         for _ in range(a["passes"]):
-            kda_recurrent(a["q"][:, heads], a["k"][:, heads], a["v"][:, heads], a["alpha"][:, heads],
+            run(a["q"][:, heads], a["k"][:, heads], a["v"][:, heads], a["alpha"][:, heads],
                           a["beta"][:, heads], None if a["S0"] is None else a["S0"][:, heads],
                           cu_seqlens=a["cu"])
         return time.perf_counter() - t0
@@ -199,13 +213,14 @@ def _cpu_prefill_worker(heads):
 def _cpu_decode_worker(pairs):
     from threadpoolctl import threadpool_limits
 
-    from oracle import kda_decode_step
+    from oracle import gdn_decode_step, kda_decode_step
     a = _CPU_INPUTS
+    step = gdn_decode_step if a["gate"] == "head" else kda_decode_step
     with threadpool_limits(limits=1):
         S = a["S"][pairs]
         t0 = time.perf_counter()
         for s in range(a["steps"]):
-            _, S = kda_decode_step(a["q"][s][pairs], a["k"][s][pairs], a["v"][s][pairs],
+            _, S = step(a["q"][s][pairs], a["k"][s][pairs], a["v"][s][pairs],
                                    a["alpha"][s][pairs], a["beta"][s][pairs], S)
         return time.perf_counter() - t0
 
@@ -221,7 +236,7 @@ def _pool_map(fn, n_items):
     return wall, sum(busy), len(groups)
 
 
-def oracle_prefill_rate(workload, max_tokens=None, passes=1):
+def oracle_prefill_rate(workload, max_tokens=None, passes=1, gate="channel"):
     """Oracle tokens/s/layer over ``workload`` (or its first ``max_tokens``
     tokens when the sequence is longer), all heads, ``passes`` repetitions."""
     from gated_delta_rule_76_amd import inputs
@@ -231,7 +246,8 @@ def oracle_prefill_rate(workload, max_tokens=None, passes=1):
     if prefix:
         lengths = [max_tokens]
     d = inputs.prefill_inputs(lengths, spec["H"], spec["D"], torch.bfloat16, spec["decay"],
-                              None if prefix else spec["s0_std"], seed=0, device="cpu")
+                              None if prefix else spec["s0_std"], seed=0, device="cpu", gate=gate)
+    _CPU_INPUTS["gate"] = gate
     _CPU_INPUTS.update({k: d[k].double().numpy() for k in ("q", "k", "v", "alpha", "beta")})
     _CPU_INPUTS["S0"] = None if d["S0"] is None else d["S0"].double().numpy()
     _CPU_INPUTS["cu"] = d["cu_seqlens"].numpy()
@@ -240,6 +256,8 @@ def oracle_prefill_rate(workload, max_tokens=None, passes=1):
     wall, busy, cores = _pool_map(_cpu_prefill_worker, spec["H"])
     _CPU_INPUTS.clear()
     what = (f"the first {T} tokens of {workload}" if prefix else f"the whole {workload} workload")
+    if gate == "head":
+        what += " with one alpha per token and head"
     return {"value": passes * T / wall, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
             "sample": f"{what} ({T} tokens x {spec['H']} heads, d={spec['D']}"
                       f"{', x%d passes' % passes if passes > 1 else ''}), numpy fp64 token-by-token "
@@ -247,23 +265,26 @@ def oracle_prefill_rate(workload, max_tokens=None, passes=1):
                       f"{busy:.1f} s CPU)"}
 
 
-def oracle_decode_rate(B=256, steps=100):
+def oracle_decode_rate(B=256, steps=100, gate="channel"):
     """Oracle steps/s: ``steps`` decode steps of B sequences x 32 heads, d=128."""
     from gated_delta_rule_76_amd import inputs
     spec = inputs.WORKLOADS["decode_b256"]
     H, D = spec["H"], spec["D"]
     d = inputs.decode_inputs(B, H, D, steps, torch.bfloat16, spec["decay"], spec["s_std"], seed=0,
-                             device="cpu")
+                             device="cpu", gate=gate)
     n = B * H
+    _CPU_INPUTS["gate"] = gate
     _CPU_INPUTS["S"] = d["S"].double().numpy().reshape(n, 1, D, D)
-    for k in ("q", "k", "v", "alpha"):
+    for k in ("q", "k", "v"):
         _CPU_INPUTS[k] = d[k].double().numpy().reshape(steps, n, 1, D)
+    _CPU_INPUTS["alpha"] = d["alpha"].double().numpy().reshape((steps, n, 1) + ((D,) if gate == "channel" else ()))
     _CPU_INPUTS["beta"] = d["beta"].double().numpy().reshape(steps, n, 1)
     _CPU_INPUTS["steps"] = steps
     wall, busy, cores = _pool_map(_cpu_decode_worker, n)
     _CPU_INPUTS.clear()
     return {"value": steps / wall, "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{steps} decode steps, B={B} H={H} d={D}, numpy fp64, {cores} processes "
+            "sample": f"{steps} decode steps, B={B} H={H} d={D}"
+                      f"{', one alpha per head' if gate == 'head' else ''}, numpy fp64, {cores} processes "
                       f"over (sequence, head) groups ({wall:.2f} s wall, {busy:.1f} s CPU)"}
 
 
@@ -288,6 +309,8 @@ def oracle_rates():
     lg = oracle_prefill_rate("long_1m", max_tokens=65536)
     lg["extrapolated_seconds_for_2^20_tokens"] = (1 << 20) / lg["value"]
     out["long_1m"] = lg
+    out["prefill_4k_scalar_gate"] = oracle_prefill_rate("prefill_4k", passes=3, gate="head")
+    out["decode_b256_scalar_gate"] = oracle_decode_rate(256, 100, gate="head")
     return out
 
 
@@ -305,6 +328,40 @@ def _traffic(kernel, workload):
     if t.get("source_sha256") != sha or t.get("workload") != workload or k is None:
         return None
     return k["fetch_bytes"] + k["write_bytes"]
+
+
+def prefill_summary(pf, gate):
+    """Rate, per-kernel algorithmic bandwidth and the dominant kernel's
+    roofline of one bench_prefill result."""
+    th = pf["total_tokens"] * pf["H"]
+    kb = kernel_bytes(pf["D"], gate)
+    times = {"chunk_local_kernel": pf["phases_ms"]["chunk_local"],
+             "chunk_state_kernel": pf["phases_ms"]["state_pass"]}
+    dom = max(times, key=times.get)
+    gbs = {k: th * kb[k] / (times[k] * 1e-3) / 1e9 for k in times}
+    lb = layer_bytes(gate)
+    layer_gbs = th * lb / (pf["ms"] * 1e-3) / 1e9
+    return {"value": pf["total_tokens"] / (pf["ms"] * 1e-3), "unit": "tokens/s/layer",
+            "ms_per_step": pf["ms"],
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": gbs[dom], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs[dom] / HBM_PEAK_GBS, "traffic": None,
+                         "launch_ms": times[dom], "bytes_per_token_head": kb[dom]},
+            "kernels": {k: {"ms": times[k], "bytes_per_token_head": kb[k], "achieved_gbs": gbs[k]}
+                        for k in times},
+            "layer_roofline": {"bound": "hbm", "bytes_per_token_head": lb, "achieved": layer_gbs,
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": layer_gbs / HBM_PEAK_GBS}}
+
+
+def decode_summary(dc, gate):
+    gbs = dc["B"] * dc["H"] * decode_bytes(gate) / (dc["ms_per_step"] * 1e-3) / 1e9
+    kind = "KDA" if gate == "channel" else "scalar-gate"
+    return {"metric": "%s decode steps/s (B=%d, H=32, d=128)" % (kind, dc["B"]),
+            "value": 1e3 / dc["ms_per_step"], "unit": "steps/s", "ms_per_step": dc["ms_per_step"],
+            "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None, "bytes_per_head_step": decode_bytes(gate)},
+            "state_rmw_gbs": dc["state_rmw_gbs"]}
 
 
 def main():
@@ -337,17 +394,12 @@ def main():
     print(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
     pf = bench_prefill(args.workload, args.steps, args.warmup, dev)
-    th = pf["total_tokens"] * pf["H"]
-    tok_s = pf["total_tokens"] / (pf["ms"] * 1e-3)
-    kb = kernel_bytes(pf["D"])
-    times = {"chunk_local_kernel": pf["phases_ms"]["chunk_local"],
-             "chunk_state_kernel": pf["phases_ms"]["state_pass"]}
-    dom = max(times, key=times.get)
-    achieved = th * kb[dom] / (times[dom] * 1e-3) / 1e9
-    traffic = _traffic(dom, args.workload)
+    ps = prefill_summary(pf, "channel")
+    dom = ps["roofline"]["kernel"]
+    ps["roofline"]["traffic"] = _traffic(dom, args.workload)
     out = {
         "metric": "KDA prefill tokens/s/layer (H=32, d=128)",
-        "value": tok_s,
+        "value": ps["value"],
         "unit": "tokens/s/layer",
         "n_gpus": 1,
         "steps": args.steps,
@@ -361,28 +413,24 @@ def main():
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}, bf16 q/k/v, "
                                "fp32 alpha/beta/state/o, chunk 64",
                    "total_tokens": pf["total_tokens"], "heads": pf["H"], "head_dim": pf["D"]},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "launch_ms": times[dom], "bytes_per_token_head": kb[dom]},
-        "kernels": {k: {"ms": times[k], "bytes_per_token_head": kb[k],
-                        "achieved_gbs": th * kb[k] / (times[k] * 1e-3) / 1e9} for k in times},
-        "layer_roofline": {"bound": "hbm", "bytes_per_token_head": BYTES_LAYER,
-                           "achieved": th * BYTES_LAYER / (pf["ms"] * 1e-3) / 1e9,
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": th * BYTES_LAYER / (pf["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "roofline": ps["roofline"],
+        "kernels": ps["kernels"],
+        "layer_roofline": ps["layer_roofline"],
         "call_ms": pf["call_ms"],
     }
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
-        dc = bench_decode(args.decode_batch, dev)
-        gbs = dc["B"] * dc["H"] * BYTES_DECODE / (dc["ms_per_step"] * 1e-3) / 1e9
-        out["decode"] = {"metric": "KDA decode steps/s (B=%d, H=32, d=128)" % dc["B"],
-                         "value": 1e3 / dc["ms_per_step"], "unit": "steps/s",
-                         "ms_per_step": dc["ms_per_step"],
-                         "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": gbs,
-                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-                         "state_rmw_gbs": dc["state_rmw_gbs"]}
+        out["decode"] = decode_summary(bench_decode(args.decode_batch, dev), "channel")
+    if not args.no_variants:
+        # The scalar-gate (Gated DeltaNet) form on the same shapes.
+        print("[bench] scalar gate", file=sys.stderr, flush=True)
+        pv = bench_prefill(args.workload, args.steps, args.warmup, dev, gate="head")
+        sg = {"prefill": prefill_summary(pv, "head")}
+        sg["prefill"]["metric"] = "scalar-gate prefill tokens/s/layer (H=32, d=128)"
+        sg["prefill"]["call_ms"] = pv["call_ms"]
+        if not args.no_decode:
+            sg["decode"] = decode_summary(bench_decode(args.decode_batch, dev, gate="head"), "head")
+        out["scalar_gate"] = sg
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -18,7 +18,8 @@
 // lanes), reduces x and y over rows with cross-lane shuffles and one LDS
 // round, and writes the state back.  Every lane loads alpha_i, k_i, q_i of
 // its own rows, and the v_j, beta it needs, before the state, so no load
-// waits on another after the state arrives.  The kernel is bound by HBM:
+// waits on another after the state arrives; q.k is summed from the rows in
+// registers.  The kernel is bound by HBM:
 // 2 x 64 KiB of state traffic per head and step against ~115 kflop.
 #include <hip/hip_runtime.h>
 
@@ -37,7 +38,7 @@ struct DecodeCfg {
   static constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0, "workgroup must be whole waves");
   static_assert(D % RPP == 0, "rows must tile evenly");
-  static_assert(NT >= D, "one lane per key channel for q.k");
+  static_assert(NT >= D, "one lane per value column in the final step");
 };
 
 template <int D, typename TIn, int GATE>
@@ -73,11 +74,21 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
   const int cj = tid < D ? tid : 0;
   const float vj = to_f32(v[nh * D + cj]);
   const float bt = beta[nh];
-  float qk_part = tid < D ? to_f32(q[nh * D + cj]) * to_f32(k[nh * D + cj]) : 0.f;
   float4 s[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) s[p] = *reinterpret_cast<const float4 *>(Sp + (int64_t)(r0 + p * RPP) * D);
+  // Every load is in flight before the first instruction that waits on one
+  // (otherwise the scheduler may move the q.k shuffles, which wait for q and
+  // k, above the state loads and serialise two memory round trips).
+  __builtin_amdgcn_sched_barrier(0);
 
+  // q.k from the rows already in registers: the lanes of column group 0
+  // hold every row exactly once.
+  float qk_part = 0.f;
+  if (cq == 0) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) qk_part += qq[p] * kk[p];
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
   float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
@@ -121,15 +132,18 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
   __syncthreads();
 
   const float w0 = s_w[cq * 4 + 0], w1 = s_w[cq * 4 + 1], w2 = s_w[cq * 4 + 2], w3 = s_w[cq * 4 + 3];
+  // The new state goes out with non-temporal stores: it is read again only
+  // at the next step, after the whole batch has streamed through, so keeping
+  // it in the caches only displaces lines still being read.
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int r = r0 + p * RPP;
-    float4 n;
-    n.x = a[p] * s[p].x + kk[p] * w0;
-    n.y = a[p] * s[p].y + kk[p] * w1;
-    n.z = a[p] * s[p].z + kk[p] * w2;
-    n.w = a[p] * s[p].w + kk[p] * w3;
-    *reinterpret_cast<float4 *>(Sp + (int64_t)r * D) = n;
+    f32x4 n;
+    n[0] = a[p] * s[p].x + kk[p] * w0;
+    n[1] = a[p] * s[p].y + kk[p] * w1;
+    n[2] = a[p] * s[p].z + kk[p] * w2;
+    n[3] = a[p] * s[p].w + kk[p] * w3;
+    __builtin_nontemporal_store(n, reinterpret_cast<f32x4 *>(Sp + (int64_t)r * D));
   }
 }
 
