@@ -19,9 +19,11 @@ bruteforce   the printed matrix product formed literally, fp64, tiny sizes
 exact        the printed matrix product in exact rational arithmetic
 scalar_gate  the scalar-gate (Gated DeltaNet) form: one decay rate per token
              and head instead of one per key channel
+prologue     rates, strengths and unit q, k from pre-activations, then the
+             recurrence
 
-Pins (every function is pinned by tests/test_oracle_pins.py and
-tests/test_oracle_scalar_gate.py against closed forms, invariants, a library
+Pins (every function is pinned by tests/test_oracle_pins.py,
+tests/test_oracle_scalar_gate.py and tests/test_oracle_prologue.py against closed forms, invariants, a library
 routine and a hand-worked golden example; see the module docstrings).  No function here is "parity unpinned".
 """
 
@@ -34,3 +36,4 @@ from .recurrence import (  # noqa: F401
 from .bruteforce import kda_bruteforce  # noqa: F401
 from .exact import kda_exact  # noqa: F401
 from .scalar_gate import gdn_decode_step, gdn_recurrent, gdn_step  # noqa: F401
+from . import prologue  # noqa: F401
