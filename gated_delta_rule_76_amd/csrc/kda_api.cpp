@@ -13,11 +13,10 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-// Gate kind and input form: unknown values are invalid, reserved ones unsupported.
+// Gate kind and input form: unknown values are invalid.
 kda_status_t check_kinds(const kda_shape_t *s) {
   if (s->gate != KDA_GATE_CHANNEL && s->gate != KDA_GATE_HEAD) return KDA_ERR_INVALID_ARGUMENT;
   if (s->input_form != KDA_INPUT_FINAL && s->input_form != KDA_INPUT_PREACT) return KDA_ERR_INVALID_ARGUMENT;
-  if (s->input_form != KDA_INPUT_FINAL) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 

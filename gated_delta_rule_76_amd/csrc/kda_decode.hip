@@ -41,7 +41,13 @@ struct DecodeCfg {
   static_assert(NT >= D, "one lane per value column in the final step");
 };
 
-template <int D, typename TIn, int GATE>
+// Pre-activation inputs (KDA_INPUT_PREACT): alpha = exp(-softplus(a)) =
+// 1 / (1 + e^a), beta = sigmoid(b), and q, k scaled by 1 / max(||.||_2, 1e-12).
+__device__ __forceinline__ float decay_from_preact(float a) { return 1.f / (1.f + expf(a)); }
+__device__ __forceinline__ float strength_from_preact(float b) { return 1.f / (1.f + expf(-b)); }
+__device__ __forceinline__ float inv_norm(float ss) { return 1.f / fmaxf(sqrtf(ss), 1e-12f); }
+
+template <int D, typename TIn, int GATE, int FORM>
 __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ S,
@@ -50,7 +56,7 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
   constexpr int TPR = Cfg::TPR, RPP = Cfg::RPP, PASSES = Cfg::PASSES, NW = Cfg::NW;
 
   __shared__ float s_red[NW][2][D];
-  __shared__ float s_qk[NW];
+  __shared__ float s_qk[NW][3];  // q.k, then ||k||^2, ||q||^2 (pre-activation inputs)
   __shared__ float s_w[D];
 
   const int tid = threadIdx.x;
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
   }
   const int cj = tid < D ? tid : 0;
   const float vj = to_f32(v[nh * D + cj]);
-  const float bt = beta[nh];
+  float bt = beta[nh];
   float4 s[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) s[p] = *reinterpret_cast<const float4 *>(Sp + (int64_t)(r0 + p * RPP) * D);
@@ -82,15 +88,35 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
   // k, above the state loads and serialise two memory round trips).
   __builtin_amdgcn_sched_barrier(0);
 
-  // q.k from the rows already in registers: the lanes of column group 0
-  // hold every row exactly once.
-  float qk_part = 0.f;
+  constexpr bool kPre = FORM == KDA_INPUT_PREACT;
+  if constexpr (kPre) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) a[p] = decay_from_preact(a[p]);
+    bt = strength_from_preact(bt);
+  }
+  // q.k (and the squared norms of raw q and k) from the rows already in
+  // registers: the lanes of column group 0 hold every row exactly once.  The
+  // unit-length scaling is applied to the reduced sums (x and y are linear
+  // in k and q).
+  float qk_part = 0.f, kn_part = 0.f, qn_part = 0.f;
   if (cq == 0) {
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) qk_part += qq[p] * kk[p];
+    for (int p = 0; p < PASSES; ++p) {
+      qk_part += qq[p] * kk[p];
+      if constexpr (kPre) {
+        kn_part += kk[p] * kk[p];
+        qn_part += qq[p] * qq[p];
+      }
+    }
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
+  for (int off = 32; off > 0; off >>= 1) {
+    qk_part += __shfl_xor(qk_part, off);
+    if constexpr (kPre) {
+      kn_part += __shfl_xor(kn_part, off);
+      qn_part += __shfl_xor(qn_part, off);
+    }
+  }
   float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
@@ -114,19 +140,35 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
       s_red[wave][1][cq * 4 + j] = y[j];
     }
   }
-  if (lane == 0) s_qk[wave] = qk_part;
+  if (lane == 0) {
+    s_qk[wave][0] = qk_part;
+    s_qk[wave][1] = kn_part;
+    s_qk[wave][2] = qn_part;
+  }
   __syncthreads();
 
   if (tid < D) {
-    float xs = 0.f, ys = 0.f, qk = 0.f;
+    float xs = 0.f, ys = 0.f, qk = 0.f, kn = 0.f, qn = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       xs += s_red[w][0][tid];
       ys += s_red[w][1][tid];
-      qk += s_qk[w];
+      qk += s_qk[w][0];
+      if constexpr (kPre) {
+        kn += s_qk[w][1];
+        qn += s_qk[w][2];
+      }
+    }
+    float ik = 1.f, iq = 1.f;
+    if constexpr (kPre) {
+      ik = inv_norm(kn);
+      iq = inv_norm(qn);
+      xs *= ik;
+      ys *= iq;
+      qk *= ik * iq;
     }
     const float wv = bt * (vj - xs);
-    s_w[tid] = wv;
+    s_w[tid] = kPre ? wv * ik : wv;  // the update adds k_i w_j with unit k
     o[nh * D + tid] = ys + qk * wv;
   }
   __syncthreads();
@@ -147,35 +189,43 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
   }
 }
 
-template <int D, typename TIn, int GATE>
+template <int D, typename TIn, int GATE, int FORM>
 hipError_t launch_decode_t(const kda_shape_t &s, const void *q, const void *k, const void *v,
                            const float *alpha, const float *beta, float *S, float *o,
                            hipStream_t stream) {
   using Cfg = DecodeCfg<D>;
   const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
-  hipLaunchKernelGGL((decode_kernel<D, TIn, GATE>), dim3((unsigned)blocks), dim3(Cfg::NT), 0, stream,
+  hipLaunchKernelGGL((decode_kernel<D, TIn, GATE, FORM>), dim3((unsigned)blocks), dim3(Cfg::NT), 0, stream,
                      static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                      static_cast<const TIn *>(v), alpha, beta, S, o);
   return hipGetLastError();
 }
 
-template <typename TIn, int GATE>
+template <typename TIn, int GATE, int FORM>
 hipError_t dispatch_d(const kda_shape_t &s, const void *q, const void *k, const void *v,
                       const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
   switch (s.d_k) {
-    case 16: return launch_decode_t<16, TIn, GATE>(s, q, k, v, alpha, beta, S, o, st);
-    case 32: return launch_decode_t<32, TIn, GATE>(s, q, k, v, alpha, beta, S, o, st);
-    case 64: return launch_decode_t<64, TIn, GATE>(s, q, k, v, alpha, beta, S, o, st);
-    case 128: return launch_decode_t<128, TIn, GATE>(s, q, k, v, alpha, beta, S, o, st);
+    case 16: return launch_decode_t<16, TIn, GATE, FORM>(s, q, k, v, alpha, beta, S, o, st);
+    case 32: return launch_decode_t<32, TIn, GATE, FORM>(s, q, k, v, alpha, beta, S, o, st);
+    case 64: return launch_decode_t<64, TIn, GATE, FORM>(s, q, k, v, alpha, beta, S, o, st);
+    case 128: return launch_decode_t<128, TIn, GATE, FORM>(s, q, k, v, alpha, beta, S, o, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename TIn>
+template <typename TIn, int FORM>
 hipError_t dispatch_gate(const kda_shape_t &s, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
-  if (s.gate == KDA_GATE_HEAD) return dispatch_d<TIn, KDA_GATE_HEAD>(s, q, k, v, alpha, beta, S, o, st);
-  return dispatch_d<TIn, KDA_GATE_CHANNEL>(s, q, k, v, alpha, beta, S, o, st);
+  if (s.gate == KDA_GATE_HEAD) return dispatch_d<TIn, KDA_GATE_HEAD, FORM>(s, q, k, v, alpha, beta, S, o, st);
+  return dispatch_d<TIn, KDA_GATE_CHANNEL, FORM>(s, q, k, v, alpha, beta, S, o, st);
+}
+
+template <typename TIn>
+hipError_t dispatch_form(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
+  if (s.input_form == KDA_INPUT_PREACT)
+    return dispatch_gate<TIn, KDA_INPUT_PREACT>(s, q, k, v, alpha, beta, S, o, st);
+  return dispatch_gate<TIn, KDA_INPUT_FINAL>(s, q, k, v, alpha, beta, S, o, st);
 }
 
 }  // namespace
@@ -183,8 +233,8 @@ hipError_t dispatch_gate(const kda_shape_t &s, const void *q, const void *k, con
 hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, float *S, float *o,
                          hipStream_t stream) {
-  if (s.qkv_dtype == KDA_BF16) return dispatch_gate<__bf16>(s, q, k, v, alpha, beta, S, o, stream);
-  return dispatch_gate<float>(s, q, k, v, alpha, beta, S, o, stream);
+  if (s.qkv_dtype == KDA_BF16) return dispatch_form<__bf16>(s, q, k, v, alpha, beta, S, o, stream);
+  return dispatch_form<float>(s, q, k, v, alpha, beta, S, o, stream);
 }
 
 }  // namespace kda

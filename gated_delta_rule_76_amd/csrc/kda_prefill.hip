@@ -61,6 +61,14 @@ constexpr float kTinyBlock = 7.888609052210118e-31f;  // 2^-100
 // an access at an offset past num_records is dropped (stores) or reads 0.
 constexpr int kBufferWord3 = 0x00020000;
 
+// Pre-activation inputs (KDA_INPUT_PREACT): decay rate exp(-softplus(a)),
+// written as 1 / (1 + e^a) (the same value; 0 for a -> +inf, 1 for
+// a -> -inf), and update strength sigmoid(b).
+__device__ __forceinline__ float decay_from_preact(float a) { return 1.f / (1.f + expf(a)); }
+__device__ __forceinline__ float strength_from_preact(float b) { return 1.f / (1.f + expf(-b)); }
+// 1 / max(||x||_2, 1e-12) from the sum of squares.
+__device__ __forceinline__ float inv_norm(float ss) { return 1.f / fmaxf(sqrtf(ss), 1e-12f); }
+
 // ---------------------------------------------------------------------------
 // LDS operand planes: a ROWS x COLS fp32 matrix stored either as a bf16
 // hi/lo pair (SplitBF16) or as fp32 (F32), padded so that the 16 lanes of a
@@ -496,7 +504,7 @@ __device__ __forceinline__ int gram_plane(int R, int J) {
 __device__ __forceinline__ int tb_ct(int u) { return u < 4 ? u >> 1 : u - 2; }
 __device__ __forceinline__ int tb_kb(int u) { return u < 4 ? u & 1 : 1; }
 
-template <int D, typename TIn, typename P, int GATE>
+template <int D, typename TIn, typename P, int GATE, int FORM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void chunk_local_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ alpha,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
@@ -511,6 +519,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
   __shared__ float s_X[C * MP];
   __shared__ __attribute__((aligned(16))) float s_bt[4 * DK];
   __shared__ float s_beta[C];
+  __shared__ float s_inv[2][C];  // KDA_INPUT_PREACT: 1 / ||k||, 1 / ||q|| per token
   __shared__ int s_flag[4];
   float *s_L = reinterpret_cast<float *>(s_u);
   float *s_M = s_L + C * LP;
@@ -562,7 +571,50 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     qr[kb].load(q + off);
   }
   for (int e = tid; e < C * MP; e += NT) s_X[e] = 0.f;
-  if (tid < C) s_beta[tid] = tid < nvalid ? bv : 0.f;
+  if (tid < C)
+    s_beta[tid] = tid < nvalid ? (FORM == KDA_INPUT_PREACT ? strength_from_preact(bv) : bv) : 0.f;
+  constexpr bool kPre = FORM == KDA_INPUT_PREACT;
+  if constexpr (kPre) {
+    if constexpr (GATE == KDA_GATE_HEAD) {
+      ah = decay_from_preact(ah);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        ar0[kb].x = decay_from_preact(ar0[kb].x); ar0[kb].y = decay_from_preact(ar0[kb].y);
+        ar0[kb].z = decay_from_preact(ar0[kb].z); ar0[kb].w = decay_from_preact(ar0[kb].w);
+        ar1[kb].x = decay_from_preact(ar1[kb].x); ar1[kb].y = decay_from_preact(ar1[kb].y);
+        ar1[kb].z = decay_from_preact(ar1[kb].z); ar1[kb].w = decay_from_preact(ar1[kb].w);
+      }
+    }
+  }
+  // Raw q and k are scaled to unit length: sums of squares over the lane's
+  // channels, then over the four lanes (g) that share the token.
+  float inv_k = 1.f, inv_q = 1.f;
+  if constexpr (kPre) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (kb * 32 + 8 * g < D) {
+        float t[8];
+        kr[kb].to_f32(t);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sk += t[j] * t[j];
+        qr[kb].to_f32(t);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sq += t[j] * t[j];
+      }
+    }
+    sk += __shfl_xor(sk, 16);
+    sq += __shfl_xor(sq, 16);
+    sk += __shfl_xor(sk, 32);
+    sq += __shfl_xor(sq, 32);
+    inv_k = inv_norm(sk);
+    inv_q = inv_norm(sq);
+    if (g == 0) {
+      s_inv[0][r] = inv_k;
+      s_inv[1][r] = inv_q;
+    }
+  }
 
   // ---- in-block decay products -------------------------------------------------
   float bp[NKB][8], bs[NKB][8];
@@ -640,8 +692,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     float xa[8], xq[8], x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      kf[j] = ok ? kf[j] : 0.f;
-      qf[j] = ok ? qf[j] : 0.f;
+      kf[j] = ok ? kf[j] * inv_k : 0.f;
+      qf[j] = ok ? qf[j] * inv_q : 0.f;
       xa[j] = kf[j] * bp[kb][j];
       xq[j] = qf[j] * bp[kb][j];
     }
@@ -728,12 +780,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
       if (rr < nvalid && jj < nvalid) {
         for (int ch = 0; ch < D; ++ch) {
           float f = 1.f;
-          for (int s = jj + 1; s <= rr; ++s)
-            f *= GATE == KDA_GATE_HEAD ? alpha[(t0 + s) * H + h] : alpha[((t0 + s) * H + h) * D + ch];
+          for (int s = jj + 1; s <= rr; ++s) {
+            const float as =
+                GATE == KDA_GATE_HEAD ? alpha[(t0 + s) * H + h] : alpha[((t0 + s) * H + h) * D + ch];
+            f *= kPre ? decay_from_preact(as) : as;
+          }
           const int64_t orr = ((t0 + rr) * H + h) * D + ch, ojj = ((t0 + jj) * H + h) * D + ch;
-          const float kj = to_f32(k[ojj]) * f;
-          a_acc += to_f32(k[orr]) * kj;
-          m_acc += to_f32(q[orr]) * kj;
+          const float kj = to_f32(k[ojj]) * (kPre ? s_inv[0][jj] : 1.f) * f;
+          a_acc += to_f32(k[orr]) * (kPre ? s_inv[0][rr] : 1.f) * kj;
+          m_acc += to_f32(q[orr]) * (kPre ? s_inv[1][rr] : 1.f) * kj;
         }
       }
       s_L[rr * LP + jj] = (jl < rl) ? a_acc * s_beta[rr] : 0.f;
@@ -1162,7 +1217,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   }
 }
 
-template <int D, typename TIn, typename P, int GATE>
+template <int D, typename TIn, typename P, int GATE, int FORM>
 hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, const int32_t *cu,
                             const float *S0, float *o, float *S_T, void *workspace,
@@ -1180,7 +1235,7 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (mc > 0) {
-      hipLaunchKernelGGL((chunk_local_kernel<D, TIn, P, GATE>), dim3((unsigned)(mc * H)), dim3(NT), 0, stream,
+      hipLaunchKernelGGL((chunk_local_kernel<D, TIn, P, GATE, FORM>), dim3((unsigned)(mc * H)), dim3(NT), 0, stream,
                          qp, kp, alpha, beta, cu, s.seq_len, N, H, s.total_tokens, mc, base, recs);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1197,7 +1252,7 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   return e;
 }
 
-template <typename TIn, int GATE>
+template <typename TIn, int GATE, int FORM>
 hipError_t dispatch_prefill(const kda_shape_t &s, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, const int32_t *cu,
                             const float *S0, float *o, float *S_T, void *ws, hipStream_t st,
@@ -1206,21 +1261,30 @@ hipError_t dispatch_prefill(const kda_shape_t &s, const void *q, const void *k, 
   // 16-wide heads) the fp32 matrix-core path.
   using PB = typename std::conditional<std::is_same<TIn, __bf16>::value, SplitBF16, F32>::type;
   switch (s.d_k) {
-    case 16: return launch_prefill_t<16, TIn, F32, GATE>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 32: return launch_prefill_t<32, TIn, PB, GATE>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 64: return launch_prefill_t<64, TIn, PB, GATE>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 128: return launch_prefill_t<128, TIn, PB, GATE>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 16: return launch_prefill_t<16, TIn, F32, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 32: return launch_prefill_t<32, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 64: return launch_prefill_t<64, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 128: return launch_prefill_t<128, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename TIn>
+template <typename TIn, int FORM>
 hipError_t dispatch_gate(const kda_shape_t &s, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, const int32_t *cu, const float *S0,
                          float *o, float *S_T, void *ws, hipStream_t st, int ph) {
   if (s.gate == KDA_GATE_HEAD)
-    return dispatch_prefill<TIn, KDA_GATE_HEAD>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-  return dispatch_prefill<TIn, KDA_GATE_CHANNEL>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    return dispatch_prefill<TIn, KDA_GATE_HEAD, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+  return dispatch_prefill<TIn, KDA_GATE_CHANNEL, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+}
+
+template <typename TIn>
+hipError_t dispatch_form(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, const int32_t *cu, const float *S0,
+                         float *o, float *S_T, void *ws, hipStream_t st, int ph) {
+  if (s.input_form == KDA_INPUT_PREACT)
+    return dispatch_gate<TIn, KDA_INPUT_PREACT>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+  return dispatch_gate<TIn, KDA_INPUT_FINAL>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
 }
 
 }  // namespace
@@ -1230,9 +1294,9 @@ hipError_t launch_prefill(const kda_shape_t &s, const void *q, const void *k, co
                           const float *S0, float *o, float *S_T, void *workspace,
                           hipStream_t stream, int phases) {
   if (s.qkv_dtype == KDA_BF16)
-    return dispatch_gate<__bf16>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
+    return dispatch_form<__bf16>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
                                  phases);
-  return dispatch_gate<float>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
+  return dispatch_form<float>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
                               phases);
 }
 

@@ -17,6 +17,10 @@ Distributions (per the workloads the layer is measured on):
            ~0.14, the prefill/decode workloads), -4 ("weak", mean ~0.97);
            with gate="head" the same law with one draw per (token, head)
            (the scalar-gate form);
+  form     "final" gives the tensors above; "preact" gives what they are
+           made from: raw q, k (N(0,1), not normalised, cast to the q/k/v
+           dtype), a = N(0,1) + shift in alpha's place and b = N(0,1) in
+           beta's (the same draws);
   state    std * N(0,1) fp32 (std 0.02 for the varlen and decode workloads);
   lengths  uniform integers in [lo, hi] inclusive.
 
@@ -66,7 +70,7 @@ def varlen_lengths(n, lo, hi, seed=0):
 
 
 def token_inputs(T, H, D, dtype=torch.bfloat16, decay="strong", seed=0, device="cpu", dv=None,
-                 gate="channel"):
+                 gate="channel", form="final"):
     """q, k, v, alpha, beta for T tokens x H heads (token-major layout).
 
     Returns a dict: q, k [T,H,D] and v [T,H,dv] in ``dtype``; alpha [T,H,D]
@@ -74,15 +78,20 @@ def token_inputs(T, H, D, dtype=torch.bfloat16, decay="strong", seed=0, device="
     """
     if gate not in ("channel", "head"):
         raise ValueError("gate is 'channel' or 'head'")
+    if form not in ("final", "preact"):
+        raise ValueError("form is 'final' or 'preact'")
+    pre = form == "preact"
     dv = D if dv is None else dv
     shift = DECAY_SHIFT[decay]
-    q = _unit(_randn_tokens((T, H, D), seed, _STREAM["q"], device)).to(dtype)
-    k = _unit(_randn_tokens((T, H, D), seed, _STREAM["k"], device)).to(dtype)
+    unit = (lambda x: x) if pre else _unit
+    q = unit(_randn_tokens((T, H, D), seed, _STREAM["q"], device)).to(dtype)
+    k = unit(_randn_tokens((T, H, D), seed, _STREAM["k"], device)).to(dtype)
     v = _randn_tokens((T, H, dv), seed, _STREAM["v"], device).to(dtype)
     a = _randn_tokens((T, H, D) if gate == "channel" else (T, H), seed, _STREAM["alpha"], device)
-    alpha = torch.exp(-torch.nn.functional.softplus(a + shift))
+    alpha = a + shift if pre else torch.exp(-torch.nn.functional.softplus(a + shift))
     del a
-    beta = torch.sigmoid(_randn_tokens((T, H), seed, _STREAM["beta"], device))
+    b = _randn_tokens((T, H), seed, _STREAM["beta"], device)
+    beta = b if pre else torch.sigmoid(b)
     return {"q": q, "k": k, "v": v, "alpha": alpha.contiguous(), "beta": beta.contiguous()}
 
 
@@ -94,7 +103,7 @@ def state(N, H, D, std=0.02, seed=0, device="cpu", dv=None, stream_offset=0):
 
 
 def prefill_inputs(lengths, H, D, dtype=torch.bfloat16, decay="strong", s0_std=None,
-                   seed=0, device="cpu", gate="channel"):
+                   seed=0, device="cpu", gate="channel", form="final"):
     """Packed prefill batch for sequences of the given lengths.
 
     Returns token_inputs(...) plus ``cu_seqlens`` (int32 [N+1], on device),
@@ -103,7 +112,7 @@ def prefill_inputs(lengths, H, D, dtype=torch.bfloat16, decay="strong", s0_std=N
     """
     lengths = [int(x) for x in lengths]
     T = sum(lengths)
-    d = token_inputs(T, H, D, dtype, decay, seed, device, gate=gate)
+    d = token_inputs(T, H, D, dtype, decay, seed, device, gate=gate, form=form)
     cu = [0]
     for L in lengths:
         cu.append(cu[-1] + L)
@@ -114,14 +123,14 @@ def prefill_inputs(lengths, H, D, dtype=torch.bfloat16, decay="strong", s0_std=N
 
 
 def decode_inputs(B, H, D, steps, dtype=torch.bfloat16, decay="strong", s_std=0.02,
-                  seed=0, device="cpu", gate="channel"):
+                  seed=0, device="cpu", gate="channel", form="final"):
     """State [B,H,D,D] plus ``steps`` per-step token sets stacked on axis 0.
 
     Returns dict: S fp32 [B,H,D,D]; q, k, v [steps,B,H,D]; alpha [steps,B,H,D]
     (or [steps,B,H] with gate="head"); beta [steps,B,H].  Step s uses token row s*B .. s*B+B-1 of one draw of
     steps*B tokens.
     """
-    t = token_inputs(steps * B, H, D, dtype, decay, seed, device, gate=gate)
+    t = token_inputs(steps * B, H, D, dtype, decay, seed, device, gate=gate, form=form)
     out = {name: x.reshape((steps, B) + tuple(x.shape[1:])) for name, x in t.items()}
     out["S"] = state(B, H, D, s_std, seed, device)
     return out

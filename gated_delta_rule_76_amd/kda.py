@@ -155,7 +155,7 @@ class PrefillCall:
     and ``state_pass()`` are its two phases (run in that order)."""
 
     def __init__(self, q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
-                 output_final_state=True, workspace=None, out=None, final_state=None):
+                 output_final_state=True, workspace=None, out=None, final_state=None, preact=False):
         for name, t in (("q", q), ("k", k), ("v", v)):
             _require_gpu(name, t)
         if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -188,7 +188,8 @@ class PrefillCall:
             _require_gpu("initial_state", initial_state, torch.float32)
             if tuple(initial_state.shape) != (N, H, D, D):
                 raise ValueError(f"initial_state must be {(N, H, D, D)}")
-        self.shape = make_shape(N, seq_len, total, H, D, q.dtype, gate)
+        self.shape = make_shape(N, seq_len, total, H, D, q.dtype, gate,
+                                KDA_INPUT_PREACT if preact else KDA_INPUT_FINAL)
         self.o = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=dev)
         _require_gpu("out", self.o, torch.float32)
         self.S_T = None
@@ -233,7 +234,7 @@ class PrefillCall:
 
 
 def prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
-            output_final_state=True, workspace=None, out=None, final_state=None):
+            output_final_state=True, workspace=None, out=None, final_state=None, preact=False):
     """Chunked KDA prefill.  Returns (o, S_T).
 
     Layouts: q, k, alpha [T, H, D] with v [T, H, D] (one sequence, or a
@@ -241,20 +242,23 @@ def prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
     [B, T, H, D] for a dense batch of B equal-length sequences; beta
     [T, H] / [B, T, H].  q, k, v are bf16 or fp32; alpha, beta fp32.
     alpha of beta's shape (one rate per token and head) selects the
-    scalar-gate form.
+    scalar-gate form.  With ``preact=True``, q and k are raw (the library
+    scales them to unit length), alpha holds decay pre-activations a
+    (alpha = exp(-softplus(a))) and beta holds b (beta = sigmoid(b)).
     initial_state [N, H, D, D] fp32 or None (zeros).  o is fp32 with v's
     shape; S_T is [N, H, D, D] fp32 (None if output_final_state is False).
     ``final_state`` may be ``initial_state`` for an in-place update.
     """
     return PrefillCall(q, k, v, alpha, beta, initial_state, cu_seqlens,
                        output_final_state=output_final_state, workspace=workspace, out=out,
-                       final_state=final_state).run()
+                       final_state=final_state, preact=preact).run()
 
 
-def decode_step(q, k, v, alpha, beta, state, out=None):
+def decode_step(q, k, v, alpha, beta, state, out=None, preact=False):
     """One decode step for N sequences: q, k, v, alpha [N, H, D]; beta [N, H];
     state [N, H, D, D] fp32 updated in place.  Returns o [N, H, D] fp32.
-    alpha [N, H] (one rate per head) selects the scalar-gate form."""
+    alpha [N, H] (one rate per head) selects the scalar-gate form;
+    ``preact=True`` as for ``prefill``."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require_gpu(name, t)
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -272,7 +276,7 @@ def decode_step(q, k, v, alpha, beta, state, out=None):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
     o = out if out is not None else torch.empty((N, H, D), dtype=torch.float32, device=q.device)
     _require_gpu("out", o, torch.float32)
-    shape = make_shape(N, 1, N, H, D, q.dtype, gate)
+    shape = make_shape(N, 1, N, H, D, q.dtype, gate, KDA_INPUT_PREACT if preact else KDA_INPUT_FINAL)
     st = lib().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(state), _ptr(o), _stream(q.device))
     _check(st, "kda_decode_step")

@@ -48,7 +48,7 @@
  *    errors at the caller's next synchronisation, as for any HIP kernel.
  *  - Supported sizes: d_k == d_v in {16, 32, 64, 128}; H >= 1.
  *  - Device-side preconditions (not checked, a check would need a sync):
- *    0 <= alpha <= 1; beta, q, k, v finite; cu_seqlens[0] == 0,
+ *    0 <= alpha <= 1 (KDA_INPUT_FINAL); beta, q, k, v finite; cu_seqlens[0] == 0,
  *    non-decreasing, cu_seqlens[N] == total_tokens; outputs do not overlap
  *    inputs except where aliasing is stated below.  Non-finite inputs give
  *    non-finite outputs; they do not fault.
@@ -86,8 +86,16 @@ typedef enum kda_gate {
     KDA_GATE_HEAD = 1     /* alpha [tokens][H] */
 } kda_gate_t;
 
-/* What q, k, alpha and beta hold.  KDA_INPUT_FINAL: the values the update
- * rule uses.  KDA_INPUT_PREACT is reserved (rejected as unsupported). */
+/* What q, k, alpha and beta hold.
+ *  - KDA_INPUT_FINAL: the values the update rule uses.
+ *  - KDA_INPUT_PREACT: the layer's gate pre-activations and raw q, k; the
+ *    library forms, per token and head, inside the kernels' load stage
+ *        alpha = exp(-softplus(a)) = 1 / (1 + e^a)   from a in `alpha`
+ *        beta  = sigmoid(b)        = 1 / (1 + e^-b)  from b in `beta`
+ *        q <- q / max(||q||_2, 1e-12),  k <- k / max(||k||_2, 1e-12)
+ *    (norms over the d_k key channels).  The attention page says each key
+ *    channel decays at a learned, data-driven rate but prints no
+ *    parameterisation; this one is the reading taken.  v is used as given. */
 typedef enum kda_input_form {
     KDA_INPUT_FINAL = 0,
     KDA_INPUT_PREACT = 1

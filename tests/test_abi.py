@@ -122,7 +122,7 @@ def test_gate_and_input_form_validation(L):
     assert prefill(L, shape(gate=2)) == INVALID
     assert prefill(L, shape(gate=-1)) == INVALID
     assert prefill(L, shape(form=2)) == INVALID
-    assert prefill(L, shape(form=1)) == UNSUPPORTED
+    assert prefill(L, shape(form=1), ws_bytes=need - 1) == WS_SMALL        # accepted
     assert L.kda_prefill_workspace_size(ctypes.byref(shape(gate=3)), ctypes.byref(out)) == INVALID
     # the workspace size does not depend on the gate kind
     assert L.kda_prefill_workspace_size(ctypes.byref(shape(gate=1)), ctypes.byref(out)) == OK
@@ -135,7 +135,7 @@ def test_gate_and_input_form_validation(L):
     d = lambda **kw: kda.KdaShape(4, 1, 4, 2, 128, 128, 1, kw.get("gate", 0), kw.get("form", 0))
     assert decode(L, d(gate=2)) == INVALID
     assert decode(L, d(form=2)) == INVALID
-    assert decode(L, d(form=1)) == UNSUPPORTED
+    assert decode(L, kda.KdaShape(0, 1, 0, 2, 128, 128, 1, 0, 1)) == OK
     assert decode(L, d(gate=1), a=FAKE + 2) == INVALID
     assert decode(L, kda.KdaShape(0, 1, 0, 2, 128, 128, 1, 1, 0)) == OK
 

@@ -59,3 +59,13 @@ def test_scalar_gate_inputs():
     assert torch.equal(x["q"], c["q"]) and torch.equal(x["v"], c["v"])   # only alpha differs
     d = inputs.decode_inputs(4, 2, 16, steps=3, seed=2, gate="head")
     assert d["alpha"].shape == (3, 4, 2)
+
+
+def test_preact_inputs_are_what_the_final_inputs_are_made_from():
+    f = inputs.token_inputs(512, 3, 32, torch.float32, "strong", seed=4)
+    p = inputs.token_inputs(512, 3, 32, torch.float32, "strong", seed=4, form="preact")
+    unit = lambda x: x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+    assert torch.allclose(unit(p["q"]), f["q"], atol=1e-6) and torch.allclose(unit(p["k"]), f["k"], atol=1e-6)
+    assert torch.allclose(torch.exp(-torch.nn.functional.softplus(p["alpha"])), f["alpha"], rtol=1e-6)
+    assert torch.allclose(torch.sigmoid(p["beta"]), f["beta"], rtol=1e-6)
+    assert torch.equal(p["v"], f["v"])
