@@ -18,9 +18,10 @@ counter summary when it was taken on the current kernel source); the decode
 rate (B=256, H=32, d=128, 100 in-place steps) with its own roofline; and the
 fp64 CPU oracle timed on the host over the whole prefill_4k workload.
 
-The line also carries the scalar-gate form (one alpha per token and head) on
-the same prefill and decode shapes, under ``scalar_gate`` (``--no-variants``
-skips it).  ``--oracle-rates`` times only the CPU oracle, on every workload,
+The line also carries, on the same prefill and decode shapes, the
+scalar-gate form (one alpha per token and head) under ``scalar_gate`` and the
+layer fed pre-activations (gate and normalisation computed in the kernels)
+under ``preact`` (``--no-variants`` skips both).  ``--oracle-rates`` times only the CPU oracle, on every workload,
 and prints those rates as one JSON line.
 """
 
@@ -59,7 +60,7 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-variants", action="store_true",
-                   help="skip the scalar-gate measurements")
+                   help="skip the scalar-gate and pre-activation measurements")
     p.add_argument("--decode-batch", type=int, default=256)
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
@@ -106,7 +107,7 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(name, steps, warmup, dev, gate="channel"):
+def bench_prefill(name, steps, warmup, dev, gate="channel", form="final"):
     from gated_delta_rule_76_amd import inputs, kda
     spec = inputs.WORKLOADS[name]
     lens = inputs.workload_lengths(spec, seed=0)
@@ -115,9 +116,10 @@ def bench_prefill(name, steps, warmup, dev, gate="channel"):
     calls = []
     for s in range(n_sets):
         d = inputs.prefill_inputs(lens, H, D, torch.bfloat16, spec["decay"], spec["s0_std"],
-                                  seed=s, device=dev, gate=gate)
+                                  seed=s, device=dev, gate=gate, form=form)
         cu = d["cu_seqlens"] if len(lens) > 1 else None
-        calls.append(kda.PrefillCall(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], cu))
+        calls.append(kda.PrefillCall(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], cu,
+                                     preact=form == "preact"))
     total = sum(lens)
     for i in range(warmup):
         calls[i % n_sets].run()
@@ -154,23 +156,25 @@ def bench_prefill(name, steps, warmup, dev, gate="channel"):
                         "p90": float(np.percentile(per_call, 90))}}
 
 
-def bench_decode(B, dev, gate="channel"):
+def bench_decode(B, dev, gate="channel", form="final"):
     from gated_delta_rule_76_amd import inputs, kda
     spec = inputs.WORKLOADS["decode_b256"]
     H, D = spec["H"], spec["D"]
     n = spec["steps"]
     d = inputs.decode_inputs(B, H, D, n, torch.bfloat16, spec["decay"], spec["s_std"],
-                             seed=0, device=dev, gate=gate)
+                             seed=0, device=dev, gate=gate, form=form)
+    pre = form == "preact"
     S = d["S"].clone()
     o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     for s in range(10):
         kda.decode_step(d["q"][s % n], d["k"][s % n], d["v"][s % n], d["alpha"][s % n],
-                        d["beta"][s % n], S, out=o)
+                        d["beta"][s % n], S, out=o, preact=pre)
     torch.cuda.synchronize()
     e0, e1 = _events()
     e0.record()
     for s in range(n):
-        kda.decode_step(d["q"][s], d["k"][s], d["v"][s], d["alpha"][s], d["beta"][s], S, out=o)
+        kda.decode_step(d["q"][s], d["k"][s], d["v"][s], d["alpha"][s], d["beta"][s], S, out=o,
+                        preact=pre)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
@@ -199,8 +203,11 @@ def _cpu_prefill_worker(heads):
     from threadpoolctl import threadpool_limits
 
     from oracle import gdn_recurrent, kda_recurrent
+    from oracle.prologue import recurrent_from_preact
     a = _CPU_INPUTS
     run = gdn_recurrent if a["gate"] == "head" else kda_recurrent
+    if a["form"] == "preact":
+        run = recurrent_from_preact
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         for _ in range(a["passes"]):
@@ -236,7 +243,7 @@ def _pool_map(fn, n_items):
     return wall, sum(busy), len(groups)
 
 
-def oracle_prefill_rate(workload, max_tokens=None, passes=1, gate="channel"):
+def oracle_prefill_rate(workload, max_tokens=None, passes=1, gate="channel", form="final"):
     """Oracle tokens/s/layer over ``workload`` (or its first ``max_tokens``
     tokens when the sequence is longer), all heads, ``passes`` repetitions."""
     from gated_delta_rule_76_amd import inputs
@@ -246,8 +253,10 @@ def oracle_prefill_rate(workload, max_tokens=None, passes=1, gate="channel"):
     if prefix:
         lengths = [max_tokens]
     d = inputs.prefill_inputs(lengths, spec["H"], spec["D"], torch.bfloat16, spec["decay"],
-                              None if prefix else spec["s0_std"], seed=0, device="cpu", gate=gate)
+                              None if prefix else spec["s0_std"], seed=0, device="cpu", gate=gate,
+                              form=form)
     _CPU_INPUTS["gate"] = gate
+    _CPU_INPUTS["form"] = form
     _CPU_INPUTS.update({k: d[k].double().numpy() for k in ("q", "k", "v", "alpha", "beta")})
     _CPU_INPUTS["S0"] = None if d["S0"] is None else d["S0"].double().numpy()
     _CPU_INPUTS["cu"] = d["cu_seqlens"].numpy()
@@ -258,6 +267,8 @@ def oracle_prefill_rate(workload, max_tokens=None, passes=1, gate="channel"):
     what = (f"the first {T} tokens of {workload}" if prefix else f"the whole {workload} workload")
     if gate == "head":
         what += " with one alpha per token and head"
+    if form == "preact":
+        what += " from pre-activations"
     return {"value": passes * T / wall, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
             "sample": f"{what} ({T} tokens x {spec['H']} heads, d={spec['D']}"
                       f"{', x%d passes' % passes if passes > 1 else ''}), numpy fp64 token-by-token "
@@ -311,6 +322,7 @@ def oracle_rates():
     out["long_1m"] = lg
     out["prefill_4k_scalar_gate"] = oracle_prefill_rate("prefill_4k", passes=3, gate="head")
     out["decode_b256_scalar_gate"] = oracle_decode_rate(256, 100, gate="head")
+    out["prefill_4k_preact"] = oracle_prefill_rate("prefill_4k", passes=3, form="preact")
     return out
 
 
@@ -353,9 +365,9 @@ def prefill_summary(pf, gate):
                                "frac": layer_gbs / HBM_PEAK_GBS}}
 
 
-def decode_summary(dc, gate):
+def decode_summary(dc, gate, form="final"):
     gbs = dc["B"] * dc["H"] * decode_bytes(gate) / (dc["ms_per_step"] * 1e-3) / 1e9
-    kind = "KDA" if gate == "channel" else "scalar-gate"
+    kind = ("KDA" if gate == "channel" else "scalar-gate") + (" pre-activation" if form == "preact" else "")
     return {"metric": "%s decode steps/s (B=%d, H=32, d=128)" % (kind, dc["B"]),
             "value": 1e3 / dc["ms_per_step"], "unit": "steps/s", "ms_per_step": dc["ms_per_step"],
             "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": gbs,
@@ -431,6 +443,17 @@ def main():
         if not args.no_decode:
             sg["decode"] = decode_summary(bench_decode(args.decode_batch, dev, gate="head"), "head")
         out["scalar_gate"] = sg
+        # Pre-activation inputs (gate and normalisation prologue in the load
+        # stage); the bytes moved are the same as for activated inputs.
+        print("[bench] pre-activation inputs", file=sys.stderr, flush=True)
+        pp = bench_prefill(args.workload, args.steps, args.warmup, dev, form="preact")
+        pa = {"prefill": prefill_summary(pp, "channel")}
+        pa["prefill"]["metric"] = "KDA prefill from pre-activations, tokens/s/layer (H=32, d=128)"
+        pa["prefill"]["call_ms"] = pp["call_ms"]
+        if not args.no_decode:
+            pa["decode"] = decode_summary(bench_decode(args.decode_batch, dev, form="preact"), "channel",
+                                          "preact")
+        out["preact"] = pa
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -21,9 +21,12 @@ scalar_gate  the scalar-gate (Gated DeltaNet) form: one decay rate per token
              and head instead of one per key channel
 prologue     rates, strengths and unit q, k from pre-activations, then the
              recurrence
+speculative  several tokens per sequence from a live state, every
+             intermediate state kept, and the rollback to the accepted one
 
 Pins (every function is pinned by tests/test_oracle_pins.py,
-tests/test_oracle_scalar_gate.py and tests/test_oracle_prologue.py against closed forms, invariants, a library
+tests/test_oracle_scalar_gate.py, tests/test_oracle_prologue.py and
+tests/test_oracle_speculative.py against closed forms, invariants, a library
 routine and a hand-worked golden example; see the module docstrings).  No function here is "parity unpinned".
 """
 
@@ -36,4 +39,4 @@ from .recurrence import (  # noqa: F401
 from .bruteforce import kda_bruteforce  # noqa: F401
 from .exact import kda_exact  # noqa: F401
 from .scalar_gate import gdn_decode_step, gdn_recurrent, gdn_step  # noqa: F401
-from . import prologue  # noqa: F401
+from . import prologue, speculative  # noqa: F401
