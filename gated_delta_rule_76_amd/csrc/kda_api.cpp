@@ -146,26 +146,71 @@ kda_status_t kda_prefill_state_pass(const kda_shape_t *shape, const void *q, con
                      stream, kda::kPhaseState);
 }
 
-kda_status_t kda_decode_step(const kda_shape_t *shape, const void *q, const void *k, const void *v,
-                             const float *alpha, const float *beta, float *S, float *o,
-                             void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the decode entry points: a dense batch of num_seqs sequences of
+// seq_len tokens (seq_len == 1 for kda_decode_step).
+kda_status_t check_decode_call(const kda_shape_t *shape, bool one_token, const void *q, const void *k,
+                               const void *v, const float *alpha, const float *beta, const float *S,
+                               const float *o) {
   if (shape == nullptr) return KDA_ERR_INVALID_ARGUMENT;
   const kda_shape_t &s = *shape;
-  if (s.num_seqs < 0 || s.num_heads < 1 || s.seq_len != 1 || s.total_tokens != s.num_seqs)
+  if (s.num_seqs < 0 || s.num_heads < 1 || s.seq_len < 1 || (one_token && s.seq_len != 1) ||
+      s.total_tokens != (int64_t)s.num_seqs * s.seq_len)
     return KDA_ERR_INVALID_ARGUMENT;
   if (s.qkv_dtype != KDA_F32 && s.qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARGUMENT;
   if (s.d_k < 1 || s.d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (s.gate != KDA_GATE_CHANNEL && s.gate != KDA_GATE_HEAD) return KDA_ERR_INVALID_ARGUMENT;
   if (s.input_form != KDA_INPUT_FINAL && s.input_form != KDA_INPUT_PREACT) return KDA_ERR_INVALID_ARGUMENT;
   if (s.d_k != s.d_v || !supported_dim(s.d_k)) return KDA_ERR_UNSUPPORTED;
-  if (check_kinds(shape) != KDA_OK) return check_kinds(shape);
   if (s.num_seqs == 0) return KDA_OK;
   if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !alpha_aligned(shape, alpha) || !aligned4(beta) ||
       !aligned16(S) || !aligned16(o))
     return KDA_ERR_INVALID_ARGUMENT;
-  if ((int64_t)s.num_seqs * s.num_heads * (s.d_v / (s.d_v >= 64 ? 64 : s.d_v)) >= ((int64_t)1 << 31))
-    return KDA_ERR_UNSUPPORTED;
+  // One workgroup per (sequence, head).
+  if ((int64_t)s.num_seqs * s.num_heads >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_decode_tokens(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta, float *S, float *o, float *S_hist,
+                               void *stream) {
+  kda_status_t st = check_decode_call(shape, false, q, k, v, alpha, beta, S, o);
+  if (st != KDA_OK || shape->num_seqs == 0) return st;
+  if (S_hist != nullptr && !aligned16(S_hist)) return KDA_ERR_INVALID_ARGUMENT;
+  hipError_t e = kda::launch_decode_tokens(*shape, q, k, v, alpha, beta, S, o, S_hist,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_state_commit(const kda_shape_t *shape, float *S, const float *S_hist,
+                              const int32_t *accepted, void *stream) {
+  if (shape == nullptr) return KDA_ERR_INVALID_ARGUMENT;
+  const kda_shape_t &s = *shape;
+  if (s.num_seqs < 0 || s.num_heads < 1 || s.seq_len < 1 || s.d_k < 1 || s.d_v < 1)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (s.d_k != s.d_v || !supported_dim(s.d_k)) return KDA_ERR_UNSUPPORTED;
+  if (s.num_seqs == 0) return KDA_OK;
+  if (!S || !S_hist || !accepted || !aligned16(S) || !aligned16(S_hist) || !aligned4(accepted))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)s.num_seqs * s.num_heads >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  hipError_t e = kda::launch_commit(s, S, S_hist, accepted, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_decode_step(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta, float *S, float *o,
+                             void *stream) {
+  kda_status_t st = check_decode_call(shape, true, q, k, v, alpha, beta, S, o);
+  if (st != KDA_OK || shape->num_seqs == 0) return st;
+  const kda_shape_t &s = *shape;
   hipError_t e = kda::launch_decode(s, q, k, v, alpha, beta, S, o, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

@@ -23,6 +23,8 @@
 // 2 x 64 KiB of state traffic per head and step against ~115 kflop.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -189,43 +191,238 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_kernel(
   }
 }
 
-template <int D, typename TIn, int GATE, int FORM>
-hipError_t launch_decode_t(const kda_shape_t &s, const void *q, const void *k, const void *v,
-                           const float *alpha, const float *beta, float *S, float *o,
-                           hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// Several tokens per sequence from the live state (speculative verification
+// of drafted tokens, or plain multi-token decode).  One workgroup per
+// (sequence, head) as above; the state stays in registers across the
+// sequence's tokens, each token's small inputs are loaded while the previous
+// token computes.  With a history buffer (HIST) the state after every token is
+// written there and S is left as it was (the caller rolls back or commits);
+// without one S is advanced in place by all the tokens.
+// ---------------------------------------------------------------------------
+template <int D, typename TIn>
+struct TokenIn {
   using Cfg = DecodeCfg<D>;
-  const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
-  hipLaunchKernelGGL((decode_kernel<D, TIn, GATE, FORM>), dim3((unsigned)blocks), dim3(Cfg::NT), 0, stream,
-                     static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                     static_cast<const TIn *>(v), alpha, beta, S, o);
-  return hipGetLastError();
+  float a[Cfg::PASSES];
+  TIn k[Cfg::PASSES], q[Cfg::PASSES];
+  TIn v;
+  float b;
+};
+
+template <int D, typename TIn, int GATE>
+__device__ __forceinline__ void load_token_in(TokenIn<D, TIn> &x, const TIn *__restrict__ q,
+                                              const TIn *__restrict__ k, const TIn *__restrict__ v,
+                                              const float *__restrict__ alpha,
+                                              const float *__restrict__ beta, int64_t th, int r0,
+                                              int cj) {
+  using Cfg = DecodeCfg<D>;
+#pragma unroll
+  for (int p = 0; p < Cfg::PASSES; ++p) {
+    const int r = r0 + p * Cfg::RPP;
+    x.a[p] = GATE == KDA_GATE_HEAD ? alpha[th] : alpha[th * D + r];
+    x.k[p] = k[th * D + r];
+    x.q[p] = q[th * D + r];
+  }
+  x.v = v[th * D + cj];
+  x.b = beta[th];
 }
 
-template <typename TIn, int GATE, int FORM>
-hipError_t dispatch_d(const kda_shape_t &s, const void *q, const void *k, const void *v,
-                      const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
+template <int D, typename TIn, int GATE, int FORM, bool HIST>
+__global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ S,
+    float *__restrict__ o, float *__restrict__ hist, int ntok, int H) {
+  using Cfg = DecodeCfg<D>;
+  constexpr int TPR = Cfg::TPR, RPP = Cfg::RPP, PASSES = Cfg::PASSES, NW = Cfg::NW;
+  constexpr bool kPre = FORM == KDA_INPUT_PREACT;
+
+  __shared__ float s_red[NW][2][D];
+  __shared__ float s_qk[NW][3];
+  __shared__ float s_w[D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t nh = (int64_t)blockIdx.x;  // n * H + h
+  const int64_t n = nh / H, h = nh % H;
+  const int cq = tid % TPR;
+  const int r0 = tid / TPR;
+  const int cj = tid < D ? tid : 0;
+
+  TokenIn<D, TIn> cur, nxt;
+  load_token_in<D, TIn, GATE>(cur, q, k, v, alpha, beta, n * ntok * H + h, r0, cj);
+  float *Sp = S + nh * (int64_t)(D * D) + cq * 4;
+  float4 s[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) s[p] = *reinterpret_cast<const float4 *>(Sp + (int64_t)(r0 + p * RPP) * D);
+
+  for (int t = 0; t < ntok; ++t) {
+    const int64_t th = (n * ntok + t) * H + h;  // token row * H + head
+    // The next token's inputs (the last token reloads its own: no branch).
+    const int tn = t + 1 < ntok ? t + 1 : t;
+    load_token_in<D, TIn, GATE>(nxt, q, k, v, alpha, beta, (n * ntok + tn) * H + h, r0, cj);
+
+    float a[PASSES], kk[PASSES], qq[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      a[p] = kPre ? decay_from_preact(cur.a[p]) : cur.a[p];
+      kk[p] = to_f32(cur.k[p]);
+      qq[p] = to_f32(cur.q[p]);
+    }
+    const float bt = kPre ? strength_from_preact(cur.b) : cur.b;
+    const float vj = to_f32(cur.v);
+
+    float qk_part = 0.f, kn_part = 0.f, qn_part = 0.f;
+    if (cq == 0) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        qk_part += qq[p] * kk[p];
+        if constexpr (kPre) {
+          kn_part += kk[p] * kk[p];
+          qn_part += qq[p] * qq[p];
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      qk_part += __shfl_xor(qk_part, off);
+      if constexpr (kPre) {
+        kn_part += __shfl_xor(kn_part, off);
+        qn_part += __shfl_xor(qn_part, off);
+      }
+    }
+    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const float ka = a[p] * kk[p], qa = a[p] * qq[p];
+      x[0] += ka * s[p].x; x[1] += ka * s[p].y; x[2] += ka * s[p].z; x[3] += ka * s[p].w;
+      y[0] += qa * s[p].x; y[1] += qa * s[p].y; y[2] += qa * s[p].z; y[3] += qa * s[p].w;
+    }
+#pragma unroll
+    for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] += __shfl_xor(x[j], off);
+        y[j] += __shfl_xor(y[j], off);
+      }
+    }
+    if (lane < TPR) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s_red[wave][0][cq * 4 + j] = x[j];
+        s_red[wave][1][cq * 4 + j] = y[j];
+      }
+    }
+    if (lane == 0) {
+      s_qk[wave][0] = qk_part;
+      s_qk[wave][1] = kn_part;
+      s_qk[wave][2] = qn_part;
+    }
+    __syncthreads();
+    if (tid < D) {
+      float xs = 0.f, ys = 0.f, qk = 0.f, kn = 0.f, qn = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        xs += s_red[w][0][tid];
+        ys += s_red[w][1][tid];
+        qk += s_qk[w][0];
+        if constexpr (kPre) {
+          kn += s_qk[w][1];
+          qn += s_qk[w][2];
+        }
+      }
+      float ik = 1.f, iq = 1.f;
+      if constexpr (kPre) {
+        ik = inv_norm(kn);
+        iq = inv_norm(qn);
+        xs *= ik;
+        ys *= iq;
+        qk *= ik * iq;
+      }
+      const float wv = bt * (vj - xs);
+      s_w[tid] = kPre ? wv * ik : wv;
+      o[th * D + tid] = ys + qk * wv;
+    }
+    __syncthreads();
+    const float w0 = s_w[cq * 4 + 0], w1 = s_w[cq * 4 + 1], w2 = s_w[cq * 4 + 2], w3 = s_w[cq * 4 + 3];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      s[p].x = a[p] * s[p].x + kk[p] * w0;
+      s[p].y = a[p] * s[p].y + kk[p] * w1;
+      s[p].z = a[p] * s[p].z + kk[p] * w2;
+      s[p].w = a[p] * s[p].w + kk[p] * w3;
+    }
+    if constexpr (HIST) {
+      float *Hp = hist + th * (int64_t)(D * D) + cq * 4;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const f32x4 nv = {s[p].x, s[p].y, s[p].z, s[p].w};
+        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(Hp + (int64_t)(r0 + p * RPP) * D));
+      }
+    }
+    cur = nxt;
+  }
+  if constexpr (!HIST) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const f32x4 nv = {s[p].x, s[p].y, s[p].z, s[p].w};
+      __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(Sp + (int64_t)(r0 + p * RPP) * D));
+    }
+  }
+}
+
+// Rollback / commit: S[n, h] <- hist[n, j - 1, h] with j = accepted[n]
+// capped at ntok; j <= 0 leaves S[n, h] as it is.  One workgroup per
+// (sequence, head), float4 copies.
+__global__ __launch_bounds__(256) void commit_kernel(float *__restrict__ S, const float *__restrict__ hist,
+                                                     const int32_t *__restrict__ accepted, int ntok, int H,
+                                                     int dd) {
+  const int64_t nh = (int64_t)blockIdx.x;
+  const int64_t n = nh / H, h = nh % H;
+  int j = accepted[n];
+  if (j <= 0) return;
+  if (j > ntok) j = ntok;
+  const float4 *src = reinterpret_cast<const float4 *>(hist + ((n * ntok + (j - 1)) * H + h) * (int64_t)dd);
+  float4 *dst = reinterpret_cast<float4 *>(S + nh * (int64_t)dd);
+  for (int i = threadIdx.x; i < dd / 4; i += 256) dst[i] = src[i];
+}
+
+// Template dispatch on head size, q/k/v dtype, gate kind and input form: f
+// is called with (Int<D>, TypeTag<TIn>, Int<GATE>, Int<FORM>).
+template <typename T>
+struct TypeTag {
+  using type = T;
+};
+template <int V>
+using Int = std::integral_constant<int, V>;
+
+template <typename TIn, int GATE, int FORM, typename F>
+hipError_t by_dim(const kda_shape_t &s, F &f) {
   switch (s.d_k) {
-    case 16: return launch_decode_t<16, TIn, GATE, FORM>(s, q, k, v, alpha, beta, S, o, st);
-    case 32: return launch_decode_t<32, TIn, GATE, FORM>(s, q, k, v, alpha, beta, S, o, st);
-    case 64: return launch_decode_t<64, TIn, GATE, FORM>(s, q, k, v, alpha, beta, S, o, st);
-    case 128: return launch_decode_t<128, TIn, GATE, FORM>(s, q, k, v, alpha, beta, S, o, st);
+    case 16: return f(Int<16>{}, TypeTag<TIn>{}, Int<GATE>{}, Int<FORM>{});
+    case 32: return f(Int<32>{}, TypeTag<TIn>{}, Int<GATE>{}, Int<FORM>{});
+    case 64: return f(Int<64>{}, TypeTag<TIn>{}, Int<GATE>{}, Int<FORM>{});
+    case 128: return f(Int<128>{}, TypeTag<TIn>{}, Int<GATE>{}, Int<FORM>{});
   }
   return hipErrorInvalidValue;
 }
 
-template <typename TIn, int FORM>
-hipError_t dispatch_gate(const kda_shape_t &s, const void *q, const void *k, const void *v,
-                         const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
-  if (s.gate == KDA_GATE_HEAD) return dispatch_d<TIn, KDA_GATE_HEAD, FORM>(s, q, k, v, alpha, beta, S, o, st);
-  return dispatch_d<TIn, KDA_GATE_CHANNEL, FORM>(s, q, k, v, alpha, beta, S, o, st);
+template <typename TIn, int FORM, typename F>
+hipError_t by_gate(const kda_shape_t &s, F &f) {
+  if (s.gate == KDA_GATE_HEAD) return by_dim<TIn, KDA_GATE_HEAD, FORM>(s, f);
+  return by_dim<TIn, KDA_GATE_CHANNEL, FORM>(s, f);
 }
 
-template <typename TIn>
-hipError_t dispatch_form(const kda_shape_t &s, const void *q, const void *k, const void *v,
-                         const float *alpha, const float *beta, float *S, float *o, hipStream_t st) {
-  if (s.input_form == KDA_INPUT_PREACT)
-    return dispatch_gate<TIn, KDA_INPUT_PREACT>(s, q, k, v, alpha, beta, S, o, st);
-  return dispatch_gate<TIn, KDA_INPUT_FINAL>(s, q, k, v, alpha, beta, S, o, st);
+template <typename TIn, typename F>
+hipError_t by_form(const kda_shape_t &s, F &f) {
+  if (s.input_form == KDA_INPUT_PREACT) return by_gate<TIn, KDA_INPUT_PREACT>(s, f);
+  return by_gate<TIn, KDA_INPUT_FINAL>(s, f);
+}
+
+template <typename F>
+hipError_t dispatch(const kda_shape_t &s, F &&f) {
+  if (s.qkv_dtype == KDA_BF16) return by_form<__bf16>(s, f);
+  return by_form<float>(s, f);
 }
 
 }  // namespace
@@ -233,8 +430,45 @@ hipError_t dispatch_form(const kda_shape_t &s, const void *q, const void *k, con
 hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, float *S, float *o,
                          hipStream_t stream) {
-  if (s.qkv_dtype == KDA_BF16) return dispatch_form<__bf16>(s, q, k, v, alpha, beta, S, o, stream);
-  return dispatch_form<float>(s, q, k, v, alpha, beta, S, o, stream);
+  return dispatch(s, [&](auto d, auto t, auto g, auto f) {
+    constexpr int D = decltype(d)::value;
+    using TIn = typename decltype(t)::type;
+    const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
+    hipLaunchKernelGGL((decode_kernel<D, TIn, decltype(g)::value, decltype(f)::value>), dim3((unsigned)blocks),
+                       dim3(DecodeCfg<D>::NT), 0, stream, static_cast<const TIn *>(q),
+                       static_cast<const TIn *>(k), static_cast<const TIn *>(v), alpha, beta, S, o);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, float *S, float *o, float *hist,
+                                hipStream_t stream) {
+  return dispatch(s, [&](auto d, auto t, auto g, auto f) {
+    constexpr int D = decltype(d)::value;
+    using TIn = typename decltype(t)::type;
+    constexpr int G = decltype(g)::value, F = decltype(f)::value;
+    const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
+    const TIn *qp = static_cast<const TIn *>(q), *kp = static_cast<const TIn *>(k),
+              *vp = static_cast<const TIn *>(v);
+    if (hist != nullptr)
+      hipLaunchKernelGGL((decode_tokens_kernel<D, TIn, G, F, true>), dim3((unsigned)blocks),
+                         dim3(DecodeCfg<D>::NT), 0, stream, qp, kp, vp, alpha, beta, S, o, hist, s.seq_len,
+                         s.num_heads);
+    else
+      hipLaunchKernelGGL((decode_tokens_kernel<D, TIn, G, F, false>), dim3((unsigned)blocks),
+                         dim3(DecodeCfg<D>::NT), 0, stream, qp, kp, vp, alpha, beta, S, o, hist, s.seq_len,
+                         s.num_heads);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, const int32_t *accepted,
+                         hipStream_t stream) {
+  const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
+  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, S, hist, accepted, s.seq_len,
+                     s.num_heads, s.d_k * s.d_v);
+  return hipGetLastError();
 }
 
 }  // namespace kda

@@ -52,6 +52,14 @@ hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, con
                          const float *alpha, const float *beta, float *S, float *o,
                          hipStream_t stream);
 
+// s.seq_len tokens per sequence; hist == nullptr advances S in place.
+hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, float *S, float *o, float *hist,
+                                hipStream_t stream);
+
+hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, const int32_t *accepted,
+                         hipStream_t stream);
+
 // Prefill phases (bit mask): the chunk table and chunk-local matrices, then
 // the sequential state pass.
 constexpr int kPhaseLocal = 1;

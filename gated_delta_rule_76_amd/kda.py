@@ -87,6 +87,10 @@ def lib():
     L.kda_prefill_state_pass.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_decode_tokens.restype = ctypes.c_int
+    L.kda_decode_tokens.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_state_commit.restype = ctypes.c_int
+    L.kda_state_commit.argtypes = [shp, vp, vp, vp, vp]
     if L.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{_LIB_PATH} has ABI version {L.kda_abi_version()}, this binding "
                            f"needs {ABI_VERSION}; rebuild with `python -m gated_delta_rule_76_amd.build`")
@@ -281,3 +285,62 @@ def decode_step(q, k, v, alpha, beta, state, out=None, preact=False):
                                _ptr(state), _ptr(o), _stream(q.device))
     _check(st, "kda_decode_step")
     return o
+
+
+def decode_tokens(q, k, v, alpha, beta, state, keep_states=False, preact=False, out=None,
+                  states=None):
+    """k new tokens for each of N sequences from the live states.
+
+    q, k, v [N, k, H, D]; alpha [N, k, H, D] (or [N, k, H]: scalar gate);
+    beta [N, k, H]; state [N, H, D, D] fp32.  Returns o [N, k, H, D] fp32.
+    keep_states=False advances ``state`` in place by all k tokens.
+    keep_states=True leaves ``state`` as it is and also returns the state
+    after every token, [N, k, H, D, D] fp32 (``states`` may be given), for
+    ``state_commit``: returns (o, states).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_gpu(name, t)
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float32 or bfloat16")
+    _require_gpu("alpha", alpha, torch.float32)
+    _require_gpu("beta", beta, torch.float32)
+    _require_gpu("state", state, torch.float32)
+    if q.dim() != 4:
+        raise ValueError("multi-token decode inputs are [N, k, H, D]")
+    N, K, H, D = q.shape
+    gate = _gate_of(alpha, q)
+    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("beta", beta, q.shape[:-1]),
+                         ("state", state, (N, H, D, D))):
+        if tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
+    o = out if out is not None else torch.empty((N, K, H, D), dtype=torch.float32, device=q.device)
+    _require_gpu("out", o, torch.float32)
+    hist = None
+    if keep_states:
+        hist = states if states is not None else torch.empty((N, K, H, D, D), dtype=torch.float32,
+                                                             device=q.device)
+        _require_gpu("states", hist, torch.float32)
+        if tuple(hist.shape) != (N, K, H, D, D):
+            raise ValueError(f"states must be {(N, K, H, D, D)}")
+    shape = make_shape(N, K, N * K, H, D, q.dtype, gate, KDA_INPUT_PREACT if preact else KDA_INPUT_FINAL)
+    _check(lib().kda_decode_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(state), _ptr(o), _ptr(hist), _stream(q.device)),
+           "kda_decode_tokens")
+    return (o, hist) if keep_states else o
+
+
+def state_commit(state, states, accepted):
+    """state[n] <- states[n, accepted[n] - 1] for accepted[n] >= 1 (capped at
+    k); accepted[n] <= 0 keeps state[n].  accepted: int32 [N] on the GPU."""
+    _require_gpu("state", state, torch.float32)
+    _require_gpu("states", states, torch.float32)
+    _require_gpu("accepted", accepted, torch.int32)
+    if states.dim() != 5 or state.dim() != 4:
+        raise ValueError("state is [N, H, D, D] and states [N, k, H, D, D]")
+    N, K, H, D, _ = states.shape
+    if tuple(state.shape) != (N, H, D, D) or tuple(accepted.shape) != (N,):
+        raise ValueError("state, states and accepted disagree in shape")
+    shape = make_shape(N, K, N * K, H, D, torch.float32)
+    _check(lib().kda_state_commit(ctypes.byref(shape), _ptr(state), _ptr(states), _ptr(accepted),
+                                  _stream(state.device)), "kda_state_commit")
+    return state

@@ -205,6 +205,42 @@ kda_status_t kda_decode_step(const kda_shape_t *shape,
                              float *S, float *o,
                              void *stream);
 
+/* Several new tokens per sequence from the live state: speculative
+ * verification of drafted tokens (the ainewsfeed.tech page on the
+ * GLM-5.3-Flash architecture stack: one MTP draft layer, drafted tokens
+ * checked in parallel, rejected ones rolled back), or plain multi-token
+ * decode.  Each token is one step of the update rule, in order; the state
+ * is read once and kept in registers across a sequence's tokens.
+ *   shape       num_seqs = N, seq_len = k >= 1 tokens per sequence,
+ *               total_tokens must be N * k, no cu_seqlens
+ *   q, k        [N * k][H][d_k]   (sequence n owns rows n*k .. n*k+k-1)
+ *   v           [N * k][H][d_v]
+ *   alpha       [N * k][H][d_k] fp32 ([N * k][H] with KDA_GATE_HEAD)
+ *   beta        [N * k][H]     fp32
+ *   S           [N][H][d_k][d_v] fp32 live states
+ *   o           [N * k][H][d_v] fp32 output for every token
+ *   S_hist      [N][k][H][d_k][d_v] fp32, or NULL.  NULL: S is advanced in
+ *               place by all k tokens.  Non-NULL: S is left unchanged and
+ *               S_hist[n][t] receives the state after token t of sequence n
+ *               (for kda_state_commit); it must not overlap S.
+ * Gate kind and input form as for the other calls. */
+kda_status_t kda_decode_tokens(const kda_shape_t *shape,
+                               const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta,
+                               float *S, float *o, float *S_hist,
+                               void *stream);
+
+/* After verification: for every sequence n with j = accepted[n] >= 1,
+ * S[n] <- S_hist[n][min(j, k) - 1] (the state after its j accepted tokens);
+ * j <= 0 leaves S[n] unchanged (every draft rejected).
+ *   shape       num_seqs = N, seq_len = k (as passed to kda_decode_tokens),
+ *               num_heads, d_k == d_v; the other fields are not used
+ *   S           [N][H][d_k][d_v] fp32, updated
+ *   S_hist      [N][k][H][d_k][d_v] fp32 from kda_decode_tokens
+ *   accepted    [N] int32 device array */
+kda_status_t kda_state_commit(const kda_shape_t *shape, float *S, const float *S_hist,
+                              const int32_t *accepted, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,9 +49,10 @@ def decode(L, s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, o=FAKE):
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["kda_abi_version", "kda_decode_step", "kda_prefill",
-                                    "kda_prefill_chunk_local", "kda_prefill_state_pass",
-                                    "kda_prefill_workspace_size", "kda_status_string"]
+    assert declared_functions() == ["kda_abi_version", "kda_decode_step", "kda_decode_tokens",
+                                    "kda_prefill", "kda_prefill_chunk_local", "kda_prefill_state_pass",
+                                    "kda_prefill_workspace_size", "kda_state_commit",
+                                    "kda_status_string"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -170,6 +171,35 @@ def test_decode_validation(L):
     for field in ("q", "k", "v", "a", "S", "o"):
         assert decode(L, good, **{field: FAKE + 4}) == INVALID, field
     assert decode(L, kda.KdaShape(0, 1, 0, 2, 128, 128, 1)) == OK
+
+
+def test_decode_tokens_and_commit_validation(L):
+    def tok(s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, o=FAKE, hist=None):
+        return L.kda_decode_tokens(ctypes.byref(s) if s is not None else None, q, k, v, a, b, S, o, hist,
+                                   None)
+    sh = lambda N=4, K=3, total=None, d=128, gate=0: kda.KdaShape(N, K, N * K if total is None else total,
+                                                                  2, d, d, 1, gate, 0)
+    assert tok(None) == INVALID
+    assert tok(sh(K=0)) == INVALID                     # at least one token per sequence
+    assert tok(sh(total=11)) == INVALID                # total must be N * k
+    assert tok(sh(d=96)) == UNSUPPORTED
+    assert tok(sh(N=0, total=0)) == OK                 # nothing to do, nothing launched
+    for field in ("q", "k", "v", "a", "b", "S", "o"):
+        assert tok(sh(), **{field: None}) == INVALID, field
+        assert tok(sh(), **{field: FAKE + 2}) == INVALID, field
+    assert tok(sh(), hist=FAKE + 8) == INVALID
+    assert tok(sh(gate=1), a=FAKE + 2) == INVALID
+    com = lambda s, S=FAKE, hist=FAKE, acc=FAKE: L.kda_state_commit(
+        ctypes.byref(s) if s is not None else None, S, hist, acc, None)
+    assert com(None) == INVALID
+    assert com(sh(K=0)) == INVALID
+    assert com(sh(d=48)) == UNSUPPORTED
+    assert com(sh(N=0, total=0)) == OK
+    assert com(sh(), S=None) == INVALID
+    assert com(sh(), hist=None) == INVALID
+    assert com(sh(), acc=None) == INVALID
+    assert com(sh(), acc=FAKE + 2) == INVALID
+    assert com(sh(), hist=FAKE + 4) == INVALID
 
 
 def test_binding_takes_the_gate_kind_from_alpha():
