@@ -21,7 +21,9 @@ fp64 CPU oracle timed on the host over the whole prefill_4k workload.
 The line also carries, on the same prefill and decode shapes, the
 scalar-gate form (one alpha per token and head) under ``scalar_gate`` and the
 layer fed pre-activations (gate and normalisation computed in the kernels)
-under ``preact`` (``--no-variants`` skips both).  ``--oracle-rates`` times only the CPU oracle, on every workload,
+under ``preact``, and speculative verification of two tokens per sequence
+(kda_decode_tokens with the state history, then kda_state_commit) under
+``verify`` (``--no-variants`` skips all three).  ``--oracle-rates`` times only the CPU oracle, on every workload,
 and prints those rates as one JSON line.
 """
 
@@ -60,7 +62,7 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-variants", action="store_true",
-                   help="skip the scalar-gate and pre-activation measurements")
+                   help="skip the scalar-gate, pre-activation and verify measurements")
     p.add_argument("--decode-batch", type=int, default=256)
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
@@ -89,6 +91,12 @@ def layer_bytes(gate):
 
 def decode_bytes(gate):
     return 2 * 128 * 128 * 4 + 768 + ALPHA_BYTES[gate] + 4 + 512
+
+
+def verify_bytes(k):
+    """k tokens of one (sequence, head) with the state history: the state
+    read once, k states written, each token's q, k, v, alpha, beta, o."""
+    return 128 * 128 * 4 * (1 + k) + k * (768 + 512 + 4 + 512)
 
 
 def record_bytes_per_token(d):
@@ -191,6 +199,61 @@ def bench_decode(B, dev, gate="channel", form="final"):
     return {"B": B, "H": H, "D": D, "steps": n, "ms_per_step": ms, "state_rmw_gbs": rmw_gbs}
 
 
+def bench_verify(B, K, dev, steps=50):
+    """Speculative verification of K tokens per sequence (the next token and
+    K - 1 drafts): kda_decode_tokens with the state history, then
+    kda_state_commit of a seeded accepted count per sequence.  Returns the
+    per-call times of both."""
+    from gated_delta_rule_76_amd import inputs, kda
+    spec = inputs.WORKLOADS["decode_b256"]
+    H, D = spec["H"], spec["D"]
+    sets = []
+    for i in range(N_SETS):
+        d = inputs.decode_inputs(B * K, H, D, 1, torch.bfloat16, spec["decay"], spec["s_std"], seed=i,
+                                 device=dev)
+        sets.append({key: d[key][0].reshape((B, K) + tuple(d[key].shape[2:])).contiguous()
+                     for key in ("q", "k", "v", "alpha", "beta")})
+    S = inputs.state(B, H, D, spec["s_std"], seed=0, device=dev)
+    o = torch.empty((B, K, H, D), dtype=torch.float32, device=dev)
+    hist = torch.empty((B, K, H, D, D), dtype=torch.float32, device=dev)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(0)
+    accepted = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev)
+    run = lambda t: kda.decode_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, keep_states=True,
+                                      out=o, states=hist)
+    for i in range(5):
+        run(sets[i % N_SETS])
+        kda.state_commit(S, hist, accepted)
+    torch.cuda.synchronize()
+    ev = [_events() for _ in range(steps)]
+    ec = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        run(sets[i % N_SETS])
+        ev[i][1].record()
+        kda.state_commit(S, hist, accepted)
+        ec[i].record()
+    torch.cuda.synchronize()
+    vt = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ct = float(np.mean([ev[i][1].elapsed_time(ec[i]) for i in range(steps)]))
+    n_acc = int((accepted > 0).sum())
+    return {"B": B, "K": K, "H": H, "verify_ms": vt, "commit_ms": ct, "committed_seqs": n_acc}
+
+
+def verify_summary(vf):
+    B, K, H = vf["B"], vf["K"], vf["H"]
+    gbs = B * H * verify_bytes(K) / (vf["verify_ms"] * 1e-3) / 1e9
+    return {"metric": "speculative verify steps/s (B=%d, %d tokens per sequence, H=32, d=128)" % (B, K),
+            "value": 1e3 / (vf["verify_ms"] + vf["commit_ms"]), "unit": "steps/s",
+            "verify_ms": vf["verify_ms"], "commit_ms": vf["commit_ms"],
+            "tokens_per_s": B * K / (vf["verify_ms"] * 1e-3),
+            "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None, "bytes_per_seq_head": verify_bytes(K)},
+            "commit": {"sequences_committed": vf["committed_seqs"],
+                       "achieved_gbs": vf["committed_seqs"] * H * 2 * 128 * 128 * 4 / (vf["commit_ms"] * 1e-3) / 1e9}}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle as it stands, one process per group of heads
 # (or of (sequence, head) pairs for decode) on the host cores.  Runs before
@@ -229,6 +292,20 @@ def _cpu_decode_worker(pairs):
         for s in range(a["steps"]):
             _, S = step(a["q"][s][pairs], a["k"][s][pairs], a["v"][s][pairs],
                                    a["alpha"][s][pairs], a["beta"][s][pairs], S)
+        return time.perf_counter() - t0
+
+
+def _cpu_verify_worker(seqs):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import speculative
+    a = _CPU_INPUTS
+    K = a["K"]
+    rows = (seqs[:, None] * K + np.arange(K)[None, :]).ravel()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        speculative.decode_tokens(a["q"][rows], a["k"][rows], a["v"][rows], a["alpha"][rows],
+                                  a["beta"][rows], a["S"][seqs], K)
         return time.perf_counter() - t0
 
 
@@ -299,6 +376,26 @@ def oracle_decode_rate(B=256, steps=100, gate="channel"):
                       f"over (sequence, head) groups ({wall:.2f} s wall, {busy:.1f} s CPU)"}
 
 
+def oracle_verify_rate(B=256, K=2):
+    """Oracle steps/s of speculative verification: K tokens for each of B
+    sequences x 32 heads with every intermediate state kept."""
+    from gated_delta_rule_76_amd import inputs
+    spec = inputs.WORKLOADS["decode_b256"]
+    H, D = spec["H"], spec["D"]
+    d = inputs.decode_inputs(B * K, H, D, 1, torch.bfloat16, spec["decay"], spec["s_std"], seed=0,
+                             device="cpu")
+    for key in ("q", "k", "v", "alpha", "beta"):
+        _CPU_INPUTS[key] = d[key][0].double().numpy()
+    _CPU_INPUTS["S"] = d["S"][:B].double().numpy()
+    _CPU_INPUTS["K"] = K
+    wall, busy, cores = _pool_map(_cpu_verify_worker, B)
+    _CPU_INPUTS.clear()
+    return {"value": 1.0 / wall, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"one verify step, B={B} sequences x {K} tokens, H={H} d={D}, states kept, "
+                      f"numpy fp64, {cores} processes over sequence groups ({wall:.2f} s wall, "
+                      f"{busy:.1f} s CPU)"}
+
+
 def cpu_baseline():
     return oracle_prefill_rate("prefill_4k", passes=3)
 
@@ -323,6 +420,7 @@ def oracle_rates():
     out["prefill_4k_scalar_gate"] = oracle_prefill_rate("prefill_4k", passes=3, gate="head")
     out["decode_b256_scalar_gate"] = oracle_decode_rate(256, 100, gate="head")
     out["prefill_4k_preact"] = oracle_prefill_rate("prefill_4k", passes=3, form="preact")
+    out["verify_b256_k2"] = oracle_verify_rate(256, 2)
     return out
 
 
@@ -454,6 +552,9 @@ def main():
             pa["decode"] = decode_summary(bench_decode(args.decode_batch, dev, form="preact"), "channel",
                                           "preact")
         out["preact"] = pa
+        if not args.no_decode:
+            print("[bench] speculative verify", file=sys.stderr, flush=True)
+            out["verify"] = verify_summary(bench_verify(args.decode_batch, 2, dev))
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
