@@ -23,10 +23,12 @@ prologue     rates, strengths and unit q, k from pre-activations, then the
              recurrence
 speculative  several tokens per sequence from a live state, every
              intermediate state kept, and the rollback to the accepted one
+backward     gradients of the recurrence with respect to q, k, v, alpha, beta
+             and the initial state, for given dL/do and dL/dS_T
 
 Pins (every function is pinned by tests/test_oracle_pins.py,
-tests/test_oracle_scalar_gate.py, tests/test_oracle_prologue.py and
-tests/test_oracle_speculative.py against closed forms, invariants, a library
+tests/test_oracle_scalar_gate.py, tests/test_oracle_prologue.py,
+tests/test_oracle_speculative.py and tests/test_oracle_backward.py against closed forms, invariants, a library
 routine and a hand-worked golden example; see the module docstrings).  No function here is "parity unpinned".
 """
 
@@ -39,4 +41,4 @@ from .recurrence import (  # noqa: F401
 from .bruteforce import kda_bruteforce  # noqa: F401
 from .exact import kda_exact  # noqa: F401
 from .scalar_gate import gdn_decode_step, gdn_recurrent, gdn_step  # noqa: F401
-from . import prologue, speculative  # noqa: F401
+from . import backward, prologue, speculative  # noqa: F401
