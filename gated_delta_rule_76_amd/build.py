@@ -23,7 +23,7 @@ OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libkda.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_backward.hip"]
 ARCH = "gfx950"
 
 

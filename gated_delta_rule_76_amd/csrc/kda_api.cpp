@@ -215,4 +215,47 @@ kda_status_t kda_decode_step(const kda_shape_t *shape, const void *q, const void
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status_t kda_backward_workspace_size(const kda_shape_t *shape, size_t *bytes) {
+  if (bytes == nullptr || shape == nullptr) return KDA_ERR_INVALID_ARGUMENT;
+  kda_status_t st = check_prefill_shape(shape, /*varlen=*/true);
+  if (st != KDA_OK) return st;
+  if (shape->input_form != KDA_INPUT_FINAL) return KDA_ERR_UNSUPPORTED;
+  *bytes = kda::backward_layout(*shape).bytes;
+  return KDA_OK;
+}
+
+kda_status_t kda_backward(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                          const float *S0, const float *dO, const float *dS_T, float *dq, float *dk,
+                          float *dv, float *dalpha, float *dbeta, float *dS0, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  const bool varlen = cu_seqlens != nullptr;
+  kda_status_t st = check_prefill_shape(shape, varlen);
+  if (st != KDA_OK) return st;
+  if (shape->input_form != KDA_INPUT_FINAL) return KDA_ERR_UNSUPPORTED;
+  const kda_shape_t &s = *shape;
+  if (s.total_tokens > 0) {
+    if (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha || !dbeta)
+      return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !alpha_aligned(shape, alpha) ||
+        !aligned4(beta) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        !alpha_aligned(shape, dalpha) || !aligned4(dbeta))
+      return KDA_ERR_INVALID_ARGUMENT;
+  }
+  if ((S0 && !aligned16(S0)) || (dS_T && !aligned16(dS_T)) || (dS0 && !aligned16(dS0)) ||
+      (cu_seqlens && !aligned4(cu_seqlens)))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (s.num_seqs == 0) return s.total_tokens > 0 ? KDA_ERR_INVALID_ARGUMENT : KDA_OK;
+  // One workgroup per (sequence, head, 16 value columns).
+  if ((int64_t)s.num_seqs * s.num_heads * (s.d_v < 16 ? 1 : s.d_v / 16) >= ((int64_t)1 << 31))
+    return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda::backward_layout(s).bytes;
+  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kda::kWorkspaceAlign - 1)) != 0)
+    return KDA_ERR_INVALID_ARGUMENT;
+  kda::BwdArgs a{q, k, v, alpha, beta, cu_seqlens, S0, dO, dS_T, dq, dk, dv, dalpha, dbeta, dS0, workspace};
+  hipError_t e = kda::launch_backward(s, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 }  // extern "C"

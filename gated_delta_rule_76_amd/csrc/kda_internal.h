@@ -60,6 +60,43 @@ hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void 
 hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, const int32_t *accepted,
                          hipStream_t stream);
 
+// Backward pass.  Workspace: state checkpoints every kBwdBlock tokens per
+// (sequence, head) -- at most floor(T / kBwdBlock) + N slots of d_k x d_v
+// floats per head -- then per-slice partial sums of dq, dk, dalpha and dbeta
+// over the d_v / 16 column slices ([slices][T][H][d], dalpha [slices][T][H]
+// for one rate per head, dbeta [slices][T][H]).
+constexpr int kBwdBlock = 16;
+
+struct BwdLayout {
+  size_t ckpt_off, part_q_off, part_k_off, part_a_off, part_b_off, bytes;
+};
+
+inline BwdLayout backward_layout(const kda_shape_t &s) {
+  const size_t d = (size_t)s.d_k, H = (size_t)s.num_heads, T = (size_t)s.total_tokens;
+  const size_t slices = d < 16 ? 1 : d / 16;
+  const size_t slots = (size_t)(s.total_tokens / kBwdBlock) + (size_t)s.num_seqs;
+  const size_t da = s.gate == KDA_GATE_HEAD ? 1 : d;
+  BwdLayout L;
+  L.ckpt_off = 0;
+  L.part_q_off = align_up(L.ckpt_off + sizeof(float) * slots * H * d * (size_t)s.d_v, kWorkspaceAlign);
+  L.part_k_off = align_up(L.part_q_off + sizeof(float) * slices * T * H * d, kWorkspaceAlign);
+  L.part_a_off = align_up(L.part_k_off + sizeof(float) * slices * T * H * d, kWorkspaceAlign);
+  L.part_b_off = align_up(L.part_a_off + sizeof(float) * slices * T * H * da, kWorkspaceAlign);
+  L.bytes = align_up(L.part_b_off + sizeof(float) * slices * T * H, kWorkspaceAlign);
+  return L;
+}
+
+struct BwdArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  const int32_t *cu;
+  const float *S0, *dO, *dS_T;
+  float *dq, *dk, *dv, *dalpha, *dbeta, *dS0;
+  void *workspace;
+};
+
+hipError_t launch_backward(const kda_shape_t &s, const BwdArgs &a, hipStream_t stream);
+
 // Prefill phases (bit mask): the chunk table and chunk-local matrices, then
 // the sequential state pass.
 constexpr int kPhaseLocal = 1;

@@ -39,7 +39,8 @@ import torch
 DECAY_SHIFT = {"medium": 0.0, "strong": 2.0, "weak": -4.0}
 BLOCK_TOKENS = 65536
 
-_STREAM = {"q": 1, "k": 2, "v": 3, "alpha": 4, "beta": 5, "state": 6, "lengths": 7}
+_STREAM = {"q": 1, "k": 2, "v": 3, "alpha": 4, "beta": 5, "state": 6, "lengths": 7, "dO": 8,
+           "dS_T": 9}
 
 
 def _generator(device, seed, stream, block):
@@ -134,6 +135,18 @@ def decode_inputs(B, H, D, steps, dtype=torch.bfloat16, decay="strong", s_std=0.
     out = {name: x.reshape((steps, B) + tuple(x.shape[1:])) for name, x in t.items()}
     out["S"] = state(B, H, D, s_std, seed, device)
     return out
+
+
+def grad_inputs(T, H, D, N, seed=0, device="cpu", dS_std=0.02):
+    """Upstream gradients for the backward pass: dL/do ~ N(0,1) fp32
+    [T, H, D] and dL/dS_T ~ dS_std * N(0,1) fp32 [N, H, D, D] (None when
+    dS_std is None)."""
+    dO = _randn_tokens((T, H, D), seed, _STREAM["dO"], device)
+    dST = None
+    if dS_std is not None:
+        g = _generator(device, seed, _STREAM["dS_T"], 0)
+        dST = (dS_std * torch.randn((N, H, D, D), generator=g, device=device)).contiguous()
+    return dO, dST
 
 
 # The measured workloads, named by what they are.

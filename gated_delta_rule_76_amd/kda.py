@@ -91,6 +91,10 @@ def lib():
     L.kda_decode_tokens.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_state_commit.restype = ctypes.c_int
     L.kda_state_commit.argtypes = [shp, vp, vp, vp, vp]
+    L.kda_backward_workspace_size.restype = ctypes.c_int
+    L.kda_backward_workspace_size.argtypes = [shp, ctypes.POINTER(sz)]
+    L.kda_backward.restype = ctypes.c_int
+    L.kda_backward.argtypes = [shp] + [vp] * 16 + [sz, vp]
     if L.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{_LIB_PATH} has ABI version {L.kda_abi_version()}, this binding "
                            f"needs {ABI_VERSION}; rebuild with `python -m gated_delta_rule_76_amd.build`")
@@ -344,3 +348,69 @@ def state_commit(state, states, accepted):
     _check(lib().kda_state_commit(ctypes.byref(shape), _ptr(state), _ptr(states), _ptr(accepted),
                                   _stream(state.device)), "kda_state_commit")
     return state
+
+
+def backward_workspace_size(num_seqs, total_tokens, num_heads, d, dtype=torch.bfloat16, gate=KDA_GATE_CHANNEL):
+    shape = make_shape(num_seqs, 0, total_tokens, num_heads, d, dtype, gate)
+    out = ctypes.c_size_t(0)
+    _check(lib().kda_backward_workspace_size(ctypes.byref(shape), ctypes.byref(out)),
+           "kda_backward_workspace_size")
+    return int(out.value)
+
+
+def backward(q, k, v, alpha, beta, dO, initial_state=None, dS_T=None, cu_seqlens=None, *,
+             want_dS0=True, workspace=None):
+    """Gradients of the layer: returns (dq, dk, dv, dalpha, dbeta, dS0), all
+    fp32 (dS0 None if want_dS0 is False).  Inputs as for ``prefill`` (packed
+    [T, H, D] with optional cu_seqlens, or [B, T, H, D]); dO has v's shape
+    (fp32), dS_T the final states' shape (fp32) or None for zero."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_gpu(name, t)
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float32 or bfloat16")
+    _require_gpu("alpha", alpha, torch.float32)
+    _require_gpu("beta", beta, torch.float32)
+    _require_gpu("dO", dO, torch.float32)
+    dev = q.device
+    if q.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens needs the packed [T, H, D] layout")
+        B, T, H, D = q.shape
+        N, seq_len, total = B, T, B * T
+    elif q.dim() == 3:
+        T, H, D = q.shape
+        total = T
+        if cu_seqlens is None:
+            N, seq_len = 1, T
+        else:
+            _require_gpu("cu_seqlens", cu_seqlens, torch.int32)
+            N, seq_len = cu_seqlens.numel() - 1, 0
+    else:
+        raise ValueError("q must be [T, H, D] or [B, T, H, D]")
+    gate = _gate_of(alpha, q)
+    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("beta", beta, q.shape[:-1]),
+                         ("dO", dO, v.shape)):
+        if tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
+    for name, t in (("initial_state", initial_state), ("dS_T", dS_T)):
+        if t is not None:
+            _require_gpu(name, t, torch.float32)
+            if tuple(t.shape) != (N, H, D, D):
+                raise ValueError(f"{name} must be {(N, H, D, D)}")
+    shape = make_shape(N, seq_len, total, H, D, q.dtype, gate)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32)
+    dalpha, dbeta = torch.empty(alpha.shape, **f32), torch.empty(beta.shape, **f32)
+    dS0 = torch.empty((N, H, D, D), **f32) if want_dS0 else None
+    need = ctypes.c_size_t(0)
+    _check(lib().kda_backward_workspace_size(ctypes.byref(shape), ctypes.byref(need)),
+           "kda_backward_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=dev)
+    _require_gpu("workspace", workspace)
+    _check(lib().kda_backward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                              _ptr(cu_seqlens), _ptr(initial_state), _ptr(dO), _ptr(dS_T), _ptr(dq),
+                              _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(dbeta), _ptr(dS0), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(dev)),
+           "kda_backward")
+    return dq, dk, dv, dalpha, dbeta, dS0

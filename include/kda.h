@@ -241,6 +241,43 @@ kda_status_t kda_decode_tokens(const kda_shape_t *shape,
 kda_status_t kda_state_commit(const kda_shape_t *shape, float *S, const float *S_hist,
                               const int32_t *accepted, void *stream);
 
+/* Backward pass (training): gradients of L with respect to q, k, v, alpha,
+ * beta and the initial states, given dL/do for every token (dO) and dL/dS_T
+ * for every final state (dS_T, or NULL for zero).  It differentiates the
+ * same update rule and read-out as kda_prefill, token by token in reverse:
+ * with X = Diag(alpha_t) S_{t-1}, w = v_t - X^T k_t and G = dL/dS_t,
+ *     dv_t = beta_t G^T k_t,  dbeta_t = (G^T k_t) . w,
+ *     dk_t = beta_t (G w - X G^T k_t),  dq_t = S_t dO_t,
+ *     dalpha_t = rowsum((G - beta_t k_t k_t^T G) * S_{t-1})  (summed over all
+ *     entries with KDA_GATE_HEAD),
+ *     dL/dS_{t-1} = Diag(alpha_t) (G - beta_t k_t k_t^T G) + q_{t-1} dO_{t-1}^T.
+ * The states are recomputed from S0 (checkpoints every 16 tokens in the
+ * workspace); nothing from a forward call is needed.
+ *   shape, q, k, v, alpha, beta, cu_seqlens, S0  as for kda_prefill
+ *                 (input_form must be KDA_INPUT_FINAL, else UNSUPPORTED)
+ *   dO            [total_tokens][H][d_v] fp32
+ *   dS_T          [N][H][d_k][d_v] fp32, or NULL (zero)
+ *   dq, dk        [total_tokens][H][d_k] fp32 outputs
+ *   dv            [total_tokens][H][d_v] fp32 output
+ *   dalpha        alpha's layout, fp32 output
+ *   dbeta         [total_tokens][H] fp32 output
+ *   dS0           [N][H][d_k][d_v] fp32 output, or NULL to skip
+ *   workspace     at least kda_backward_workspace_size() bytes, 256-byte
+ *                 aligned: state checkpoints (floor(T/16) + N per head) and
+ *                 per-16-column partial sums of dq, dk, dalpha, dbeta
+ *                 (4 (3 d + 1) (d/16) T H bytes at most)
+ * Outputs must not overlap inputs.  Results are deterministic (the partial
+ * sums are added in a fixed order). */
+kda_status_t kda_backward_workspace_size(const kda_shape_t *shape, size_t *bytes);
+kda_status_t kda_backward(const kda_shape_t *shape,
+                          const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta,
+                          const int32_t *cu_seqlens, const float *S0,
+                          const float *dO, const float *dS_T,
+                          float *dq, float *dk, float *dv, float *dalpha, float *dbeta,
+                          float *dS0,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

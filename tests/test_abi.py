@@ -49,8 +49,9 @@ def decode(L, s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, o=FAKE):
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["kda_abi_version", "kda_decode_step", "kda_decode_tokens",
-                                    "kda_prefill", "kda_prefill_chunk_local", "kda_prefill_state_pass",
+    assert declared_functions() == ["kda_abi_version", "kda_backward", "kda_backward_workspace_size",
+                                    "kda_decode_step", "kda_decode_tokens", "kda_prefill",
+                                    "kda_prefill_chunk_local", "kda_prefill_state_pass",
                                     "kda_prefill_workspace_size", "kda_state_commit",
                                     "kda_status_string"]
 
@@ -200,6 +201,42 @@ def test_decode_tokens_and_commit_validation(L):
     assert com(sh(), acc=None) == INVALID
     assert com(sh(), acc=FAKE + 2) == INVALID
     assert com(sh(), hist=FAKE + 4) == INVALID
+
+
+def test_backward_validation_and_workspace(L):
+    s = shape(N=2, T=40, H=3, d=128, dtype=1)
+    out = ctypes.c_size_t(0)
+    assert L.kda_backward_workspace_size(ctypes.byref(s), ctypes.byref(out)) == OK
+    slots, slices, T, H, d = 40 * 2 // 16 + 2, 8, 80, 3, 128
+    al = lambda x: -(-x // 256) * 256
+    want = al(4 * slots * H * d * d)
+    want = al(want + 4 * slices * T * H * d)      # dq partials
+    want = al(want + 4 * slices * T * H * d)      # dk partials
+    want = al(want + 4 * slices * T * H * d)      # dalpha partials
+    want = al(want + 4 * slices * T * H)          # dbeta partials
+    assert out.value == want
+    assert L.kda_backward_workspace_size(ctypes.byref(shape(form=1)), ctypes.byref(out)) == UNSUPPORTED
+    need = out.value
+    def bwd(sh, ws_bytes=1 << 40, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, cu=None, S0=None, dO=FAKE, dST=None, dq=FAKE,
+                 dk=FAKE, dv=FAKE, da=FAKE, db=FAKE, dS0=None, ws=FAKE)
+        a.update(kw)
+        return L.kda_backward(ctypes.byref(sh) if sh is not None else None, a["q"], a["k"], a["v"], a["a"],
+                              a["b"], a["cu"], a["S0"], a["dO"], a["dST"], a["dq"], a["dk"], a["dv"],
+                              a["da"], a["db"], a["dS0"], a["ws"], ws_bytes, None)
+    small = shape(N=1, T=32, H=2, d=16)
+    assert bwd(None) == INVALID
+    assert bwd(shape(form=1)) == UNSUPPORTED
+    assert bwd(shape(d=48)) == UNSUPPORTED
+    for field in ("q", "k", "v", "a", "b", "dO", "dq", "dk", "dv", "da", "db"):
+        assert bwd(small, **{field: None}) == INVALID, field
+        assert bwd(small, **{field: FAKE + 2}) == INVALID, field
+    assert bwd(small, dS0=FAKE + 8) == INVALID
+    assert bwd(small, dST=FAKE + 8) == INVALID
+    assert bwd(small, ws=None) == WS_SMALL
+    assert bwd(small, ws_bytes=10) == WS_SMALL
+    assert bwd(small, ws=FAKE + 16) == INVALID
+    assert bwd(shape(N=0, T=0)) == OK
 
 
 def test_binding_takes_the_gate_kind_from_alpha():
