@@ -21,9 +21,10 @@ fp64 CPU oracle timed on the host over the whole prefill_4k workload.
 The line also carries, on the same prefill and decode shapes, the
 scalar-gate form (one alpha per token and head) under ``scalar_gate`` and the
 layer fed pre-activations (gate and normalisation computed in the kernels)
-under ``preact``, and speculative verification of two tokens per sequence
+under ``preact``, speculative verification of two tokens per sequence
 (kda_decode_tokens with the state history, then kda_state_commit) under
-``verify`` (``--no-variants`` skips all three).  ``--oracle-rates`` times only the CPU oracle, on every workload,
+``verify``, and the backward pass over the prefill_4k workload under
+``backward`` (``--no-variants`` skips all four).  ``--oracle-rates`` times only the CPU oracle, on every workload,
 and prints those rates as one JSON line.
 """
 
@@ -62,7 +63,7 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-variants", action="store_true",
-                   help="skip the scalar-gate, pre-activation and verify measurements")
+                   help="skip the scalar-gate, pre-activation, verify and backward measurements")
     p.add_argument("--decode-batch", type=int, default=256)
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
@@ -91,6 +92,12 @@ def layer_bytes(gate):
 
 def decode_bytes(gate):
     return 2 * 128 * 128 * 4 + 768 + ALPHA_BYTES[gate] + 4 + 512
+
+
+def backward_bytes():
+    """Per token and head: q, k, v (bf16), alpha, beta, dO read; dq, dk, dv,
+    dalpha, dbeta written (fp32)."""
+    return 768 + 512 + 4 + 512 + 4 * 512 + 4
 
 
 def verify_bytes(k):
@@ -240,6 +247,38 @@ def bench_verify(B, K, dev, steps=50):
     return {"B": B, "K": K, "H": H, "verify_ms": vt, "commit_ms": ct, "committed_seqs": n_acc}
 
 
+def bench_backward(name, dev, steps=10):
+    """kda_backward over the prefill workload (upstream gradients dO ~ N(0,1),
+    dS_T ~ 0.02 N(0,1)); HIP events around each call on the launch stream."""
+    from gated_delta_rule_76_amd import inputs, kda
+    spec = inputs.WORKLOADS[name]
+    lens = inputs.workload_lengths(spec, seed=0)
+    H, D = spec["H"], spec["D"]
+    d = inputs.prefill_inputs(lens, H, D, torch.bfloat16, spec["decay"], spec["s0_std"], seed=0, device=dev)
+    T = sum(lens)
+    dO, dST = inputs.grad_inputs(T, H, D, len(lens), seed=0, device=dev)
+    cu = d["cu_seqlens"] if len(lens) > 1 else None
+    ws = torch.empty(kda.backward_workspace_size(len(lens), T, H, D), dtype=torch.uint8, device=dev)
+    run = lambda: kda.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dO, d["S0"], dST, cu,
+                               workspace=ws)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = T * H * backward_bytes() / (ms * 1e-3) / 1e9
+    return {"metric": "KDA backward tokens/s/layer (%s)" % name, "value": T / (ms * 1e-3),
+            "unit": "tokens/s/layer", "ms_per_step": ms, "workspace_bytes": int(ws.numel()),
+            "roofline": {"bound": "hbm", "kernel": "bwd_kernel + bwd_reduce_kernel", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "bytes_per_token_head": backward_bytes()}}
+
+
 def verify_summary(vf):
     B, K, H = vf["B"], vf["K"], vf["H"]
     gbs = B * H * verify_bytes(K) / (vf["verify_ms"] * 1e-3) / 1e9
@@ -306,6 +345,18 @@ def _cpu_verify_worker(seqs):
         t0 = time.perf_counter()
         speculative.decode_tokens(a["q"][rows], a["k"][rows], a["v"][rows], a["alpha"][rows],
                                   a["beta"][rows], a["S"][seqs], K)
+        return time.perf_counter() - t0
+
+
+def _cpu_backward_worker(heads):
+    from threadpoolctl import threadpool_limits
+
+    from oracle.backward import kda_backward
+    a = _CPU_INPUTS
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kda_backward(a["q"][:, heads], a["k"][:, heads], a["v"][:, heads], a["alpha"][:, heads],
+                     a["beta"][:, heads], a["dO"][:, heads], None, a["dST"][:, heads])
         return time.perf_counter() - t0
 
 
@@ -396,6 +447,22 @@ def oracle_verify_rate(B=256, K=2):
                       f"{busy:.1f} s CPU)"}
 
 
+def oracle_backward_rate():
+    """Oracle tokens/s/layer of the backward pass over the prefill_4k workload."""
+    from gated_delta_rule_76_amd import inputs
+    spec = inputs.WORKLOADS["prefill_4k"]
+    T, H, D = spec["lengths"][0], spec["H"], spec["D"]
+    d = inputs.prefill_inputs([T], H, D, torch.bfloat16, spec["decay"], None, seed=0, device="cpu")
+    dO, dST = inputs.grad_inputs(T, H, D, 1, seed=0, device="cpu")
+    _CPU_INPUTS.update({k: d[k].double().numpy() for k in ("q", "k", "v", "alpha", "beta")})
+    _CPU_INPUTS["dO"], _CPU_INPUTS["dST"] = dO.double().numpy(), dST.double().numpy()
+    wall, busy, cores = _pool_map(_cpu_backward_worker, H)
+    _CPU_INPUTS.clear()
+    return {"value": T / wall, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
+            "sample": f"backward of the whole prefill_4k workload ({T} tokens x {H} heads, d={D}), numpy "
+                      f"fp64, {cores} processes over head groups ({wall:.2f} s wall, {busy:.1f} s CPU)"}
+
+
 def cpu_baseline():
     return oracle_prefill_rate("prefill_4k", passes=3)
 
@@ -421,6 +488,7 @@ def oracle_rates():
     out["decode_b256_scalar_gate"] = oracle_decode_rate(256, 100, gate="head")
     out["prefill_4k_preact"] = oracle_prefill_rate("prefill_4k", passes=3, form="preact")
     out["verify_b256_k2"] = oracle_verify_rate(256, 2)
+    out["backward_prefill_4k"] = oracle_backward_rate()
     return out
 
 
@@ -555,6 +623,8 @@ def main():
         if not args.no_decode:
             print("[bench] speculative verify", file=sys.stderr, flush=True)
             out["verify"] = verify_summary(bench_verify(args.decode_batch, 2, dev))
+        print("[bench] backward", file=sys.stderr, flush=True)
+        out["backward"] = bench_backward(args.workload if args.workload == "prefill_4k" else "prefill_4k", dev)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
