@@ -13,19 +13,27 @@
 //   dL/dS_{t-1} = Diag(alpha_t) E + q_{t-1} dO_{t-1}^T.
 //
 // Value columns never mix in G's recurrence, so the work splits by 16 value
-// columns: one 256-thread workgroup per (sequence, head, column slice),
-// thread (rg, c) holding rows rg*RPT .. +RPT-1 of column c.  Per workgroup:
+// columns: one 256-thread workgroup per (sequence, head, column slice).
+// Lane layout: the 16 lanes of a DPP row hold one column (lane rg of the row
+// keeps rows rg*RPT .. +RPT-1), so a wave holds 4 columns and the workgroup
+// 16.  Tokens go in blocks of CK (16; 8 for fp32 inputs at d = 128).  Per
+// workgroup:
 //   pass 1  the forward recurrence over the sequence from S0, storing the
-//           state at the start of every 16-token block (workspace);
+//           state at the start of every block (workspace);
 //   pass 2  blocks from last to first: re-run the block forward from its
 //           checkpoint, keeping every S_{t-1} in LDS (each thread keeps its
 //           own elements, so no barrier guards the ring), then the tokens
 //           backward with G in registers.
-// Column sums (X^T k, G^T k) cross the 16 row groups: two shuffles in the
-// wave, one LDS round across the 4 waves (double-buffered, one barrier per
-// token).  Row sums over the 16 columns (dk, dq, dalpha) are DPP reductions
-// inside a 16-lane row; they are per-slice partials, summed over the slices
-// in a fixed order by a second kernel (deterministic results).
+// A block's inputs (k, q, alpha, beta and the slice's v, dO) are staged in
+// LDS; the next block's are loaded into registers while the current block
+// computes, so the steps never wait on global memory.
+// The column sums the recurrences need (X^T k, G^T k) stay inside a DPP row:
+// four DPP adds, no barrier, so the forward steps never synchronise the
+// workgroup.  The row sums over the 16 columns (dk, dq, dalpha, and dbeta)
+// are outputs only: a lane-swap reduction over the wave's 4 columns, then
+// one LDS round across the 4 waves (double-buffered, one barrier per
+// backward token); they are per-slice partials, summed over the slices in a
+// fixed order by a second kernel (deterministic results).
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -37,67 +45,65 @@ namespace {
 constexpr int kBwdThreads = 256;
 constexpr int kBwdVW = 16;  // value columns per workgroup
 
-template <int D>
+template <int D, typename TIn, int GATE>
 struct BwdCfg {
-  static constexpr int VW = kBwdVW < D ? kBwdVW : D;
-  static constexpr int SL = D / VW;                // column slices per head
-  static constexpr int TPC = kBwdThreads / VW;     // row groups
-  static constexpr int RPT = D / TPC;              // rows per thread
+  static constexpr int VW = kBwdVW < D ? kBwdVW : D;  // columns per workgroup
+  static constexpr int SL = D / VW;                   // column slices per head
+  static constexpr int RPT = D / 16;                  // rows per thread (16 lanes per column)
   static constexpr int NW = kBwdThreads / 64;
-  static_assert(VW == 16 && RPT >= 1 && D % TPC == 0, "layout");
+  static constexpr int NRED = 3 * D + 2;              // row sums per token: dk, dq, dalpha, dbeta, dalpha/head
+  static constexpr int CK = bwd_block(D, sizeof(TIn) == 4);
+  static constexpr int DA = GATE == KDA_GATE_HEAD ? 1 : D;  // rates per token
+  // 16-byte chunks of one block's rows, and chunks per token row
+  static constexpr int KCT = D * (int)sizeof(TIn) / 16;    // k or q
+  static constexpr int ACT = GATE == KDA_GATE_HEAD ? 0 : D / 4;
+  static constexpr int VCT = VW * (int)sizeof(TIn) / 16;  // v slice
+  static constexpr int OCT = VW / 4;                       // dO slice
+  static constexpr int NK = CK * KCT, NA = CK * ACT, NV = CK * VCT, NO = CK * OCT;
+  static constexpr int PK = (NK + kBwdThreads - 1) / kBwdThreads;  // chunks per thread
+  static constexpr int PA = (NA + kBwdThreads - 1) / kBwdThreads;
+  static_assert(VW == 16 && RPT >= 1 && D % 16 == 0 && NV <= kBwdThreads && NO <= kBwdThreads, "layout");
 };
 
-// Sum over the 16 lanes of a DPP row (lanes 16j .. 16j+15); the total lands
-// in the row's last lane.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));  // row_shr:1
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));  // row_shr:2
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));  // row_shr:4
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));  // row_shr:8
+// Sum over the 16 lanes of a DPP row, every lane receiving the total
+// (xor 1 and xor 2 within quads, then rotations by 4 and 8 within the row).
+__device__ __forceinline__ float row16_allsum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false)); // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)); // row_ror:8
   return x;
 }
 
+// x[lane] + x[lane ^ 16] + x[lane ^ 32] + x[lane ^ 48]: the sum over the four
+// DPP rows of the wave, for every lane (lane-swap instructions, no LDS).
+__device__ __forceinline__ float rows4_allsum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One block's inputs in LDS.
 template <int D, typename TIn, int GATE>
-struct BwdTok {
-  using Cf = BwdCfg<D>;
-  float a[GATE == KDA_GATE_HEAD ? 1 : Cf::RPT];
-  TIn k[Cf::RPT], q[Cf::RPT];
-  TIn v;
-  float b, dO;
+struct BlockIn {
+  using Cf = BwdCfg<D, TIn, GATE>;
+  TIn k[Cf::CK][D];
+  TIn q[Cf::CK][D];
+  float a[Cf::CK][Cf::DA];
+  TIn v[Cf::CK][Cf::VW];
+  float dO[Cf::CK][Cf::VW];
+  float b[Cf::CK];
 };
 
-// The decay rate of row r0 + i (per key channel), or the head's one rate.
+// The next block's inputs in flight, in registers (16-byte chunks; thread
+// tid holds chunks tid, tid + 256, ... of each array).
 template <int D, typename TIn, int GATE>
-__device__ __forceinline__ float rate(const BwdTok<D, TIn, GATE> &x, int i) {
-  if constexpr (GATE == KDA_GATE_HEAD) {
-    return x.a[0];
-  } else {
-    return x.a[i];
-  }
-}
-
-template <int D, typename TIn, int GATE>
-__device__ __forceinline__ void load_tok(BwdTok<D, TIn, GATE> &x, const TIn *__restrict__ q,
-                                         const TIn *__restrict__ k, const TIn *__restrict__ v,
-                                         const float *__restrict__ alpha, const float *__restrict__ beta,
-                                         const float *__restrict__ dO, int64_t th, int r0, int col,
-                                         bool want_q) {
-  using Cf = BwdCfg<D>;
-  if constexpr (GATE == KDA_GATE_HEAD) {
-    x.a[0] = alpha[th];
-  } else {
-#pragma unroll
-    for (int i = 0; i < Cf::RPT; ++i) x.a[i] = alpha[th * D + r0 + i];
-  }
-#pragma unroll
-  for (int i = 0; i < Cf::RPT; ++i) {
-    x.k[i] = k[th * D + r0 + i];
-    x.q[i] = want_q ? q[th * D + r0 + i] : x.k[i];
-  }
-  x.v = v[th * D + col];
-  x.b = beta[th];
-  x.dO = want_q ? dO[th * D + col] : 0.f;
-}
+struct BlockRaw {
+  using Cf = BwdCfg<D, TIn, GATE>;
+  uint4 k[Cf::PK], q[Cf::PK], a[Cf::PA > 0 ? Cf::PA : 1], v, o;
+  float b, ah;
+};
 
 template <int D, typename TIn, int GATE>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
@@ -107,16 +113,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     const float *__restrict__ dO, const float *__restrict__ dS_T, float *__restrict__ dv,
     float *__restrict__ dS0, float *__restrict__ ckpt, float *__restrict__ part_q,
     float *__restrict__ part_k, float *__restrict__ part_a, float *__restrict__ part_b) {
-  using Cf = BwdCfg<D>;
-  constexpr int RPT = Cf::RPT, VW = Cf::VW, SL = Cf::SL, NW = Cf::NW;
-  constexpr int CK = kBwdBlock;
+  using Cf = BwdCfg<D, TIn, GATE>;
+  constexpr int RPT = Cf::RPT, VW = Cf::VW, SL = Cf::SL, NW = Cf::NW, NRED = Cf::NRED, CK = Cf::CK;
 
   __shared__ float s_ring[CK][kBwdThreads][RPT];  // S_{t-1} of the block's tokens, per thread
-  __shared__ float s_red[2][NW][2][VW];   // column sums, double-buffered
-  __shared__ float s_ah[2][NW];           // scalar gate: dalpha over the rows
+  __shared__ float s_red[2][NW][NRED];            // per-wave row sums, double-buffered
+  __shared__ __attribute__((aligned(16))) BlockIn<D, TIn, GATE> s_in;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid % VW, rg = tid / VW;
+  const int c = tid >> 4, rg = tid & 15;  // column of the slice, row group
   const int r0 = rg * RPT;
   const int sl = blockIdx.x % SL;
   const int nh = blockIdx.x / SL;
@@ -138,158 +143,229 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   const int64_t nblk = (len + CK - 1) / CK;
   const int64_t blk0 = start / CK + n;  // first checkpoint slot of this sequence
   const int64_t sbase = (((int64_t)n * H + h) * D) * D;  // [n][h] state offset
-  auto ck_at = [&](int64_t j) { return ckpt + (((blk0 + j) * H + h) * SL + sl) * (int64_t)(D * VW); };
+  // A checkpoint slot holds the slice as [thread][RPT] (each thread reads back
+  // what it wrote).
+  auto ck_at = [&](int64_t j) {
+    return ckpt + (((blk0 + j) * H + h) * SL + sl) * (int64_t)(D * VW) + tid * RPT;
+  };
+  // (token row * H + head) of token t of the block starting at tb; tokens past
+  // the sequence re-read its last token (their values are never used).
+  auto trow = [&](int64_t tb, int t) {
+    int64_t tt = tb + t;
+    tt = tt < len ? tt : len - 1;
+    return (start + tt) * H + h;
+  };
 
-  int par = 0;
-  // Column sums of (x1, x2) over all rows of column c (every thread gets its
-  // column's totals).
-  auto col_sum2 = [&](float &x1, float &x2) __attribute__((always_inline)) {
-    x1 += __shfl_xor(x1, 16);
-    x2 += __shfl_xor(x2, 16);
-    x1 += __shfl_xor(x1, 32);
-    x2 += __shfl_xor(x2, 32);
-    if (lane < VW) {
-      s_red[par][wave][0][c] = x1;
-      s_red[par][wave][1][c] = x2;
-    }
-    __syncthreads();
-    float a1 = 0.f, a2 = 0.f;
+  // ---- block inputs: global -> registers -> LDS -----------------------------------
+  auto fetch = [&](int64_t tb, BlockRaw<D, TIn, GATE> &R) __attribute__((always_inline)) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      a1 += s_red[par][w][0][c];
-      a2 += s_red[par][w][1][c];
+    for (int m = 0; m < Cf::PK; ++m) {
+      const int idx = tid + kBwdThreads * m;
+      if (Cf::NK % kBwdThreads == 0 || idx < Cf::NK) {
+        const int64_t off = trow(tb, idx / Cf::KCT) * D * (int64_t)sizeof(TIn) + (idx % Cf::KCT) * 16;
+        R.k[m] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(k) + off);
+        R.q[m] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(q) + off);
+      }
     }
-    x1 = a1;
-    x2 = a2;
-    par ^= 1;
+    if constexpr (Cf::NA > 0) {
+#pragma unroll
+      for (int m = 0; m < Cf::PA; ++m) {
+        const int idx = tid + kBwdThreads * m;
+        if (Cf::NA % kBwdThreads == 0 || idx < Cf::NA) {
+          const int64_t off = trow(tb, idx / Cf::ACT) * D + (idx % Cf::ACT) * 4;
+          R.a[m] = *reinterpret_cast<const uint4 *>(alpha + off);
+        }
+      }
+    }
+    if (tid < Cf::NV) {
+      const int64_t off = (trow(tb, tid / Cf::VCT) * D + sl * VW) * (int64_t)sizeof(TIn) + (tid % Cf::VCT) * 16;
+      R.v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(v) + off);
+    }
+    if (tid < Cf::NO)
+      R.o = *reinterpret_cast<const uint4 *>(dO + trow(tb, tid / Cf::OCT) * D + sl * VW + (tid % Cf::OCT) * 4);
+    if (tid < CK) {
+      R.b = beta[trow(tb, tid)];
+      if constexpr (GATE == KDA_GATE_HEAD) R.ah = alpha[trow(tb, tid)];
+    }
+  };
+  auto stash = [&](const BlockRaw<D, TIn, GATE> &R) __attribute__((always_inline)) {
+    char *bk = reinterpret_cast<char *>(&s_in.k[0][0]), *bq = reinterpret_cast<char *>(&s_in.q[0][0]);
+#pragma unroll
+    for (int m = 0; m < Cf::PK; ++m) {
+      const int idx = tid + kBwdThreads * m;
+      if (Cf::NK % kBwdThreads == 0 || idx < Cf::NK) {
+        *reinterpret_cast<uint4 *>(bk + 16 * idx) = R.k[m];
+        *reinterpret_cast<uint4 *>(bq + 16 * idx) = R.q[m];
+      }
+    }
+    if constexpr (Cf::NA > 0) {
+#pragma unroll
+      for (int m = 0; m < Cf::PA; ++m) {
+        const int idx = tid + kBwdThreads * m;
+        if (Cf::NA % kBwdThreads == 0 || idx < Cf::NA)
+          *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&s_in.a[0][0]) + 16 * idx) = R.a[m];
+      }
+    }
+    if (tid < Cf::NV) *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&s_in.v[0][0]) + 16 * tid) = R.v;
+    if (tid < Cf::NO) *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&s_in.dO[0][0]) + 16 * tid) = R.o;
+    if (tid < CK) {
+      s_in.b[tid] = R.b;
+      if constexpr (GATE == KDA_GATE_HEAD) s_in.a[tid][0] = R.ah;
+    }
+  };
+
+  // Token j of the staged block: this thread's rows of k (and q, alpha).
+  auto rate = [&](int j, int i) -> float {
+    if constexpr (GATE == KDA_GATE_HEAD) {
+      return s_in.a[j][0];
+    } else {
+      return s_in.a[j][r0 + i];
+    }
   };
 
   // ---- pass 1: forward, checkpoint at every block start -----------------------
   float s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) s[i] = S0 != nullptr ? S0[sbase + (int64_t)(r0 + i) * D + col] : 0.f;
-  auto fwd_step = [&](const BwdTok<D, TIn, GATE> &x) __attribute__((always_inline)) {
+  auto fwd_step = [&](int j) __attribute__((always_inline)) {
     float ak[RPT];
-    float xk = 0.f, dummy = 0.f;
+    float xk = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      s[i] *= rate(x, i);
-      ak[i] = to_f32(x.k[i]);
+      s[i] *= rate(j, i);
+      ak[i] = to_f32(s_in.k[j][r0 + i]);
       xk += s[i] * ak[i];
     }
-    col_sum2(xk, dummy);
-    const float w = x.b * (to_f32(x.v) - xk);
+    xk = row16_allsum(xk);
+    const float w = s_in.b[j] * (to_f32(s_in.v[j][c]) - xk);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] += ak[i] * w;
   };
-  {
-    BwdTok<D, TIn, GATE> cur, nxt;
-    if (len > 0) load_tok<D, TIn, GATE>(cur, q, k, v, alpha, beta, dO, start * H + h, r0, col, false);
-    for (int64_t t = 0; t < len; ++t) {
-      const int64_t tn = t + 1 < len ? t + 1 : t;
-      load_tok<D, TIn, GATE>(nxt, q, k, v, alpha, beta, dO, (start + tn) * H + h, r0, col, false);
-      if (t % CK == 0) {
-        float *cp = ck_at(t / CK);
+
+  BlockRaw<D, TIn, GATE> R;
+  if (nblk > 0) {
+    fetch(0, R);
+    stash(R);
+  }
+  for (int64_t b = 0; b < nblk; ++b) {
+    __syncthreads();  // block b is in LDS
+    // next block needed: b + 1, or (after the last) the one before it for pass 2
+    const int64_t nb = b + 1 < nblk ? b + 1 : (b > 0 ? b - 1 : b);
+    fetch(nb * CK, R);
+    {
+      float *cp = ck_at(b);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) cp[(r0 + i) * VW + c] = s[i];
-      }
-      fwd_step(cur);
-      cur = nxt;
+      for (int i = 0; i < RPT; ++i) cp[i] = s[i];
+    }
+    const int nt = (int)(len - b * CK < CK ? len - b * CK : CK);
+    for (int j = 0; j < nt; ++j) fwd_step(j);
+    if (b + 1 < nblk) {
+      __syncthreads();  // every wave is done with block b
+      stash(R);
     }
   }
   // Each thread reads back only the checkpoint elements it wrote.
   __threadfence_block();
 
   // ---- pass 2: backward ---------------------------------------------------------
+  // LDS holds the last block; R holds the one before it.
   float G[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) G[i] = dS_T != nullptr ? dS_T[sbase + (int64_t)(r0 + i) * D + col] : 0.f;
+  int par = 0;
   for (int64_t b = nblk - 1; b >= 0; --b) {
     const int64_t tb = b * CK;
     const int nt = (int)(len - tb < CK ? len - tb : CK);
+    if (b < nblk - 1) {
+      __syncthreads();  // every wave is done with block b + 1
+      stash(R);
+      __syncthreads();
+      fetch((b > 0 ? b - 1 : 0) * CK, R);
+    }
     {
       const float *cp = ck_at(b);
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) s[i] = cp[(r0 + i) * VW + c];
+      for (int i = 0; i < RPT; ++i) s[i] = cp[i];
     }
-    BwdTok<D, TIn, GATE> cur, nxt;
-    load_tok<D, TIn, GATE>(cur, q, k, v, alpha, beta, dO, (start + tb) * H + h, r0, col, false);
     for (int j = 0; j < nt; ++j) {
-      const int jn = j + 1 < nt ? j + 1 : j;
-      load_tok<D, TIn, GATE>(nxt, q, k, v, alpha, beta, dO, (start + tb + jn) * H + h, r0, col, false);
 #pragma unroll
       for (int i = 0; i < RPT; ++i) s_ring[j][tid][i] = s[i];
-      fwd_step(cur);
-      cur = nxt;
+      fwd_step(j);
     }
-    load_tok<D, TIn, GATE>(cur, q, k, v, alpha, beta, dO, (start + tb + nt - 1) * H + h, r0, col, true);
     for (int j = nt - 1; j >= 0; --j) {
       const int64_t th = (start + tb + j) * H + h;
-      const int jp = j > 0 ? j - 1 : 0;
-      load_tok<D, TIn, GATE>(nxt, q, k, v, alpha, beta, dO, (start + tb + jp) * H + h, r0, col, true);
+      const float dOc = s_in.dO[j][c];
       float sp[RPT], X[RPT], kf[RPT];
       float xk = 0.f, gk = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float a = rate(cur, i);
         sp[i] = s_ring[j][tid][i];
-        kf[i] = to_f32(cur.k[i]);
-        G[i] += to_f32(cur.q[i]) * cur.dO;
-        X[i] = a * sp[i];
+        kf[i] = to_f32(s_in.k[j][r0 + i]);
+        G[i] += to_f32(s_in.q[j][r0 + i]) * dOc;
+        X[i] = rate(j, i) * sp[i];
         xk += X[i] * kf[i];
         gk += G[i] * kf[i];
       }
-      col_sum2(xk, gk);
-      const float bt = cur.b;
-      const float w = to_f32(cur.v) - xk;
+      xk = row16_allsum(xk);
+      gk = row16_allsum(gk);
+      const float bt = s_in.b[j];
+      const float w = to_f32(s_in.v[j][c]) - xk;
       if (rg == 0) dv[th * D + col] = bt * gk;
-      const float db = row16_sum(gk * w);
-      if (tid == VW - 1) part_b[(int64_t)sl * total * H + th] = db;
       float dkp[RPT], dqp[RPT], dap[RPT];
       float da_all = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float a = rate(cur, i);
         const float st = X[i] + bt * kf[i] * w;  // S_t
         dkp[i] = bt * (G[i] * w - X[i] * gk);
-        dqp[i] = st * cur.dO;
+        dqp[i] = st * dOc;
         const float e = G[i] - bt * kf[i] * gk;
         dap[i] = e * sp[i];
         da_all += dap[i];
-        G[i] = a * e;
+        G[i] = rate(j, i) * e;
       }
+      // Row sums over the slice's 16 columns: the wave's 4 columns by lane
+      // swaps, then the 4 waves through LDS.
+      float *red = s_red[par][wave];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        dkp[i] = row16_sum(dkp[i]);
-        dqp[i] = row16_sum(dqp[i]);
-        if constexpr (GATE != KDA_GATE_HEAD) dap[i] = row16_sum(dap[i]);
+        dkp[i] = rows4_allsum(dkp[i]);
+        dqp[i] = rows4_allsum(dqp[i]);
+        if constexpr (GATE != KDA_GATE_HEAD) dap[i] = rows4_allsum(dap[i]);
       }
-      const int64_t po = ((int64_t)sl * total * H + th) * D + r0;
-      if (c == VW - 1) {
+      const float db = rows4_allsum(gk * w);
+      if (lane < 16) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-          part_k[po + i] = dkp[i];
-          part_q[po + i] = dqp[i];
-          if constexpr (GATE != KDA_GATE_HEAD) part_a[po + i] = dap[i];
+          red[r0 + i] = dkp[i];
+          red[D + r0 + i] = dqp[i];
+          if constexpr (GATE != KDA_GATE_HEAD) red[2 * D + r0 + i] = dap[i];
         }
       }
       if constexpr (GATE == KDA_GATE_HEAD) {
-        // one rate per head: dalpha sums over every row and column of the slice
-        float t = row16_sum(da_all);
-        t = __shfl(t, (lane & ~15) + 15);
-        t += __shfl_xor(t, 16);
-        t += __shfl_xor(t, 32);
-        if (lane == 0) s_ah[par][wave] = t;
-        __syncthreads();
-        if (tid == 0) {
-          float u = 0.f;
-#pragma unroll
-          for (int w2 = 0; w2 < NW; ++w2) u += s_ah[par][w2];
-          part_a[(int64_t)sl * total * H + th] = u;
-        }
-        par ^= 1;
+        // one rate per head: dalpha sums over every row and column
+        const float da = rows4_allsum(row16_allsum(da_all));
+        if (lane == 0) red[3 * D + 1] = da;
       }
-      cur = nxt;
+      if (lane == 0) red[3 * D] = db;
+      __syncthreads();
+      const int64_t pb = (int64_t)sl * total * H + th;
+      for (int e = tid; e < NRED; e += kBwdThreads) {
+        float u = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) u += s_red[par][w2][e];
+        if (e < D) {
+          part_k[pb * D + e] = u;
+        } else if (e < 2 * D) {
+          part_q[pb * D + e - D] = u;
+        } else if (e < 3 * D) {
+          if constexpr (GATE != KDA_GATE_HEAD) part_a[pb * D + e - 2 * D] = u;
+        } else if (e == 3 * D) {
+          part_b[pb] = u;
+        } else if constexpr (GATE == KDA_GATE_HEAD) {
+          part_a[pb] = u;
+        }
+      }
+      par ^= 1;
     }
   }
   if (dS0 != nullptr) {
@@ -310,7 +386,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict
 
 template <int D, typename TIn, int GATE>
 hipError_t launch_bwd_t(const kda_shape_t &s, const BwdArgs &a, hipStream_t stream) {
-  using Cf = BwdCfg<D>;
+  using Cf = BwdCfg<D, TIn, GATE>;
   const BwdLayout L = backward_layout(s);
   char *ws = static_cast<char *>(a.workspace);
   float *ckpt = reinterpret_cast<float *>(ws + L.ckpt_off);

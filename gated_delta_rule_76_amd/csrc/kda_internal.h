@@ -60,12 +60,13 @@ hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void 
 hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, const int32_t *accepted,
                          hipStream_t stream);
 
-// Backward pass.  Workspace: state checkpoints every kBwdBlock tokens per
-// (sequence, head) -- at most floor(T / kBwdBlock) + N slots of d_k x d_v
+// Backward pass.  Workspace: state checkpoints every bwd_block tokens per
+// (sequence, head) -- at most floor(T / bwd_block) + N slots of d_k x d_v
 // floats per head -- then per-slice partial sums of dq, dk, dalpha and dbeta
 // over the d_v / 16 column slices ([slices][T][H][d], dalpha [slices][T][H]
-// for one rate per head, dbeta [slices][T][H]).
-constexpr int kBwdBlock = 16;
+// for one rate per head, dbeta [slices][T][H]).  The block is 16 tokens,
+// 8 for fp32 inputs at d = 128 (their per-block inputs need more LDS).
+constexpr int bwd_block(int d, bool f32_inputs) { return (f32_inputs && d >= 128) ? 8 : 16; }
 
 struct BwdLayout {
   size_t ckpt_off, part_q_off, part_k_off, part_a_off, part_b_off, bytes;
@@ -74,7 +75,8 @@ struct BwdLayout {
 inline BwdLayout backward_layout(const kda_shape_t &s) {
   const size_t d = (size_t)s.d_k, H = (size_t)s.num_heads, T = (size_t)s.total_tokens;
   const size_t slices = d < 16 ? 1 : d / 16;
-  const size_t slots = (size_t)(s.total_tokens / kBwdBlock) + (size_t)s.num_seqs;
+  const int blk = bwd_block(s.d_k, s.qkv_dtype == KDA_F32);
+  const size_t slots = (size_t)(s.total_tokens / blk) + (size_t)s.num_seqs;
   const size_t da = s.gate == KDA_GATE_HEAD ? 1 : d;
   BwdLayout L;
   L.ckpt_off = 0;
