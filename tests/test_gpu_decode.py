@@ -85,3 +85,22 @@ def test_decode_workload_b256_100_steps():
         worst = max(worst, rel_l2(got_o[s], ro))
     assert worst < 2e-3 and worst < 1e-5, worst
     assert rel_l2(np64(S[bi, hi]), S_ref) < 1e-5
+
+
+def test_decode_large_batch_streams_state():
+    """B=1024 x 32 heads (2 GiB of state: the kernel reads it with
+    non-temporal loads): three steps, every output and final state of a
+    seeded sample of 128 (sequence, head) pairs against the oracle."""
+    dev = device()
+    B, H, D, steps = 1024, 32, 128, 3
+    d = inputs.decode_inputs(B, H, D, steps, torch.bfloat16, "strong", 0.02, seed=3, device=dev)
+    S = d["S"].clone()
+    pick = seeded_sample(B * H, 128, seed=9)
+    n_idx, h_idx = pick // H, pick % H
+    S_ref = np64(d["S"][n_idx, h_idx])[:, None]
+    for s in range(steps):
+        o = kda.decode_step(d["q"][s], d["k"][s], d["v"][s], d["alpha"][s], d["beta"][s], S)
+        sel = lambda t: np64(t[s][n_idx, h_idx])[:, None]
+        ro, S_ref = kda_decode_step(sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(d["alpha"]), sel(d["beta"]), S_ref)
+        assert rel_l2(np64(o[n_idx, h_idx]), ro[:, 0]) < 1e-5, s
+    assert rel_l2(np64(S[n_idx, h_idx]), S_ref[:, 0]) < 1e-5
