@@ -995,13 +995,12 @@ __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec,
   using Cf = ScanCfg<D>;
   using Rc = Rec<D>;
   using IO = FragIO<P>;
-  // Both roles issue the same loads (V is used by the U waves, M T by the
-  // O waves; the partner wave of the same row tile reads the same M T lines):
-  // no branch separates the loads, so none of them has to be waited for early.
+  // V is loaded by the U waves only, M T by the O waves only (wave-uniform
+  // branches; the loads still issue before anything waits on them).
   const int rt = wave & 3, g = lane >> 4, m = lane & 15;
   // V through a buffer descriptor spanning the chunk's valid rows: padding
   // rows read 0.  (Offsets are 32-bit: the host requires 64 H d 4 < 2^31.)
-  {
+  if (wave < 4) {
     const uint64_t addr = reinterpret_cast<uint64_t>(v + (vt0 * H + h) * D + col0);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
@@ -1017,10 +1016,12 @@ __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec,
         B.v[i] = __builtin_bit_cast(TIn, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
     }
   }
+  if (wave >= 4) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int f = Rc::mt_frag(rt, rt < 2 ? 0 : kb);  // row tiles 0, 1: the k-block 0 block twice
-    IO::load(B.mt[kb], rec + (size_t)(Rc::MTM + f) * kFragBytes, lane);
+    for (int kb = 0; kb < 2; ++kb) {
+      const int f = Rc::mt_frag(rt, rt < 2 ? 0 : kb);  // row tiles 0, 1: the k-block 0 block twice
+      IO::load(B.mt[kb], rec + (size_t)(Rc::MTM + f) * kFragBytes, lane);
+    }
   }
   const int t = wave < Cf::NTILE ? wave : Cf::NTILE - 1;
 #pragma unroll
