@@ -259,6 +259,13 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
   if (tid == 0) base[N] = carry;
 }
 
+// A dense batch (no cu_seqlens) needs no table: every sequence has
+// ceil(seq_len / 64) chunks, so base[n] = n * that.  The kernels compute it
+// and the schedule kernel is not launched.
+__device__ __forceinline__ int64_t dense_chunks(int32_t seq_len) {
+  return seq_len > 0 ? ((int64_t)seq_len + C - 1) / C : 0;
+}
+
 // Largest n in [0, N) with base[n] <= c (base is non-decreasing, base[0] = 0).
 __device__ __forceinline__ int find_seq(const int32_t *base, int N, int64_t c) {
   int lo = 0, hi = N - 1;
@@ -531,12 +538,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
   float *s_Yw = s_M + C * LP + 256 * wave;
   const int64_t c = (int64_t)(blockIdx.x / H);
   const int h = blockIdx.x % H;
-  const int64_t nchunks = base[N] < max_chunks ? (int64_t)base[N] : max_chunks;
-  if (c >= nchunks || total_tokens <= 0) return;
-  const int n = find_seq(base, N, c);
+  int64_t nchunks, cfirst;  // chunks of the batch; first chunk of this sequence
+  int n;
+  if (cu == nullptr) {
+    const int64_t cps = dense_chunks(seq_len);
+    nchunks = (int64_t)N * cps < max_chunks ? (int64_t)N * cps : max_chunks;
+    if (c >= nchunks || total_tokens <= 0) return;
+    n = (int)(c / cps);
+    cfirst = n * cps;
+  } else {
+    nchunks = base[N] < max_chunks ? (int64_t)base[N] : max_chunks;
+    if (c >= nchunks || total_tokens <= 0) return;
+    n = find_seq(base, N, c);
+    cfirst = base[n];
+  }
   int64_t sstart, slen;
   seq_range(cu, seq_len, n, sstart, slen);
-  const ChunkTok ct = chunk_tokens(sstart, slen, c - base[n], total_tokens);
+  const ChunkTok ct = chunk_tokens(sstart, slen, c - cfirst, total_tokens);
   const int64_t t0 = ct.t0;
   const int nvalid = ct.valid;
   char *rec = recs + ((size_t)h * max_chunks + c) * Rc::BYTES;
@@ -1074,8 +1092,9 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 
   int64_t sstart, slen;
   seq_range(cu, seq_len, n, sstart, slen);
-  const int64_t cbeg = base[n];
-  int64_t cend = base[n + 1];
+  const int64_t cps = dense_chunks(seq_len);
+  const int64_t cbeg = cu == nullptr ? n * cps : (int64_t)base[n];
+  int64_t cend = cu == nullptr ? (n + 1) * cps : (int64_t)base[n + 1];
   if (cend > max_chunks) cend = max_chunks;
   if (total_tokens <= 0) cend = cbeg;
 
@@ -1232,9 +1251,11 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
             *vp = static_cast<const TIn *>(v);
   hipError_t e = hipSuccess;
   if (phases & kPhaseLocal) {
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, cu, N, s.seq_len, base);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (cu != nullptr) {  // dense batches compute their chunk table in the kernels
+      hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, cu, N, s.seq_len, base);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     if (mc > 0) {
       hipLaunchKernelGGL((chunk_local_kernel<D, TIn, P, GATE, FORM>), dim3((unsigned)(mc * H)), dim3(NT), 0, stream,
                          qp, kp, alpha, beta, cu, s.seq_len, N, H, s.total_tokens, mc, base, recs);
