@@ -60,6 +60,7 @@ constexpr float kTinyBlock = 7.888609052210118e-31f;  // 2^-100
 // Word 3 of a raw (stride 0) buffer descriptor: 32-bit data format; with it
 // an access at an offset past num_records is dropped (stores) or reads 0.
 constexpr int kBufferWord3 = 0x00020000;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Pre-activation inputs (KDA_INPUT_PREACT): decay rate exp(-softplus(a)),
 // written as 1 / (1 + e^a) (the same value; 0 for a -> +inf, 1 for
@@ -1035,16 +1036,20 @@ __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec,
     }
   }
   if (wave >= 4) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int f = Rc::mt_frag(rt, rt < 2 ? 0 : kb);  // row tiles 0, 1: the k-block 0 block twice
-      IO::load(B.mt[kb], rec + (size_t)(Rc::MTM + f) * kFragBytes, lane);
-    }
+    // (row tiles 0 and 1 use only their k-block 0 block)
+    IO::load(B.mt[0], rec + (size_t)(Rc::MTM + Rc::mt_frag(rt, 0)) * kFragBytes, lane);
+    if (rt >= 2) IO::load(B.mt[1], rec + (size_t)(Rc::MTM + Rc::mt_frag(rt, 1)) * kFragBytes, lane);
   }
   const int t = wave < Cf::NTILE ? wave : Cf::NTILE - 1;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) IO::load(B.p[kb], rec + (size_t)(Rc::PMAT + 2 * t + kb) * kFragBytes, lane);
-  B.gam = *reinterpret_cast<const float4 *>(rec + Rc::GAM + sizeof(float) * (16 * t + 4 * g));
+  {
+    // rows 16 t .. 16 t + 15 at a wave-uniform address (scalar loads); each
+    // lane keeps the four of its row group
+    const float4 *gp = reinterpret_cast<const float4 *>(rec + Rc::GAM + sizeof(float) * 16 * t);
+    const float4 g0 = gp[0], g1 = gp[1], g2 = gp[2], g3 = gp[3];
+    B.gam = g == 0 ? g0 : g == 1 ? g1 : g == 2 ? g2 : g3;
+  }
 }
 
 // Two waves per SIMD: the two register sets of record fragments take about
@@ -1064,6 +1069,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 
   __shared__ Plane<P, VW, DK> Sop;     // S^T in operand form (rows = value columns)
   __shared__ Plane<P, VW, C> Uop;      // U^T in operand form
+  __shared__ float s_ot[4][16][20];    // o tile of each O wave, row-major (16-byte rows)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1119,11 +1125,11 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   };
 
   // o of a chunk is stored during the next chunk's first phase by the O
-  // waves, through a buffer descriptor spanning exactly the chunk's valid
-  // rows: the hardware drops the stores of padding rows (and all stores of
-  // the U waves, whose descriptor is empty), so no branch guards them and
-  // both roles issue the same memory instructions.  (Offsets are 32-bit:
-  // the host requires 64 H d 4 < 2^31.)
+  // waves: the wave's 16 x 16 tile goes through LDS so that each lane stores
+  // four consecutive columns of one row, through a buffer descriptor
+  // spanning exactly the chunk's valid rows (the hardware drops the stores
+  // of padding rows).  (Offsets are 32-bit: the host requires
+  // 64 H d 4 < 2^31.)
   f32x4 opend = zero4();
   int64_t pend_t0 = 0;
   int pend_valid = 0;
@@ -1136,14 +1142,16 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     const int nbytes = __builtin_amdgcn_readfirstlane(pend_valid * H * D * (int)sizeof(float));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<float *>(((uint64_t)hi << 32) | lo), 0, nbytes, kBufferWord3);
+    float(*ot)[20] = s_ot[rt];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * g + i;
-      // (__float_as_uint, not __builtin_bit_cast: the latter applied to an
-      // element of a vector type reads element 0 with this compiler)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(opend[i]), rs,
-                                            (r * H * D + m) * (int)sizeof(float), 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) ot[4 * g + i][m] = opend[i];
+    // (one wave writes and reads its own tile: LDS executes a wave's
+    // accesses in order)
+    __builtin_amdgcn_wave_barrier();
+    const int r = lane >> 2, cq = lane & 3;
+    const float4 x = *reinterpret_cast<const float4 *>(&ot[r][4 * cq]);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs,
+                                           ((16 * rt + r) * H * D + 4 * cq) * (int)sizeof(float), 0, 0);
   };
 
   // The loads of the next record are spread over this chunk's two phases,
@@ -1167,7 +1175,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
       __builtin_amdgcn_sched_barrier(0);
     }
     Nx.tch = touch(cn + 1 < cend ? cn + 1 : cn);
-    store_o();  // the previous chunk's o (O waves), while the U waves form U
+    if (!uwave) store_o();  // the previous chunk's o, while the U waves form U
     f32x4 ov;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = acc0[i] + acc1[i];
@@ -1227,7 +1235,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     process(c + 1, bufB, bufA, c + 2 < cend ? c + 2 : c + 1);
   }
   if (c < cend) process(c, bufA, bufB, c);
-  store_o();
+  if (!uwave) store_o();
   if (N < 0) o[sink & 1] = 0.f;  // never taken (N >= 0): keeps the touches alive
 
   if (S_T != nullptr && wave < NTILE) {
