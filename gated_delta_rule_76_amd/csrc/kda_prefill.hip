@@ -983,7 +983,8 @@ struct ScanCfg {
 template <int D, typename TIn>
 struct ScanBuf {
   using Cf = ScanCfg<D>;
-  TIn v[4];                 // U waves: V rows 16 rt + 4 g + i, column m
+  // U waves: V row 16 rt + lane / 4, columns 4 (lane & 3) .. + 3 (one load)
+  uint32_t v[2 * sizeof(TIn) / 2];
   FragRaw mt[2];            // O waves: M T, row tile rt
   FragRaw a[Cf::NKB];       // Khat (U waves) or Qhat (O waves), row tile rt
   FragRaw p[2];             // Ktil^T T, state tile = wave
@@ -1007,34 +1008,42 @@ __device__ __forceinline__ void load_scan_a(ScanBuf<D, TIn> &B, int kk, const ch
   FragIO<P>::load(B.a[kk], rec + (size_t)(abase + Cf::NKB * rt + kb) * kFragBytes, lane);
 }
 
-template <int D, typename TIn, typename P>
-__device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec, const TIn *v,
-                                            int64_t vt0, int valid, int64_t total, int h, int H,
+// V of a chunk (U waves), issued with the first row-tile load of the
+// previous chunk so that it has arrived before the chunk starts: one load
+// per lane, through a buffer descriptor spanning the chunk's valid rows
+// (padding rows read 0).  (Offsets are 32-bit: the host requires
+// 64 H d 4 < 2^31.)
+template <int D, typename TIn>
+__device__ __forceinline__ void load_scan_v(ScanBuf<D, TIn> &B, const TIn *v, int64_t vt0, int valid, int h, int H,
                                             int col0, int wave, int lane) {
+  const int rt = wave & 3;
+  const uint64_t addr = reinterpret_cast<uint64_t>(v + (vt0 * H + h) * D + col0);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  const int nbytes = __builtin_amdgcn_readfirstlane(valid * H * D * (int)sizeof(TIn));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, nbytes, kBufferWord3);
+  const int off = ((16 * rt + (lane >> 2)) * H * D + 4 * (lane & 3)) * (int)sizeof(TIn);
+  if constexpr (sizeof(TIn) == 2) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    B.v[0] = x[0];
+    B.v[1] = x[1];
+  } else {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    B.v[0] = x[0];
+    B.v[1] = x[1];
+    B.v[2] = x[2];
+    B.v[3] = x[3];
+  }
+}
+
+template <int D, typename TIn, typename P>
+__device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec, int wave, int lane) {
   using Cf = ScanCfg<D>;
   using Rc = Rec<D>;
   using IO = FragIO<P>;
-  // V is loaded by the U waves only, M T by the O waves only (wave-uniform
-  // branches; the loads still issue before anything waits on them).
-  const int rt = wave & 3, g = lane >> 4, m = lane & 15;
-  // V through a buffer descriptor spanning the chunk's valid rows: padding
-  // rows read 0.  (Offsets are 32-bit: the host requires 64 H d 4 < 2^31.)
-  if (wave < 4) {
-    const uint64_t addr = reinterpret_cast<uint64_t>(v + (vt0 * H + h) * D + col0);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
-    const int nbytes = __builtin_amdgcn_readfirstlane(valid * H * D * (int)sizeof(TIn));
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, nbytes, kBufferWord3);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int off = ((16 * rt + 4 * g + i) * H * D + m) * (int)sizeof(TIn);
-      if constexpr (sizeof(TIn) == 2)
-        B.v[i] = __builtin_bit_cast(TIn, __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
-      else
-        B.v[i] = __builtin_bit_cast(TIn, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-    }
-  }
+  // M T is loaded by the O waves only (a wave-uniform branch).
+  const int rt = wave & 3, g = lane >> 4;
   if (wave >= 4) {
     // (row tiles 0 and 1 use only their k-block 0 block)
     IO::load(B.mt[0], rec + (size_t)(Rc::MTM + Rc::mt_frag(rt, 0)) * kFragBytes, lane);
@@ -1069,7 +1078,8 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 
   __shared__ Plane<P, VW, DK> Sop;     // S^T in operand form (rows = value columns)
   __shared__ Plane<P, VW, C> Uop;      // U^T in operand form
-  __shared__ float s_ot[4][16][20];    // o tile of each O wave, row-major (16-byte rows)
+  __shared__ __attribute__((aligned(16))) float s_ot[4][16][20];  // o tile of each O wave, row-major
+  __shared__ __attribute__((aligned(16))) TIn s_vt[4][16][16];  // V tile of each U wave, row-major
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1120,8 +1130,13 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 
   Buf bufA, bufB;
   auto prefetch_b = [&](int64_t cc, Buf &B) __attribute__((always_inline)) {
-    const ChunkTok cn = chunk_tokens(sstart, slen, cc - cbeg, total_tokens);
-    load_scan_b<D, TIn, P>(B, rec_of(cc), v, cn.t0, cn.valid, total_tokens, h, H, col0, wave, lane);
+    load_scan_b<D, TIn, P>(B, rec_of(cc), wave, lane);
+  };
+  auto prefetch_v = [&](int64_t cc, Buf &B) __attribute__((always_inline)) {
+    if (uwave) {
+      const ChunkTok cn = chunk_tokens(sstart, slen, cc - cbeg, total_tokens);
+      load_scan_v<D, TIn>(B, v, cn.t0, cn.valid, h, H, col0, wave, lane);
+    }
   };
 
   // o of a chunk is stored during the next chunk's first phase by the O
@@ -1166,12 +1181,28 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     typename P::Frag Bs[NKB];
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) Bs[kk] = Sop.load8(m, ((kk + cg) % NKB) * 32 + 8 * g);
+    // This chunk's V (U waves) to the accumulator layout through LDS: rows
+    // 16 rt + 4 g + i, column m.
+    float vf[4] = {0.f, 0.f, 0.f, 0.f};
+    if (uwave) {
+      if constexpr (sizeof(TIn) == 2) {
+        *reinterpret_cast<uint2 *>(&s_vt[rt][lane >> 2][4 * (lane & 3)]) = make_uint2(U.v[0], U.v[1]);
+      } else {
+        *reinterpret_cast<uint4 *>(&s_vt[rt][lane >> 2][4 * (lane & 3)]) = make_uint4(U.v[0], U.v[1], U.v[2], U.v[3]);
+      }
+      // (one wave writes and reads its own tile: LDS executes a wave's
+      // accesses in order)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vf[i] = to_f32(s_vt[rt][4 * g + i][m]);
+    }
     f32x4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {  // register slot kk holds k-block (kk + cg) mod NKB
       P::mma((kk & 1) ? acc1 : acc0, IO::frag(U.a[kk]), Bs[kk]);
       __builtin_amdgcn_sched_barrier(0);
       load_scan_a<D, TIn, P>(Nx, kk, rn, wave, lane, cg);
+      if (kk == 0) prefetch_v(cn, Nx);
       __builtin_amdgcn_sched_barrier(0);
     }
     Nx.tch = touch(cn + 1 < cend ? cn + 1 : cn);
@@ -1184,7 +1215,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
-        u[i] = (r < ct.valid ? to_f32(U.v[i]) : 0.f) - ov[i];
+        u[i] = (r < ct.valid ? vf[i] : 0.f) - ov[i];
       }
       Uop.store4(m, 16 * rt + 4 * g, u);
     }
@@ -1223,6 +1254,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   if (cbeg < cend) {
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) load_scan_a<D, TIn, P>(bufA, kk, rec_of(cbeg), wave, lane, cg);
+    prefetch_v(cbeg, bufA);
     prefetch_b(cbeg, bufA);
     bufA.tch = touch(cbeg);
   }
