@@ -43,6 +43,8 @@ namespace kda {
 namespace {
 
 constexpr int kBwdThreads = 256;
+// (a native vector type: the in-flight block stays in registers)
+typedef uint32_t bu32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBwdVW = 16;  // value columns per workgroup
 
 template <int D, typename TIn, int GATE>
@@ -101,7 +103,7 @@ struct BlockIn {
 template <int D, typename TIn, int GATE>
 struct BlockRaw {
   using Cf = BwdCfg<D, TIn, GATE>;
-  uint4 k[Cf::PK], q[Cf::PK], a[Cf::PA > 0 ? Cf::PA : 1], v, o;
+  bu32x4 k[Cf::PK], q[Cf::PK], a[Cf::PA > 0 ? Cf::PA : 1], v, o;
   float b, ah;
 };
 
@@ -163,8 +165,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
       const int idx = tid + kBwdThreads * m;
       if (Cf::NK % kBwdThreads == 0 || idx < Cf::NK) {
         const int64_t off = trow(tb, idx / Cf::KCT) * D * (int64_t)sizeof(TIn) + (idx % Cf::KCT) * 16;
-        R.k[m] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(k) + off);
-        R.q[m] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(q) + off);
+        R.k[m] = *reinterpret_cast<const bu32x4 *>(reinterpret_cast<const char *>(k) + off);
+        R.q[m] = *reinterpret_cast<const bu32x4 *>(reinterpret_cast<const char *>(q) + off);
       }
     }
     if constexpr (Cf::NA > 0) {
@@ -173,16 +175,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
         const int idx = tid + kBwdThreads * m;
         if (Cf::NA % kBwdThreads == 0 || idx < Cf::NA) {
           const int64_t off = trow(tb, idx / Cf::ACT) * D + (idx % Cf::ACT) * 4;
-          R.a[m] = *reinterpret_cast<const uint4 *>(alpha + off);
+          R.a[m] = *reinterpret_cast<const bu32x4 *>(alpha + off);
         }
       }
     }
     if (tid < Cf::NV) {
       const int64_t off = (trow(tb, tid / Cf::VCT) * D + sl * VW) * (int64_t)sizeof(TIn) + (tid % Cf::VCT) * 16;
-      R.v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(v) + off);
+      R.v = *reinterpret_cast<const bu32x4 *>(reinterpret_cast<const char *>(v) + off);
     }
     if (tid < Cf::NO)
-      R.o = *reinterpret_cast<const uint4 *>(dO + trow(tb, tid / Cf::OCT) * D + sl * VW + (tid % Cf::OCT) * 4);
+      R.o = *reinterpret_cast<const bu32x4 *>(dO + trow(tb, tid / Cf::OCT) * D + sl * VW + (tid % Cf::OCT) * 4);
     if (tid < CK) {
       R.b = beta[trow(tb, tid)];
       if constexpr (GATE == KDA_GATE_HEAD) R.ah = alpha[trow(tb, tid)];
@@ -194,8 +196,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     for (int m = 0; m < Cf::PK; ++m) {
       const int idx = tid + kBwdThreads * m;
       if (Cf::NK % kBwdThreads == 0 || idx < Cf::NK) {
-        *reinterpret_cast<uint4 *>(bk + 16 * idx) = R.k[m];
-        *reinterpret_cast<uint4 *>(bq + 16 * idx) = R.q[m];
+        *reinterpret_cast<bu32x4 *>(bk + 16 * idx) = R.k[m];
+        *reinterpret_cast<bu32x4 *>(bq + 16 * idx) = R.q[m];
       }
     }
     if constexpr (Cf::NA > 0) {
@@ -203,11 +205,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
       for (int m = 0; m < Cf::PA; ++m) {
         const int idx = tid + kBwdThreads * m;
         if (Cf::NA % kBwdThreads == 0 || idx < Cf::NA)
-          *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&s_in.a[0][0]) + 16 * idx) = R.a[m];
+          *reinterpret_cast<bu32x4 *>(reinterpret_cast<char *>(&s_in.a[0][0]) + 16 * idx) = R.a[m];
       }
     }
-    if (tid < Cf::NV) *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&s_in.v[0][0]) + 16 * tid) = R.v;
-    if (tid < Cf::NO) *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(&s_in.dO[0][0]) + 16 * tid) = R.o;
+    if (tid < Cf::NV) *reinterpret_cast<bu32x4 *>(reinterpret_cast<char *>(&s_in.v[0][0]) + 16 * tid) = R.v;
+    if (tid < Cf::NO) *reinterpret_cast<bu32x4 *>(reinterpret_cast<char *>(&s_in.dO[0][0]) + 16 * tid) = R.o;
     if (tid < CK) {
       s_in.b[tid] = R.b;
       if constexpr (GATE == KDA_GATE_HEAD) s_in.a[tid][0] = R.ah;
