@@ -13,11 +13,13 @@
 //   dL/dS_{t-1} = Diag(alpha_t) E + q_{t-1} dO_{t-1}^T.
 //
 // Value columns never mix in G's recurrence, so the work splits by 16 value
-// columns: one 256-thread workgroup per (sequence, head, column slice).
-// Lane layout: the 16 lanes of a DPP row hold one column (lane rg of the row
-// keeps rows rg*RPT .. +RPT-1), so a wave holds 4 columns and the workgroup
-// 16.  Tokens go in blocks of CK (16; 8 for fp32 inputs at d = 128).  Per
-// workgroup:
+// columns: one workgroup per (sequence, head, column slice).  Lane layout:
+// LPC lanes hold one column (64 at d >= 64, i.e. one wave per column; 32 at
+// d = 32; one 16-lane DPP row at d = 16), lane rg of a column keeping rows
+// rg*RPT .. +RPT-1, so the workgroup has 16 LPC threads (1024 at d >= 64:
+// four waves per SIMD, which hide each other's latencies).  Tokens go in
+// blocks of CK (16; at d = 128, 12 for bf16 and 8 for fp32 inputs, so that a
+// block's states and inputs fit in LDS).  Per workgroup:
 //   pass 1  the forward recurrence over the sequence from S0, storing the
 //           state at the start of every block (workspace);
 //   pass 2  blocks from last to first: re-run the block forward from its
@@ -27,13 +29,14 @@
 // A block's inputs (k, q, alpha, beta and the slice's v, dO) are staged in
 // LDS; the next block's are loaded into registers while the current block
 // computes, so the steps never wait on global memory.
-// The column sums the recurrences need (X^T k, G^T k) stay inside a DPP row:
-// four DPP adds, no barrier, so the forward steps never synchronise the
-// workgroup.  The row sums over the 16 columns (dk, dq, dalpha, and dbeta)
-// are outputs only: a lane-swap reduction over the wave's 4 columns, then
-// one LDS round across the 4 waves (double-buffered, one barrier per
-// backward token); they are per-slice partials, summed over the slices in a
-// fixed order by a second kernel (deterministic results).
+// The column sums the recurrences need (X^T k, G^T k) stay inside the wave:
+// DPP adds within rows and lane swaps between them, no barrier, so the
+// forward steps never synchronise the workgroup.  The row sums over the 16
+// columns (dk, dq, dalpha, and dbeta) are outputs only: lane swaps over the
+// wave's columns (when it holds more than one), then one LDS round across
+// the waves (double-buffered, one barrier per backward token); they are
+// per-slice partials, summed over the slices in a fixed order by a second
+// kernel (deterministic results).
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
@@ -42,7 +45,6 @@
 namespace kda {
 namespace {
 
-constexpr int kBwdThreads = 256;
 // (a native vector type: the in-flight block stays in registers)
 typedef uint32_t bu32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBwdVW = 16;  // value columns per workgroup
@@ -51,8 +53,10 @@ template <int D, typename TIn, int GATE>
 struct BwdCfg {
   static constexpr int VW = kBwdVW < D ? kBwdVW : D;  // columns per workgroup
   static constexpr int SL = D / VW;                   // column slices per head
-  static constexpr int RPT = D / 16;                  // rows per thread (16 lanes per column)
-  static constexpr int NW = kBwdThreads / 64;
+  static constexpr int LPC = D >= 64 ? 64 : D >= 32 ? 32 : 16;  // lanes per column
+  static constexpr int NT = VW * LPC;                 // threads per workgroup
+  static constexpr int RPT = D / LPC;                 // rows per thread
+  static constexpr int NW = NT / 64;
   static constexpr int NRED = 3 * D + 2;              // row sums per token: dk, dq, dalpha, dbeta, dalpha/head
   static constexpr int CK = bwd_block(D, sizeof(TIn) == 4);
   static constexpr int DA = GATE == KDA_GATE_HEAD ? 1 : D;  // rates per token
@@ -62,9 +66,9 @@ struct BwdCfg {
   static constexpr int VCT = VW * (int)sizeof(TIn) / 16;  // v slice
   static constexpr int OCT = VW / 4;                       // dO slice
   static constexpr int NK = CK * KCT, NA = CK * ACT, NV = CK * VCT, NO = CK * OCT;
-  static constexpr int PK = (NK + kBwdThreads - 1) / kBwdThreads;  // chunks per thread
-  static constexpr int PA = (NA + kBwdThreads - 1) / kBwdThreads;
-  static_assert(VW == 16 && RPT >= 1 && D % 16 == 0 && NV <= kBwdThreads && NO <= kBwdThreads, "layout");
+  static constexpr int PK = (NK + NT - 1) / NT;  // chunks per thread
+  static constexpr int PA = (NA + NT - 1) / NT;
+  static_assert(VW == 16 && RPT >= 1 && D % LPC == 0 && NV <= NT && NO <= NT, "layout");
 };
 
 // Sum over the 16 lanes of a DPP row, every lane receiving the total
@@ -77,13 +81,31 @@ __device__ __forceinline__ float row16_allsum(float x) {
   return x;
 }
 
-// x[lane] + x[lane ^ 16] + x[lane ^ 32] + x[lane ^ 48]: the sum over the four
-// DPP rows of the wave, for every lane (lane-swap instructions, no LDS).
-__device__ __forceinline__ float rows4_allsum(float x) {
+// x[lane] + x[lane ^ 16] and x[lane] + x[lane ^ 32], for every lane
+// (lane-swap instructions, no LDS).
+__device__ __forceinline__ float xor16_sum(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the LPC lanes of one column (16: one DPP row; 32: two), and over
+// the wave's columns (the other lanes), every lane receiving the total.
+template <int LPC>
+__device__ __forceinline__ float column_sum(float x) {
+  x = row16_allsum(x);
+  if constexpr (LPC >= 32) x = xor16_sum(x);
+  if constexpr (LPC == 64) x = xor32_sum(x);
+  return x;
+}
+template <int LPC>
+__device__ __forceinline__ float across_columns(float x) {
+  if constexpr (LPC == 16) x = xor16_sum(x);
+  if constexpr (LPC <= 32) x = xor32_sum(x);
+  return x;
 }
 
 // One block's inputs in LDS.
@@ -108,7 +130,7 @@ struct BlockRaw {
 };
 
 template <int D, typename TIn, int GATE>
-__global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
+__global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     int32_t seq_len, int N, int H, int64_t total, const float *__restrict__ S0,
@@ -117,13 +139,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     float *__restrict__ part_k, float *__restrict__ part_a, float *__restrict__ part_b) {
   using Cf = BwdCfg<D, TIn, GATE>;
   constexpr int RPT = Cf::RPT, VW = Cf::VW, SL = Cf::SL, NW = Cf::NW, NRED = Cf::NRED, CK = Cf::CK;
+  constexpr int NT = Cf::NT, LPC = Cf::LPC;
 
-  __shared__ float s_ring[CK][kBwdThreads][RPT];  // S_{t-1} of the block's tokens, per thread
+  __shared__ float s_ring[CK][NT][RPT];  // S_{t-1} of the block's tokens, per thread
   __shared__ float s_red[2][NW][NRED];            // per-wave row sums, double-buffered
   __shared__ __attribute__((aligned(16))) BlockIn<D, TIn, GATE> s_in;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid >> 4, rg = tid & 15;  // column of the slice, row group
+  const int c = tid / LPC, rg = tid % LPC;  // column of the slice, row group
   const int r0 = rg * RPT;
   const int sl = blockIdx.x % SL;
   const int nh = blockIdx.x / SL;
@@ -162,8 +185,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   auto fetch = [&](int64_t tb, BlockRaw<D, TIn, GATE> &R) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < Cf::PK; ++m) {
-      const int idx = tid + kBwdThreads * m;
-      if (Cf::NK % kBwdThreads == 0 || idx < Cf::NK) {
+      const int idx = tid + NT * m;
+      if (Cf::NK % NT == 0 || idx < Cf::NK) {
         const int64_t off = trow(tb, idx / Cf::KCT) * D * (int64_t)sizeof(TIn) + (idx % Cf::KCT) * 16;
         R.k[m] = *reinterpret_cast<const bu32x4 *>(reinterpret_cast<const char *>(k) + off);
         R.q[m] = *reinterpret_cast<const bu32x4 *>(reinterpret_cast<const char *>(q) + off);
@@ -172,8 +195,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     if constexpr (Cf::NA > 0) {
 #pragma unroll
       for (int m = 0; m < Cf::PA; ++m) {
-        const int idx = tid + kBwdThreads * m;
-        if (Cf::NA % kBwdThreads == 0 || idx < Cf::NA) {
+        const int idx = tid + NT * m;
+        if (Cf::NA % NT == 0 || idx < Cf::NA) {
           const int64_t off = trow(tb, idx / Cf::ACT) * D + (idx % Cf::ACT) * 4;
           R.a[m] = *reinterpret_cast<const bu32x4 *>(alpha + off);
         }
@@ -194,8 +217,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     char *bk = reinterpret_cast<char *>(&s_in.k[0][0]), *bq = reinterpret_cast<char *>(&s_in.q[0][0]);
 #pragma unroll
     for (int m = 0; m < Cf::PK; ++m) {
-      const int idx = tid + kBwdThreads * m;
-      if (Cf::NK % kBwdThreads == 0 || idx < Cf::NK) {
+      const int idx = tid + NT * m;
+      if (Cf::NK % NT == 0 || idx < Cf::NK) {
         *reinterpret_cast<bu32x4 *>(bk + 16 * idx) = R.k[m];
         *reinterpret_cast<bu32x4 *>(bq + 16 * idx) = R.q[m];
       }
@@ -203,8 +226,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     if constexpr (Cf::NA > 0) {
 #pragma unroll
       for (int m = 0; m < Cf::PA; ++m) {
-        const int idx = tid + kBwdThreads * m;
-        if (Cf::NA % kBwdThreads == 0 || idx < Cf::NA)
+        const int idx = tid + NT * m;
+        if (Cf::NA % NT == 0 || idx < Cf::NA)
           *reinterpret_cast<bu32x4 *>(reinterpret_cast<char *>(&s_in.a[0][0]) + 16 * idx) = R.a[m];
       }
     }
@@ -238,7 +261,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
       ak[i] = to_f32(s_in.k[j][r0 + i]);
       xk += s[i] * ak[i];
     }
-    xk = row16_allsum(xk);
+    xk = column_sum<LPC>(xk);
     const float w = s_in.b[j] * (to_f32(s_in.v[j][c]) - xk);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] += ak[i] * w;
@@ -308,8 +331,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
         xk += X[i] * kf[i];
         gk += G[i] * kf[i];
       }
-      xk = row16_allsum(xk);
-      gk = row16_allsum(gk);
+      xk = column_sum<LPC>(xk);
+      gk = column_sum<LPC>(gk);
       const float bt = s_in.b[j];
       const float w = to_f32(s_in.v[j][c]) - xk;
       if (rg == 0) dv[th * D + col] = bt * gk;
@@ -330,12 +353,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
       float *red = s_red[par][wave];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        dkp[i] = rows4_allsum(dkp[i]);
-        dqp[i] = rows4_allsum(dqp[i]);
-        if constexpr (GATE != KDA_GATE_HEAD) dap[i] = rows4_allsum(dap[i]);
+        dkp[i] = across_columns<LPC>(dkp[i]);
+        dqp[i] = across_columns<LPC>(dqp[i]);
+        if constexpr (GATE != KDA_GATE_HEAD) dap[i] = across_columns<LPC>(dap[i]);
       }
-      const float db = rows4_allsum(gk * w);
-      if (lane < 16) {
+      const float db = across_columns<LPC>(gk * w);
+      if (lane < LPC) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           red[r0 + i] = dkp[i];
@@ -345,13 +368,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
       }
       if constexpr (GATE == KDA_GATE_HEAD) {
         // one rate per head: dalpha sums over every row and column
-        const float da = rows4_allsum(row16_allsum(da_all));
+        const float da = across_columns<LPC>(column_sum<LPC>(da_all));
         if (lane == 0) red[3 * D + 1] = da;
       }
       if (lane == 0) red[3 * D] = db;
       __syncthreads();
       const int64_t pb = (int64_t)sl * total * H + th;
-      for (int e = tid; e < NRED; e += kBwdThreads) {
+      for (int e = tid; e < NRED; e += NT) {
         float u = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) u += s_red[par][w2][e];
@@ -397,7 +420,7 @@ hipError_t launch_bwd_t(const kda_shape_t &s, const BwdArgs &a, hipStream_t stre
   float *pa = reinterpret_cast<float *>(ws + L.part_a_off);
   float *pb = reinterpret_cast<float *>(ws + L.part_b_off);
   const int64_t blocks = (int64_t)s.num_seqs * s.num_heads * Cf::SL;
-  hipLaunchKernelGGL((bwd_kernel<D, TIn, GATE>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_kernel<D, TIn, GATE>), dim3((unsigned)blocks), dim3(Cf::NT), 0, stream,
                      static_cast<const TIn *>(a.q), static_cast<const TIn *>(a.k),
                      static_cast<const TIn *>(a.v), a.alpha, a.beta, a.cu, s.seq_len, s.num_seqs, s.num_heads,
                      s.total_tokens, a.S0, a.dO, a.dS_T, a.dv, a.dS0, ckpt, pq, pk, pa, pb);

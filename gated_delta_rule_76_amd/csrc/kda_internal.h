@@ -64,9 +64,10 @@ hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, cons
 // (sequence, head) -- at most floor(T / bwd_block) + N slots of d_k x d_v
 // floats per head -- then per-slice partial sums of dq, dk, dalpha and dbeta
 // over the d_v / 16 column slices ([slices][T][H][d], dalpha [slices][T][H]
-// for one rate per head, dbeta [slices][T][H]).  The block is 16 tokens,
-// 8 for fp32 inputs at d = 128 (their per-block inputs need more LDS).
-constexpr int bwd_block(int d, bool f32_inputs) { return (f32_inputs && d >= 128) ? 8 : 16; }
+// for one rate per head, dbeta [slices][T][H]).  The block is 16 tokens at
+// d <= 64; at d = 128, 12 for bf16 inputs and 8 for fp32 ones (the block's
+// states and inputs have to fit in LDS).
+constexpr int bwd_block(int d, bool f32_inputs) { return d >= 128 ? (f32_inputs ? 8 : 12) : 16; }
 
 struct BwdLayout {
   size_t ckpt_off, part_q_off, part_k_off, part_a_off, part_b_off, bytes;

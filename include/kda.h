@@ -251,8 +251,9 @@ kda_status_t kda_state_commit(const kda_shape_t *shape, float *S, const float *S
  *     dalpha_t = rowsum((G - beta_t k_t k_t^T G) * S_{t-1})  (summed over all
  *     entries with KDA_GATE_HEAD),
  *     dL/dS_{t-1} = Diag(alpha_t) (G - beta_t k_t k_t^T G) + q_{t-1} dO_{t-1}^T.
- * The states are recomputed from S0 (checkpoints every 16 tokens in the
- * workspace); nothing from a forward call is needed.
+ * The states are recomputed from S0 (checkpoints in the workspace every 16
+ * tokens at d <= 64; at d = 128 every 12 for bf16 inputs, every 8 for fp32
+ * ones); nothing from a forward call is needed.
  *   shape, q, k, v, alpha, beta, cu_seqlens, S0  as for kda_prefill
  *                 (input_form must be KDA_INPUT_FINAL, else UNSUPPORTED)
  *   dO            [total_tokens][H][d_v] fp32
@@ -263,7 +264,8 @@ kda_status_t kda_state_commit(const kda_shape_t *shape, float *S, const float *S
  *   dbeta         [total_tokens][H] fp32 output
  *   dS0           [N][H][d_k][d_v] fp32 output, or NULL to skip
  *   workspace     at least kda_backward_workspace_size() bytes, 256-byte
- *                 aligned: state checkpoints (floor(T/16) + N per head) and
+ *                 aligned: state checkpoints (floor(T/B) + N per head, B the
+ *                 checkpoint interval above) and
  *                 per-16-column partial sums of dq, dk, dalpha, dbeta
  *                 (4 (3 d + 1) (d/16) T H bytes at most)
  * Outputs must not overlap inputs.  Results are deterministic (the partial
