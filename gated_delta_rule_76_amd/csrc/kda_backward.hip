@@ -298,6 +298,13 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
 #pragma unroll
   for (int i = 0; i < RPT; ++i) G[i] = dS_T != nullptr ? dS_T[sbase + (int64_t)(r0 + i) * D + col] : 0.f;
   int par = 0;
+  // The checkpoint of the block before is loaded while a block runs.
+  float ckn[RPT];
+  if (nblk > 0) {
+    const float *cp = ck_at(nblk - 1);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) ckn[i] = cp[i];
+  }
   for (int64_t b = nblk - 1; b >= 0; --b) {
     const int64_t tb = b * CK;
     const int nt = (int)(len - tb < CK ? len - tb : CK);
@@ -307,10 +314,12 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       __syncthreads();
       fetch((b > 0 ? b - 1 : 0) * CK, R);
     }
-    {
-      const float *cp = ck_at(b);
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) s[i] = cp[i];
+    for (int i = 0; i < RPT; ++i) s[i] = ckn[i];
+    if (b > 0) {
+      const float *cp = ck_at(b - 1);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) ckn[i] = cp[i];
     }
     for (int j = 0; j < nt; ++j) {
 #pragma unroll
