@@ -283,7 +283,11 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       for (int i = 0; i < RPT; ++i) cp[i] = s[i];
     }
     const int nt = (int)(len - b * CK < CK ? len - b * CK : CK);
-    for (int j = 0; j < nt; ++j) fwd_step(j);
+    // (loops over a block's tokens are unrolled, so LDS addresses are
+    // immediate offsets rather than per-lane pointer increments)
+#pragma unroll
+    for (int j = 0; j < CK; ++j)
+      if (j < nt) fwd_step(j);
     if (b + 1 < nblk) {
       __syncthreads();  // every wave is done with block b
       stash(R);
@@ -321,12 +325,16 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
 #pragma unroll
       for (int i = 0; i < RPT; ++i) ckn[i] = cp[i];
     }
-    for (int j = 0; j < nt; ++j) {
+#pragma unroll
+    for (int j = 0; j < CK; ++j) {
+      if (j >= nt) break;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) s_ring[j][tid][i] = s[i];
       fwd_step(j);
     }
-    for (int j = nt - 1; j >= 0; --j) {
+#pragma unroll
+    for (int j = CK - 1; j >= 0; --j) {
+      if (j >= nt) continue;
       const int64_t th = (start + tb + j) * H + h;
       const float dOc = s_in.dO[j][c];
       float sp[RPT], X[RPT], kf[RPT];
