@@ -57,7 +57,8 @@ struct BwdCfg {
   static constexpr int NT = VW * LPC;                 // threads per workgroup
   static constexpr int RPT = D / LPC;                 // rows per thread
   static constexpr int NW = NT / 64;
-  static constexpr int NRED = 3 * D + 2;              // row sums per token: dk, dq, dalpha, dbeta, dalpha/head
+  static constexpr int NRED = bwd_row_sums(D, GATE == KDA_GATE_HEAD);  // row sums per token
+  static constexpr int EB = GATE == KDA_GATE_HEAD ? 2 * D : 3 * D;     // index of dbeta
   static constexpr int CK = bwd_block(D, sizeof(TIn) == 4);
   static constexpr int DA = GATE == KDA_GATE_HEAD ? 1 : D;  // rates per token
   // 16-byte chunks of one block's rows, and chunks per token row
@@ -135,8 +136,7 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
     const float *__restrict__ alpha, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     int32_t seq_len, int N, int H, int64_t total, const float *__restrict__ S0,
     const float *__restrict__ dO, const float *__restrict__ dS_T, float *__restrict__ dv,
-    float *__restrict__ dS0, float *__restrict__ ckpt, float *__restrict__ part_q,
-    float *__restrict__ part_k, float *__restrict__ part_a, float *__restrict__ part_b) {
+    float *__restrict__ dS0, float *__restrict__ ckpt, float *__restrict__ part) {
   using Cf = BwdCfg<D, TIn, GATE>;
   constexpr int RPT = Cf::RPT, VW = Cf::VW, SL = Cf::SL, NW = Cf::NW, NRED = Cf::NRED, CK = Cf::CK;
   constexpr int NT = Cf::NT, LPC = Cf::LPC;
@@ -352,7 +352,7 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       gk = column_sum<LPC>(gk);
       const float bt = s_in.b[j];
       const float w = to_f32(s_in.v[j][c]) - xk;
-      if (rg == 0) dv[th * D + col] = bt * gk;
+      dv[th * D + col] = bt * gk;  // (the column's lanes store the same value)
       float dkp[RPT], dqp[RPT], dap[RPT];
       float da_all = 0.f;
 #pragma unroll
@@ -365,8 +365,8 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
         da_all += dap[i];
         G[i] = rate(j, i) * e;
       }
-      // Row sums over the slice's 16 columns: the wave's 4 columns by lane
-      // swaps, then the 4 waves through LDS.
+      // Row sums over the slice's 16 columns: the wave's columns by lane
+      // swaps (when it holds more than one), then the waves through LDS.
       float *red = s_red[par][wave];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
@@ -386,25 +386,20 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       if constexpr (GATE == KDA_GATE_HEAD) {
         // one rate per head: dalpha sums over every row and column
         const float da = across_columns<LPC>(column_sum<LPC>(da_all));
-        if (lane == 0) red[3 * D + 1] = da;
+        if (lane == 0) red[Cf::EB + 1] = da;
       }
-      if (lane == 0) red[3 * D] = db;
+      if (lane == 0) red[Cf::EB] = db;
       __syncthreads();
-      const int64_t pb = (int64_t)sl * total * H + th;
-      for (int e = tid; e < NRED; e += NT) {
-        float u = 0.f;
+      // The slice's partial row sums of this token, in one contiguous row.
+      float *prow = part + ((int64_t)sl * total * H + th) * NRED;
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) u += s_red[par][w2][e];
-        if (e < D) {
-          part_k[pb * D + e] = u;
-        } else if (e < 2 * D) {
-          part_q[pb * D + e - D] = u;
-        } else if (e < 3 * D) {
-          if constexpr (GATE != KDA_GATE_HEAD) part_a[pb * D + e - 2 * D] = u;
-        } else if (e == 3 * D) {
-          part_b[pb] = u;
-        } else if constexpr (GATE == KDA_GATE_HEAD) {
-          part_a[pb] = u;
+      for (int u0 = 0; u0 < NRED; u0 += NT) {
+        const int e = u0 + tid;
+        if (e < NRED) {
+          float u = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < NW; ++w2) u += s_red[par][w2][e];
+          prow[e] = u;
         }
       }
       par ^= 1;
@@ -416,13 +411,31 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
   }
 }
 
-// dq, dk, dalpha (and dbeta) = sums of the per-slice partials, slice order fixed.
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part, float *__restrict__ out,
-                                                         int64_t n, int slices) {
+// dk, dq, dalpha and dbeta = sums of the per-slice partial rows, slice order
+// fixed, scattered to their outputs.
+template <int D, int GATE>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part, float *__restrict__ dk,
+                                                         float *__restrict__ dq, float *__restrict__ dalpha,
+                                                         float *__restrict__ dbeta, int64_t rows, int slices) {
+  constexpr int NRED = bwd_row_sums(D, GATE == KDA_GATE_HEAD);
+  constexpr int EB = GATE == KDA_GATE_HEAD ? 2 * D : 3 * D;
+  const int64_t n = rows * NRED;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float acc = 0.f;
     for (int s = 0; s < slices; ++s) acc += part[(int64_t)s * n + i];
-    out[i] = acc;
+    const int64_t th = i / NRED;
+    const int e = (int)(i - th * NRED);
+    if (e < D) {
+      dk[th * D + e] = acc;
+    } else if (e < 2 * D) {
+      dq[th * D + e - D] = acc;
+    } else if (e < EB) {
+      dalpha[th * D + e - 2 * D] = acc;
+    } else if (e == EB) {
+      dbeta[th] = acc;
+    } else {
+      dalpha[th] = acc;  // one rate per head
+    }
   }
 }
 
@@ -432,28 +445,20 @@ hipError_t launch_bwd_t(const kda_shape_t &s, const BwdArgs &a, hipStream_t stre
   const BwdLayout L = backward_layout(s);
   char *ws = static_cast<char *>(a.workspace);
   float *ckpt = reinterpret_cast<float *>(ws + L.ckpt_off);
-  float *pq = reinterpret_cast<float *>(ws + L.part_q_off);
-  float *pk = reinterpret_cast<float *>(ws + L.part_k_off);
-  float *pa = reinterpret_cast<float *>(ws + L.part_a_off);
-  float *pb = reinterpret_cast<float *>(ws + L.part_b_off);
+  float *part = reinterpret_cast<float *>(ws + L.part_off);
   const int64_t blocks = (int64_t)s.num_seqs * s.num_heads * Cf::SL;
   hipLaunchKernelGGL((bwd_kernel<D, TIn, GATE>), dim3((unsigned)blocks), dim3(Cf::NT), 0, stream,
                      static_cast<const TIn *>(a.q), static_cast<const TIn *>(a.k),
                      static_cast<const TIn *>(a.v), a.alpha, a.beta, a.cu, s.seq_len, s.num_seqs, s.num_heads,
-                     s.total_tokens, a.S0, a.dO, a.dS_T, a.dv, a.dS0, ckpt, pq, pk, pa, pb);
+                     s.total_tokens, a.S0, a.dO, a.dS_T, a.dv, a.dS0, ckpt, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t th = s.total_tokens * s.num_heads;
-  const int64_t nd = th * D, na = GATE == KDA_GATE_HEAD ? th : nd;
-  struct {
-    const float *p;
-    float *o;
-    int64_t n;
-  } jobs[4] = {{pq, a.dq, nd}, {pk, a.dk, nd}, {pa, a.dalpha, na}, {pb, a.dbeta, th}};
-  for (const auto &j : jobs) {
-    if (j.n == 0) continue;
-    const int64_t g = (j.n + 255) / 256 < 8192 ? (j.n + 255) / 256 : 8192;
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)g), dim3(256), 0, stream, j.p, j.o, j.n, Cf::SL);
+  const int64_t rows = s.total_tokens * s.num_heads;
+  const int64_t n = rows * Cf::NRED;
+  if (n > 0) {
+    const int64_t g = (n + 255) / 256 < 16384 ? (n + 255) / 256 : 16384;
+    hipLaunchKernelGGL((bwd_reduce_kernel<D, GATE>), dim3((unsigned)g), dim3(256), 0, stream, part, a.dk, a.dq,
+                       a.dalpha, a.dbeta, rows, Cf::SL);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -62,15 +62,16 @@ hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, cons
 
 // Backward pass.  Workspace: state checkpoints every bwd_block tokens per
 // (sequence, head) -- at most floor(T / bwd_block) + N slots of d_k x d_v
-// floats per head -- then per-slice partial sums of dq, dk, dalpha and dbeta
-// over the d_v / 16 column slices ([slices][T][H][d], dalpha [slices][T][H]
-// for one rate per head, dbeta [slices][T][H]).  The block is 16 tokens at
-// d <= 64; at d = 128, 12 for bf16 inputs and 8 for fp32 ones (the block's
-// states and inputs have to fit in LDS).
+// floats per head -- then the per-slice partial row sums over the d_v / 16
+// column slices, [slices][T][H][bwd_row_sums] floats: per (token, head) dk
+// (d), dq (d), then dalpha (d) and dbeta, or with one rate per head dbeta and
+// dalpha.  The block is 16 tokens at d <= 64; at d = 128, 12 for bf16 inputs
+// and 8 for fp32 ones (the block's states and inputs have to fit in LDS).
 constexpr int bwd_block(int d, bool f32_inputs) { return d >= 128 ? (f32_inputs ? 8 : 12) : 16; }
+constexpr int bwd_row_sums(int d, bool head_gate) { return head_gate ? 2 * d + 2 : 3 * d + 1; }
 
 struct BwdLayout {
-  size_t ckpt_off, part_q_off, part_k_off, part_a_off, part_b_off, bytes;
+  size_t ckpt_off, part_off, bytes;
 };
 
 inline BwdLayout backward_layout(const kda_shape_t &s) {
@@ -78,14 +79,11 @@ inline BwdLayout backward_layout(const kda_shape_t &s) {
   const size_t slices = d < 16 ? 1 : d / 16;
   const int blk = bwd_block(s.d_k, s.qkv_dtype == KDA_F32);
   const size_t slots = (size_t)(s.total_tokens / blk) + (size_t)s.num_seqs;
-  const size_t da = s.gate == KDA_GATE_HEAD ? 1 : d;
+  const size_t nred = (size_t)bwd_row_sums(s.d_k, s.gate == KDA_GATE_HEAD);
   BwdLayout L;
   L.ckpt_off = 0;
-  L.part_q_off = align_up(L.ckpt_off + sizeof(float) * slots * H * d * (size_t)s.d_v, kWorkspaceAlign);
-  L.part_k_off = align_up(L.part_q_off + sizeof(float) * slices * T * H * d, kWorkspaceAlign);
-  L.part_a_off = align_up(L.part_k_off + sizeof(float) * slices * T * H * d, kWorkspaceAlign);
-  L.part_b_off = align_up(L.part_a_off + sizeof(float) * slices * T * H * da, kWorkspaceAlign);
-  L.bytes = align_up(L.part_b_off + sizeof(float) * slices * T * H, kWorkspaceAlign);
+  L.part_off = align_up(L.ckpt_off + sizeof(float) * slots * H * d * (size_t)s.d_v, kWorkspaceAlign);
+  L.bytes = align_up(L.part_off + sizeof(float) * slices * T * H * nred, kWorkspaceAlign);
   return L;
 }
 

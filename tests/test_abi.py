@@ -211,10 +211,7 @@ def test_backward_validation_and_workspace(L):
     slots, slices, T, H, d = 40 * 2 // 12 + 2, 8, 80, 3, 128
     al = lambda x: -(-x // 256) * 256
     want = al(4 * slots * H * d * d)
-    want = al(want + 4 * slices * T * H * d)      # dq partials
-    want = al(want + 4 * slices * T * H * d)      # dk partials
-    want = al(want + 4 * slices * T * H * d)      # dalpha partials
-    want = al(want + 4 * slices * T * H)          # dbeta partials
+    want = al(want + 4 * slices * T * H * (3 * d + 1))   # partial rows: dk, dq, dalpha, dbeta
     assert out.value == want
     assert L.kda_backward_workspace_size(ctypes.byref(shape(form=1)), ctypes.byref(out)) == UNSUPPORTED
     need = out.value
