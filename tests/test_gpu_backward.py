@@ -105,3 +105,19 @@ def test_backward_4k_workload():
     want = _oracle(d, dO, np64(dST[:, heads]), heads=heads)
     sub = [g[:, heads] for g in got]
     _check(sub, want, 1e-4, "backward 4k")
+
+
+def test_backward_long_varlen_weak_decay():
+    """Two sequences of 9,000 and 7,385 tokens (varlen, neither a multiple of
+    the checkpoint interval), H=2, d=128, bf16, weak decay (the gradients
+    reach far back) with S0 and dS_T: every gradient against the oracle.
+    Checks checkpoint and partial-sum indexing well past a few blocks."""
+    dev = device()
+    lens = [9000, 7385]
+    d = inputs.prefill_inputs(lens, 2, 128, torch.bfloat16, "weak", 0.02, seed=11, device=dev)
+    T = sum(lens)
+    dO, dST = inputs.grad_inputs(T, 2, 128, len(lens), seed=11, device=dev)
+    got = kda.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dO, d["S0"], dST, d["cu_seqlens"])
+    cu = np.asarray(d["cu_seqlens"].cpu())
+    want = _oracle(d, dO, np64(dST), cu=cu, S0=np64(d["S0"]))
+    _check(got, want, 1e-4, "backward long varlen")
