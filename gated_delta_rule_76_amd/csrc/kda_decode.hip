@@ -49,10 +49,12 @@ __device__ __forceinline__ float decay_from_preact(float a) { return 1.f / (1.f 
 __device__ __forceinline__ float strength_from_preact(float b) { return 1.f / (1.f + expf(-b)); }
 __device__ __forceinline__ float inv_norm(float ss) { return 1.f / fmaxf(sqrtf(ss), 1e-12f); }
 
-// Batches whose states exceed this many bytes (several times the 256 MB
-// Infinity Cache) also read the state with non-temporal loads: measured on
-// the decode kernel, non-temporal stores alone are best at 512 MiB of state
-// (75% vs 73.5% of HBM peak with both), both at 2 GiB (72% vs 65%).
+// Threshold for reading the state with non-temporal loads as well (several
+// times the 256 MB Infinity Cache).  The single-token step applies it to the
+// state's size: non-temporal stores alone are best at 512 MiB of state (75%
+// vs 73.5% of HBM peak with both), both at 2 GiB (72% vs 65%).  The
+// multi-token kernel applies it to the bytes it moves (the state read plus
+// every state written), which pass it at two tokens with history at B = 256.
 constexpr int64_t kStreamStateBytes = (int64_t)1 << 30;
 
 template <int D, typename TIn, int GATE, int FORM, bool NTL>
@@ -241,7 +243,7 @@ __device__ __forceinline__ void load_token_in(TokenIn<D, TIn> &x, const TIn *__r
   x.b = beta[th];
 }
 
-template <int D, typename TIn, int GATE, int FORM, bool HIST>
+template <int D, typename TIn, int GATE, int FORM, bool HIST, bool NTL>
 __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ S,
@@ -268,7 +270,15 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
   float *Sp = S + nh * (int64_t)(D * D) + cq * 4;
   float4 s[PASSES];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) s[p] = *reinterpret_cast<const float4 *>(Sp + (int64_t)(r0 + p * RPP) * D);
+  for (int p = 0; p < PASSES; ++p) {
+    const float *src = Sp + (int64_t)(r0 + p * RPP) * D;
+    if constexpr (NTL) {
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
+      s[p] = make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+      s[p] = *reinterpret_cast<const float4 *>(src);
+    }
+  }
 
   for (int t = 0; t < ntok; ++t) {
     const int64_t th = (n * ntok + t) * H + h;  // token row * H + head
@@ -472,14 +482,25 @@ hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void 
     const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
     const TIn *qp = static_cast<const TIn *>(q), *kp = static_cast<const TIn *>(k),
               *vp = static_cast<const TIn *>(v);
-    if (hist != nullptr)
-      hipLaunchKernelGGL((decode_tokens_kernel<D, TIn, G, F, true>), dim3((unsigned)blocks),
+    // The state is read once; once the bytes the call moves (that read plus
+    // every state written) pass 1 GiB it is read with non-temporal loads too
+    // (two tokens with history at B=256, 1.5 GiB: 336 -> 299 us per call).
+    const int64_t state_bytes = blocks * (int64_t)(D * D) * (int64_t)sizeof(float);
+    const int64_t writes = hist != nullptr ? (int64_t)s.seq_len : 1;
+    const bool ntl = state_bytes * (1 + writes) > kStreamStateBytes;
+    auto go = [&](auto hist_c, auto ntl_c) {
+      constexpr bool HI = decltype(hist_c)::value, NL = decltype(ntl_c)::value;
+      hipLaunchKernelGGL((decode_tokens_kernel<D, TIn, G, F, HI, NL>), dim3((unsigned)blocks),
                          dim3(DecodeCfg<D>::NT), 0, stream, qp, kp, vp, alpha, beta, S, o, hist, s.seq_len,
                          s.num_heads);
-    else
-      hipLaunchKernelGGL((decode_tokens_kernel<D, TIn, G, F, false>), dim3((unsigned)blocks),
-                         dim3(DecodeCfg<D>::NT), 0, stream, qp, kp, vp, alpha, beta, S, o, hist, s.seq_len,
-                         s.num_heads);
+    };
+    if (hist != nullptr) {
+      if (ntl) go(std::true_type{}, std::true_type{});
+      else go(std::true_type{}, std::false_type{});
+    } else {
+      if (ntl) go(std::false_type{}, std::true_type{});
+      else go(std::false_type{}, std::false_type{});
+    }
     return hipGetLastError();
   });
 }
