@@ -67,6 +67,16 @@ def test_prefill_decay_regimes(decay, dtype):
     _check(o, ST, ro, rST, TOL[dtype], f"decay {decay}")
 
 
+def test_prefill_fp32_many_chunks_weak_decay():
+    """fp32 path at d=128 over many chunks with the longest memory: two
+    packed sequences (16 chunks + a 40-token tail, 5 chunks + 13), S0."""
+    dev = device()
+    d = inputs.prefill_inputs([1064, 333], 2, 128, torch.float32, "weak", 0.5, seed=23, device=dev)
+    o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
+    ro, rST = _oracle(d, cu=np.asarray(d["cu_seqlens"].cpu()), S0=np64(d["S0"]))
+    _check(o, ST, ro, rST, 1e-5, "fp32 many chunks")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 def test_prefill_varlen_ragged_and_empty(dtype):
     dev = device()
