@@ -45,6 +45,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 N_SETS = 5                     # input sets rotated between timed calls
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_prefill_4k.json")
 KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_prefill.hip")
+DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_decode_b256.json")
+DECODE_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_decode.hip")
 COPY_BYTES = 256 << 20         # --calibrate-copy: bytes read (and written) by the copy
 
 WORKLOAD_TEXT = {
@@ -492,13 +494,16 @@ def oracle_rates():
     return out
 
 
-def _traffic(kernel, workload):
-    """HBM bytes per launch of ``kernel`` from the committed counter summary,
-    or None when it is missing or was taken on other kernel source."""
+def _traffic(kernel, workload, summary=None, source=None):
+    """HBM bytes per launch of ``kernel`` from a committed counter summary
+    (the prefill one unless ``summary`` / ``source`` name another), or None
+    when it is missing or was taken on other kernel source."""
+    summary = TRAFFIC_SUMMARY if summary is None else summary
+    source = KERNEL_SOURCE if source is None else source
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(summary) as f:
             t = json.load(f)
-        with open(KERNEL_SOURCE, "rb") as f:
+        with open(source, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
@@ -533,12 +538,15 @@ def prefill_summary(pf, gate):
 
 def decode_summary(dc, gate, form="final"):
     gbs = dc["B"] * dc["H"] * decode_bytes(gate) / (dc["ms_per_step"] * 1e-3) / 1e9
+    # (the counter summary covers the per-channel decode kernel on activated inputs)
+    traffic = (_traffic("decode_kernel", "decode_b%d" % dc["B"], DECODE_TRAFFIC_SUMMARY, DECODE_SOURCE)
+               if gate == "channel" and form == "final" else None)
     kind = ("KDA" if gate == "channel" else "scalar-gate") + (" pre-activation" if form == "preact" else "")
     return {"metric": "%s decode steps/s (B=%d, H=32, d=128)" % (kind, dc["B"]),
             "value": 1e3 / dc["ms_per_step"], "unit": "steps/s", "ms_per_step": dc["ms_per_step"],
             "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": None, "bytes_per_head_step": decode_bytes(gate)},
+                         "traffic": traffic, "bytes_per_head_step": decode_bytes(gate)},
             "state_rmw_gbs": dc["state_rmw_gbs"]}
 
 

@@ -1,4 +1,5 @@
-"""HBM traffic of the prefill kernels from two rocprofv3 counter runs of bench.py.
+"""HBM traffic of the prefill or decode kernels from two rocprofv3 counter
+runs of bench.py.
 
     rocprofv3 --pmc FETCH_SIZE -d DIR_F -o f --output-format csv -- \\
         python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-decode --calibrate-copy
@@ -7,11 +8,18 @@
     python -m gated_delta_rule_76_amd.counters DIR_F/f_counter_collection.csv \\
         DIR_W/w_counter_collection.csv --workload prefill_4k > profiles/traffic_prefill_4k.json
 
+and for the decode step (bench.py without --no-decode, with --no-variants so
+that only the per-channel decode kernel runs):
+
+    python -m gated_delta_rule_76_amd.counters F.csv W.csv --target decode \\
+        --workload decode_b256 > profiles/traffic_decode_b256.json
+
 FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB).  Each is scaled by
 the factor that maps the same counter of a plain elementwise float64 copy
 of 256 MiB (the --calibrate-copy kernel, which reads and writes exactly
-that, in 16-byte accesses like the prefill kernels) to its true size.  The summary records the sha256 of the prefill source it
-was taken on; bench.py reports the traffic only while the source matches.
+that, in 16-byte accesses like the library's kernels) to its true size.
+The summary records the sha256 of the kernel source it was taken on;
+bench.py reports the traffic only while the source matches.
 """
 
 from __future__ import annotations
@@ -24,12 +32,17 @@ import os
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_prefill.hip")
+CSRC = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc")
 COPY_BYTES = 256 << 20
-KERNELS = ("chunk_local_kernel", "chunk_state_kernel")
+# kernel source and kernel names per target ("decode_kernel" is not a
+# substring of "decode_tokens_kernel")
+TARGETS = {
+    "prefill": ("kda_prefill.hip", ("chunk_local_kernel", "chunk_state_kernel")),
+    "decode": ("kda_decode.hip", ("decode_kernel", "decode_tokens_kernel", "commit_kernel")),
+}
 
 
-def _per_kernel(path, counter):
+def _per_kernel(path, counter, kernels):
     vals = defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
@@ -37,7 +50,7 @@ def _per_kernel(path, counter):
                 continue
             name = r["Kernel_Name"]
             key = None
-            for k in KERNELS:
+            for k in kernels:
                 if k in name:
                     key = k
             low = name.lower()
@@ -48,21 +61,22 @@ def _per_kernel(path, counter):
     return vals
 
 
-def summarize(fetch_csv, write_csv, workload):
-    fv = _per_kernel(fetch_csv, "FETCH_SIZE")
-    wv = _per_kernel(write_csv, "WRITE_SIZE")
+def summarize(fetch_csv, write_csv, workload, target="prefill"):
+    source, kernels = TARGETS[target]
+    fv = _per_kernel(fetch_csv, "FETCH_SIZE", kernels)
+    wv = _per_kernel(write_csv, "WRITE_SIZE", kernels)
     # the copy runs three times; take the median dispatch
     cf = sorted(fv["copy"])[len(fv["copy"]) // 2]
     cw = sorted(wv["copy"])[len(wv["copy"]) // 2]
     f_fetch, f_write = COPY_BYTES / cf, COPY_BYTES / cw
-    with open(SOURCE, "rb") as f:
+    with open(os.path.join(CSRC, source), "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     out = {"workload": workload, "source_sha256": sha,
            "calibration": {"copy_bytes": COPY_BYTES, "copy_fetch_counter_bytes": cf,
                            "copy_write_counter_bytes": cw, "fetch_factor": f_fetch,
                            "write_factor": f_write},
            "kernels": {}}
-    for k in KERNELS:
+    for k in kernels:
         if fv.get(k) and wv.get(k):
             fr = sum(fv[k]) / len(fv[k])
             wr = sum(wv[k]) / len(wv[k])
@@ -77,8 +91,9 @@ def main():
     p.add_argument("fetch_csv")
     p.add_argument("write_csv")
     p.add_argument("--workload", default="prefill_4k")
+    p.add_argument("--target", default="prefill", choices=sorted(TARGETS))
     a = p.parse_args()
-    print(json.dumps(summarize(a.fetch_csv, a.write_csv, a.workload), indent=1))
+    print(json.dumps(summarize(a.fetch_csv, a.write_csv, a.workload, a.target), indent=1))
 
 
 if __name__ == "__main__":

@@ -45,6 +45,17 @@ def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch)
     assert bench._traffic("chunk_state_kernel", "prefill_4k") is None
 
 
+def test_decode_traffic_matches_its_algorithmic_bytes():
+    # the committed decode summary was taken on the committed decode source;
+    # its counters read within 1% of the algorithmic bytes of a B=256 step
+    t = bench._traffic("decode_kernel", "decode_b256", bench.DECODE_TRAFFIC_SUMMARY, bench.DECODE_SOURCE)
+    assert t is not None
+    algorithmic = 256 * 32 * bench.decode_bytes("channel")
+    assert abs(t / algorithmic - 1) < 0.01
+    assert bench._traffic("decode_kernel", "decode_b1024", bench.DECODE_TRAFFIC_SUMMARY,
+                          bench.DECODE_SOURCE) is None
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
