@@ -47,6 +47,24 @@ def test_backward_sizes(D, dtype, T):
     _check(got, want, 1e-5, f"D={D} T={T} {dtype}")
 
 
+@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (128, torch.float32), (64, torch.float32)],
+                         ids=["128-bf16", "128-f32", "64-f32"])
+def test_backward_dense_batch(D, dtype):
+    """[B, T, H, D] inputs without cu_seqlens: three sequences of 40 tokens
+    (not a multiple of the checkpoint interval), S0 and dS_T per sequence."""
+    dev = device()
+    B, T, H = 3, 40, 2
+    d = inputs.prefill_inputs([T] * B, H, D, dtype, "medium", 0.5, seed=70 + D, device=dev)
+    dO, dST = inputs.grad_inputs(B * T, H, D, B, seed=70 + D, device=dev, dS_std=0.5)
+    shp = lambda t: t.reshape((B, T) + tuple(t.shape[1:]))
+    got = kda.backward(shp(d["q"]), shp(d["k"]), shp(d["v"]), shp(d["alpha"]), shp(d["beta"]), shp(dO),
+                       d["S0"], dST)
+    assert got[0].shape == (B, T, H, D) and got[3].shape == (B, T, H, D) and got[4].shape == (B, T, H)
+    flat = [g.reshape((B * T,) + tuple(g.shape[2:])) for g in got[:5]] + [got[5]]
+    want = _oracle(d, dO, np64(dST), cu=np.asarray(d["cu_seqlens"].cpu()), S0=np64(d["S0"]))
+    _check(flat, want, 1e-5, f"dense batch D={D} {dtype}")
+
+
 @pytest.mark.parametrize("gate", ["channel", "head"])
 def test_backward_varlen_without_states(gate):
     dev = device()

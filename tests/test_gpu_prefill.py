@@ -88,13 +88,14 @@ def test_prefill_varlen_ragged_and_empty(dtype):
     assert torch.equal(ST[0], d["S0"][0]) and torch.equal(ST[6], d["S0"][6])   # empty sequences
 
 
-def test_prefill_dense_batch_layout():
+@pytest.mark.parametrize("D", [32, 128])
+def test_prefill_dense_batch_layout(D):
     dev = device()
-    d = inputs.prefill_inputs([100] * 3, 2, 32, torch.bfloat16, "strong", 0.1, seed=6, device=dev)
+    d = inputs.prefill_inputs([100] * 3, 2, D, torch.bfloat16, "strong", 0.1, seed=6, device=dev)
     shp = lambda t: t.reshape((3, 100) + tuple(t.shape[1:]))
     o, ST = kda.prefill(shp(d["q"]), shp(d["k"]), shp(d["v"]), shp(d["alpha"]), shp(d["beta"]), d["S0"])
     ro, rST = _oracle(d, cu=np.asarray(d["cu_seqlens"].cpu()), S0=np64(d["S0"]))
-    _check(o.reshape(300, 2, 32), ST, ro, rST, 2e-3, "dense batch")
+    _check(o.reshape(300, 2, D), ST, ro, rST, 2e-3, "dense batch")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
