@@ -15,9 +15,13 @@ start and the chunk's decay, Gram and UT factors
 and everything else of a chunk (dq, dk, dv, dalpha, dbeta) comes from
 matrix products of that chunk's own quantities, so on a GPU every chunk's
 gradients could be formed in parallel once the reverse pass has produced
-each chunk's G'.  The decay enters through cumulative log-rates
-g = cumsum(log alpha) here, so the model needs alpha > 0 (a kernel would use
-products of alpha and exclude alpha_s instead of dividing by it).
+each chunk's G'.
+
+Every decay factor is a product of rates, E[r, j] = prod_{j < s <= r}
+alpha_s (never a quotient), and dalpha_t collects, for every factor that
+contains alpha_t, the product of its other rates, through three linear
+recurrences per channel (see _decay_grad).  So the model, like the
+token-level kernels, is exact when a rate is 0.
 """
 
 from __future__ import annotations
@@ -27,30 +31,72 @@ import numpy as np
 C = 64
 
 
-def _masked_decay(g, inclusive):
-    """exp(g_r - g_j) per channel for j < r (or j <= r), zero elsewhere:
-    [C, C, d]."""
-    n = g.shape[0]
-    r, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
-    keep = (j <= r) if inclusive else (j < r)
-    diff = np.where(keep[:, :, None], g[:, None, :] - g[None, :, :], -np.inf)
-    return np.exp(diff), keep
+def _range_products(alpha):
+    """E[r, j, c] = prod over j < s <= r of alpha[s, c] for j <= r (1 on the
+    diagonal), 0 above it: [C, C, d]."""
+    n = alpha.shape[0]
+    E = np.zeros((n, n, alpha.shape[1]))
+    for j in range(n):
+        E[j, j] = 1.0
+        for r in range(j + 1, n):
+            E[r, j] = E[r - 1, j] * alpha[r]
+    return E
 
 
 def _factors(k, q, alpha, beta):
     """The chunk's forward factors from padded k, q, alpha [C, d], beta [C]."""
-    g = np.cumsum(np.log(alpha), axis=0)
-    Es, strict = _masked_decay(g, inclusive=False)
-    Ei, incl = _masked_decay(g, inclusive=True)
+    Ei = _range_products(alpha)
+    idx = np.arange(C)
+    incl = idx[None, :] <= idx[:, None]     # [r, j]: j <= r
+    strict = idx[None, :] < idx[:, None]
+    Es = np.where(strict[:, :, None], Ei, 0.0)
     A = np.einsum("rc,jc,rjc->rj", k, k, Es)
     M = np.einsum("rc,jc,rjc->rj", q, k, Ei)
     L = np.eye(C) + beta[:, None] * A
     X = np.linalg.inv(L)
     T = X * beta[None, :]
-    Gam = np.exp(g)
+    Gam = np.cumprod(alpha, axis=0)          # Gamma_r = prod_{s <= r} alpha_s
     GC = Gam[-1]
-    return dict(g=g, Es=Es, Ei=Ei, strict=strict, incl=incl, A=A, M=M, X=X, T=T, Gam=Gam, GC=GC,
-                Khat=Gam * k, Qhat=Gam * q, Ktil=(GC[None, :] / Gam) * k)
+    Etail = Ei[-1]                           # [r, c] = prod_{r < s < C} alpha_s
+    return dict(Es=Es, Ei=Ei, strict=strict, incl=incl, A=A, M=M, X=X, T=T, Gam=Gam, GC=GC,
+                Etail=Etail, Khat=Gam * k, Qhat=Gam * q, Ktil=Etail * k)
+
+
+def _decay_grad(alpha, F, kc, qc, dKhat, dQhat, dKtil, dGC, dA, dM):
+    """dL/dalpha_t [C, d] of one chunk, from the gradients of the factors
+    that contain rates:
+      Gamma_r (in Khat, Qhat; Gamma_C in the state's decay): the other rates
+        of Gamma_r are Gamma_{t-1} E[r, t];
+      Etail_r (in Ktil): E[C-1, t] E[t-1, r] for r < t;
+      E[r, j] (in A, M): E[r, t] E[t-1, j] for j < t <= r.
+    Each sum over the factors runs as a linear recurrence in t."""
+    n, d = alpha.shape
+    E = F["Ei"]
+    one = np.ones(d)
+    # Gamma terms: R_t = sum_{r >= t} E[r, t] y_r
+    y = dKhat * kc + dQhat * qc
+    y[-1] = y[-1] + dGC
+    R = np.zeros((n, d))
+    R[-1] = y[-1]
+    for t in range(n - 2, -1, -1):
+        R[t] = y[t] + alpha[t + 1] * R[t + 1]
+    before = np.vstack([one, F["Gam"][:-1]])          # Gamma_{t-1}, 1 for t = 0
+    out = before * R
+    # Ktil terms: P_t = sum_{r < t} E[t-1, r] z_r
+    z = dKtil * kc
+    P = np.zeros((n, d))
+    for t in range(1, n):
+        P[t] = alpha[t - 1] * P[t - 1] + z[t - 1] if t > 1 else z[0]
+    out += E[-1] * P                                   # E[C-1, t] P_t
+    # Gram terms: W_t[j] = sum_{r >= t} E[r, t] V[r, j] (j < t), then
+    # D_t = sum_{j < t} E[t-1, j] W_t[j]
+    V = (dA[:, :, None] * kc[:, None, :] + dM[:, :, None] * qc[:, None, :]) * kc[None, :, :]
+    V = np.where(F["strict"][:, :, None], V, 0.0)
+    Wt = np.zeros((n, d))                              # W_t[j] for the current t, all j
+    for t in range(n - 1, 0, -1):
+        Wt = V[t] + (alpha[t + 1] * Wt if t + 1 < n else 0.0)
+        out[t] += np.sum(E[t - 1, :t] * Wt[:t], axis=0)
+    return out
 
 
 def _pad(x, n, fill):
@@ -100,27 +146,16 @@ def backward_one(q, k, v, alpha, beta, dO, S0, dST):
         # decayed Gram matrices A (k against k) and M (q against k)
         Es, Ei = F["Es"], F["Ei"]
         dk = np.einsum("rj,jc,rjc->rc", dA, kc, Es) + np.einsum("rj,rc,rjc->jc", dA, kc, Es)
-        pa = np.einsum("rj,rc,jc,rjc->rjc", dA, kc, kc, Es)
-        dg = pa.sum(axis=1) - pa.sum(axis=0)
         dq = np.einsum("rj,jc,rjc->rc", dM, kc, Ei)
         dk += np.einsum("rj,rc,rjc->jc", dM, qc, Ei)
-        pm = np.einsum("rj,rc,jc,rjc->rjc", dM, qc, kc, Ei)
-        dg += pm.sum(axis=1) - pm.sum(axis=0)
-        # decayed keys and queries, and the chunk's total decay
-        Gam, GC = F["Gam"], F["GC"]
-        dk += dKhat * Gam
-        dg += dKhat * F["Khat"]
-        dq += dQhat * Gam
-        dg += dQhat * F["Qhat"]
-        dk += dKtil * (GC[None, :] / Gam)
-        dg -= dKtil * F["Ktil"]
-        dg[-1] += np.sum(dKtil * F["Ktil"], axis=0) + dGC * GC
-        # g = cumsum(log alpha)
-        dlog = np.cumsum(dg[::-1], axis=0)[::-1]
+        # decayed keys and queries
+        dk += dKhat * F["Gam"] + dKtil * F["Etail"]
+        dq += dQhat * F["Gam"]
+        dalpha = _decay_grad(ac, F, kc, qc, dKhat, dQhat, dKtil, dGC, dA, dM)
         gq[c0:c0 + n] = dq[:n]
         gk[c0:c0 + n] = dk[:n]
         gv[c0:c0 + n] = dU[:n]
-        ga[c0:c0 + n] = (dlog / ac)[:n]
+        ga[c0:c0 + n] = dalpha[:n]
         gb[c0:c0 + n] = dbeta[:n]
         G = dS
     return gq, gk, gv, ga, gb, G

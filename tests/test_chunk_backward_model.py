@@ -59,3 +59,23 @@ def test_chunked_backward_scalar_gate():
 
 def test_chunked_backward_wider_heads():
     _compare(_case(5, [129], 1, 32, "weak"))
+
+
+def test_chunked_backward_exact_with_zero_rates():
+    # rates of exactly 0 (history erased) at a chunk's first and last token,
+    # mid-chunk, over a stretch of tokens, and tiny rates: the product form
+    # never divides by a rate
+    q, k, v, alpha, beta, dO, S0, dST, cu = _case(6, [150], 1, 16, "medium")
+    alpha[0, 0, 3] = 0.0
+    alpha[63, 0, 5] = 0.0
+    alpha[64, 0, :] = 0.0
+    alpha[90:95, 0, 7] = 0.0
+    alpha[120, 0, 2] = 1e-30
+    _compare((q, k, v, alpha, beta, dO, S0, dST, cu))
+
+
+def test_chunked_backward_scalar_gate_zero_rate():
+    q, k, v, alpha, beta, dO, S0, dST, cu = _case(7, [100], 2, 16, "strong", per_head=True)
+    alpha[10, 0] = 0.0
+    alpha[70, 1] = 0.0
+    _compare((q, k, v, alpha, beta, dO, S0, dST, cu))
