@@ -1052,13 +1052,9 @@ __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec,
   const int t = wave < Cf::NTILE ? wave : Cf::NTILE - 1;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) IO::load(B.p[kb], rec + (size_t)(Rc::PMAT + 2 * t + kb) * kFragBytes, lane);
-  {
-    // rows 16 t .. 16 t + 15 at a wave-uniform address (scalar loads); each
-    // lane keeps the four of its row group
-    const float4 *gp = reinterpret_cast<const float4 *>(rec + Rc::GAM + sizeof(float) * 16 * t);
-    const float4 g0 = gp[0], g1 = gp[1], g2 = gp[2], g3 = gp[3];
-    B.gam = g == 0 ? g0 : g == 1 ? g1 : g == 2 ? g2 : g3;
-  }
+  // rows 16 t + 4 g .. + 3, the lane's row group (a vector load: a scalar
+  // load here would be waited for at the next barrier, with the LDS stores)
+  B.gam = *reinterpret_cast<const float4 *>(rec + Rc::GAM + sizeof(float) * (16 * t + 4 * g));
 }
 
 // Two waves per SIMD: the two register sets of record fragments take about
