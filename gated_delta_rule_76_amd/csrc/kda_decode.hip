@@ -398,34 +398,29 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
 // Rollback / commit: S[n, h] <- hist[n, j - 1, h] with j = accepted[n]
 // capped at ntok; j <= 0 leaves S[n, h] as it is.  One workgroup per
 // (sequence, head), float4 copies.
+template <int D>
 __global__ __launch_bounds__(256) void commit_kernel(float *__restrict__ S, const float *__restrict__ hist,
-                                                     const int32_t *__restrict__ accepted, int ntok, int H,
-                                                     int dd) {
+                                                     const int32_t *__restrict__ accepted, int ntok, int H) {
+  constexpr int N4 = D * D / 4;                      // 16-byte pieces of one state
+  constexpr int U = N4 >= 256 ? N4 / 256 : 1;        // pieces per lane
   const int64_t nh = (int64_t)blockIdx.x;
   const int64_t n = nh / H, h = nh % H;
   int j = accepted[n];
   if (j <= 0) return;
   if (j > ntok) j = ntok;
-  const f32x4 *src = reinterpret_cast<const f32x4 *>(hist + ((n * ntok + (j - 1)) * H + h) * (int64_t)dd);
-  f32x4 *dst = reinterpret_cast<f32x4 *>(S + nh * (int64_t)dd);
-  // Sixteen 16-byte loads per lane in flight before the stores.  The
-  // history is read once, with non-temporal loads (132 -> 124 us at B=256,
-  // two tokens); non-temporal stores of S measured slower (150 us).
-  constexpr int U = 16;
-  const int n4 = dd / 4;
-  for (int b = 0; b < n4; b += 256 * U) {
-    f32x4 x[U];
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(hist + ((n * ntok + (j - 1)) * H + h) * (int64_t)(D * D));
+  f32x4 *dst = reinterpret_cast<f32x4 *>(S + nh * (int64_t)(D * D));
+  // All of a lane's loads in flight before the stores (the trip counts are
+  // compile-time, so no guard or loop sits between them to force a wait).
+  // The history is read once, with non-temporal loads (132 -> 124 us at
+  // B=256, two tokens); non-temporal stores of S measured slower (150 us).
+  const int t = (int)threadIdx.x;
+  if (N4 < 256 && t >= N4) return;
+  f32x4 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = b + u * 256 + (int)threadIdx.x;
-      if (i < n4) x[u] = __builtin_nontemporal_load(src + i);
-    }
+  for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(src + u * 256 + t);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = b + u * 256 + (int)threadIdx.x;
-      if (i < n4) dst[i] = x[u];
-    }
-  }
+  for (int u = 0; u < U; ++u) dst[u * 256 + t] = x[u];
 }
 
 // Template dispatch on head size, q/k/v dtype, gate kind and input form: f
@@ -525,8 +520,26 @@ hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void 
 hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, const int32_t *accepted,
                          hipStream_t stream) {
   const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
-  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, S, hist, accepted, s.seq_len,
-                     s.num_heads, s.d_k * s.d_v);
+  switch (s.d_k) {
+    case 16:
+      hipLaunchKernelGGL(commit_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, S, hist, accepted,
+                         s.seq_len, s.num_heads);
+      break;
+    case 32:
+      hipLaunchKernelGGL(commit_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, S, hist, accepted,
+                         s.seq_len, s.num_heads);
+      break;
+    case 64:
+      hipLaunchKernelGGL(commit_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, S, hist, accepted,
+                         s.seq_len, s.num_heads);
+      break;
+    case 128:
+      hipLaunchKernelGGL(commit_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, S, hist, accepted,
+                         s.seq_len, s.num_heads);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
