@@ -12,9 +12,12 @@ set in the 256 MB Infinity Cache.  W untimed steps, then K steps between
 two synchronisations timed with HIP events on the launch stream.
 
 Prints one JSON line: the prefill rate as ``value``; per-call median and
-p10/p90; the roofline of the dominant kernel (algorithmic bytes per launch
-over its event-timed duration; ``traffic`` from the committed hardware
-counter summary when it was taken on the current kernel source); the decode
+p10/p90; the roofline of the dominant kernel (the layer's algorithmic bytes,
+1,796 per token and head, times the token-heads of one call, over that
+kernel's event-timed duration; ``traffic`` from the committed hardware
+counter summary when it was taken on the current kernel source); the
+matrix-core rate of the call (issued, from the committed counter summary of
+the same source, and useful); the decode
 rate (B=256, H=32, d=128, 100 in-place steps) with its own roofline; and the
 fp64 CPU oracle timed on the host over the whole prefill_4k workload.
 
@@ -47,6 +50,12 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_prefill_4k.json")
 KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_prefill.hip")
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_decode_b256.json")
 DECODE_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_decode.hip")
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_prefill_4k.json")
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+# Useful matrix work of the chunked form per token and head at d = 128, C = 64:
+# the decayed Gram blocks, the triangular transform and the state products
+# counted once (no precision split), 139,264 flop.
+USEFUL_FLOP_PER_TOKEN_HEAD = 139264
 COPY_BYTES = 256 << 20         # --calibrate-copy: bytes read (and written) by the copy
 
 WORKLOAD_TEXT = {
@@ -211,8 +220,10 @@ def bench_decode(B, dev, gate="channel", form="final"):
 def bench_verify(B, K, dev, steps=50):
     """Speculative verification of K tokens per sequence (the next token and
     K - 1 drafts): kda_decode_tokens with the state history, then
-    kda_state_commit of a seeded accepted count per sequence.  Returns the
-    per-call times of both."""
+    kda_state_commit of a seeded accepted count per sequence.  Each figure is
+    one event pair around ``steps`` back-to-back calls on the launch stream:
+    verify + commit pairs (the step rate), then verify alone, then commit
+    alone (the per-kernel times)."""
     from gated_delta_rule_76_amd import inputs, kda
     spec = inputs.WORKLOADS["decode_b256"]
     H, D = spec["H"], spec["D"]
@@ -230,23 +241,27 @@ def bench_verify(B, K, dev, steps=50):
     accepted = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev)
     run = lambda t: kda.decode_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, keep_states=True,
                                       out=o, states=hist)
+    commit = lambda: kda.state_commit(S, hist, accepted)
     for i in range(5):
         run(sets[i % N_SETS])
-        kda.state_commit(S, hist, accepted)
+        commit()
     torch.cuda.synchronize()
-    ev = [_events() for _ in range(steps)]
-    ec = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        run(sets[i % N_SETS])
-        ev[i][1].record()
-        kda.state_commit(S, hist, accepted)
-        ec[i].record()
-    torch.cuda.synchronize()
-    vt = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    ct = float(np.mean([ev[i][1].elapsed_time(ec[i]) for i in range(steps)]))
+
+    def timed(body):
+        e0, e1 = _events()
+        e0.record()
+        for i in range(steps):
+            body(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    pair = timed(lambda i: (run(sets[i % N_SETS]), commit()))
+    vt = timed(lambda i: run(sets[i % N_SETS]))
+    ct = timed(lambda i: commit())
     n_acc = int((accepted > 0).sum())
-    return {"B": B, "K": K, "H": H, "verify_ms": vt, "commit_ms": ct, "committed_seqs": n_acc}
+    return {"B": B, "K": K, "H": H, "step_ms": pair, "verify_ms": vt, "commit_ms": ct,
+            "committed_seqs": n_acc}
 
 
 def bench_backward(name, dev, steps=10):
@@ -285,7 +300,7 @@ def verify_summary(vf):
     B, K, H = vf["B"], vf["K"], vf["H"]
     gbs = B * H * verify_bytes(K) / (vf["verify_ms"] * 1e-3) / 1e9
     return {"metric": "speculative verify steps/s (B=%d, %d tokens per sequence, H=32, d=128)" % (B, K),
-            "value": 1e3 / (vf["verify_ms"] + vf["commit_ms"]), "unit": "steps/s",
+            "value": 1e3 / vf["step_ms"], "unit": "steps/s", "step_ms": vf["step_ms"],
             "verify_ms": vf["verify_ms"], "commit_ms": vf["commit_ms"],
             "tokens_per_s": B * K / (vf["verify_ms"] * 1e-3),
             "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel", "achieved": gbs,
@@ -513,27 +528,72 @@ def _traffic(kernel, workload, summary=None, source=None):
     return k["fetch_bytes"] + k["write_bytes"]
 
 
-def prefill_summary(pf, gate):
-    """Rate, per-kernel algorithmic bandwidth and the dominant kernel's
-    roofline of one bench_prefill result."""
+def _mfma_issued(workload):
+    """Issued matrix-core flops per prefill call from the committed counter
+    summary, per kernel, or None when it is missing or was taken on other
+    kernel source."""
+    try:
+        with open(MFMA_SUMMARY) as f:
+            t = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sha or t.get("workload") != workload:
+        return None
+    return {k: v["issued_flop"] for k, v in t.get("kernels", {}).items()}
+
+
+def prefill_summary(pf, gate, workload=None):
+    """Rate, the dominant kernel's roofline and the matrix-core figures of
+    one bench_prefill result.
+
+    ``roofline`` follows the layer's algorithmic bytes: 1,796 bytes per token
+    and head (q, k, v, alpha, beta read, o written; 1,288 with one alpha per
+    head) times the token-heads of one call, over the dominant kernel's
+    event-timed duration.  ``kernels`` gives each kernel's time and the
+    bytes it moves itself, its workspace record included.  ``mfma`` gives the
+    issued matrix-core rate (counters) and the useful one (139,264 flop per
+    token and head) over the call, and the call's rate against the lower of
+    the HBM and matrix-core ceilings."""
     th = pf["total_tokens"] * pf["H"]
     kb = kernel_bytes(pf["D"], gate)
     times = {"chunk_local_kernel": pf["phases_ms"]["chunk_local"],
              "chunk_state_kernel": pf["phases_ms"]["state_pass"]}
     dom = max(times, key=times.get)
-    gbs = {k: th * kb[k] / (times[k] * 1e-3) / 1e9 for k in times}
+    own = {k: th * kb[k] / (times[k] * 1e-3) / 1e9 for k in times}
     lb = layer_bytes(gate)
+    alg = th * lb / (times[dom] * 1e-3) / 1e9
     layer_gbs = th * lb / (pf["ms"] * 1e-3) / 1e9
-    return {"value": pf["total_tokens"] / (pf["ms"] * 1e-3), "unit": "tokens/s/layer",
+    value = pf["total_tokens"] / (pf["ms"] * 1e-3)
+    issued = _mfma_issued(workload) if workload is not None and gate == "channel" else None
+    hbm_ceiling = HBM_PEAK_GBS * 1e9 / (lb * pf["H"])
+    mf = {"peak_tflops": MFMA_PEAK_TFLOPS, "useful_flop_per_token_head": USEFUL_FLOP_PER_TOKEN_HEAD,
+          "useful_tflops": th * USEFUL_FLOP_PER_TOKEN_HEAD / (pf["ms"] * 1e-3) / 1e12,
+          "issued_tflops": None, "issued_frac": None, "issued_flop_per_token_head": None,
+          "counters": None}
+    mf["useful_frac"] = mf["useful_tflops"] / MFMA_PEAK_TFLOPS
+    ceiling = hbm_ceiling
+    if issued is not None and all(k in issued for k in times):
+        per_call = sum(issued[k] for k in times)
+        mf["issued_flop_per_token_head"] = per_call / th
+        mf["issued_tflops"] = per_call / (pf["ms"] * 1e-3) / 1e12
+        mf["issued_frac"] = mf["issued_tflops"] / MFMA_PEAK_TFLOPS
+        mf["counters"] = os.path.relpath(MFMA_SUMMARY, ROOT)
+        ceiling = min(hbm_ceiling, MFMA_PEAK_TFLOPS * 1e12 / (per_call / th * pf["H"]))
+    mf["ceiling_tokens_per_s"] = ceiling
+    mf["frac_of_ceiling"] = value / ceiling
+    return {"value": value, "unit": "tokens/s/layer",
             "ms_per_step": pf["ms"],
-            "roofline": {"bound": "hbm", "kernel": dom, "achieved": gbs[dom], "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": gbs[dom] / HBM_PEAK_GBS, "traffic": None,
-                         "launch_ms": times[dom], "bytes_per_token_head": kb[dom]},
-            "kernels": {k: {"ms": times[k], "bytes_per_token_head": kb[k], "achieved_gbs": gbs[k]}
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": alg, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": alg / HBM_PEAK_GBS, "traffic": None,
+                         "launch_ms": times[dom], "bytes_per_token_head": lb},
+            "kernels": {k: {"ms": times[k], "own_bytes_per_token_head": kb[k], "own_gbs": own[k]}
                         for k in times},
             "layer_roofline": {"bound": "hbm", "bytes_per_token_head": lb, "achieved": layer_gbs,
                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": layer_gbs / HBM_PEAK_GBS}}
+                               "frac": layer_gbs / HBM_PEAK_GBS},
+            "mfma": mf}
 
 
 def decode_summary(dc, gate, form="final"):
@@ -580,7 +640,7 @@ def main():
     print(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
     pf = bench_prefill(args.workload, args.steps, args.warmup, dev)
-    ps = prefill_summary(pf, "channel")
+    ps = prefill_summary(pf, "channel", args.workload)
     dom = ps["roofline"]["kernel"]
     ps["roofline"]["traffic"] = _traffic(dom, args.workload)
     out = {
@@ -602,6 +662,7 @@ def main():
         "roofline": ps["roofline"],
         "kernels": ps["kernels"],
         "layer_roofline": ps["layer_roofline"],
+        "mfma": ps["mfma"],
         "call_ms": pf["call_ms"],
     }
     if not args.no_decode:

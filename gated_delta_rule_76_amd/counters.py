@@ -20,6 +20,18 @@ of 256 MiB (the --calibrate-copy kernel, which reads and writes exactly
 that, in 16-byte accesses like the library's kernels) to its true size.
 The summary records the sha256 of the kernel source it was taken on;
 bench.py reports the traffic only while the source matches.
+
+Matrix-core work of the prefill kernels, from one counter run:
+
+    rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 -d DIR_M -o m \
+        --output-format csv -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline \
+        --no-decode --no-variants
+    python -m gated_delta_rule_76_amd.counters --mfma DIR_M/m_counter_collection.csv \
+        --workload prefill_4k > profiles/mfma_prefill_4k.json
+
+Each MOPS unit is 512 floating-point operations (one per multiply and one
+per add of the matrix product); the summary gives the issued flops per
+dispatch of each kernel, which bench.py divides by the event-timed call.
 """
 
 from __future__ import annotations
@@ -86,14 +98,52 @@ def summarize(fetch_csv, write_csv, workload, target="prefill"):
     return out
 
 
+FLOP_PER_MOP = 512
+
+
+def _raw_per_kernel(path, counter, kernels):
+    vals = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = None
+            for k in kernels:
+                if k in r["Kernel_Name"]:
+                    key = k
+            if key is not None:
+                vals[key].append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_mfma(csv_path, workload, target="prefill"):
+    source, kernels = TARGETS[target]
+    bf = _raw_per_kernel(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kernels)
+    f32 = _raw_per_kernel(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_F32", kernels)
+    with open(os.path.join(CSRC, source), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    out = {"workload": workload, "source_sha256": sha, "flop_per_mop": FLOP_PER_MOP, "kernels": {}}
+    for k in kernels:
+        if bf.get(k):
+            b = sum(bf[k]) / len(bf[k])
+            x = sum(f32[k]) / len(f32[k]) if f32.get(k) else 0.0
+            out["kernels"][k] = {"dispatches": len(bf[k]), "mops_bf16": b, "mops_f32": x,
+                                 "issued_flop": (b + x) * FLOP_PER_MOP}
+    return out
+
+
 def main():
     p = argparse.ArgumentParser()
-    p.add_argument("fetch_csv")
-    p.add_argument("write_csv")
+    p.add_argument("csv", nargs="+", help="FETCH_SIZE and WRITE_SIZE csv files, or with --mfma the "
+                                          "MFMA counter csv")
+    p.add_argument("--mfma", action="store_true")
     p.add_argument("--workload", default="prefill_4k")
     p.add_argument("--target", default="prefill", choices=sorted(TARGETS))
     a = p.parse_args()
-    print(json.dumps(summarize(a.fetch_csv, a.write_csv, a.workload, a.target), indent=1))
+    if a.mfma:
+        print(json.dumps(summarize_mfma(a.csv[0], a.workload, a.target), indent=1))
+    else:
+        print(json.dumps(summarize(a.csv[0], a.csv[1], a.workload, a.target), indent=1))
 
 
 if __name__ == "__main__":

@@ -3,6 +3,8 @@
 // contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
+
 #include "kda.h"
 #include "kda_internal.h"
 
@@ -53,7 +55,12 @@ extern "C" {
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 const char *kda_status_string(kda_status_t status) {
-  switch (status) {
+  // A C caller may pass any int.  Reading a value outside the enumerators as
+  // kda_status_t is undefined in C++, so the argument is read as an int.
+  int code;
+  static_assert(sizeof(code) == sizeof(status), "kda_status_t is int-sized");
+  std::memcpy(&code, &status, sizeof code);
+  switch (code) {
     case KDA_OK: return "KDA_OK";
     case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
@@ -94,7 +101,8 @@ kda_status_t check_prefill_call(const kda_shape_t *shape, const void *q, const v
         (need_beta && !aligned4(beta)) || (need_o && !aligned16(o)))
       return KDA_ERR_INVALID_ARGUMENT;
   }
-  if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T)) || (cu_seqlens && !aligned16(cu_seqlens)))
+  // cu_seqlens is read one int32 at a time: 4-byte alignment, as for kda_backward.
+  if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T)) || (cu_seqlens && !aligned4(cu_seqlens)))
     return KDA_ERR_INVALID_ARGUMENT;
   if (shape->num_seqs == 0) return has_tokens ? KDA_ERR_INVALID_ARGUMENT : KDA_OK;
   const size_t need = kda::prefill_workspace_bytes(*shape);

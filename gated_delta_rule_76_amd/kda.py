@@ -14,7 +14,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkda.so")
+# KDA_LIBRARY may name another build of the same sources (the ABI tests use
+# the host-sanitized build, lib/libkda_hostsan.so).
+_LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "lib", "libkda.so")
 
 KDA_OK = 0
 KDA_ERR_INVALID_ARGUMENT = 1
@@ -130,6 +133,13 @@ def _require_gpu(name, t, dtype=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _require_shape(name, t, shape):
+    """Outputs the caller supplies must have exactly the shape the call
+    writes: a smaller buffer would be written past its end on the device."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def make_shape(num_seqs, seq_len, total_tokens, num_heads, d, dtype, gate=KDA_GATE_CHANNEL,
                input_form=KDA_INPUT_FINAL):
     return KdaShape(int(num_seqs), int(seq_len), int(total_tokens), int(num_heads), int(d), int(d),
@@ -200,11 +210,13 @@ class PrefillCall:
                                 KDA_INPUT_PREACT if preact else KDA_INPUT_FINAL)
         self.o = out if out is not None else torch.empty(v.shape, dtype=torch.float32, device=dev)
         _require_gpu("out", self.o, torch.float32)
+        _require_shape("out", self.o, v.shape)
         self.S_T = None
         if output_final_state:
             self.S_T = (final_state if final_state is not None
                         else torch.empty((N, H, D, D), dtype=torch.float32, device=dev))
             _require_gpu("final_state", self.S_T, torch.float32)
+            _require_shape("final_state", self.S_T, (N, H, D, D))
         need = prefill_workspace_size(N, total, H, D, q.dtype)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -284,6 +296,7 @@ def decode_step(q, k, v, alpha, beta, state, out=None, preact=False):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
     o = out if out is not None else torch.empty((N, H, D), dtype=torch.float32, device=q.device)
     _require_gpu("out", o, torch.float32)
+    _require_shape("out", o, (N, H, D))
     shape = make_shape(N, 1, N, H, D, q.dtype, gate, KDA_INPUT_PREACT if preact else KDA_INPUT_FINAL)
     st = lib().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(state), _ptr(o), _stream(q.device))
@@ -319,6 +332,7 @@ def decode_tokens(q, k, v, alpha, beta, state, keep_states=False, preact=False, 
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
     o = out if out is not None else torch.empty((N, K, H, D), dtype=torch.float32, device=q.device)
     _require_gpu("out", o, torch.float32)
+    _require_shape("out", o, (N, K, H, D))
     hist = None
     if keep_states:
         hist = states if states is not None else torch.empty((N, K, H, D, D), dtype=torch.float32,

@@ -26,7 +26,10 @@
  * Conventions shared by every entry point
  * ----------------------------------------
  *  - Tensor arguments are DEVICE pointers to contiguous, row-major arrays
- *    on the current HIP device, aligned to 16 bytes (beta: 4 bytes).
+ *    on the current HIP device, aligned to 16 bytes, except beta,
+ *    cu_seqlens, accepted and a per-head alpha (KDA_GATE_HEAD), which need
+ *    4 bytes (they are read one element at a time), and the workspace,
+ *    which needs 256 bytes.  The same rule holds for every entry point.
  *    Layouts are token-major:
  *        q, k          [tokens][H][d_k]
  *        alpha         [tokens][H][d_k]  (KDA_GATE_CHANNEL)
@@ -206,9 +209,10 @@ kda_status_t kda_decode_step(const kda_shape_t *shape,
                              void *stream);
 
 /* Several new tokens per sequence from the live state: speculative
- * verification of drafted tokens (the ainewsfeed.tech page on the
- * GLM-5.3-Flash architecture stack: one MTP draft layer, drafted tokens
- * checked in parallel, rejected ones rolled back), or plain multi-token
+ * verification of drafted tokens (the kongchang.com page "18B Active for
+ * Just $0.045: How GLM-5.3-Flash Beat Claude with Hybrid Attention", section
+ * "The Architecture Stack: How Linear and Sparse Interleave": one MTP draft
+ * layer; drafted tokens checked in parallel, rejected ones rolled back), or plain multi-token
  * decode.  Each token is one step of the update rule, in order; the state
  * is read once and kept in registers across a sequence's tokens.
  *   shape       num_seqs = N, seq_len = k >= 1 tokens per sequence,

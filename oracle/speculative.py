@@ -3,8 +3,11 @@ state kept for rollback (speculative verification), fp64.
 
 TEST INFRASTRUCTURE (see the package docstring): the HIP path never uses it.
 
-Source.  The ainewsfeed.tech page on the GLM-5.3-Flash architecture stack
-(the passage on speculative decoding and the one MTP draft layer) describes
+Source.  The kongchang.com page "18B Active for Just $0.045: How
+GLM-5.3-Flash Beat Claude with Hybrid Attention", section "The Architecture
+Stack: How Linear and Sparse Interleave" (the fifth item of its list, one MTP
+draft layer for speculative decoding, and the paragraph on speculative
+decoding after it) describes
 the scheme: a draft proposes several tokens, the target model checks them
 in parallel, accepted tokens are kept and the rest are rolled back.  For a
 recurrent layer the reading is: run the k proposed tokens of each sequence

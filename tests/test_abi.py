@@ -251,3 +251,27 @@ def test_binding_refuses_cpu_tensors():
         kda.prefill(x, x, x, x, torch.zeros(4, 2))
     with pytest.raises(ValueError, match="GPU"):
         kda.decode_step(x, x, x, x, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))
+
+
+def test_cu_seqlens_alignment_is_four_bytes_everywhere(L):
+    """cu_seqlens is read one int32 at a time: every entry point that takes
+    it accepts a 4-byte aligned pointer (e.g. a view starting at element 1)
+    and rejects a 2-byte aligned one."""
+    s = kda.KdaShape(2, 0, 64, 2, 16, 16, 0)
+    need = kda.prefill_workspace_size(2, 64, 2, 16, torch.float32)
+    # accepted: the call reaches the workspace check
+    assert prefill(L, s, cu=FAKE + 4, ws_bytes=need - 1) == WS_SMALL
+    assert prefill(L, s, cu=FAKE + 2, ws_bytes=need - 1) == INVALID
+    sp = ctypes.byref(s)
+    assert L.kda_prefill_chunk_local(sp, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, need - 1, None) == WS_SMALL
+    assert L.kda_prefill_chunk_local(sp, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, need - 1, None) == INVALID
+    assert L.kda_prefill_state_pass(sp, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None, FAKE, None, FAKE, need - 1,
+                                    None) == WS_SMALL
+    assert L.kda_prefill_state_pass(sp, FAKE, FAKE, FAKE, FAKE, FAKE + 2, None, FAKE, None, FAKE, need - 1,
+                                    None) == INVALID
+    out = ctypes.c_size_t(0)
+    assert L.kda_backward_workspace_size(sp, ctypes.byref(out)) == OK
+    bw = lambda cu: L.kda_backward(sp, FAKE, FAKE, FAKE, FAKE, FAKE, cu, None, FAKE, None, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, None, FAKE, out.value - 1, None)
+    assert bw(FAKE + 4) == WS_SMALL
+    assert bw(FAKE + 2) == INVALID

@@ -61,3 +61,23 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_prefill_roofline_uses_the_layer_bytes():
+    """roofline.achieved = 1,796 B per token-head x token-heads of one call /
+    the dominant kernel's time; the kernels' own record traffic is reported
+    separately."""
+    pf = {"total_tokens": 4096, "H": 32, "D": 128, "ms": 0.25,
+          "phases_ms": {"chunk_local": 0.10, "state_pass": 0.14}}
+    s = bench.prefill_summary(pf, "channel")
+    r = s["roofline"]
+    assert r["kernel"] == "chunk_state_kernel" and r["bytes_per_token_head"] == 1796
+    assert abs(r["achieved"] - 4096 * 32 * 1796 / 0.14e-3 / 1e9) < 1e-6
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-12
+    assert s["kernels"]["chunk_state_kernel"]["own_bytes_per_token_head"] == bench.kernel_bytes(128)[
+        "chunk_state_kernel"]
+    m = s["mfma"]
+    assert abs(m["useful_tflops"] - 4096 * 32 * 139264 / 0.25e-3 / 1e12) < 1e-9
+    # without a counter summary for the source, the issued rate is not reported
+    assert m["issued_tflops"] is None
+    assert abs(m["ceiling_tokens_per_s"] - 8e12 / (1796 * 32)) < 1e-3

@@ -16,7 +16,8 @@ import torch
 from gated_delta_rule_76_amd import inputs, kda
 from oracle import rel_l2
 from oracle.prologue import decode_step_from_preact, recurrent_from_preact
-from tests.gpu_util import device, np64, seeded_sample
+from tests.gpu_util import device, np64, parity, seeded_sample
+from tests.oracle_pool import per_head
 
 pytestmark = pytest.mark.gpu
 
@@ -30,9 +31,8 @@ def _oracle(d, heads=None, cu=None, S0=None):
                                  np64(sel(d["alpha"])), np64(sel(d["beta"])), S0, cu_seqlens=cu)
 
 
-def _check(o, ST, ro, rST, tol, what):
-    eo, es = rel_l2(np64(o), ro), rel_l2(np64(ST), rST)
-    assert eo < tol and es < tol, f"{what}: o {eo:.3e}  S_T {es:.3e}  (tol {tol})"
+def _check(o, ST, ro, rST, tol, what, cu=None):
+    parity(o, ST, ro, rST, tol, what, cu)
 
 
 @pytest.mark.parametrize("gate", ["channel", "head"])
@@ -57,8 +57,9 @@ def test_preact_varlen_ragged_and_empty(gate, dtype):
                               form="preact")
     o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"],
                         preact=True)
-    ro, rST = _oracle(d, cu=np.asarray(d["cu_seqlens"].cpu()), S0=np64(d["S0"]))
-    _check(o, ST, ro, rST, TOL[dtype], "varlen")
+    cu = np.asarray(d["cu_seqlens"].cpu())
+    ro, rST = _oracle(d, cu=cu, S0=np64(d["S0"]))
+    _check(o, ST, ro, rST, TOL[dtype], "varlen", cu)
     assert torch.equal(ST[0], d["S0"][0]) and torch.equal(ST[6], d["S0"][6])
 
 
@@ -105,15 +106,14 @@ def test_preact_matches_activated_form():
 @pytest.mark.parametrize("gate", ["channel", "head"])
 def test_preact_prefill_4k_workload(gate):
     """B=1, H=32, T=4096, d=128, bf16 raw q/k, a = N(0,1) + 2, b = N(0,1):
-    a seeded sample of 6 heads over all 4096 tokens."""
+    o of every token and head and every S_T."""
     dev = device()
     spec = inputs.WORKLOADS["prefill_4k"]
     d = inputs.prefill_inputs(spec["lengths"], spec["H"], spec["D"], torch.bfloat16, "strong", None,
                               seed=0, device=dev, gate=gate, form="preact")
     o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], preact=True)
-    heads = seeded_sample(spec["H"], 6, seed=5)
-    ro, rST = _oracle(d, heads=heads)
-    _check(o[:, heads], ST[:, heads], ro, rST, 2e-3, f"preact prefill_4k {gate}")
+    ro, rST = per_head(recurrent_from_preact, *(np64(d[x]) for x in ("q", "k", "v", "alpha", "beta")))
+    _check(o, ST, ro, rST, 2e-3, f"preact prefill_4k {gate}")
 
 
 @pytest.mark.parametrize("gate", ["channel", "head"])

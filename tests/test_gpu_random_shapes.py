@@ -3,11 +3,12 @@
 Each case draws the sequence count and lengths (around the 64-token chunk
 edges and up to 300 tokens, empty sequences included), heads, head size,
 q/k/v dtype, gate kind, input form, decay regime and initial state, then
-checks prefill (o and S_T), the backward pass (all six gradients) or
+checks prefill (o and S_T, rel-L2 over each whole tensor and over every
+(sequence, head) slice), the backward pass (rel-L2 per gradient) or
 multi-token verification (outputs, per-token states, live state untouched)
-element by element against the oracle, with the tolerances of the dedicated
+against the oracle on the same inputs, with the tolerances of the dedicated
 tests: 2e-3 (bf16 prefill), 1e-5 (fp32 prefill, verification), 2e-5
-(backward, rel-L2 per gradient).
+(backward).
 """
 
 import random
@@ -20,7 +21,7 @@ from gated_delta_rule_76_amd import inputs, kda
 from oracle import gdn_recurrent, kda_recurrent, rel_l2, speculative
 from oracle.backward import kda_backward
 from oracle.prologue import recurrent_from_preact
-from tests.gpu_util import device, np64
+from tests.gpu_util import device, np64, parity
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +51,12 @@ def _prefill_case(rng, dev, D, H, dtype, decay, seed):
         ro, rS = (kda_recurrent if gate == "channel" else gdn_recurrent)(*args, cu_seqlens=cu)
     tol = 1e-5 if dtype == torch.float32 else 2e-3
     what = f"prefill lens={lens} {gate} {form} S0={s0}"
-    return [(what + " o", rel_l2(np64(o), ro), tol), (what + " S_T", rel_l2(np64(ST), rS), tol)]
+    try:
+        rep = parity(o, ST, ro, rS, tol, what, cu)
+    except AssertionError as e:
+        return [(str(e), float("inf"), tol)]
+    return [(what + " o, worst (seq, head)", rep["worst_o"][0], tol),
+            (what + " S_T, worst (seq, head)", rep["worst_S_T"][0], tol)]
 
 
 def _backward_case(rng, dev, D, H, dtype, decay, seed):

@@ -14,7 +14,8 @@ import torch
 
 from gated_delta_rule_76_amd import inputs, kda
 from oracle import gdn_decode_step, gdn_recurrent, rel_l2
-from tests.gpu_util import device, np64, seeded_sample
+from tests.gpu_util import device, np64, parity, seeded_sample
+from tests.oracle_pool import per_head
 
 pytestmark = pytest.mark.gpu
 
@@ -27,9 +28,8 @@ def _oracle(d, heads=None, cu=None, S0=None):
                          np64(sel(d["alpha"])), np64(sel(d["beta"])), S0, cu_seqlens=cu)
 
 
-def _check(o, ST, ro, rST, tol, what):
-    eo, es = rel_l2(np64(o), ro), rel_l2(np64(ST), rST)
-    assert eo < tol and es < tol, f"{what}: o {eo:.3e}  S_T {es:.3e}  (tol {tol})"
+def _check(o, ST, ro, rST, tol, what, cu=None):
+    parity(o, ST, ro, rST, tol, what, cu)
 
 
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
@@ -78,8 +78,9 @@ def test_scalar_gate_varlen_ragged_and_empty(dtype):
     lens = [0, 1, 63, 64, 65, 130, 0, 200]
     d = inputs.prefill_inputs(lens, 2, 64, dtype, "medium", 0.3, seed=23, device=dev, gate="head")
     o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
-    ro, rST = _oracle(d, cu=np.asarray(d["cu_seqlens"].cpu()), S0=np64(d["S0"]))
-    _check(o, ST, ro, rST, TOL[dtype], "varlen")
+    cu = np.asarray(d["cu_seqlens"].cpu())
+    ro, rST = _oracle(d, cu=cu, S0=np64(d["S0"]))
+    _check(o, ST, ro, rST, TOL[dtype], "varlen", cu)
     assert torch.equal(ST[0], d["S0"][0]) and torch.equal(ST[6], d["S0"][6])
 
 
@@ -100,15 +101,14 @@ def test_scalar_gate_zero_rate(dtype):
 
 def test_scalar_gate_prefill_4k_workload():
     """B=1, H=32, T=4096, d=128, bf16, alpha = exp(-softplus(N(0,1)+2)) per
-    (token, head): a seeded sample of 6 heads over all 4096 tokens."""
+    (token, head): o of every token and head and every S_T."""
     dev = device()
     spec = inputs.WORKLOADS["prefill_4k"]
     d = inputs.prefill_inputs(spec["lengths"], spec["H"], spec["D"], torch.bfloat16, "strong", None,
                               seed=0, device=dev, gate="head")
     o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
-    heads = seeded_sample(spec["H"], 6, seed=3)
-    ro, rST = _oracle(d, heads=heads)
-    _check(o[:, heads], ST[:, heads], ro, rST, 2e-3, "scalar-gate prefill_4k")
+    ro, rST = per_head(gdn_recurrent, *(np64(d[x]) for x in ("q", "k", "v", "alpha", "beta")))
+    _check(o, ST, ro, rST, 2e-3, "scalar-gate prefill_4k")
 
 
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
