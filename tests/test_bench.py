@@ -33,15 +33,19 @@ def test_kernel_bytes_follow_the_record_size():
 
 
 def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):
-    with open(bench.TRAFFIC_SUMMARY) as f:
-        summary = json.load(f)
-    k = summary["kernels"]["chunk_state_kernel"]
-    # the committed summary was taken on the committed kernel source
-    assert bench._traffic("chunk_state_kernel", "prefill_4k") == k["fetch_bytes"] + k["write_bytes"]
+    import hashlib
+    src = tmp_path / "kda_prefill.hip"
+    src.write_text("// a kernel source\n")
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    summary = tmp_path / "traffic.json"
+    summary.write_text(json.dumps({"workload": "prefill_4k", "source_sha256": sha, "kernels": {
+        "chunk_state_kernel": {"fetch_bytes": 3.0, "write_bytes": 4.0}}}))
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(summary))
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    assert bench._traffic("chunk_state_kernel", "prefill_4k") == 7.0
     assert bench._traffic("chunk_state_kernel", "varlen_8seq") is None
-    other = tmp_path / "kda_prefill.hip"
-    other.write_text("// another kernel source\n")
-    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(other))
+    assert bench._traffic("chunk_local_kernel", "prefill_4k") is None
+    src.write_text("// another kernel source\n")
     assert bench._traffic("chunk_state_kernel", "prefill_4k") is None
 
 
