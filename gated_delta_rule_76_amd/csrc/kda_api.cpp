@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -152,6 +153,66 @@ kda_status_t kda_prefill_state_pass(const kda_shape_t *shape, const void *q, con
                                     size_t workspace_bytes, void *stream) {
   return run_prefill(shape, q, k, v, alpha, nullptr, cu_seqlens, S0, o, S_T, workspace, workspace_bytes,
                      stream, kda::kPhaseState);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// kda_prefill_noalloc: kda_prefill with its workspace in a file-scope device
+// array, for callers that cannot allocate device memory.  Each GPU the
+// library runs on holds its own copy of the array (KDA_NOALLOC_WORKSPACE_BYTES)
+// until the process ends.  In host code `scratch` only names the symbol; its
+// device address on the current GPU comes from hipGetSymbolAddress, looked
+// up once per device and cached.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) unsigned char scratch[KDA_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device; null = not looked up
+
+hipError_t scratch_on_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & (kda::kWorkspaceAlign - 1)) != 0)
+      return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_prefill_noalloc(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                                 const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                                 const float *S0, float *o, float *S_T, void *stream) {
+  size_t need = 0;
+  kda_status_t st = kda_prefill_workspace_size(shape, &need);
+  if (st != KDA_OK) return st;
+  if (need > (size_t)KDA_NOALLOC_WORKSPACE_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  // Every argument check before the first HIP call (the workspace stands in
+  // with a placeholder of the scratch's size and alignment).
+  st = check_prefill_call(shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T,
+                          reinterpret_cast<const void *>(kda::kWorkspaceAlign),
+                          (size_t)KDA_NOALLOC_WORKSPACE_BYTES, true, true, true);
+  if (st != KDA_OK || shape->num_seqs == 0) return st;
+  void *ws = nullptr;
+  if (scratch_on_current_device(&ws) != hipSuccess) return KDA_ERR_LAUNCH;
+  hipError_t e = kda::launch_prefill(*shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, ws,
+                                     static_cast<hipStream_t>(stream), kda::kPhaseLocal | kda::kPhaseState);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -30,7 +30,8 @@ KDA_GATE_CHANNEL = 0
 KDA_GATE_HEAD = 1
 KDA_INPUT_FINAL = 0
 KDA_INPUT_PREACT = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
+NOALLOC_WORKSPACE_BYTES = 128 << 20   # KDA_NOALLOC_WORKSPACE_BYTES
 CHUNK = 64
 
 _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
@@ -86,6 +87,8 @@ def lib():
     L.kda_prefill.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kda_prefill_chunk_local.restype = ctypes.c_int
     L.kda_prefill_chunk_local.argtypes = [shp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kda_prefill_noalloc.restype = ctypes.c_int
+    L.kda_prefill_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_prefill_state_pass.restype = ctypes.c_int
     L.kda_prefill_state_pass.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kda_decode_step.restype = ctypes.c_int
@@ -173,7 +176,8 @@ class PrefillCall:
     and ``state_pass()`` are its two phases (run in that order)."""
 
     def __init__(self, q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
-                 output_final_state=True, workspace=None, out=None, final_state=None, preact=False):
+                 output_final_state=True, workspace=None, out=None, final_state=None, preact=False,
+                 allocate_workspace=True):
         for name, t in (("q", q), ("k", k), ("v", v)):
             _require_gpu(name, t)
         if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -217,15 +221,18 @@ class PrefillCall:
                         else torch.empty((N, H, D, D), dtype=torch.float32, device=dev))
             _require_gpu("final_state", self.S_T, torch.float32)
             _require_shape("final_state", self.S_T, (N, H, D, D))
-        need = prefill_workspace_size(N, total, H, D, q.dtype)
-        if workspace is None:
+        if workspace is None and allocate_workspace:
+            need = prefill_workspace_size(N, total, H, D, q.dtype)
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        _require_gpu("workspace", workspace)
+        if workspace is not None:
+            _require_gpu("workspace", workspace)
         self.workspace = workspace
         self.device = dev
         self._t = (q, k, v, alpha, beta, cu_seqlens, initial_state)
 
     def _ws(self):
+        if self.workspace is None:
+            return None, 0
         return _ptr(self.workspace), self.workspace.numel() * self.workspace.element_size()
 
     def run(self):
@@ -234,6 +241,15 @@ class PrefillCall:
         _check(lib().kda_prefill(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                  _ptr(beta), _ptr(cu), _ptr(S0), _ptr(self.o), _ptr(self.S_T), ws, nb,
                                  _stream(self.device)), "kda_prefill")
+        return self.o, self.S_T
+
+    def run_noalloc(self):
+        """kda_prefill_noalloc: the same call with the library's static
+        workspace (no workspace tensor is used or needed)."""
+        q, k, v, alpha, beta, cu, S0 = self._t
+        _check(lib().kda_prefill_noalloc(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                         _ptr(beta), _ptr(cu), _ptr(S0), _ptr(self.o), _ptr(self.S_T),
+                                         _stream(self.device)), "kda_prefill_noalloc")
         return self.o, self.S_T
 
     def chunk_local(self):
@@ -272,6 +288,18 @@ def prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
     return PrefillCall(q, k, v, alpha, beta, initial_state, cu_seqlens,
                        output_final_state=output_final_state, workspace=workspace, out=out,
                        final_state=final_state, preact=preact).run()
+
+
+def prefill_noalloc(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
+                    output_final_state=True, out=None, final_state=None, preact=False):
+    """``prefill`` through kda_prefill_noalloc: the library's static device
+    workspace instead of a workspace tensor (for callers that cannot allocate
+    device memory; shapes whose workspace exceeds NOALLOC_WORKSPACE_BYTES are
+    rejected).  Outputs are allocated here unless ``out`` / ``final_state``
+    are given."""
+    return PrefillCall(q, k, v, alpha, beta, initial_state, cu_seqlens,
+                       output_final_state=output_final_state, out=out, final_state=final_state,
+                       preact=preact, allocate_workspace=False).run_noalloc()
 
 
 def decode_step(q, k, v, alpha, beta, state, out=None, preact=False):

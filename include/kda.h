@@ -40,9 +40,11 @@
  *    q, k, v are fp32 or bf16 (shape->qkv_dtype); alpha, beta, state and o
  *    are always fp32.
  *  - The caller owns every buffer, including the prefill workspace.  The
- *    library allocates no device memory, keeps no mutable global state and
- *    never synchronises: every call only enqueues kernels on `stream` (a
- *    hipStream_t passed as void*; NULL = the default stream) and returns.
+ *    library allocates no device memory at run time and never synchronises:
+ *    every call only enqueues kernels on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream) and returns.  Its only global state
+ *    is the static scratch of kda_prefill_noalloc (a device array per GPU)
+ *    and that array's cached addresses.
  *    Calls on different streams may run concurrently.
  *  - Errors: every call returns a kda_status_t and never throws, aborts or
  *    prints.  Argument validation happens on the host before any HIP call,
@@ -66,7 +68,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 #define KDA_CHUNK 64 /* prefill chunk length (tokens); not a semantic parameter */
 
 typedef enum kda_status {
@@ -191,6 +193,32 @@ kda_status_t kda_prefill_state_pass(const kda_shape_t *shape,
                                     float *o, float *S_T,
                                     void *workspace, size_t workspace_bytes,
                                     void *stream);
+
+/* Prefill without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc).  Arguments, results and errors are those of
+ * kda_prefill; the workspace is a static device array of the library,
+ * KDA_NOALLOC_WORKSPACE_BYTES (128 MiB) on each GPU the library runs on,
+ * held from the library's first use on that GPU until the process ends.
+ *  - Shapes whose kda_prefill_workspace_size exceeds it are rejected with
+ *    KDA_ERR_WORKSPACE_TOO_SMALL before any HIP call (at d = 128 a record
+ *    is 108.5 KiB per 64-token chunk and head: e.g. one sequence of up to
+ *    2,367 tokens at 32 heads).
+ *  - The call allocates nothing: no hipMalloc, no allocating library call.
+ *    Its first call on a device looks up the array's address there
+ *    (hipGetSymbolAddress) and caches it.
+ *  - Every call on one GPU uses that GPU's one array, whose contents on
+ *    entry do not matter.  Calls that overlap in time on the same GPU (two
+ *    streams, or two host threads) race on it and give wrong results; order
+ *    them (one stream, or events). */
+#define KDA_NOALLOC_WORKSPACE_BYTES (128u << 20)
+kda_status_t kda_prefill_noalloc(const kda_shape_t *shape,
+                                 const void *q, const void *k, const void *v,
+                                 const float *alpha, const float *beta,
+                                 const int32_t *cu_seqlens,
+                                 const float *S0,
+                                 float *o, float *S_T,
+                                 void *stream);
 
 /* Decode: one new token for each of N sequences; every head state is read
  * once, advanced one step and written back in place.

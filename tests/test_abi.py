@@ -51,9 +51,9 @@ def decode(L, s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, o=FAKE):
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["kda_abi_version", "kda_backward", "kda_backward_workspace_size",
                                     "kda_decode_step", "kda_decode_tokens", "kda_prefill",
-                                    "kda_prefill_chunk_local", "kda_prefill_state_pass",
-                                    "kda_prefill_workspace_size", "kda_state_commit",
-                                    "kda_status_string"]
+                                    "kda_prefill_chunk_local", "kda_prefill_noalloc",
+                                    "kda_prefill_state_pass", "kda_prefill_workspace_size",
+                                    "kda_state_commit", "kda_status_string"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -62,7 +62,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.kda_abi_version() == 2
+    assert L.kda_abi_version() == 3
     names = [L.kda_status_string(i).decode() for i in range(5)]
     assert names == ["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                      "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_LAUNCH"]
@@ -275,3 +275,25 @@ def test_cu_seqlens_alignment_is_four_bytes_everywhere(L):
                                    FAKE, FAKE, None, FAKE, out.value - 1, None)
     assert bw(FAKE + 4) == WS_SMALL
     assert bw(FAKE + 2) == INVALID
+
+
+def test_prefill_noalloc_validation(L):
+    """kda_prefill_noalloc checks everything on the host before its first
+    HIP call: the same argument rules as kda_prefill, and shapes whose
+    workspace exceeds the static 128 MiB are rejected."""
+    def na(s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, cu=None, S0=None, o=FAKE, ST=FAKE):
+        return L.kda_prefill_noalloc(ctypes.byref(s) if s is not None else None, q, k, v, a, b, cu, S0, o, ST,
+                                     None)
+    assert kda.NOALLOC_WORKSPACE_BYTES == 128 << 20
+    assert na(None) == INVALID
+    assert na(shape(d=48)) == UNSUPPORTED
+    assert na(shape(), q=None) == INVALID
+    assert na(shape(), o=FAKE + 4) == INVALID
+    assert na(shape(), cu=FAKE + 2) == INVALID
+    assert na(shape(N=0, T=0)) == OK                               # nothing to do, no HIP call
+    # at d = 128, H = 32: 2,367 tokens fit (37 chunks x 32 heads x 108.5 KiB), 2,368 do not
+    fits = kda.KdaShape(1, 2367, 2367, 32, 128, 128, 1)
+    assert kda.prefill_workspace_size(1, 2367, 32, 128) <= kda.NOALLOC_WORKSPACE_BYTES
+    assert kda.prefill_workspace_size(1, 2368, 32, 128) > kda.NOALLOC_WORKSPACE_BYTES
+    assert na(kda.KdaShape(1, 2368, 2368, 32, 128, 128, 1)) == WS_SMALL
+    assert na(fits, q=FAKE + 2) == INVALID                         # rejected before any HIP call

@@ -1,0 +1,44 @@
+"""kda_prefill_noalloc (the library's static device workspace) against
+kda_prefill (a workspace the caller allocates), through the C ABI.
+
+Both entry points run the same kernels on the same inputs, so their outputs
+must be bit-identical.  Calls on one GPU share its static workspace, which
+keeps the previous call's contents: the calls here run in a row, each one
+smaller than the one before, and each is compared with the workspace entry
+point.
+"""
+
+import pytest
+import torch
+
+from gated_delta_rule_76_amd import inputs, kda
+from tests.gpu_util import device
+
+pytestmark = pytest.mark.gpu
+
+# (sequence lengths, heads, head size, q/k/v dtype): largest first
+CASES = [([900, 1000, 0, 100], 32, 128, torch.bfloat16),
+         ([700], 8, 128, torch.bfloat16),
+         ([64, 1, 0, 37], 2, 16, torch.float32)]
+
+
+def test_noalloc_equals_prefill_on_calls_in_a_row():
+    dev = device()
+    for i, (lens, H, D, dtype) in enumerate(CASES):
+        print(f"noalloc case {i}: lens={lens} H={H} D={D} {dtype}", flush=True)
+        d = inputs.prefill_inputs(lens, H, D, dtype, "strong", 0.1, seed=40 + i, device=dev)
+        args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
+        assert kda.prefill_workspace_size(len(lens), sum(lens), H, D) <= kda.NOALLOC_WORKSPACE_BYTES
+        o, S = kda.prefill_noalloc(*args)
+        ref_o, ref_S = kda.prefill(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o), f"case {i}: o differs"
+        assert torch.equal(S, ref_S), f"case {i}: S_T differs"
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_scratch():
+    dev = device()
+    T, H, D = 2368, 32, 128       # needs more than the 128 MiB static workspace
+    d = inputs.prefill_inputs([T], H, D, torch.bfloat16, "strong", None, seed=3, device=dev)
+    with pytest.raises(kda.KdaError, match="WORKSPACE_TOO_SMALL"):
+        kda.prefill_noalloc(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
