@@ -76,6 +76,9 @@ def _parse():
     p.add_argument("--no-variants", action="store_true",
                    help="skip the scalar-gate, pre-activation, verify and backward measurements")
     p.add_argument("--decode-batch", type=int, default=256)
+    p.add_argument("--bounded-workspace-mib", type=int, default=0,
+                   help="also time the prefill with a workspace of this many MiB (in stripes when "
+                        "less than the recommended size)")
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -131,6 +134,37 @@ def kernel_bytes(d, gate="channel"):
 
 def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_bounded(name, steps, warmup, dev, ws_bytes):
+    """The prefill of workload ``name`` with a workspace of ws_bytes (the
+    same inputs as bench_prefill's first set): ms per call over ``steps``
+    back-to-back calls, and the stripes that workspace takes."""
+    from gated_delta_rule_76_amd import inputs, kda
+    spec = inputs.WORKLOADS[name]
+    lens = inputs.workload_lengths(spec, seed=0)
+    H, D = spec["H"], spec["D"]
+    d = inputs.prefill_inputs(lens, H, D, torch.bfloat16, spec["decay"], spec["s0_std"], seed=0, device=dev)
+    cu = d["cu_seqlens"] if len(lens) > 1 else None
+    call = kda.PrefillCall(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], cu,
+                           workspace_bytes=ws_bytes)
+    for _ in range(warmup):
+        call.run()
+    e0, e1 = _events()
+    e0.record()
+    for _ in range(steps):
+        call.run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    N, total = len(lens), sum(lens)
+    table = -(-4 * (N + 1) // 256) * 256
+    chunk_bytes = H * kda.record_bytes(D)
+    W = (ws_bytes - table) // chunk_bytes          # S_T is written, so no carry area
+    need = total // 64 + N if cu is not None else N * -(-lens[0] // 64)
+    return {"workspace_bytes": ws_bytes, "chunks_per_stripe": int(min(W, need)),
+            "stripes": int(-(-need // min(W, need))), "ms": ms,
+            "value": total / (ms * 1e-3), "unit": "tokens/s/layer"}
 
 
 def bench_prefill(name, steps, warmup, dev, gate="channel", form="final"):
@@ -665,6 +699,10 @@ def main():
         "mfma": ps["mfma"],
         "call_ms": pf["call_ms"],
     }
+    if args.bounded_workspace_mib:
+        print(f"[bench] prefill with a {args.bounded_workspace_mib} MiB workspace", file=sys.stderr, flush=True)
+        out["bounded_workspace"] = bench_bounded(args.workload, args.steps, args.warmup, dev,
+                                                 args.bounded_workspace_mib << 20)
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         out["decode"] = decode_summary(bench_decode(args.decode_batch, dev), "channel")

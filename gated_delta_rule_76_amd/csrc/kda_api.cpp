@@ -42,8 +42,11 @@ kda_status_t check_prefill_shape(const kda_shape_t *s, bool varlen) {
   }
   if (s->d_k != s->d_v || !supported_dim(s->d_k)) return KDA_ERR_UNSUPPORTED;
   if (check_kinds(s) != KDA_OK) return check_kinds(s);
-  // Grid limits: one workgroup per (chunk, head) in the chunk-local kernel.
-  if (kda::max_chunks(*s) * (int64_t)s->num_heads >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  // Grid limit of the state pass: one workgroup per (sequence, head, 16 value
+  // columns), sequences and heads padded to multiples of 8.  (The
+  // chunk-local grid, N H W, is kept below 2^31 by the choice of W.)
+  if (((int64_t)s->num_seqs * s->num_heads + 7) / 8 * 8 * (s->d_v < 16 ? 1 : s->d_v / 16) >= ((int64_t)1 << 31))
+    return KDA_ERR_UNSUPPORTED;
   // The state pass addresses one chunk's rows of v and o with 32-bit offsets.
   if ((int64_t)kda::kChunk * s->num_heads * s->d_v * 4 >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
@@ -85,12 +88,15 @@ kda_status_t kda_prefill_workspace_size(const kda_shape_t *shape, size_t *bytes)
 namespace {
 
 // Validation shared by kda_prefill and its two phases.  `need_*` say which
-// pointers the call reads or writes.
+// pointers the call reads or writes; `one_stripe` asks for a workspace that
+// holds every chunk of the batch at once (the phase entry points, which need
+// the recommended size).
+// On success *plan is the stripe plan for the workspace.
 kda_status_t check_prefill_call(const kda_shape_t *shape, const void *q, const void *k, const void *v,
                                 const float *alpha, const float *beta, const int32_t *cu_seqlens,
                                 const float *S0, const float *o, const float *S_T,
                                 const void *workspace, size_t workspace_bytes, bool need_v,
-                                bool need_beta, bool need_o) {
+                                bool need_beta, bool need_o, bool one_stripe, kda::PrefillPlan *plan) {
   const bool varlen = cu_seqlens != nullptr;
   kda_status_t st = check_prefill_shape(shape, varlen);
   if (st != KDA_OK) return st;
@@ -106,8 +112,9 @@ kda_status_t check_prefill_call(const kda_shape_t *shape, const void *q, const v
   if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T)) || (cu_seqlens && !aligned4(cu_seqlens)))
     return KDA_ERR_INVALID_ARGUMENT;
   if (shape->num_seqs == 0) return has_tokens ? KDA_ERR_INVALID_ARGUMENT : KDA_OK;
-  const size_t need = kda::prefill_workspace_bytes(*shape);
-  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  *plan = kda::prefill_plan(*shape, varlen, S_T != nullptr, workspace_bytes);
+  if (plan->W <= 0 || (one_stripe && plan->stripes != 1)) return KDA_ERR_WORKSPACE_TOO_SMALL;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kda::kWorkspaceAlign - 1)) != 0)
     return KDA_ERR_INVALID_ARGUMENT;
   return KDA_OK;
@@ -119,10 +126,11 @@ kda_status_t run_prefill(const kda_shape_t *shape, const void *q, const void *k,
                          size_t workspace_bytes, void *stream, int phases) {
   const bool state = (phases & kda::kPhaseState) != 0;
   const bool local = (phases & kda::kPhaseLocal) != 0;
+  kda::PrefillPlan plan{};
   kda_status_t st = check_prefill_call(shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace,
-                                       workspace_bytes, state, local, state);
+                                       workspace_bytes, state, local, state, !(state && local), &plan);
   if (st != KDA_OK || shape->num_seqs == 0) return st;
-  hipError_t e = kda::launch_prefill(*shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace,
+  hipError_t e = kda::launch_prefill(*shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, plan,
                                      static_cast<hipStream_t>(stream), phases);
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
@@ -198,19 +206,17 @@ extern "C" {
 kda_status_t kda_prefill_noalloc(const kda_shape_t *shape, const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, const int32_t *cu_seqlens,
                                  const float *S0, float *o, float *S_T, void *stream) {
-  size_t need = 0;
-  kda_status_t st = kda_prefill_workspace_size(shape, &need);
-  if (st != KDA_OK) return st;
-  if (need > (size_t)KDA_NOALLOC_WORKSPACE_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
   // Every argument check before the first HIP call (the workspace stands in
-  // with a placeholder of the scratch's size and alignment).
-  st = check_prefill_call(shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T,
-                          reinterpret_cast<const void *>(kda::kWorkspaceAlign),
-                          (size_t)KDA_NOALLOC_WORKSPACE_BYTES, true, true, true);
+  // with a placeholder of the scratch's size and alignment); a shape whose
+  // one chunk per (sequence, head) does not fit is rejected.
+  kda::PrefillPlan plan{};
+  kda_status_t st = check_prefill_call(shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T,
+                                       reinterpret_cast<const void *>(kda::kWorkspaceAlign),
+                                       (size_t)KDA_NOALLOC_WORKSPACE_BYTES, true, true, true, false, &plan);
   if (st != KDA_OK || shape->num_seqs == 0) return st;
   void *ws = nullptr;
   if (scratch_on_current_device(&ws) != hipSuccess) return KDA_ERR_LAUNCH;
-  hipError_t e = kda::launch_prefill(*shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, ws,
+  hipError_t e = kda::launch_prefill(*shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, ws, plan,
                                      static_cast<hipStream_t>(stream), kda::kPhaseLocal | kda::kPhaseState);
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

@@ -39,13 +39,66 @@ inline int64_t max_chunks(const kda_shape_t &s) {
   return s.total_tokens / kChunk + (int64_t)s.num_seqs;
 }
 
-// Workspace layout: [chunk base table: (N+1) int32, padded to 256 B]
-//                   [records: max_chunks * H * record_bytes(d)]
+// Prefill workspace: [chunk table: (N+1) int32, padded to 256 B]
+//                    [records: W H, slot h W + c - j0]
+//                    [carry: N H d_k d_v floats, only if needed]
+// The chunks of the batch are numbered in packed order (sequence after
+// sequence; the table holds each sequence's first chunk, built on the device
+// for a varlen batch and implied by seq_len for a dense one).  The prefill
+// runs in stripes of W consecutive packed chunks: stripe i builds the records
+// of chunks j0 = iW .. j0+W-1, then the state pass carries the state of every
+// sequence with chunks in the stripe across them.  A sequence that continues
+// past the stripe leaves its state in S_T, or when S_T is NULL in the carry
+// area, for the next stripe.  So W follows from the workspace the caller
+// provides and the workspace need not grow with the context:
+//   recommended size  table + (floor(T/64) + N) H records: every chunk in
+//                     one stripe (the fastest; what the phase entry points
+//                     need)
+//   minimum size      table + H records (+ the carry area if S_T is NULL)
 inline size_t schedule_bytes(const kda_shape_t &s) {
   return align_up(sizeof(int32_t) * (size_t)(s.num_seqs + 1), kWorkspaceAlign);
 }
 inline size_t prefill_workspace_bytes(const kda_shape_t &s) {
   return schedule_bytes(s) + (size_t)max_chunks(s) * (size_t)s.num_heads * record_bytes(s.d_k);
+}
+inline size_t carry_bytes(const kda_shape_t &s) {
+  return align_up(sizeof(float) * (size_t)s.num_seqs * (size_t)s.num_heads * (size_t)s.d_k * (size_t)s.d_v,
+                  kWorkspaceAlign);
+}
+
+struct PrefillPlan {
+  int64_t chunks;    // packed chunks to cover (exact for a dense batch, an upper bound for varlen)
+  int64_t W;         // packed chunks per stripe (>= 1); 0 = the workspace is too small
+  int64_t stripes;   // ceil(chunks / W), at least 1
+  size_t carry_off;  // offset of the carry area in the workspace, or 0 = none (S_T carries)
+};
+
+inline PrefillPlan prefill_plan(const kda_shape_t &s, bool varlen, bool has_final_state,
+                                size_t workspace_bytes) {
+  PrefillPlan p{0, 0, 1, 0};
+  if (s.num_seqs <= 0 || s.num_heads <= 0) return p;
+  const int64_t per_seq = s.seq_len > 0 ? ((int64_t)s.seq_len + kChunk - 1) / kChunk : 0;
+  p.chunks = varlen ? max_chunks(s) : (int64_t)s.num_seqs * per_seq;
+  const int64_t need = p.chunks > 0 ? p.chunks : 1;
+  const size_t table = schedule_bytes(s);
+  const size_t rec = (size_t)s.num_heads * record_bytes(s.d_k);  // one packed chunk, all heads
+  // grid limit of the chunk-local kernel: W H < 2^31
+  const int64_t wmax = ((int64_t)1 << 31) / s.num_heads - 1;
+  auto fit = [&](size_t reserve) -> int64_t {
+    if (workspace_bytes < table + reserve) return 0;
+    int64_t w = (int64_t)((workspace_bytes - table - reserve) / rec);
+    return w < need ? (w < wmax ? w : wmax) : (need < wmax ? need : wmax);
+  };
+  int64_t W = fit(0);
+  if (W < need && !has_final_state) {  // several stripes: the carry needs room too
+    W = fit(carry_bytes(s));
+    p.carry_off = table + (size_t)W * rec;  // records are multiples of 256 B
+  }
+  if (W <= 0) return p;
+  p.W = W;
+  p.stripes = (need + W - 1) / W;
+  if (p.stripes == 1) p.carry_off = 0;
+  return p;
 }
 
 hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, const void *v,
@@ -103,9 +156,11 @@ hipError_t launch_backward(const kda_shape_t &s, const BwdArgs &a, hipStream_t s
 constexpr int kPhaseLocal = 1;
 constexpr int kPhaseState = 2;
 
+// Runs the stripes of `plan` (phases: both, or one of them for a one-stripe
+// plan).
 hipError_t launch_prefill(const kda_shape_t &s, const void *q, const void *k, const void *v,
                           const float *alpha, const float *beta, const int32_t *cu_seqlens,
                           const float *S0, float *o, float *S_T, void *workspace,
-                          hipStream_t stream, int phases);
+                          const PrefillPlan &plan, hipStream_t stream, int phases);
 
 }  // namespace kda

@@ -25,19 +25,24 @@
 // A tail chunk is padded with alpha = 1, beta = 0, q = k = v = 0, which is an
 // exact identity step.
 //
-// Three kernels:
+// Three kernels; the last two run per stripe of W consecutive chunks in
+// packed order (W follows from the workspace; with the recommended workspace
+// the whole batch is one stripe):
 //   schedule_kernel     varlen packing: chunk counts per sequence -> table
 //                       of first-chunk indices (exclusive scan).
-//   chunk_local_kernel  one workgroup per (chunk, head), fully parallel:
+//   chunk_local_kernel  one workgroup per (chunk of the stripe, head), fully
+//                       parallel:
 //                       A and M on the matrix cores, T by a blocked
 //                       triangular inverse, Ktil^T T and M T on the matrix
 //                       cores; writes the chunk's record (Khat, Qhat,
 //                       Ktil^T T, M T, Gamma_C as operand fragments).
 //   chunk_state_kernel  one workgroup per (sequence, head, 16 value
-//                       columns), sequential over the chunks of its
-//                       sequence: the state slice stays in registers (fp32)
-//                       across chunks; every product runs on the matrix
-//                       cores with operands streamed from the records.
+//                       columns), sequential over the sequence's chunks in
+//                       the stripe: the state slice stays in registers (fp32)
+//                       across chunks and is handed to the next stripe
+//                       through S_T (or a carry area); every product runs on
+//                       the matrix cores with operands streamed from the
+//                       records.
 //
 // Decay factors are formed as running products of alpha (never as exp of
 // differences of cumulative logs), so no factor exceeds 1 except 1/Gamma
@@ -281,10 +286,24 @@ __device__ __forceinline__ int find_seq(const int32_t *base, int N, int64_t c) {
 }
 
 
+
+// Packed chunks [first, first + count) of sequence n.
+__device__ __forceinline__ void seq_chunk_range(const int32_t *cu, const int32_t *base, int32_t seq_len, int n,
+                                                int64_t &first, int64_t &count) {
+  if (cu == nullptr) {
+    count = dense_chunks(seq_len);
+    first = (int64_t)n * count;
+  } else {
+    first = base[n];
+    count = (int64_t)base[n + 1] - first;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Chunk records: per (chunk, head), operand fragments in the order the state
-// pass consumes them.  Records are head-major (record h * max_chunks + c), so
-// the chunks one state-pass workgroup walks through are contiguous in memory.  A fragment is one 16-row x 32-column operand block of
+// pass consumes them.  Records are head-major (slot h W + c - j0 for packed
+// chunk c of the stripe that starts at j0), so the chunks one state-pass
+// workgroup walks through are contiguous in memory.  A fragment is one 16-row x 32-column operand block of
 // the matrix-core product (lane 16g+m holds row m, columns 8g..8g+7), 2 KiB:
 // for SplitBF16 the bf16 hi plane (lane l at byte 16 l) then the lo plane
 // (at 1024 + 16 l); for F32 eight floats per lane (at byte 32 l).
@@ -516,7 +535,8 @@ template <int D, typename TIn, typename P, int GATE, int FORM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void chunk_local_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ alpha,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
-    int64_t total_tokens, int64_t max_chunks, const int32_t *__restrict__ base, char *__restrict__ recs) {
+    int64_t total_tokens, int64_t W, int64_t j0, const int32_t *__restrict__ base,
+    char *__restrict__ recs) {
   using Cf = LocCfg<D>;
   using Rc = Rec<D>;
   using IO = FragIO<P>;
@@ -537,19 +557,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
   float *s_Yw = s_M + C * LP + 256 * wave;
-  const int64_t c = (int64_t)(blockIdx.x / H);
-  const int h = blockIdx.x % H;
-  int64_t nchunks, cfirst;  // chunks of the batch; first chunk of this sequence
+  // Work item: head h, packed chunk c = j0 + j of the stripe.
+  const int h = (int)(blockIdx.x % (unsigned)H);
+  const int64_t j = (int64_t)(blockIdx.x / (unsigned)H);
+  const int64_t c = j0 + j;
+  if (total_tokens <= 0) return;
   int n;
+  int64_t cfirst;  // first packed chunk of sequence n
   if (cu == nullptr) {
     const int64_t cps = dense_chunks(seq_len);
-    nchunks = (int64_t)N * cps < max_chunks ? (int64_t)N * cps : max_chunks;
-    if (c >= nchunks || total_tokens <= 0) return;
+    if (c >= (int64_t)N * cps) return;
     n = (int)(c / cps);
     cfirst = n * cps;
   } else {
-    nchunks = base[N] < max_chunks ? (int64_t)base[N] : max_chunks;
-    if (c >= nchunks || total_tokens <= 0) return;
+    if (c >= (int64_t)base[N]) return;
     n = find_seq(base, N, c);
     cfirst = base[n];
   }
@@ -558,7 +579,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
   const ChunkTok ct = chunk_tokens(sstart, slen, c - cfirst, total_tokens);
   const int64_t t0 = ct.t0;
   const int nvalid = ct.valid;
-  char *rec = recs + ((size_t)h * max_chunks + c) * Rc::BYTES;
+  char *rec = recs + ((size_t)h * W + j) * Rc::BYTES;
 
   // ---- loads: token 16 w + m, channels kb*32 + 8g .. +7 (rows past the
   // chunk and channels past d are padding: k = q = 0, alpha = 1) ------------
@@ -1062,9 +1083,8 @@ __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec,
 template <int D, typename TIn, typename P>
 __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_state_kernel(
     const TIn *__restrict__ v, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
-    int64_t total_tokens, int64_t max_chunks, const int32_t *__restrict__ base,
-    const char *__restrict__ recs, const float *__restrict__ S0, float *__restrict__ o,
-    float *__restrict__ S_T) {
+    int64_t total_tokens, int64_t W, int64_t j0, const int32_t *__restrict__ base,
+    const char *__restrict__ recs, const float *S0, float *carry, float *__restrict__ o, float *S_T) {
   using Cf = ScanCfg<D>;
   using Rc = Rec<D>;
   using IO = FragIO<P>;
@@ -1091,26 +1111,40 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   const int n = (int)(pair / H), h = (int)(pair % H);
   const int col0 = VW * cg;
 
+  // The sequence's packed chunks in this stripe, [lo, hi).  A sequence with
+  // none there has nothing to do, except that the first stripe gives an
+  // empty sequence S_T = S0.
+  int64_t first, count;
+  seq_chunk_range(cu, base, seq_len, n, first, count);
+  if (total_tokens <= 0) count = 0;
+  const int64_t lo = first > j0 ? first : j0;
+  const int64_t hi = first + count < j0 + W ? first + count : j0 + W;
+  if (!(lo < hi || (count == 0 && j0 == 0))) return;
+  // the state comes from S0 if the sequence starts here, else from the
+  // previous stripe; it goes to S_T if the sequence ends here, else on
+  const float *sin = lo == first ? S0 : carry;
+  float *sout = hi == first + count ? S_T : carry;
+
   if constexpr (DK > D) {
     for (int e = tid; e < VW * (DK - D); e += NTH) Sop.store(e / (DK - D), D + e % (DK - D), 0.f);
   }
   f32x4 sreg = zero4();
-  const float *S0p = S0 ? S0 + (size_t)pair * D * D : nullptr;
+  const float *S0p = sin ? sin + (size_t)pair * D * D : nullptr;
   if (wave < NTILE) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sreg[i] = S0p ? S0p[(size_t)(16 * wave + 4 * g + i) * D + col0 + m] : 0.f;
     Sop.store4(m, 16 * wave + 4 * g, sreg);
   }
 
+  // This stripe's chunks of the sequence, numbered within the sequence.
   int64_t sstart, slen;
   seq_range(cu, seq_len, n, sstart, slen);
-  const int64_t cps = dense_chunks(seq_len);
-  const int64_t cbeg = cu == nullptr ? n * cps : (int64_t)base[n];
-  int64_t cend = cu == nullptr ? (n + 1) * cps : (int64_t)base[n + 1];
-  if (cend > max_chunks) cend = max_chunks;
-  if (total_tokens <= 0) cend = cbeg;
+  const int64_t cbeg = lo - first;
+  const int64_t cend = lo < hi ? hi - first : cbeg;
 
-  auto rec_of = [&](int64_t cc) __attribute__((always_inline)) { return recs + ((size_t)h * max_chunks + cc) * Rc::BYTES; };
+  auto rec_of = [&](int64_t cc) __attribute__((always_inline)) {
+    return recs + ((size_t)h * W + (first + cc - j0)) * Rc::BYTES;
+  };
   // The workgroups of a head split the cache lines of the record two chunks
   // ahead and each reads one word per line, so that the record is in L2 by
   // the time all of them load it in full.
@@ -1130,7 +1164,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   };
   auto prefetch_v = [&](int64_t cc, Buf &B) __attribute__((always_inline)) {
     if (uwave) {
-      const ChunkTok cn = chunk_tokens(sstart, slen, cc - cbeg, total_tokens);
+      const ChunkTok cn = chunk_tokens(sstart, slen, cc, total_tokens);
       load_scan_v<D, TIn>(B, v, cn.t0, cn.valid, h, H, col0, wave, lane);
     }
   };
@@ -1169,7 +1203,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   // between its matrix-core products, so that each wave keeps computing
   // while its loads queue.
   auto process = [&](int64_t c, const Buf &U, Buf &Nx, int64_t cn) __attribute__((always_inline)) {
-    const ChunkTok ct = chunk_tokens(sstart, slen, c - cbeg, total_tokens);
+    const ChunkTok ct = chunk_tokens(sstart, slen, c, total_tokens);
     const char *rn = rec_of(cn);  // unconditional (the last chunk re-reads itself)
 
     // Khat S (U waves) or Qhat S (O waves) for row tile rt.  All S operand
@@ -1266,8 +1300,10 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   if (!uwave) store_o();
   if (N < 0) o[sink & 1] = 0.f;  // never taken (N >= 0): keeps the touches alive
 
-  if (S_T != nullptr && wave < NTILE) {
-    float *STp = S_T + (size_t)pair * D * D;
+  // The state after this stripe: the final state, or the carry into the
+  // next stripe.
+  if (sout != nullptr && wave < NTILE) {
+    float *STp = sout + (size_t)pair * D * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) STp[(size_t)(16 * wave + 4 * g + i) * D + col0 + m] = sreg[i];
   }
@@ -1277,35 +1313,38 @@ template <int D, typename TIn, typename P, int GATE, int FORM>
 hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, const int32_t *cu,
                             const float *S0, float *o, float *S_T, void *workspace,
-                            hipStream_t stream, int phases) {
+                            const PrefillPlan &plan, hipStream_t stream, int phases) {
   char *ws = static_cast<char *>(workspace);
   int32_t *base = reinterpret_cast<int32_t *>(ws);
   char *recs = ws + schedule_bytes(s);
+  // the state between stripes: S_T, or the carry area when S_T is NULL
+  float *carry = plan.carry_off != 0 ? reinterpret_cast<float *>(ws + plan.carry_off) : S_T;
   const int N = s.num_seqs, H = s.num_heads;
-  const int64_t mc = max_chunks(s);
+  const int64_t W = plan.W;
   const TIn *qp = static_cast<const TIn *>(q), *kp = static_cast<const TIn *>(k),
             *vp = static_cast<const TIn *>(v);
+  const int64_t sblocks = ((int64_t)N * H + 7) / 8 * 8 * ScanCfg<D>::G;
   hipError_t e = hipSuccess;
-  if (phases & kPhaseLocal) {
-    if (cu != nullptr) {  // dense batches compute their chunk table in the kernels
-      hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, cu, N, s.seq_len, base);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    if (mc > 0) {
-      hipLaunchKernelGGL((chunk_local_kernel<D, TIn, P, GATE, FORM>), dim3((unsigned)(mc * H)), dim3(NT), 0, stream,
-                         qp, kp, alpha, beta, cu, s.seq_len, N, H, s.total_tokens, mc, base, recs);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  if (phases & kPhaseState) {
-    const int64_t pairs = (int64_t)N * H;
-    const int64_t blocks = (pairs + 7) / 8 * 8 * ScanCfg<D>::G;
-    hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P>), dim3((unsigned)blocks), dim3(ScanCfg<D>::NTH), 0, stream,
-                       vp, cu,
-                       s.seq_len, N, H, s.total_tokens, mc, base, recs, S0, o, S_T);
+  if ((phases & kPhaseLocal) && cu != nullptr) {  // dense batches compute their table in the kernels
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, cu, N, s.seq_len, base);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  for (int64_t i = 0; i < plan.stripes; ++i) {
+    const int64_t j0 = i * W;
+    const int64_t wi = plan.chunks - j0 < W ? plan.chunks - j0 : W;  // chunks of this stripe
+    if ((phases & kPhaseLocal) && wi > 0) {
+      hipLaunchKernelGGL((chunk_local_kernel<D, TIn, P, GATE, FORM>), dim3((unsigned)(wi * H)), dim3(NT), 0,
+                         stream, qp, kp, alpha, beta, cu, s.seq_len, N, H, s.total_tokens, W, j0, base, recs);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (phases & kPhaseState) {
+      hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P>), dim3((unsigned)sblocks), dim3(ScanCfg<D>::NTH), 0,
+                         stream, vp, cu, s.seq_len, N, H, s.total_tokens, W, j0, base, recs, S0, carry, o, S_T);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return e;
 }
@@ -1313,16 +1352,16 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
 template <typename TIn, int GATE, int FORM>
 hipError_t dispatch_prefill(const kda_shape_t &s, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, const int32_t *cu,
-                            const float *S0, float *o, float *S_T, void *ws, hipStream_t st,
-                            int ph) {
+                            const float *S0, float *o, float *S_T, void *ws, const PrefillPlan &pl,
+                            hipStream_t st, int ph) {
   // bf16 inputs run the split-bf16 matrix-core path; fp32 inputs (and the
   // 16-wide heads) the fp32 matrix-core path.
   using PB = typename std::conditional<std::is_same<TIn, __bf16>::value, SplitBF16, F32>::type;
   switch (s.d_k) {
-    case 16: return launch_prefill_t<16, TIn, F32, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 32: return launch_prefill_t<32, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 64: return launch_prefill_t<64, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-    case 128: return launch_prefill_t<128, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    case 16: return launch_prefill_t<16, TIn, F32, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, pl, st, ph);
+    case 32: return launch_prefill_t<32, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, pl, st, ph);
+    case 64: return launch_prefill_t<64, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, pl, st, ph);
+    case 128: return launch_prefill_t<128, TIn, PB, GATE, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, pl, st, ph);
   }
   return hipErrorInvalidValue;
 }
@@ -1330,19 +1369,19 @@ hipError_t dispatch_prefill(const kda_shape_t &s, const void *q, const void *k, 
 template <typename TIn, int FORM>
 hipError_t dispatch_gate(const kda_shape_t &s, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, const int32_t *cu, const float *S0,
-                         float *o, float *S_T, void *ws, hipStream_t st, int ph) {
+                         float *o, float *S_T, void *ws, const PrefillPlan &pl, hipStream_t st, int ph) {
   if (s.gate == KDA_GATE_HEAD)
-    return dispatch_prefill<TIn, KDA_GATE_HEAD, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-  return dispatch_prefill<TIn, KDA_GATE_CHANNEL, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    return dispatch_prefill<TIn, KDA_GATE_HEAD, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, pl, st, ph);
+  return dispatch_prefill<TIn, KDA_GATE_CHANNEL, FORM>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, pl, st, ph);
 }
 
 template <typename TIn>
 hipError_t dispatch_form(const kda_shape_t &s, const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta, const int32_t *cu, const float *S0,
-                         float *o, float *S_T, void *ws, hipStream_t st, int ph) {
+                         float *o, float *S_T, void *ws, const PrefillPlan &pl, hipStream_t st, int ph) {
   if (s.input_form == KDA_INPUT_PREACT)
-    return dispatch_gate<TIn, KDA_INPUT_PREACT>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
-  return dispatch_gate<TIn, KDA_INPUT_FINAL>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, st, ph);
+    return dispatch_gate<TIn, KDA_INPUT_PREACT>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, pl, st, ph);
+  return dispatch_gate<TIn, KDA_INPUT_FINAL>(s, q, k, v, alpha, beta, cu, S0, o, S_T, ws, pl, st, ph);
 }
 
 }  // namespace
@@ -1350,11 +1389,11 @@ hipError_t dispatch_form(const kda_shape_t &s, const void *q, const void *k, con
 hipError_t launch_prefill(const kda_shape_t &s, const void *q, const void *k, const void *v,
                           const float *alpha, const float *beta, const int32_t *cu_seqlens,
                           const float *S0, float *o, float *S_T, void *workspace,
-                          hipStream_t stream, int phases) {
+                          const PrefillPlan &plan, hipStream_t stream, int phases) {
   if (s.qkv_dtype == KDA_BF16)
-    return dispatch_form<__bf16>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
+    return dispatch_form<__bf16>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, plan, stream,
                                  phases);
-  return dispatch_form<float>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, stream,
+  return dispatch_form<float>(s, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, workspace, plan, stream,
                               phases);
 }
 

@@ -30,7 +30,7 @@ KDA_GATE_CHANNEL = 0
 KDA_GATE_HEAD = 1
 KDA_INPUT_FINAL = 0
 KDA_INPUT_PREACT = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 NOALLOC_WORKSPACE_BYTES = 128 << 20   # KDA_NOALLOC_WORKSPACE_BYTES
 CHUNK = 64
 
@@ -162,7 +162,10 @@ def _gate_of(alpha, q):
 
 
 def prefill_workspace_size(num_seqs, total_tokens, num_heads, d, dtype=torch.bfloat16):
-    """Workspace bytes kda_prefill needs (depends on N, T, H only)."""
+    """Recommended workspace bytes for kda_prefill (depends on N, T, H, d
+    only): every chunk in one stripe.  Less works too, in stripes, down to
+    the chunk table plus one record per head (plus the carried states when
+    there is no final-state output)."""
     shape = make_shape(num_seqs, 0, total_tokens, num_heads, d, dtype)
     out = ctypes.c_size_t(0)
     _check(lib().kda_prefill_workspace_size(ctypes.byref(shape), ctypes.byref(out)),
@@ -170,14 +173,24 @@ def prefill_workspace_size(num_seqs, total_tokens, num_heads, d, dtype=torch.bfl
     return int(out.value)
 
 
+def record_bytes(d, dtype=torch.bfloat16):
+    """Bytes of one chunk record (the workspace unit: one per 64-token chunk
+    and head)."""
+    # one sequence of 64 tokens, one head: the 256-byte chunk table + 2 records
+    return (prefill_workspace_size(1, 64, 1, d, dtype) - 256) // 2
+
+
 class PrefillCall:
     """A validated prefill problem: tensors, outputs and workspace bound to
-    the three C entry points.  ``run()`` is kda_prefill; ``chunk_local()``
-    and ``state_pass()`` are its two phases (run in that order)."""
+    the C entry points.  ``run()`` is kda_prefill; ``chunk_local()`` and
+    ``state_pass()`` are its two phases (run in that order; they need the
+    recommended workspace).  Without ``workspace`` the recommended size is
+    allocated, or ``workspace_bytes`` when given (the prefill then runs in
+    stripes if that is less)."""
 
     def __init__(self, q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
                  output_final_state=True, workspace=None, out=None, final_state=None, preact=False,
-                 allocate_workspace=True):
+                 allocate_workspace=True, workspace_bytes=None):
         for name, t in (("q", q), ("k", k), ("v", v)):
             _require_gpu(name, t)
         if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -222,7 +235,8 @@ class PrefillCall:
             _require_gpu("final_state", self.S_T, torch.float32)
             _require_shape("final_state", self.S_T, (N, H, D, D))
         if workspace is None and allocate_workspace:
-            need = prefill_workspace_size(N, total, H, D, q.dtype)
+            need = (workspace_bytes if workspace_bytes is not None
+                    else prefill_workspace_size(N, total, H, D, q.dtype))
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         if workspace is not None:
             _require_gpu("workspace", workspace)
@@ -270,7 +284,8 @@ class PrefillCall:
 
 
 def prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
-            output_final_state=True, workspace=None, out=None, final_state=None, preact=False):
+            output_final_state=True, workspace=None, out=None, final_state=None, preact=False,
+            workspace_bytes=None):
     """Chunked KDA prefill.  Returns (o, S_T).
 
     Layouts: q, k, alpha [T, H, D] with v [T, H, D] (one sequence, or a
@@ -284,18 +299,20 @@ def prefill(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
     initial_state [N, H, D, D] fp32 or None (zeros).  o is fp32 with v's
     shape; S_T is [N, H, D, D] fp32 (None if output_final_state is False).
     ``final_state`` may be ``initial_state`` for an in-place update.
+    ``workspace`` (uint8 device tensor) or ``workspace_bytes`` bound the
+    scratch memory; by default the recommended size is allocated.
     """
     return PrefillCall(q, k, v, alpha, beta, initial_state, cu_seqlens,
                        output_final_state=output_final_state, workspace=workspace, out=out,
-                       final_state=final_state, preact=preact).run()
+                       final_state=final_state, preact=preact, workspace_bytes=workspace_bytes).run()
 
 
 def prefill_noalloc(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, *,
                     output_final_state=True, out=None, final_state=None, preact=False):
     """``prefill`` through kda_prefill_noalloc: the library's static device
     workspace instead of a workspace tensor (for callers that cannot allocate
-    device memory; shapes whose workspace exceeds NOALLOC_WORKSPACE_BYTES are
-    rejected).  Outputs are allocated here unless ``out`` / ``final_state``
+    device memory; longer batches run in stripes, and batches whose minimum
+    workspace exceeds NOALLOC_WORKSPACE_BYTES are rejected).  Outputs are allocated here unless ``out`` / ``final_state``
     are given."""
     return PrefillCall(q, k, v, alpha, beta, initial_state, cu_seqlens,
                        output_final_state=output_final_state, out=out, final_state=final_state,

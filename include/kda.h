@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 #define KDA_CHUNK 64 /* prefill chunk length (tokens); not a semantic parameter */
 
 typedef enum kda_status {
@@ -128,12 +128,22 @@ int kda_abi_version(void);
 /* Human-readable name of a status code; never NULL. */
 const char *kda_status_string(kda_status_t status);
 
-/* Bytes of device workspace kda_prefill needs for `shape` (written to
- * *bytes).  The size depends on N, H, d and total_tokens only: an upper bound
- * on the number of 64-token chunks, floor(total_tokens/64) + N, times one
- * record of chunk operands per chunk and head (108.5 KiB at d = 128), plus a
- * small schedule table.  Returns KDA_ERR_INVALID_ARGUMENT /
- * KDA_ERR_UNSUPPORTED for a shape kda_prefill would reject. */
+/* Recommended bytes of device workspace for kda_prefill of `shape` (written
+ * to *bytes): a chunk table of N+1 int32 (padded to 256 B), then one record
+ * of chunk operands (108.5 KiB at d = 128) per head and per 64-token chunk,
+ * for an upper bound on the batch's chunks, floor(total_tokens/64) + N.  It
+ * depends on N, H, d and total_tokens only.  With it every chunk of the batch
+ * is built in one pass (the fastest; the two phase entry points need it).
+ *
+ * kda_prefill also accepts less, down to the table plus H records (plus N H
+ * d_k d_v floats when S_T is NULL and the batch needs more than one stripe):
+ * it then runs in stripes of W consecutive chunks of the batch (sequence
+ * after sequence), W = the records the workspace holds divided by H, and
+ * hands each sequence's state from one stripe to the next through S_T.  So
+ * the workspace need not grow with the context: a 2^20-token sequence at
+ * H = 32, d = 128 runs in 1 GiB as well as in the recommended 58 GB.
+ * Returns KDA_ERR_INVALID_ARGUMENT / KDA_ERR_UNSUPPORTED for a shape
+ * kda_prefill would reject. */
 kda_status_t kda_prefill_workspace_size(const kda_shape_t *shape, size_t *bytes);
 
 /* Prefill (chunked): run the update over every token of every sequence and
@@ -149,9 +159,10 @@ kda_status_t kda_prefill_workspace_size(const kda_shape_t *shape, size_t *bytes)
  *   o           [total_tokens][H][d_v] fp32 output
  *   S_T         [N][H][d_k][d_v] fp32 final states, or NULL to skip; may be
  *               the same pointer as S0 (in-place update)
- *   workspace   device scratch of at least kda_prefill_workspace_size()
- *               bytes, 256-byte aligned; its contents on entry do not
- *               matter and are clobbered
+ *   workspace   device scratch, 256-byte aligned: the recommended size of
+ *               kda_prefill_workspace_size, or less down to the minimum
+ *               given there (KDA_ERR_WORKSPACE_TOO_SMALL below it); its
+ *               contents on entry do not matter and are clobbered
  * A zero-length sequence gets S_T[n] = S0[n] (zeros if S0 == NULL).
  * Sequences and heads are independent. */
 kda_status_t kda_prefill(const kda_shape_t *shape,
@@ -165,8 +176,11 @@ kda_status_t kda_prefill(const kda_shape_t *shape,
 
 /* The two phases of kda_prefill, for callers that schedule them separately
  * (e.g. phase 1 of the next batch on another stream while phase 2 of this
- * one runs).  kda_prefill(...) is exactly phase 1 followed by phase 2 on the
- * same stream with the same arguments.
+ * one runs).  They need a workspace that holds every chunk of the batch in
+ * one stripe (the recommended size of kda_prefill_workspace_size always does;
+ * one that would need stripes is KDA_ERR_WORKSPACE_TOO_SMALL), with which
+ * kda_prefill(...) is exactly phase 1 followed by phase 2 on the same stream
+ * with the same arguments.
  *
  * Phase 1 (fully parallel over chunks and heads): builds the per-sequence
  * chunk table and, for every 64-token chunk and head, the chunk-local
@@ -200,10 +214,12 @@ kda_status_t kda_prefill_state_pass(const kda_shape_t *shape,
  * kda_prefill; the workspace is a static device array of the library,
  * KDA_NOALLOC_WORKSPACE_BYTES (128 MiB) on each GPU the library runs on,
  * held from the library's first use on that GPU until the process ends.
- *  - Shapes whose kda_prefill_workspace_size exceeds it are rejected with
- *    KDA_ERR_WORKSPACE_TOO_SMALL before any HIP call (at d = 128 a record
- *    is 108.5 KiB per 64-token chunk and head: e.g. one sequence of up to
- *    2,367 tokens at 32 heads).
+ *  - Any batch runs, in stripes when it needs more than the recommended
+ *    workspace (as kda_prefill with a workspace of that size), provided the
+ *    chunk table and H records (108.5 KiB each at d = 128: up to 1,208 heads)
+ *    fit, and when S_T is NULL and the batch needs stripes, also the N H
+ *    carried states (64 KiB each at d = 128: about 60 sequences at H = 32).
+ *    Otherwise KDA_ERR_WORKSPACE_TOO_SMALL, before any HIP call.
  *  - The call allocates nothing: no hipMalloc, no allocating library call.
  *    Its first call on a device looks up the array's address there
  *    (hipGetSymbolAddress) and caches it.

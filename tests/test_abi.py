@@ -62,7 +62,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.kda_abi_version() == 3
+    assert L.kda_abi_version() == 4
     names = [L.kda_status_string(i).decode() for i in range(5)]
     assert names == ["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                      "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_LAUNCH"]
@@ -78,6 +78,7 @@ def test_workspace_size_formula(N, T, H, d):
     frags = 4 * nkb * 2 + (d // 16) * 2 + 6           # Khat, Qhat, Ktil^T T, M T
     record = -(-(frags * 2048 + 4 * d) // 256) * 256   # + Gamma_C, 256-byte aligned
     assert need == sched + chunks * H * record
+    assert kda.record_bytes(d) == record
     if d == 128:
         assert record == 111104                          # 108.5 KiB per chunk and head
 
@@ -90,7 +91,9 @@ def test_workspace_size_rejects(L):
 
 
 def test_prefill_validation(L):
-    need = kda.prefill_workspace_size(1, 64, 2, 16, torch.float32)
+    # smallest workspace: the chunk table and one record per head; with S_T
+    # NULL and more than one stripe, also room for the carried states
+    need = 256 + kda.record_bytes(16) * 2
     assert prefill(L, None) == INVALID
     assert prefill(L, shape(N=-1)) == INVALID
     assert prefill(L, shape(H=0)) == INVALID
@@ -116,10 +119,13 @@ def test_prefill_validation(L):
     assert prefill(L, shape(), ws=FAKE + 16, ws_bytes=need) == INVALID  # workspace not 256-aligned
     assert prefill(L, shape(N=0, T=0)) == OK                      # nothing to do, nothing launched
     assert prefill(L, kda.KdaShape(0, 0, 5, 2, 16, 16, 0), cu=FAKE) == INVALID   # tokens, no sequences
+    # two stripes without S_T: the carried states need room after the records
+    carry = 256    # 2 heads x 16 x 16 floats, 256-byte aligned
+    assert prefill(L, shape(T=128), ST=None, ws_bytes=need + carry - 1) == WS_SMALL
 
 
 def test_gate_and_input_form_validation(L):
-    need = kda.prefill_workspace_size(1, 64, 2, 16, torch.float32)
+    need = 256 + kda.record_bytes(16) * 2    # the smallest workspace of shape()
     out = ctypes.c_size_t(0)
     assert prefill(L, shape(gate=2)) == INVALID
     assert prefill(L, shape(gate=-1)) == INVALID
@@ -128,7 +134,7 @@ def test_gate_and_input_form_validation(L):
     assert L.kda_prefill_workspace_size(ctypes.byref(shape(gate=3)), ctypes.byref(out)) == INVALID
     # the workspace size does not depend on the gate kind
     assert L.kda_prefill_workspace_size(ctypes.byref(shape(gate=1)), ctypes.byref(out)) == OK
-    assert out.value == need
+    assert out.value == kda.prefill_workspace_size(1, 64, 2, 16, torch.float32)
     # a per-head alpha needs 4-byte alignment only: FAKE + 4 passes the
     # alignment checks (and the call stops at the workspace check)
     assert prefill(L, shape(gate=1), a=FAKE + 2) == INVALID
@@ -148,7 +154,9 @@ def test_prefill_phase_validation(L):
     # phase 1 reads q, k, alpha, beta; it does not need v, o
     assert L.kda_prefill_chunk_local(s, FAKE, FAKE, FAKE, None, None, FAKE, need, None) == INVALID
     assert L.kda_prefill_chunk_local(s, None, FAKE, FAKE, FAKE, None, FAKE, need, None) == INVALID
-    assert L.kda_prefill_chunk_local(s, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == WS_SMALL
+    # the phases need every chunk in one stripe: here the table and 1 chunk x 2 heads
+    one = 256 + 2 * kda.record_bytes(16)
+    assert L.kda_prefill_chunk_local(s, FAKE, FAKE, FAKE, FAKE, None, FAKE, one - 1, None) == WS_SMALL
     # phase 2 needs v and o but not beta
     assert L.kda_prefill_state_pass(s, FAKE, FAKE, None, FAKE, None, None, FAKE, None, FAKE, need,
                                     None) == INVALID
@@ -260,8 +268,8 @@ def test_cu_seqlens_alignment_is_four_bytes_everywhere(L):
     s = kda.KdaShape(2, 0, 64, 2, 16, 16, 0)
     need = kda.prefill_workspace_size(2, 64, 2, 16, torch.float32)
     # accepted: the call reaches the workspace check
-    assert prefill(L, s, cu=FAKE + 4, ws_bytes=need - 1) == WS_SMALL
-    assert prefill(L, s, cu=FAKE + 2, ws_bytes=need - 1) == INVALID
+    assert prefill(L, s, cu=FAKE + 4, ws_bytes=255) == WS_SMALL
+    assert prefill(L, s, cu=FAKE + 2, ws_bytes=255) == INVALID
     sp = ctypes.byref(s)
     assert L.kda_prefill_chunk_local(sp, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, need - 1, None) == WS_SMALL
     assert L.kda_prefill_chunk_local(sp, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, need - 1, None) == INVALID
@@ -291,9 +299,13 @@ def test_prefill_noalloc_validation(L):
     assert na(shape(), o=FAKE + 4) == INVALID
     assert na(shape(), cu=FAKE + 2) == INVALID
     assert na(shape(N=0, T=0)) == OK                               # nothing to do, no HIP call
-    # at d = 128, H = 32: 2,367 tokens fit (37 chunks x 32 heads x 108.5 KiB), 2,368 do not
-    fits = kda.KdaShape(1, 2367, 2367, 32, 128, 128, 1)
-    assert kda.prefill_workspace_size(1, 2367, 32, 128) <= kda.NOALLOC_WORKSPACE_BYTES
-    assert kda.prefill_workspace_size(1, 2368, 32, 128) > kda.NOALLOC_WORKSPACE_BYTES
-    assert na(kda.KdaShape(1, 2368, 2368, 32, 128, 128, 1)) == WS_SMALL
+    # any length runs in stripes, down to the chunk table and one record of
+    # 108.5 KiB per head at d = 128: 1,208 heads fit in 128 MiB, 1,209 do not
+    rec = kda.record_bytes(128)
+    assert 256 + 1208 * rec <= kda.NOALLOC_WORKSPACE_BYTES < 256 + 1209 * rec
+    assert na(kda.KdaShape(1, 64, 64, 1209, 128, 128, 1)) == WS_SMALL
+    # without S_T, a batch that needs stripes also needs the carried states
+    # (64 KiB per sequence and head): 62 x 32 fit beside 32 records, 63 x 32 do not
+    assert na(kda.KdaShape(63, 4096, 63 * 4096, 32, 128, 128, 1), ST=None) == WS_SMALL
+    fits = kda.KdaShape(1, 1 << 20, 1 << 20, 32, 128, 128, 1)   # a 2^20-token sequence
     assert na(fits, q=FAKE + 2) == INVALID                         # rejected before any HIP call

@@ -9,10 +9,14 @@ The oracle always consumes the exact tensors the GPU consumed, copied back.
 Sizes span several chunks and ragged tails; the measured workloads
 (4096 tokens x 32 heads; eight packed sequences, 79,966 tokens x 32 heads)
 are compared in full, every token and head, with the oracle run over head
-groups in child processes.  The 2^20-token workload is checked on its first
-65,536 tokens, on a window from zero for its tail and S_T (history older than
-~1000 tokens weighs below 1e-300 under its decay), and by the split-in-halves
-state carry.
+groups in child processes.  The 2^20-token workload runs in a 1 GiB
+workspace (in stripes) and is checked on its first 65,536 tokens, on a
+window from zero for its tail and S_T (history older than ~1000 tokens weighs
+below 1e-300 under its decay), by the split-in-halves state carry, and
+against the same call with the recommended (58 GB) workspace, bit for bit.
+A workspace below the recommended size makes the prefill run in stripes;
+those results must equal the one-stripe results bit for bit (the same
+chunks, the same arithmetic, the state handed over in fp32).
 """
 
 import numpy as np
@@ -211,6 +215,50 @@ def test_two_phase_calls_equal_prefill():
     assert torch.equal(o, ref_o) and torch.equal(S, ref_S)
 
 
+def _table_bytes(N):
+    return -(-4 * (N + 1) // 256) * 256
+
+
+# (lengths, dense batch?, heads, head size, dtype, S0)
+STRIPE_CASES = [([300, 300], True, 3, 64, torch.bfloat16, 0.3),
+                ([0, 100, 37, 500, 0, 64, 1, 129], False, 2, 128, torch.bfloat16, 0.1),
+                ([0, 0, 250], False, 2, 32, torch.float32, None),
+                ([200], False, 4, 16, torch.float32, 0.5)]
+
+
+@pytest.mark.parametrize("case", range(len(STRIPE_CASES)))
+def test_striped_workspace_equals_one_stripe(case):
+    """Workspaces of w chunk records per head (w = 1, 2, 3, 7: many stripes,
+    stripe edges inside and between sequences, empty sequences) give the
+    one-stripe results bit for bit: with S_T, without S_T (the state is handed
+    over in the carry area after the records), and in place (S_T = S0)."""
+    lens, dense, H, D, dtype, s0 = STRIPE_CASES[case]
+    dev = device()
+    d = inputs.prefill_inputs(lens, H, D, dtype, "medium", s0, seed=60 + case, device=dev)
+    N = len(lens)
+    q, k, v, a, b = (d[x] for x in ("q", "k", "v", "alpha", "beta"))
+    cu = d["cu_seqlens"]
+    if dense:
+        q, k, v, a = (t.reshape(N, lens[0], H, D) for t in (q, k, v, a))
+        b, cu = b.reshape(N, lens[0], H), None
+    S0 = None if d["S0"] is None else d["S0"]
+    ref_o, ref_S = kda.prefill(q, k, v, a, b, S0, cu)
+    rec = kda.record_bytes(D, dtype)
+    carry = -(-N * H * D * D * 4 // 256) * 256
+    for w in (1, 2, 3, 7):
+        ws = _table_bytes(N) + w * H * rec
+        print(f"stripes: case {case} w={w}", flush=True)
+        o, S = kda.prefill(q, k, v, a, b, S0, cu, workspace_bytes=ws)
+        assert torch.equal(o, ref_o), f"w={w}: o differs"
+        assert torch.equal(S, ref_S), f"w={w}: S_T differs"
+        o2, none = kda.prefill(q, k, v, a, b, S0, cu, output_final_state=False, workspace_bytes=ws + carry)
+        assert none is None and torch.equal(o2, ref_o), f"w={w}: o differs without S_T"
+        if S0 is not None:
+            S_in = S0.clone()
+            o3, S3 = kda.prefill(q, k, v, a, b, S_in, cu, final_state=S_in, workspace_bytes=ws)
+            assert torch.equal(o3, ref_o) and torch.equal(S3, ref_S), f"w={w}: in-place differs"
+
+
 def test_prefill_long_1m_workload():
     """B=1, H=32, T=2^20, d=128, bf16, strong decay, S0 = 0 (a 1M-token
     context).  On every head: o of the first 65,536 tokens against the
@@ -221,8 +269,12 @@ def test_prefill_long_1m_workload():
     spec = inputs.WORKLOADS["long_1m"]
     T, H, D = spec["lengths"][0], spec["H"], spec["D"]
     d = inputs.prefill_inputs([T], H, D, torch.bfloat16, "strong", None, seed=0, device=dev)
-    ws = torch.empty(kda.prefill_workspace_size(1, T, H, D), dtype=torch.uint8, device=dev)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)        # 302 chunks per stripe
     o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], workspace=ws)
+    full = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"])  # one stripe, 58 GB
+    assert torch.equal(full[0], o) and torch.equal(full[1], ST)
+    del full
+    torch.cuda.empty_cache()
     P, W = 65536, 1024
     ro, rST = per_head(kda_recurrent, *(np64(d[x][:P]) for x in ("q", "k", "v", "alpha", "beta")))
     parity(o[:P], rST, ro, rST, 2e-3, "long_1m prefix (o only; the prefix has no final state)")

@@ -2,10 +2,11 @@
 kda_prefill (a workspace the caller allocates), through the C ABI.
 
 Both entry points run the same kernels on the same inputs, so their outputs
-must be bit-identical.  Calls on one GPU share its static workspace, which
-keeps the previous call's contents: the calls here run in a row, each one
-smaller than the one before, and each is compared with the workspace entry
-point.
+must be bit-identical (a batch whose recommended workspace exceeds the
+static one runs in stripes there, which gives the same bits).  Calls on one
+GPU share its static workspace, which keeps the previous call's contents:
+the calls here run in a row, each one smaller than the one before, and each
+is compared with the workspace entry point.
 """
 
 import pytest
@@ -16,8 +17,10 @@ from tests.gpu_util import device
 
 pytestmark = pytest.mark.gpu
 
-# (sequence lengths, heads, head size, q/k/v dtype): largest first
-CASES = [([900, 1000, 0, 100], 32, 128, torch.bfloat16),
+# (sequence lengths, heads, head size, q/k/v dtype): largest first; the first
+# has a recommended workspace of 1.1 GB and runs in stripes
+CASES = [([20000], 32, 128, torch.bfloat16),
+         ([900, 1000, 0, 100], 32, 128, torch.bfloat16),
          ([700], 8, 128, torch.bfloat16),
          ([64, 1, 0, 37], 2, 16, torch.float32)]
 
@@ -28,7 +31,6 @@ def test_noalloc_equals_prefill_on_calls_in_a_row():
         print(f"noalloc case {i}: lens={lens} H={H} D={D} {dtype}", flush=True)
         d = inputs.prefill_inputs(lens, H, D, dtype, "strong", 0.1, seed=40 + i, device=dev)
         args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
-        assert kda.prefill_workspace_size(len(lens), sum(lens), H, D) <= kda.NOALLOC_WORKSPACE_BYTES
         o, S = kda.prefill_noalloc(*args)
         ref_o, ref_S = kda.prefill(*args)
         torch.cuda.synchronize()
@@ -36,9 +38,22 @@ def test_noalloc_equals_prefill_on_calls_in_a_row():
         assert torch.equal(S, ref_S), f"case {i}: S_T differs"
 
 
+def test_noalloc_without_final_state_in_stripes():
+    """No S_T: the stripes hand the states over in a carry area of the static
+    workspace."""
+    dev = device()
+    d = inputs.prefill_inputs([3000, 0, 2000], 32, 128, torch.bfloat16, "strong", 0.1, seed=7, device=dev)
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
+    assert kda.prefill_workspace_size(3, 5000, 32, 128) > kda.NOALLOC_WORKSPACE_BYTES
+    o, none = kda.prefill_noalloc(*args, output_final_state=False)
+    ref_o, _ = kda.prefill(*args)
+    torch.cuda.synchronize()
+    assert none is None and torch.equal(o, ref_o)
+
+
 def test_noalloc_rejects_a_workspace_beyond_its_scratch():
     dev = device()
-    T, H, D = 2368, 32, 128       # needs more than the 128 MiB static workspace
+    T, H, D = 64, 1209, 128       # 1,209 records of 108.5 KiB: more than the 128 MiB static workspace
     d = inputs.prefill_inputs([T], H, D, torch.bfloat16, "strong", None, seed=3, device=dev)
     with pytest.raises(kda.KdaError, match="WORKSPACE_TOO_SMALL"):
         kda.prefill_noalloc(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
