@@ -298,9 +298,11 @@ def bench_verify(B, K, dev, steps=50):
             "committed_seqs": n_acc}
 
 
-def bench_backward(name, dev, steps=10):
+def bench_backward(name, dev, steps=10, ws_bytes=None):
     """kda_backward over the prefill workload (upstream gradients dO ~ N(0,1),
-    dS_T ~ 0.02 N(0,1)); HIP events around each call on the launch stream."""
+    dS_T ~ 0.02 N(0,1)); one event pair on the launch stream around ``steps``
+    back-to-back calls.  ws_bytes: the workspace (default the recommended
+    size; less runs the sequences in pieces)."""
     from gated_delta_rule_76_amd import inputs, kda
     spec = inputs.WORKLOADS[name]
     lens = inputs.workload_lengths(spec, seed=0)
@@ -309,7 +311,9 @@ def bench_backward(name, dev, steps=10):
     T = sum(lens)
     dO, dST = inputs.grad_inputs(T, H, D, len(lens), seed=0, device=dev)
     cu = d["cu_seqlens"] if len(lens) > 1 else None
-    ws = torch.empty(kda.backward_workspace_size(len(lens), T, H, D), dtype=torch.uint8, device=dev)
+    if ws_bytes is None:
+        ws_bytes = kda.backward_workspace_size(len(lens), T, H, D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     run = lambda: kda.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dO, d["S0"], dST, cu,
                                workspace=ws)
     for _ in range(2):
@@ -732,6 +736,9 @@ def main():
             out["verify"] = verify_summary(bench_verify(args.decode_batch, 2, dev))
         print("[bench] backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(args.workload if args.workload == "prefill_4k" else "prefill_4k", dev)
+        if args.bounded_workspace_mib:
+            out["backward"]["bounded_workspace"] = bench_backward(
+                "prefill_4k", dev, ws_bytes=args.bounded_workspace_mib << 20)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -324,12 +324,13 @@ kda_status_t kda_backward(const kda_shape_t *shape, const void *q, const void *k
   // One workgroup per (sequence, head, 16 value columns).
   if ((int64_t)s.num_seqs * s.num_heads * (s.d_v < 16 ? 1 : s.d_v / 16) >= ((int64_t)1 << 31))
     return KDA_ERR_UNSUPPORTED;
-  const size_t need = kda::backward_layout(s).bytes;
-  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  const kda::BwdLayout L = kda::backward_plan(s, varlen, workspace_bytes);
+  if (L.pieces <= 0) return KDA_ERR_WORKSPACE_TOO_SMALL;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kda::kWorkspaceAlign - 1)) != 0)
     return KDA_ERR_INVALID_ARGUMENT;
   kda::BwdArgs a{q, k, v, alpha, beta, cu_seqlens, S0, dO, dS_T, dq, dk, dv, dalpha, dbeta, dS0, workspace};
-  hipError_t e = kda::launch_backward(s, a, static_cast<hipStream_t>(stream));
+  hipError_t e = kda::launch_backward(s, a, L, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -45,6 +45,20 @@
 namespace kda {
 namespace {
 
+// The part of every sequence one launch of the backward covers, and where
+// its state, state gradient, checkpoints and partial rows live.
+struct BwdPiece {
+  int64_t t_off;        // first token of the piece within every sequence
+  int64_t plen;         // piece length cap (tokens)
+  int64_t slot_stride;  // checkpoint slots per sequence; 0 = packed over the batch
+  int64_t row_len;      // partial rows per sequence; 0 = one row per token of the batch
+  int64_t rows;         // partial rows per head and column slice (the slice stride / H)
+  const float *S_in;    // state at the piece start (NULL = zeros)
+  const float *G_in;    // dL/dS at the piece end (NULL = zeros)
+  float *G_out;         // dL/dS at the piece start (NULL = not written)
+  float *sweep;         // forward sweep only: the state at every multiple of plen, [p-1][N][H][d][d]
+};
+
 // (a native vector type: the in-flight block stays in registers)
 typedef uint32_t bu32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBwdVW = 16;  // value columns per workgroup
@@ -134,9 +148,8 @@ template <int D, typename TIn, int GATE>
 __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta, const int32_t *__restrict__ cu,
-    int32_t seq_len, int N, int H, int64_t total, const float *__restrict__ S0,
-    const float *__restrict__ dO, const float *__restrict__ dS_T, float *__restrict__ dv,
-    float *__restrict__ dS0, float *__restrict__ ckpt, float *__restrict__ part) {
+    int32_t seq_len, int N, int H, int64_t total, const float *__restrict__ dO, float *__restrict__ dv,
+    float *__restrict__ ckpt, float *__restrict__ part, const BwdPiece pc) {
   using Cf = BwdCfg<D, TIn, GATE>;
   constexpr int RPT = Cf::RPT, VW = Cf::VW, SL = Cf::SL, NW = Cf::NW, NRED = Cf::NRED, CK = Cf::CK;
   constexpr int NT = Cf::NT, LPC = Cf::LPC;
@@ -165,8 +178,17 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
   if (start > total) start = total;
   if (len < 0) len = 0;
   if (len > total - start) len = total - start;
+  // This launch's piece of the sequence (the forward sweep runs all of it).
+  if (pc.sweep == nullptr) {
+    const int64_t off = pc.t_off < len ? pc.t_off : len;
+    start += off;
+    len -= off;
+    if (len > pc.plen) len = pc.plen;
+  }
   const int64_t nblk = (len + CK - 1) / CK;
-  const int64_t blk0 = start / CK + n;  // first checkpoint slot of this sequence
+  // first checkpoint slot and first partial row of this piece
+  const int64_t blk0 = pc.slot_stride > 0 ? (int64_t)n * pc.slot_stride : start / CK + n;
+  const int64_t row0 = pc.row_len > 0 ? (int64_t)n * pc.row_len : start;
   const int64_t sbase = (((int64_t)n * H + h) * D) * D;  // [n][h] state offset
   // A checkpoint slot holds the slice as [thread][RPT] (each thread reads back
   // what it wrote).
@@ -249,9 +271,10 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
   };
 
   // ---- pass 1: forward, checkpoint at every block start -----------------------
+  // (the forward sweep instead stores the state at every piece start)
   float s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) s[i] = S0 != nullptr ? S0[sbase + (int64_t)(r0 + i) * D + col] : 0.f;
+  for (int i = 0; i < RPT; ++i) s[i] = pc.S_in != nullptr ? pc.S_in[sbase + (int64_t)(r0 + i) * D + col] : 0.f;
   auto fwd_step = [&](int j) __attribute__((always_inline)) {
     float ak[RPT];
     float xk = 0.f;
@@ -277,10 +300,14 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
     // next block needed: b + 1, or (after the last) the one before it for pass 2
     const int64_t nb = b + 1 < nblk ? b + 1 : (b > 0 ? b - 1 : b);
     fetch(nb * CK, R);
-    {
+    if (pc.sweep == nullptr) {
       float *cp = ck_at(b);
 #pragma unroll
       for (int i = 0; i < RPT; ++i) cp[i] = s[i];
+    } else if (b > 0 && (b * CK) % pc.plen == 0) {  // (plen is a multiple of CK)
+      float *sp = pc.sweep + ((b * CK) / pc.plen - 1) * (int64_t)N * H * D * D + sbase;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) sp[(int64_t)(r0 + i) * D + col] = s[i];
     }
     const int nt = (int)(len - b * CK < CK ? len - b * CK : CK);
     // (loops over a block's tokens are unrolled, so LDS addresses are
@@ -293,6 +320,7 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       stash(R);
     }
   }
+  if (pc.sweep != nullptr) return;
   // Each thread reads back only the checkpoint elements it wrote.
   __threadfence_block();
 
@@ -300,7 +328,7 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
   // LDS holds the last block; R holds the one before it.
   float G[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) G[i] = dS_T != nullptr ? dS_T[sbase + (int64_t)(r0 + i) * D + col] : 0.f;
+  for (int i = 0; i < RPT; ++i) G[i] = pc.G_in != nullptr ? pc.G_in[sbase + (int64_t)(r0 + i) * D + col] : 0.f;
   int par = 0;
   // The checkpoint of the block before is loaded while a block runs.
   float ckn[RPT];
@@ -392,7 +420,7 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       if (lane == 0) red[Cf::EB] = db;
       __syncthreads();
       // The slice's partial row sums of this token, in one contiguous row.
-      float *prow = part + ((int64_t)sl * total * H + th) * NRED;
+      float *prow = part + ((int64_t)sl * pc.rows * H + (row0 + tb + j) * H + h) * NRED;
 #pragma unroll
       for (int u0 = 0; u0 < NRED; u0 += NT) {
         const int e = u0 + tid;
@@ -406,10 +434,43 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       par ^= 1;
     }
   }
-  if (dS0 != nullptr) {
+  if (pc.G_out != nullptr) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) dS0[sbase + (int64_t)(r0 + i) * D + col] = G[i];
+    for (int i = 0; i < RPT; ++i) pc.G_out[sbase + (int64_t)(r0 + i) * D + col] = G[i];
   }
+}
+
+// Partial row -> (token row * H + head) of the batch, or -1 for a row past
+// its sequence's piece (never written).  row_len = 0: the rows are the
+// batch's token rows.
+struct RowMap {
+  const int32_t *cu;
+  int32_t seq_len;
+  int H;
+  int64_t total, t_off, plen, row_len;
+};
+
+__device__ __forceinline__ int64_t map_row(const RowMap &m, int64_t r) {
+  if (m.row_len == 0) return r;
+  const int64_t tok = r / m.H;
+  const int h = (int)(r - tok * m.H);
+  const int n = (int)(tok / m.row_len);
+  const int64_t lt = tok - (int64_t)n * m.row_len;
+  int64_t start, len;
+  if (m.cu != nullptr) {
+    start = m.cu[n];
+    len = (int64_t)m.cu[n + 1] - start;
+  } else {
+    start = (int64_t)n * m.seq_len;
+    len = m.seq_len;
+  }
+  if (start < 0) start = 0;
+  if (start > m.total) start = m.total;
+  if (len < 0) len = 0;
+  if (len > m.total - start) len = m.total - start;
+  const int64_t off = m.t_off < len ? m.t_off : len;
+  const int64_t plen = len - off < m.plen ? len - off : m.plen;
+  return lt < plen ? (start + off + lt) * m.H + h : -1;
 }
 
 // dk, dq, dalpha and dbeta = sums of the per-slice partial rows, slice order
@@ -417,12 +478,15 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
 // every slice starts on a 16-byte boundary, with the loads of all slices in
 // flight together.
 template <int D, int GATE>
-__device__ __forceinline__ void bwd_put(int64_t i, float acc, float *__restrict__ dk, float *__restrict__ dq,
-                                        float *__restrict__ dalpha, float *__restrict__ dbeta) {
+__device__ __forceinline__ void bwd_put(const RowMap &m, int64_t i, float acc, float *__restrict__ dk,
+                                        float *__restrict__ dq, float *__restrict__ dalpha,
+                                        float *__restrict__ dbeta) {
   constexpr int NRED = bwd_row_sums(D, GATE == KDA_GATE_HEAD);
   constexpr int EB = GATE == KDA_GATE_HEAD ? 2 * D : 3 * D;
-  const int64_t th = i / NRED;
-  const int e = (int)(i - th * NRED);
+  const int64_t r = i / NRED;
+  const int e = (int)(i - r * NRED);
+  const int64_t th = map_row(m, r);
+  if (th < 0) return;
   if (e < D) {
     dk[th * D + e] = acc;
   } else if (e < 2 * D) {
@@ -439,7 +503,7 @@ __device__ __forceinline__ void bwd_put(int64_t i, float acc, float *__restrict_
 template <int D, int GATE, int SL>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part, float *__restrict__ dk,
                                                          float *__restrict__ dq, float *__restrict__ dalpha,
-                                                         float *__restrict__ dbeta, int64_t rows) {
+                                                         float *__restrict__ dbeta, int64_t rows, const RowMap m) {
   constexpr int NRED = bwd_row_sums(D, GATE == KDA_GATE_HEAD);
   const int64_t n = rows * NRED;
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -459,10 +523,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict
         acc.z += x[s].z;
         acc.w += x[s].w;
       }
-      bwd_put<D, GATE>(4 * v, acc.x, dk, dq, dalpha, dbeta);
-      bwd_put<D, GATE>(4 * v + 1, acc.y, dk, dq, dalpha, dbeta);
-      bwd_put<D, GATE>(4 * v + 2, acc.z, dk, dq, dalpha, dbeta);
-      bwd_put<D, GATE>(4 * v + 3, acc.w, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE>(m, 4 * v, acc.x, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE>(m, 4 * v + 1, acc.y, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE>(m, 4 * v + 2, acc.z, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE>(m, 4 * v + 3, acc.w, dk, dq, dalpha, dbeta);
     }
   } else {
     for (int64_t i = first; i < n; i += stride) {
@@ -472,60 +536,85 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict
       float acc = x[0];
 #pragma unroll
       for (int s = 1; s < SL; ++s) acc += x[s];
-      bwd_put<D, GATE>(i, acc, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE>(m, i, acc, dk, dq, dalpha, dbeta);
     }
   }
 }
 
 template <int D, typename TIn, int GATE>
-hipError_t launch_bwd_t(const kda_shape_t &s, const BwdArgs &a, hipStream_t stream) {
+hipError_t launch_bwd_t(const kda_shape_t &s, const BwdArgs &a, const BwdLayout &L, hipStream_t stream) {
   using Cf = BwdCfg<D, TIn, GATE>;
-  const BwdLayout L = backward_layout(s);
   char *ws = static_cast<char *>(a.workspace);
   float *ckpt = reinterpret_cast<float *>(ws + L.ckpt_off);
   float *part = reinterpret_cast<float *>(ws + L.part_off);
+  float *pstate = reinterpret_cast<float *>(ws + L.pstate_off);
+  float *carry = reinterpret_cast<float *>(ws + L.carry_off);
   const int64_t blocks = (int64_t)s.num_seqs * s.num_heads * Cf::SL;
-  hipLaunchKernelGGL((bwd_kernel<D, TIn, GATE>), dim3((unsigned)blocks), dim3(Cf::NT), 0, stream,
-                     static_cast<const TIn *>(a.q), static_cast<const TIn *>(a.k),
-                     static_cast<const TIn *>(a.v), a.alpha, a.beta, a.cu, s.seq_len, s.num_seqs, s.num_heads,
-                     s.total_tokens, a.S0, a.dO, a.dS_T, a.dv, a.dS0, ckpt, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t rows = s.total_tokens * s.num_heads;
-  const int64_t n = rows * Cf::NRED;
-  if (n > 0) {
+  const int64_t state = (int64_t)s.num_seqs * s.num_heads * D * D;
+  const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
+            *v = static_cast<const TIn *>(a.v);
+  auto run = [&](const BwdPiece &pc) -> hipError_t {
+    hipLaunchKernelGGL((bwd_kernel<D, TIn, GATE>), dim3((unsigned)blocks), dim3(Cf::NT), 0, stream, q, k, v,
+                       a.alpha, a.beta, a.cu, s.seq_len, s.num_seqs, s.num_heads, s.total_tokens, a.dO, a.dv,
+                       ckpt, part, pc);
+    return hipGetLastError();
+  };
+  auto reduce = [&](int64_t rows, const RowMap &m) -> hipError_t {
+    const int64_t n = rows * s.num_heads * Cf::NRED;
+    if (n <= 0) return hipSuccess;
     const int64_t w = n % 4 == 0 ? n / 4 : n;  // work items (four sums each when aligned)
     const int64_t g = (w + 255) / 256 < 8192 ? (w + 255) / 256 : 8192;
     hipLaunchKernelGGL((bwd_reduce_kernel<D, GATE, Cf::SL>), dim3((unsigned)g), dim3(256), 0, stream, part, a.dk,
-                       a.dq, a.dalpha, a.dbeta, rows);
-    e = hipGetLastError();
+                       a.dq, a.dalpha, a.dbeta, rows * s.num_heads, m);
+    return hipGetLastError();
+  };
+  hipError_t e;
+  if (L.L == 0) {  // the whole sequences at once
+    e = run(BwdPiece{0, INT64_MAX, 0, 0, s.total_tokens, a.S0, a.dS_T, a.dS0, nullptr});
+    if (e != hipSuccess) return e;
+    return reduce(s.total_tokens, RowMap{a.cu, s.seq_len, s.num_heads, s.total_tokens, 0, INT64_MAX, 0});
+  }
+  // Pieces of L tokens: the forward sweep stores the state at every piece
+  // start, then the pieces run from last to first.
+  const int64_t P = L.pieces, rows = (int64_t)s.num_seqs * L.L;
+  if (P > 1) {
+    e = run(BwdPiece{0, L.L, 0, 0, 0, a.S0, nullptr, nullptr, pstate});
+    if (e != hipSuccess) return e;
+  }
+  for (int64_t i = P - 1; i >= 0; --i) {
+    const float *S_in = i == 0 ? a.S0 : pstate + (i - 1) * state;
+    const float *G_in = i == P - 1 ? a.dS_T : carry;
+    float *G_out = i == 0 ? a.dS0 : carry;
+    e = run(BwdPiece{i * L.L, L.L, L.L / Cf::CK, L.L, rows, S_in, G_in, G_out, nullptr});
+    if (e != hipSuccess) return e;
+    e = reduce(rows, RowMap{a.cu, s.seq_len, s.num_heads, s.total_tokens, i * L.L, L.L, L.L});
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 template <typename TIn, int GATE>
-hipError_t bwd_by_dim(const kda_shape_t &s, const BwdArgs &a, hipStream_t st) {
+hipError_t bwd_by_dim(const kda_shape_t &s, const BwdArgs &a, const BwdLayout &L, hipStream_t st) {
   switch (s.d_k) {
-    case 16: return launch_bwd_t<16, TIn, GATE>(s, a, st);
-    case 32: return launch_bwd_t<32, TIn, GATE>(s, a, st);
-    case 64: return launch_bwd_t<64, TIn, GATE>(s, a, st);
-    case 128: return launch_bwd_t<128, TIn, GATE>(s, a, st);
+    case 16: return launch_bwd_t<16, TIn, GATE>(s, a, L, st);
+    case 32: return launch_bwd_t<32, TIn, GATE>(s, a, L, st);
+    case 64: return launch_bwd_t<64, TIn, GATE>(s, a, L, st);
+    case 128: return launch_bwd_t<128, TIn, GATE>(s, a, L, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename TIn>
-hipError_t bwd_by_gate(const kda_shape_t &s, const BwdArgs &a, hipStream_t st) {
-  if (s.gate == KDA_GATE_HEAD) return bwd_by_dim<TIn, KDA_GATE_HEAD>(s, a, st);
-  return bwd_by_dim<TIn, KDA_GATE_CHANNEL>(s, a, st);
+hipError_t bwd_by_gate(const kda_shape_t &s, const BwdArgs &a, const BwdLayout &L, hipStream_t st) {
+  if (s.gate == KDA_GATE_HEAD) return bwd_by_dim<TIn, KDA_GATE_HEAD>(s, a, L, st);
+  return bwd_by_dim<TIn, KDA_GATE_CHANNEL>(s, a, L, st);
 }
 
 }  // namespace
 
-hipError_t launch_backward(const kda_shape_t &s, const BwdArgs &a, hipStream_t stream) {
-  if (s.qkv_dtype == KDA_BF16) return bwd_by_gate<__bf16>(s, a, stream);
-  return bwd_by_gate<float>(s, a, stream);
+hipError_t launch_backward(const kda_shape_t &s, const BwdArgs &a, const BwdLayout &L, hipStream_t stream) {
+  if (s.qkv_dtype == KDA_BF16) return bwd_by_gate<__bf16>(s, a, L, stream);
+  return bwd_by_gate<float>(s, a, L, stream);
 }
 
 }  // namespace kda

@@ -114,30 +114,72 @@ hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, cons
                          hipStream_t stream);
 
 // Backward pass.  Workspace: state checkpoints every bwd_block tokens per
-// (sequence, head) -- at most floor(T / bwd_block) + N slots of d_k x d_v
-// floats per head -- then the per-slice partial row sums over the d_v / 16
-// column slices, [slices][T][H][bwd_row_sums] floats: per (token, head) dk
-// (d), dq (d), then dalpha (d) and dbeta, or with one rate per head dbeta and
-// dalpha.  The block is 16 tokens at d <= 64; at d = 128, 12 for bf16 inputs
-// and 8 for fp32 ones (the block's states and inputs have to fit in LDS).
+// (sequence, head) -- d_k x d_v floats per slot -- then the per-slice
+// partial row sums over the d_v / 16 column slices, [slices][rows][H]
+// [bwd_row_sums] floats: per (token, head) dk (d), dq (d), then dalpha (d) and
+// dbeta, or with one rate per head dbeta and dalpha.  The block is 16 tokens
+// at d <= 64; at d = 128, 12 for bf16 inputs and 8 for fp32 ones (the block's
+// states and inputs have to fit in LDS).
+//
+// With the recommended workspace every sequence is one piece: checkpoint
+// slots packed over the batch (at most floor(T / block) + N) and one partial
+// row per token.  With less, every sequence is cut into pieces of L tokens
+// (L a multiple of 48, so of every block size): a forward sweep stores the
+// state at each piece start, then the pieces run from last to first, the
+// state gradient handed from piece to piece through a carry buffer.  The
+// workspace then holds, in this order: the piece-start states [P-1][N][H]
+// [d_k][d_v], the carry [N][H][d_k][d_v], checkpoint slots [N][L/block][H]
+// and partial rows [slices][N][L][H] -- nothing that grows with the context
+// beyond the P-1 piece-start states.
 constexpr int bwd_block(int d, bool f32_inputs) { return d >= 128 ? (f32_inputs ? 8 : 12) : 16; }
 constexpr int bwd_row_sums(int d, bool head_gate) { return head_gate ? 2 * d + 2 : 3 * d + 1; }
+constexpr int64_t kBwdPieceUnit = 48;
 
 struct BwdLayout {
-  size_t ckpt_off, part_off, bytes;
+  int64_t pieces;    // P (1: the whole sequences at once)
+  int64_t L;         // piece length in tokens (P > 1)
+  size_t pstate_off, carry_off, ckpt_off, part_off, bytes;
 };
 
-inline BwdLayout backward_layout(const kda_shape_t &s) {
+// Layout for pieces of L tokens (L = 0: one piece, the recommended layout).
+inline BwdLayout backward_layout(const kda_shape_t &s, bool varlen = true, int64_t L = 0) {
   const size_t d = (size_t)s.d_k, H = (size_t)s.num_heads, T = (size_t)s.total_tokens;
+  const size_t N = (size_t)s.num_seqs;
   const size_t slices = d < 16 ? 1 : d / 16;
   const int blk = bwd_block(s.d_k, s.qkv_dtype == KDA_F32);
-  const size_t slots = (size_t)(s.total_tokens / blk) + (size_t)s.num_seqs;
   const size_t nred = (size_t)bwd_row_sums(s.d_k, s.gate == KDA_GATE_HEAD);
-  BwdLayout L;
-  L.ckpt_off = 0;
-  L.part_off = align_up(L.ckpt_off + sizeof(float) * slots * H * d * (size_t)s.d_v, kWorkspaceAlign);
-  L.bytes = align_up(L.part_off + sizeof(float) * slices * T * H * nred, kWorkspaceAlign);
-  return L;
+  const size_t state = sizeof(float) * N * H * d * (size_t)s.d_v;  // [N][H][d_k][d_v]
+  BwdLayout Lo{1, 0, 0, 0, 0, 0, 0};
+  if (L <= 0) {
+    const size_t slots = (size_t)(s.total_tokens / blk) + N;
+    Lo.ckpt_off = 0;
+    Lo.part_off = align_up(sizeof(float) * slots * H * d * (size_t)s.d_v, kWorkspaceAlign);
+    Lo.bytes = align_up(Lo.part_off + sizeof(float) * slices * T * H * nred, kWorkspaceAlign);
+    return Lo;
+  }
+  const int64_t maxlen = varlen ? s.total_tokens : (int64_t)s.seq_len;
+  Lo.L = L;
+  Lo.pieces = maxlen > L ? (maxlen + L - 1) / L : 1;
+  Lo.pstate_off = 0;
+  Lo.carry_off = align_up((size_t)(Lo.pieces - 1) * state, kWorkspaceAlign);
+  Lo.ckpt_off = align_up(Lo.carry_off + state, kWorkspaceAlign);
+  Lo.part_off = align_up(Lo.ckpt_off + (size_t)(L / blk) * state, kWorkspaceAlign);
+  Lo.bytes = align_up(Lo.part_off + sizeof(float) * slices * N * (size_t)L * H * nred, kWorkspaceAlign);
+  return Lo;
+}
+
+// The layout a workspace of `bytes` allows: one piece if it holds the
+// recommended layout, else the longest pieces that fit (pieces = 0: none).
+inline BwdLayout backward_plan(const kda_shape_t &s, bool varlen, size_t bytes) {
+  const BwdLayout one = backward_layout(s);
+  if (bytes >= one.bytes) return one;
+  const int64_t maxlen = varlen ? s.total_tokens : (int64_t)s.seq_len;
+  for (int64_t m = (maxlen + kBwdPieceUnit - 1) / kBwdPieceUnit; m >= 1; --m) {
+    const BwdLayout Lo = backward_layout(s, varlen, m * kBwdPieceUnit);
+    if (Lo.bytes <= bytes) return Lo;
+  }
+  BwdLayout none{};
+  return none;
 }
 
 struct BwdArgs {
@@ -149,7 +191,8 @@ struct BwdArgs {
   void *workspace;
 };
 
-hipError_t launch_backward(const kda_shape_t &s, const BwdArgs &a, hipStream_t stream);
+// Runs the backward with layout L (backward_plan of the workspace).
+hipError_t launch_backward(const kda_shape_t &s, const BwdArgs &a, const BwdLayout &L, hipStream_t stream);
 
 // Prefill phases (bit mask): the chunk table and chunk-local matrices, then
 // the sequential state pass.

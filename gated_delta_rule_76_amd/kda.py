@@ -418,11 +418,14 @@ def backward_workspace_size(num_seqs, total_tokens, num_heads, d, dtype=torch.bf
 
 
 def backward(q, k, v, alpha, beta, dO, initial_state=None, dS_T=None, cu_seqlens=None, *,
-             want_dS0=True, workspace=None):
+             want_dS0=True, workspace=None, workspace_bytes=None):
     """Gradients of the layer: returns (dq, dk, dv, dalpha, dbeta, dS0), all
     fp32 (dS0 None if want_dS0 is False).  Inputs as for ``prefill`` (packed
     [T, H, D] with optional cu_seqlens, or [B, T, H, D]); dO has v's shape
-    (fp32), dS_T the final states' shape (fp32) or None for zero."""
+    (fp32), dS_T the final states' shape (fp32) or None for zero.
+    ``workspace`` (uint8 device tensor) or ``workspace_bytes`` bound the
+    scratch memory (below the recommended size the sequences run in pieces);
+    by default the recommended size is allocated."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require_gpu(name, t)
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -465,7 +468,8 @@ def backward(q, k, v, alpha, beta, dO, initial_state=None, dS_T=None, cu_seqlens
     _check(lib().kda_backward_workspace_size(ctypes.byref(shape), ctypes.byref(need)),
            "kda_backward_workspace_size")
     if workspace is None:
-        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=dev)
+        nbytes = int(need.value) if workspace_bytes is None else int(workspace_bytes)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _require_gpu("workspace", workspace)
     _check(lib().kda_backward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                               _ptr(cu_seqlens), _ptr(initial_state), _ptr(dO), _ptr(dS_T), _ptr(dq),

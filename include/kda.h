@@ -311,11 +311,22 @@ kda_status_t kda_state_commit(const kda_shape_t *shape, float *S, const float *S
  *   dalpha        alpha's layout, fp32 output
  *   dbeta         [total_tokens][H] fp32 output
  *   dS0           [N][H][d_k][d_v] fp32 output, or NULL to skip
- *   workspace     at least kda_backward_workspace_size() bytes, 256-byte
- *                 aligned: state checkpoints (floor(T/B) + N per head, B the
- *                 checkpoint interval above) and
- *                 per-16-column partial sums of dq, dk, dalpha, dbeta
- *                 (4 (3 d + 1) (d/16) T H bytes at most)
+ *   workspace     256-byte aligned.  kda_backward_workspace_size() gives the
+ *                 recommended size: state checkpoints (floor(T/B) + N per
+ *                 head, B the checkpoint interval above) and per-16-column
+ *                 partial sums of dq, dk, dalpha, dbeta (4 (3 d + 1) (d/16)
+ *                 T H bytes at most), linear in T.  A smaller workspace also
+ *                 works: every sequence is then cut into pieces of L tokens
+ *                 (L a multiple of 48, the largest that fits), a forward
+ *                 sweep stores the state at each piece start and the pieces
+ *                 run from last to first, handing dL/dS on; it needs the
+ *                 piece-start states ((P-1) N H d_k d_v floats for P pieces
+ *                 of the longest sequence, total_tokens for varlen), a carry
+ *                 of N H d_k d_v floats and the checkpoints and partial sums
+ *                 of one piece, and costs one more forward sweep.  The
+ *                 results are bit-identical to the one-piece run.
+ *                 KDA_ERR_WORKSPACE_TOO_SMALL when not even 48-token pieces
+ *                 fit.
  * Outputs must not overlap inputs.  Results are deterministic (the partial
  * sums are added in a fixed order). */
 kda_status_t kda_backward_workspace_size(const kda_shape_t *shape, size_t *bytes);

@@ -5,6 +5,9 @@ The kernel re-runs the recurrence and its reverse in fp32 from inputs that are
 exact in fp32 (bf16 widens exactly), like the decode kernel; rel-L2 1e-5 per
 gradient (o-sized and state-sized tensors separately) is asserted for both
 input dtypes on the small cases, 1e-4 on the 4096-token workload sample.
+A workspace below the recommended size runs every sequence in pieces; those
+results must equal the one-piece results bit for bit (the same token steps
+in the same order), and the 2^20-token workload runs in 4 GiB.
 """
 
 import numpy as np
@@ -139,3 +142,106 @@ def test_backward_long_varlen_weak_decay():
     cu = np.asarray(d["cu_seqlens"].cpu())
     want = _oracle(d, dO, np64(dST), cu=cu, S0=np64(d["S0"]))
     _check(got, want, 1e-4, "backward long varlen")
+
+
+def _align(x):
+    return -(-x // 256) * 256
+
+
+def _piece_bytes(N, H, D, maxlen, L, dtype, gate="channel"):
+    """Workspace of the piece layout for pieces of L tokens (the layout
+    include/kda.h describes): piece-start states, carry, one piece's
+    checkpoints and partial rows."""
+    blk = (8 if dtype == torch.float32 else 12) if D >= 128 else 16
+    nred = 2 * D + 2 if gate == "head" else 3 * D + 1
+    state = 4 * N * H * D * D
+    P = -(-maxlen // L) if maxlen > L else 1
+    off = _align((P - 1) * state)
+    off = _align(off + state)
+    off = _align(off + (L // blk) * state)
+    return _align(off + 4 * (D // 16) * N * L * H * nred)
+
+
+# (lengths, dense batch?, heads, head size, dtype, gate)
+PIECE_CASES = [([300, 300], True, 2, 128, torch.bfloat16, "channel"),
+               ([0, 100, 37, 500, 0, 64, 1, 129], False, 2, 128, torch.bfloat16, "channel"),
+               ([0, 0, 250], False, 3, 32, torch.float32, "head"),
+               ([200, 7], False, 2, 16, torch.float32, "channel")]
+
+
+@pytest.mark.parametrize("case", range(len(PIECE_CASES)))
+def test_backward_pieces_equal_one_piece(case):
+    """Workspaces below the recommended size (pieces of 48 to 240 tokens:
+    piece edges inside sequences, empty pieces and empty sequences) give
+    every output of the one-piece run bit for bit."""
+    lens, dense, H, D, dtype, gate = PIECE_CASES[case]
+    dev = device()
+    d = inputs.prefill_inputs(lens, H, D, dtype, "medium", 0.5, seed=90 + case, device=dev, gate=gate)
+    N, T = len(lens), sum(lens)
+    dO, dST = inputs.grad_inputs(T, H, D, N, seed=90 + case, device=dev, dS_std=0.5)
+    q, k, v, a, b = (d[x] for x in ("q", "k", "v", "alpha", "beta"))
+    cu = d["cu_seqlens"]
+    if dense:
+        shp = lambda t: t.reshape((N, lens[0]) + tuple(t.shape[1:]))
+        q, k, v, a, b, dO = (shp(t) for t in (q, k, v, a, b, dO))
+        cu = None
+    args = (q, k, v, a, b, dO, d["S0"], dST, cu)
+    ref = kda.backward(*args)
+    full = kda.backward_workspace_size(N, T, H, D, dtype, kda.KDA_GATE_HEAD if gate == "head" else 0)
+    maxlen = lens[0] if dense else T
+    for L in (48, 96, 144, 240):
+        ws = _piece_bytes(N, H, D, maxlen, L, dtype, gate)
+        if ws >= full:
+            continue
+        print(f"pieces: case {case} L={L} workspace {ws} of {full}", flush=True)
+        got = kda.backward(*args, workspace_bytes=ws)
+        for name, g, r in zip(NAMES, got, ref):
+            assert torch.equal(g, r), f"L={L}: {name} differs"
+
+
+def test_backward_long_sequence_bounded_equals_recommended():
+    """One sequence of 2^17 tokens, H=8, d=128, bf16: a 1 GiB workspace
+    (pieces) against the recommended 18.5 GB one, every output bit for bit."""
+    dev = device()
+    T, H, D = 1 << 17, 8, 128
+    d = inputs.prefill_inputs([T], H, D, torch.bfloat16, "medium", 0.1, seed=21, device=dev)
+    dO, dST = inputs.grad_inputs(T, H, D, 1, seed=21, device=dev)
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], dO, d["S0"], dST)
+    small = kda.backward(*args, workspace_bytes=1 << 30)
+    torch.cuda.synchronize()
+    ref = kda.backward(*args)
+    for name, g, r in zip(NAMES, small, ref):
+        assert torch.equal(g, r), f"{name} differs"
+
+
+def test_backward_1m_tokens_in_4gib():
+    """The 2^20-token workload (B=1, H=32, d=128, bf16, strong decay, S0 = 0)
+    with dO ~ N(0,1) and dS_T ~ 0.02 N(0,1), in a 4 GiB workspace (its
+    recommended one would be ~600 GB).  Under this decay a state or state
+    gradient 1,024 tokens away weighs below 1e-300, so on a seeded sample of
+    4 heads the gradients of the first 3,072 tokens and dS0 are checked
+    against the oracle over the first 4,096 tokens (dS at token 4,096 taken
+    as 0), and those of the last 3,072 tokens against the oracle over the
+    last 4,096 (S at their start taken as 0)."""
+    dev = device()
+    spec = inputs.WORKLOADS["long_1m"]
+    T, H, D = spec["lengths"][0], spec["H"], spec["D"]
+    d = inputs.prefill_inputs([T], H, D, torch.bfloat16, "strong", None, seed=0, device=dev)
+    dO, dST = inputs.grad_inputs(T, H, D, 1, seed=0, device=dev)
+    got = kda.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dO, None, dST,
+                       workspace_bytes=4 << 30)
+    heads = seeded_sample(H, 4, seed=5)
+    W, K = 4096, 3072
+    sel = lambda t, s: np64(t[s][:, heads])
+    first = kda_backward(*(sel(d[x], slice(0, W)) for x in ("q", "k", "v", "alpha", "beta")),
+                         sel(dO, slice(0, W)), None, None)
+    for name, g, w in zip(NAMES[:5], got[:5], first[:5]):
+        e = rel_l2(sel(g, slice(0, K)), w[:K])
+        assert e < 1e-4, f"1M backward, first tokens: {name} rel-L2 {e:.3e}"
+    e = rel_l2(np64(got[5][:, heads]), first[5])
+    assert e < 1e-4, f"1M backward: dS0 rel-L2 {e:.3e}"
+    last = kda_backward(*(sel(d[x], slice(T - W, T)) for x in ("q", "k", "v", "alpha", "beta")),
+                        sel(dO, slice(T - W, T)), None, np64(dST[:, heads]))
+    for name, g, w in zip(NAMES[:5], got[:5], last[:5]):
+        e = rel_l2(sel(g, slice(T - K, T)), w[W - K:])
+        assert e < 1e-4, f"1M backward, last tokens: {name} rel-L2 {e:.3e}"
