@@ -65,6 +65,9 @@ constexpr float kTinyBlock = 7.888609052210118e-31f;  // 2^-100
 // Word 3 of a raw (stride 0) buffer descriptor: 32-bit data format; with it
 // an access at an offset past num_records is dropped (stores) or reads 0.
 constexpr int kBufferWord3 = 0x00020000;
+// State-pass workgroups of one 16-column tile above which the state pass
+// takes two tiles per workgroup (the CUs of the chip).
+constexpr int64_t kStateWideAbove = 256;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Pre-activation inputs (KDA_INPUT_PREACT): decay rate exp(-softplus(a)),
@@ -990,22 +993,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 // congruent mod 8: they share an XCD and its L2, and every record is fetched
 // from HBM once for all of them.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int CT = 1>
 struct ScanCfg {
   static constexpr int NW = 8;                   // waves per workgroup
   static constexpr int NTH = 64 * NW;
-  static constexpr int VW = 16;                  // value columns per workgroup
+  static constexpr int VW = 16 * CT;             // value columns per workgroup (CT tiles of 16)
   static constexpr int G = D / VW;               // workgroups per (sequence, head)
   static constexpr int NKB = Rec<D>::NKB;
   static constexpr int NTILE = Rec<D>::NTILE;    // state row tiles
   static_assert(NTILE <= NW, "shape");
 };
 
-template <int D, typename TIn>
+template <int D, typename TIn, int CT = 1>
 struct ScanBuf {
-  using Cf = ScanCfg<D>;
-  // U waves: V row 16 rt + lane / 4, columns 4 (lane & 3) .. + 3 (one load)
-  uint32_t v[2 * sizeof(TIn) / 2];
+  using Cf = ScanCfg<D, CT>;
+  // U waves: V row 16 rt + lane / 4, columns 4 CT (lane & 3) .. + 4 CT - 1
+  uint32_t v[CT * 2 * sizeof(TIn) / 2];
   FragRaw mt[2];            // O waves: M T, row tile rt
   FragRaw a[Cf::NKB];       // Khat (U waves) or Qhat (O waves), row tile rt
   FragRaw p[2];             // Ktil^T T, state tile = wave
@@ -1015,10 +1018,10 @@ struct ScanBuf {
 
 // Loads of one record, in two groups issued in the two phases of the
 // previous chunk: the row-tile operands (group 0) and the rest (group 1).
-template <int D, typename TIn, typename P>
-__device__ __forceinline__ void load_scan_a(ScanBuf<D, TIn> &B, int kk, const char *rec, int wave, int lane,
+template <int D, typename TIn, typename P, int CT>
+__device__ __forceinline__ void load_scan_a(ScanBuf<D, TIn, CT> &B, int kk, const char *rec, int wave, int lane,
                                             int rot) {
-  using Cf = ScanCfg<D>;
+  using Cf = ScanCfg<D, CT>;
   using Rc = Rec<D>;
   // The workgroups of one head read the same record at the same time; each
   // starts at a different k-block (register slot kk holds k-block
@@ -1034,8 +1037,8 @@ __device__ __forceinline__ void load_scan_a(ScanBuf<D, TIn> &B, int kk, const ch
 // per lane, through a buffer descriptor spanning the chunk's valid rows
 // (padding rows read 0).  (Offsets are 32-bit: the host requires
 // 64 H d 4 < 2^31.)
-template <int D, typename TIn>
-__device__ __forceinline__ void load_scan_v(ScanBuf<D, TIn> &B, const TIn *v, int64_t vt0, int valid, int h, int H,
+template <int D, typename TIn, int CT>
+__device__ __forceinline__ void load_scan_v(ScanBuf<D, TIn, CT> &B, const TIn *v, int64_t vt0, int valid, int h, int H,
                                             int col0, int wave, int lane) {
   const int rt = wave & 3;
   const uint64_t addr = reinterpret_cast<uint64_t>(v + (vt0 * H + h) * D + col0);
@@ -1044,23 +1047,26 @@ __device__ __forceinline__ void load_scan_v(ScanBuf<D, TIn> &B, const TIn *v, in
   const int nbytes = __builtin_amdgcn_readfirstlane(valid * H * D * (int)sizeof(TIn));
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, nbytes, kBufferWord3);
-  const int off = ((16 * rt + (lane >> 2)) * H * D + 4 * (lane & 3)) * (int)sizeof(TIn);
-  if constexpr (sizeof(TIn) == 2) {
+  const int off = ((16 * rt + (lane >> 2)) * H * D + 4 * CT * (lane & 3)) * (int)sizeof(TIn);
+  if constexpr (sizeof(TIn) == 2 && CT == 1) {
     const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
     B.v[0] = x[0];
     B.v[1] = x[1];
   } else {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    B.v[0] = x[0];
-    B.v[1] = x[1];
-    B.v[2] = x[2];
-    B.v[3] = x[3];
+#pragma unroll
+    for (int j = 0; j < CT * (int)sizeof(TIn) / 4; ++j) {  // 16-byte pieces
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * j, 0, 0);
+      B.v[4 * j] = x[0];
+      B.v[4 * j + 1] = x[1];
+      B.v[4 * j + 2] = x[2];
+      B.v[4 * j + 3] = x[3];
+    }
   }
 }
 
-template <int D, typename TIn, typename P>
-__device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec, int wave, int lane) {
-  using Cf = ScanCfg<D>;
+template <int D, typename TIn, typename P, int CT>
+__device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn, CT> &B, const char *rec, int wave, int lane) {
+  using Cf = ScanCfg<D, CT>;
   using Rc = Rec<D>;
   using IO = FragIO<P>;
   // M T is loaded by the O waves only (a wave-uniform branch).
@@ -1079,23 +1085,27 @@ __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn> &B, const char *rec,
 }
 
 // Two waves per SIMD: the two register sets of record fragments take about
-// half of each wave's 256 registers.
-template <int D, typename TIn, typename P>
+// half of each wave's 256 registers.  CT = 1 or 2 tiles of 16 value columns
+// per workgroup: with CT = 2 every record fragment a wave loads serves two
+// products, so a head's record is streamed to half as many CUs (batches with
+// more workgroups than CUs); with CT = 1 a head's chain spreads over twice
+// as many CUs (small batches).
+template <int D, typename TIn, typename P, int CT>
 __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_state_kernel(
     const TIn *__restrict__ v, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
     int64_t total_tokens, int64_t W, int64_t j0, const int32_t *__restrict__ base,
     const char *__restrict__ recs, const float *S0, float *carry, float *__restrict__ o, float *S_T) {
-  using Cf = ScanCfg<D>;
+  using Cf = ScanCfg<D, CT>;
   using Rc = Rec<D>;
   using IO = FragIO<P>;
-  using Buf = ScanBuf<D, TIn>;
+  using Buf = ScanBuf<D, TIn, CT>;
   constexpr int VW = Cf::VW, G = Cf::G, NKB = Cf::NKB, NTILE = Cf::NTILE, NTH = Cf::NTH;
   constexpr int DK = D < 32 ? 32 : D;
 
   __shared__ Plane<P, VW, DK> Sop;     // S^T in operand form (rows = value columns)
   __shared__ Plane<P, VW, C> Uop;      // U^T in operand form
-  __shared__ __attribute__((aligned(16))) float s_ot[4][16][20];  // o tile of each O wave, row-major
-  __shared__ __attribute__((aligned(16))) TIn s_vt[4][16][16];  // V tile of each U wave, row-major
+  __shared__ __attribute__((aligned(16))) float s_ot[4][16][VW + 4];  // o tile of each O wave, row-major
+  __shared__ __attribute__((aligned(16))) TIn s_vt[4][16][VW];        // V tile of each U wave, row-major
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1128,12 +1138,17 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   if constexpr (DK > D) {
     for (int e = tid; e < VW * (DK - D); e += NTH) Sop.store(e / (DK - D), D + e % (DK - D), 0.f);
   }
-  f32x4 sreg = zero4();
+  f32x4 sreg[CT];
   const float *S0p = sin ? sin + (size_t)pair * D * D : nullptr;
-  if (wave < NTILE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sreg[i] = S0p ? S0p[(size_t)(16 * wave + 4 * g + i) * D + col0 + m] : 0.f;
-    Sop.store4(m, 16 * wave + 4 * g, sreg);
+  for (int t = 0; t < CT; ++t) {
+    sreg[t] = zero4();
+    if (wave < NTILE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sreg[t][i] = S0p ? S0p[(size_t)(16 * wave + 4 * g + i) * D + col0 + 16 * t + m] : 0.f;
+      Sop.store4(16 * t + m, 16 * wave + 4 * g, sreg[t]);
+    }
   }
 
   // This stripe's chunks of the sequence, numbered within the sequence.
@@ -1175,7 +1190,9 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   // spanning exactly the chunk's valid rows (the hardware drops the stores
   // of padding rows).  (Offsets are 32-bit: the host requires
   // 64 H d 4 < 2^31.)
-  f32x4 opend = zero4();
+  f32x4 opend[CT];
+#pragma unroll
+  for (int t = 0; t < CT; ++t) opend[t] = zero4();
   int64_t pend_t0 = 0;
   int pend_valid = 0;
   auto store_o = [&]() __attribute__((always_inline)) {
@@ -1187,16 +1204,22 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     const int nbytes = __builtin_amdgcn_readfirstlane(pend_valid * H * D * (int)sizeof(float));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<float *>(((uint64_t)hi << 32) | lo), 0, nbytes, kBufferWord3);
-    float(*ot)[20] = s_ot[rt];
+    float(*ot)[VW + 4] = s_ot[rt];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ot[4 * g + i][m] = opend[i];
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ot[4 * g + i][16 * t + m] = opend[t][i];
     // (one wave writes and reads its own tile: LDS executes a wave's
     // accesses in order)
     __builtin_amdgcn_wave_barrier();
     const int r = lane >> 2, cq = lane & 3;
-    const float4 x = *reinterpret_cast<const float4 *>(&ot[r][4 * cq]);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs,
-                                           ((16 * rt + r) * H * D + 4 * cq) * (int)sizeof(float), 0, 0);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+      const float4 x = *reinterpret_cast<const float4 *>(&ot[r][4 * CT * cq + 4 * j]);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs,
+                                             ((16 * rt + r) * H * D + 4 * CT * cq + 4 * j) * (int)sizeof(float),
+                                             0, 0);
+    }
   };
 
   // The loads of the next record are spread over this chunk's two phases,
@@ -1208,28 +1231,40 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 
     // Khat S (U waves) or Qhat S (O waves) for row tile rt.  All S operand
     // fragments are read first, so their LDS latency is paid once.
-    typename P::Frag Bs[NKB];
+    typename P::Frag Bs[CT][NKB];
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) Bs[kk] = Sop.load8(m, ((kk + cg) % NKB) * 32 + 8 * g);
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) Bs[t][kk] = Sop.load8(16 * t + m, ((kk + cg) % NKB) * 32 + 8 * g);
     // This chunk's V (U waves) to the accumulator layout through LDS: rows
-    // 16 rt + 4 g + i, column m.
-    float vf[4] = {0.f, 0.f, 0.f, 0.f};
+    // 16 rt + 4 g + i, column 16 t + m.
+    float vf[CT][4];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) vf[t][0] = vf[t][1] = vf[t][2] = vf[t][3] = 0.f;
     if (uwave) {
-      if constexpr (sizeof(TIn) == 2) {
-        *reinterpret_cast<uint2 *>(&s_vt[rt][lane >> 2][4 * (lane & 3)]) = make_uint2(U.v[0], U.v[1]);
+      TIn *vrow = &s_vt[rt][lane >> 2][4 * CT * (lane & 3)];
+      if constexpr (sizeof(TIn) == 2 && CT == 1) {
+        *reinterpret_cast<uint2 *>(vrow) = make_uint2(U.v[0], U.v[1]);
       } else {
-        *reinterpret_cast<uint4 *>(&s_vt[rt][lane >> 2][4 * (lane & 3)]) = make_uint4(U.v[0], U.v[1], U.v[2], U.v[3]);
+#pragma unroll
+        for (int j = 0; j < CT * (int)sizeof(TIn) / 4; ++j)
+          reinterpret_cast<uint4 *>(vrow)[j] = make_uint4(U.v[4 * j], U.v[4 * j + 1], U.v[4 * j + 2], U.v[4 * j + 3]);
       }
       // (one wave writes and reads its own tile: LDS executes a wave's
       // accesses in order)
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vf[i] = to_f32(s_vt[rt][4 * g + i][m]);
+      for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vf[t][i] = to_f32(s_vt[rt][4 * g + i][16 * t + m]);
     }
-    f32x4 acc0 = zero4(), acc1 = zero4();
+    f32x4 acc[2][CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) acc[0][t] = acc[1][t] = zero4();
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {  // register slot kk holds k-block (kk + cg) mod NKB
-      P::mma((kk & 1) ? acc1 : acc0, IO::frag(U.a[kk]), Bs[kk]);
+#pragma unroll
+      for (int t = 0; t < CT; ++t) P::mma(acc[kk & 1][t], IO::frag(U.a[kk]), Bs[t][kk]);
       __builtin_amdgcn_sched_barrier(0);
       load_scan_a<D, TIn, P>(Nx, kk, rn, wave, lane, cg);
       if (kk == 0) prefetch_v(cn, Nx);
@@ -1237,44 +1272,53 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     }
     Nx.tch = touch(cn + 1 < cend ? cn + 1 : cn);
     if (!uwave) store_o();  // the previous chunk's o, while the U waves form U
-    f32x4 ov;
+    f32x4 ov[CT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ov[i] = acc0[i] + acc1[i];
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[t][i] = acc[0][t][i] + acc[1][t][i];
     if (uwave) {
-      f32x4 u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        u[i] = (r < ct.valid ? vf[i] : 0.f) - ov[i];
+      for (int t = 0; t < CT; ++t) {
+        f32x4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g + i;
+          u[i] = (r < ct.valid ? vf[t][i] : 0.f) - ov[t][i];
+        }
+        Uop.store4(16 * t + m, 16 * rt + 4 * g, u);
       }
-      Uop.store4(m, 16 * rt + 4 * g, u);
     }
     __syncthreads();
 
-    // U as an operand, in the k-order of the Ktil^T T and M T fragments:
-    // rows 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3 of column m.
-    const auto u0 = Uop.load_acc_order(m, 0, g);
-    const auto u1 = Uop.load_acc_order(m, 32, g);
-    // S <- Diag(Gamma_C) S + (Ktil^T T) U
-    if (wave < NTILE) {
-      const float gm[4] = {U.gam.x, U.gam.y, U.gam.z, U.gam.w};
-      f32x4 acc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = gm[i] * sreg[i];
-      P::mma(acc, IO::frag(U.p[0]), u0);
-      P::mma(acc, IO::frag(U.p[1]), u1);
-      sreg = acc;
-      Sop.store4(m, 16 * wave + 4 * g, acc);
-    }
-    // o = Qhat S + (M T) U
-    if (!uwave) {
-      P::mma(ov, IO::frag(U.mt[0]), u0);
-      if (rt >= 2) P::mma(ov, IO::frag(U.mt[1]), u1);
+    for (int t = 0; t < CT; ++t) {
+      // U as an operand, in the k-order of the Ktil^T T and M T fragments:
+      // rows 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3 of column 16 t + m.
+      const auto u0 = Uop.load_acc_order(16 * t + m, 0, g);
+      const auto u1 = Uop.load_acc_order(16 * t + m, 32, g);
+      // S <- Diag(Gamma_C) S + (Ktil^T T) U
+      if (wave < NTILE) {
+        const float gm[4] = {U.gam.x, U.gam.y, U.gam.z, U.gam.w};
+        f32x4 sacc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[i] = gm[i] * sreg[t][i];
+        P::mma(sacc, IO::frag(U.p[0]), u0);
+        P::mma(sacc, IO::frag(U.p[1]), u1);
+        sreg[t] = sacc;
+        Sop.store4(16 * t + m, 16 * wave + 4 * g, sacc);
+      }
+      // o = Qhat S + (M T) U
+      if (!uwave) {
+        P::mma(ov[t], IO::frag(U.mt[0]), u0);
+        if (rt >= 2) P::mma(ov[t], IO::frag(U.mt[1]), u1);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     prefetch_b(cn, Nx);
     __builtin_amdgcn_sched_barrier(0);
-    opend = ov;
+#pragma unroll
+    for (int t = 0; t < CT; ++t) opend[t] = ov[t];
     pend_t0 = ct.t0;
     pend_valid = uwave ? 0 : ct.valid;
     sink += U.tch;
@@ -1305,7 +1349,9 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   if (sout != nullptr && wave < NTILE) {
     float *STp = sout + (size_t)pair * D * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) STp[(size_t)(16 * wave + 4 * g + i) * D + col0 + m] = sreg[i];
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) STp[(size_t)(16 * wave + 4 * g + i) * D + col0 + 16 * t + m] = sreg[t][i];
   }
 }
 
@@ -1323,7 +1369,12 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   const int64_t W = plan.W;
   const TIn *qp = static_cast<const TIn *>(q), *kp = static_cast<const TIn *>(k),
             *vp = static_cast<const TIn *>(v);
-  const int64_t sblocks = ((int64_t)N * H + 7) / 8 * 8 * ScanCfg<D>::G;
+  // Two 16-column tiles per state-pass workgroup once there are more
+  // workgroups of one tile than CUs (each CU then streams a record for 32
+  // value columns instead of 16); one tile otherwise.
+  const int64_t pairs8 = ((int64_t)N * H + 7) / 8 * 8;
+  const bool wide = D >= 32 && pairs8 * (D / 16) > kStateWideAbove;
+  const int64_t sblocks = pairs8 * (wide ? ScanCfg<D, D >= 32 ? 2 : 1>::G : ScanCfg<D>::G);
   hipError_t e = hipSuccess;
   if ((phases & kPhaseLocal) && cu != nullptr) {  // dense batches compute their table in the kernels
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, cu, N, s.seq_len, base);
@@ -1340,8 +1391,14 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
       if (e != hipSuccess) return e;
     }
     if (phases & kPhaseState) {
-      hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P>), dim3((unsigned)sblocks), dim3(ScanCfg<D>::NTH), 0,
-                         stream, vp, cu, s.seq_len, N, H, s.total_tokens, W, j0, base, recs, S0, carry, o, S_T);
+      if (wide) {
+        hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P, D >= 32 ? 2 : 1>), dim3((unsigned)sblocks),
+                           dim3(ScanCfg<D>::NTH), 0, stream, vp, cu, s.seq_len, N, H, s.total_tokens, W, j0, base,
+                           recs, S0, carry, o, S_T);
+      } else {
+        hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P, 1>), dim3((unsigned)sblocks), dim3(ScanCfg<D>::NTH), 0,
+                           stream, vp, cu, s.seq_len, N, H, s.total_tokens, W, j0, base, recs, S0, carry, o, S_T);
+      }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

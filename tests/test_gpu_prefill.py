@@ -290,3 +290,37 @@ def test_prefill_long_1m_workload():
     _, S2 = kda.prefill(second["q"], second["k"], second["v"], second["alpha"], second["beta"], S1,
                         workspace=ws, out=o2[half:])
     assert torch.equal(o2, o) and torch.equal(S2, ST)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_wide_state_pass_equals_per_sequence(D, dtype):
+    """A batch with more state-pass workgroups than the chip has CUs (six
+    sequences x 24 heads) takes the state pass with two 16-column tiles per
+    workgroup; each sequence run alone takes one tile per workgroup.  The two
+    sum a chunk's key blocks in a rotated order that differs between them at
+    d = 128 (each workgroup starts at its own block), so they agree to fp32
+    rounding (rel-L2 1e-6 per sequence, bit for bit below d = 128), and the
+    batch must match the oracle."""
+    dev = device()
+    lens, H = [130, 0, 64, 1, 200, 77], 24
+    d = inputs.prefill_inputs(lens, H, D, dtype, "medium", 0.3, seed=D, device=dev)
+    o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    for i, n in enumerate(lens):
+        sl = slice(cu[i], cu[i + 1])
+        oi, Si = kda.prefill(d["q"][sl], d["k"][sl], d["v"][sl], d["alpha"][sl], d["beta"][sl],
+                             d["S0"][i:i + 1].contiguous())
+        if D < 128:
+            assert torch.equal(oi, o[sl]), f"sequence {i}: o differs"
+            assert torch.equal(Si[0], ST[i]), f"sequence {i}: S_T differs"
+        else:
+            if n:
+                assert rel_l2(np64(oi), np64(o[sl])) < 1e-6, f"sequence {i}: o differs"
+            assert rel_l2(np64(Si[0]), np64(ST[i])) < 1e-6, f"sequence {i}: S_T differs"
+    cu_np = np.asarray(d["cu_seqlens"].cpu())
+    ro, rST = per_head(kda_recurrent, *(np64(d[x]) for x in ("q", "k", "v", "alpha", "beta")),
+                       S0=np64(d["S0"]), cu_seqlens=cu_np)
+    _check(o, ST, ro, rST, TOL[dtype], f"wide state pass D={D}", cu_np)
