@@ -79,6 +79,9 @@ def _parse():
     p.add_argument("--bounded-workspace-mib", type=int, default=0,
                    help="also time the prefill with a workspace of this many MiB (in stripes when "
                         "less than the recommended size)")
+    p.add_argument("--bounded-backward-mib", type=int, default=0,
+                   help="also time the backward with a workspace of this many MiB (in pieces when "
+                        "less than the recommended size)")
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -736,9 +739,9 @@ def main():
             out["verify"] = verify_summary(bench_verify(args.decode_batch, 2, dev))
         print("[bench] backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(args.workload if args.workload == "prefill_4k" else "prefill_4k", dev)
-        if args.bounded_workspace_mib:
+        if args.bounded_backward_mib:
             out["backward"]["bounded_workspace"] = bench_backward(
-                "prefill_4k", dev, ws_bytes=args.bounded_workspace_mib << 20)
+                "prefill_4k", dev, ws_bytes=args.bounded_backward_mib << 20)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -65,8 +65,8 @@ constexpr float kTinyBlock = 7.888609052210118e-31f;  // 2^-100
 // Word 3 of a raw (stride 0) buffer descriptor: 32-bit data format; with it
 // an access at an offset past num_records is dropped (stores) or reads 0.
 constexpr int kBufferWord3 = 0x00020000;
-// State-pass workgroups of one 16-column tile above which the state pass
-// takes two tiles per workgroup (the CUs of the chip).
+// Busy state-pass workgroups of one 16-column tile above which the state
+// pass takes two tiles per workgroup (the 256 CUs of the chip).
 constexpr int64_t kStateWideAbove = 256;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -1369,11 +1369,20 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   const int64_t W = plan.W;
   const TIn *qp = static_cast<const TIn *>(q), *kp = static_cast<const TIn *>(k),
             *vp = static_cast<const TIn *>(v);
-  // Two 16-column tiles per state-pass workgroup once there are more
-  // workgroups of one tile than CUs (each CU then streams a record for 32
-  // value columns instead of 16); one tile otherwise.
+  // Two 16-column tiles per state-pass workgroup once a stripe keeps more
+  // one-tile workgroups busy than the chip has CUs (each CU then streams a
+  // record for 32 value columns instead of 16); one tile otherwise.  A
+  // stripe of W packed chunks keeps about W N / chunks + 1 sequences busy
+  // (all of them with one stripe).  (Measured: two tiles win for two dense
+  // 4k sequences, 21.0 vs 18.4 M tokens/s; one tile for the eight-sequence
+  // varlen batch in 512 MiB stripes, 19.2 vs 17.0.)
   const int64_t pairs8 = ((int64_t)N * H + 7) / 8 * 8;
-  const bool wide = D >= 32 && pairs8 * (D / 16) > kStateWideAbove;
+  int64_t busy = N;
+  if (plan.stripes > 1 && plan.chunks > 0) {
+    const int64_t est = W * N / plan.chunks + 1;
+    busy = est < N ? est : N;
+  }
+  const bool wide = D >= 32 && busy * H * (D / 16) > kStateWideAbove;
   const int64_t sblocks = pairs8 * (wide ? ScanCfg<D, D >= 32 ? 2 : 1>::G : ScanCfg<D>::G);
   hipError_t e = hipSuccess;
   if ((phases & kPhaseLocal) && cu != nullptr) {  // dense batches compute their table in the kernels
