@@ -450,8 +450,9 @@ struct RowMap {
   int64_t total, t_off, plen, row_len;
 };
 
+template <bool PIECE>
 __device__ __forceinline__ int64_t map_row(const RowMap &m, int64_t r) {
-  if (m.row_len == 0) return r;
+  if constexpr (!PIECE) return r;
   const int64_t tok = r / m.H;
   const int h = (int)(r - tok * m.H);
   const int n = (int)(tok / m.row_len);
@@ -477,7 +478,7 @@ __device__ __forceinline__ int64_t map_row(const RowMap &m, int64_t r) {
 // fixed, scattered to their outputs.  Four consecutive sums per thread when
 // every slice starts on a 16-byte boundary, with the loads of all slices in
 // flight together.
-template <int D, int GATE>
+template <int D, int GATE, bool PIECE>
 __device__ __forceinline__ void bwd_put(const RowMap &m, int64_t i, float acc, float *__restrict__ dk,
                                         float *__restrict__ dq, float *__restrict__ dalpha,
                                         float *__restrict__ dbeta) {
@@ -485,7 +486,7 @@ __device__ __forceinline__ void bwd_put(const RowMap &m, int64_t i, float acc, f
   constexpr int EB = GATE == KDA_GATE_HEAD ? 2 * D : 3 * D;
   const int64_t r = i / NRED;
   const int e = (int)(i - r * NRED);
-  const int64_t th = map_row(m, r);
+  const int64_t th = map_row<PIECE>(m, r);
   if (th < 0) return;
   if (e < D) {
     dk[th * D + e] = acc;
@@ -500,7 +501,7 @@ __device__ __forceinline__ void bwd_put(const RowMap &m, int64_t i, float acc, f
   }
 }
 
-template <int D, int GATE, int SL>
+template <int D, int GATE, int SL, bool PIECE>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part, float *__restrict__ dk,
                                                          float *__restrict__ dq, float *__restrict__ dalpha,
                                                          float *__restrict__ dbeta, int64_t rows, const RowMap m) {
@@ -523,10 +524,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict
         acc.z += x[s].z;
         acc.w += x[s].w;
       }
-      bwd_put<D, GATE>(m, 4 * v, acc.x, dk, dq, dalpha, dbeta);
-      bwd_put<D, GATE>(m, 4 * v + 1, acc.y, dk, dq, dalpha, dbeta);
-      bwd_put<D, GATE>(m, 4 * v + 2, acc.z, dk, dq, dalpha, dbeta);
-      bwd_put<D, GATE>(m, 4 * v + 3, acc.w, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE, PIECE>(m, 4 * v, acc.x, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE, PIECE>(m, 4 * v + 1, acc.y, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE, PIECE>(m, 4 * v + 2, acc.z, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE, PIECE>(m, 4 * v + 3, acc.w, dk, dq, dalpha, dbeta);
     }
   } else {
     for (int64_t i = first; i < n; i += stride) {
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict
       float acc = x[0];
 #pragma unroll
       for (int s = 1; s < SL; ++s) acc += x[s];
-      bwd_put<D, GATE>(m, i, acc, dk, dq, dalpha, dbeta);
+      bwd_put<D, GATE, PIECE>(m, i, acc, dk, dq, dalpha, dbeta);
     }
   }
 }
@@ -564,8 +565,13 @@ hipError_t launch_bwd_t(const kda_shape_t &s, const BwdArgs &a, const BwdLayout 
     if (n <= 0) return hipSuccess;
     const int64_t w = n % 4 == 0 ? n / 4 : n;  // work items (four sums each when aligned)
     const int64_t g = (w + 255) / 256 < 8192 ? (w + 255) / 256 : 8192;
-    hipLaunchKernelGGL((bwd_reduce_kernel<D, GATE, Cf::SL>), dim3((unsigned)g), dim3(256), 0, stream, part, a.dk,
-                       a.dq, a.dalpha, a.dbeta, rows * s.num_heads, m);
+    if (m.row_len == 0) {
+      hipLaunchKernelGGL((bwd_reduce_kernel<D, GATE, Cf::SL, false>), dim3((unsigned)g), dim3(256), 0, stream, part,
+                         a.dk, a.dq, a.dalpha, a.dbeta, rows * s.num_heads, m);
+    } else {
+      hipLaunchKernelGGL((bwd_reduce_kernel<D, GATE, Cf::SL, true>), dim3((unsigned)g), dim3(256), 0, stream, part,
+                         a.dk, a.dq, a.dalpha, a.dbeta, rows * s.num_heads, m);
+    }
     return hipGetLastError();
   };
   hipError_t e;
