@@ -2,14 +2,18 @@
 runs of bench.py.
 
     rocprofv3 --pmc FETCH_SIZE -d DIR_F -o f --output-format csv -- \\
-        python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-decode --calibrate-copy
+        python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-decode --no-variants \\
+        --calibrate-copy
     rocprofv3 --pmc WRITE_SIZE -d DIR_W -o w --output-format csv -- \\
-        python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-decode --calibrate-copy
+        python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-decode --no-variants \\
+        --calibrate-copy
     python -m gated_delta_rule_76_amd.counters DIR_F/f_counter_collection.csv \\
         DIR_W/w_counter_collection.csv --workload prefill_4k > profiles/traffic_prefill_4k.json
 
-and for the decode step (bench.py without --no-decode, with --no-variants so
-that only the per-channel decode kernel runs):
+(--no-variants: only the per-channel, activated-input kernels run, which
+the summary matches by name), and for the decode step (bench.py without
+--no-decode, with --no-variants so that only the per-channel decode kernel
+runs):
 
     python -m gated_delta_rule_76_amd.counters F.csv W.csv --target decode \\
         --workload decode_b256 > profiles/traffic_decode_b256.json
