@@ -379,21 +379,36 @@ __device__ __forceinline__ void mma_exact_b(f32x4 &acc, const F32::Frag &a, cons
   F32::mma(acc, a, b);
 }
 
-// Fragment indices inside one record.
-template <int D>
+// Byte offsets inside one record.
+//
+// EXACT (one decay rate per head, bf16 q/k, split-bf16 operands): Khat_r =
+// Gamma_r k_r and Qhat_r = Gamma_r q_r are a per-token scalar times a row
+// that is exact in bf16 (with pre-activation inputs the scalar also takes
+// 1/||k_r|| or 1/||q_r||), so the record holds k and q as single bf16
+// fragments (1 KiB) and the two per-token scalars, and the state pass scales
+// the rows of Khat S and Qhat S by them: 32 KiB less record per chunk and
+// two matrix-core products per k-block instead of three, with no rounding of
+// Khat or Qhat.
+template <int D, bool EXACT = false>
 struct Rec {
   static constexpr int NKB = (D < 32 ? 32 : D) / 32;  // k-blocks over key channels
   static constexpr int NTILE = D / 16;                 // 16-row tiles of key channels
-  static constexpr int KHAT = 0;                       // Khat        [row tile][kb]
-  static constexpr int QHAT = 4 * NKB;                 // Qhat        [row tile][kb]
-  static constexpr int PMAT = 8 * NKB;                 // Ktil^T T    [channel tile][kb of tokens]
-  static constexpr int MTM = 8 * NKB + 2 * NTILE;      // M T         non-zero [row tile][kb], 6 blocks
-  static constexpr int NFRAG = MTM + 6;
-  static constexpr size_t GAM = (size_t)NFRAG * kFragBytes;  // Gamma_C (D floats)
-  static constexpr size_t BYTES = (GAM + sizeof(float) * D + kWorkspaceAlign - 1) / kWorkspaceAlign *
-                                  kWorkspaceAlign;
+  static constexpr size_t AF = EXACT ? 1024 : kFragBytes;               // bytes of a Khat / Qhat fragment
+  static constexpr size_t KHAT = 0;                                     // Khat   [row tile][kb]
+  static constexpr size_t QHAT = KHAT + (size_t)4 * NKB * AF;           // Qhat   [row tile][kb]
+  static constexpr size_t PMAT = QHAT + (size_t)4 * NKB * AF;           // Ktil^T T [channel tile][kb of tokens]
+  static constexpr size_t MTM = PMAT + (size_t)2 * NTILE * kFragBytes;  // M T    non-zero [row tile][kb], 6 blocks
+  static constexpr size_t GAM = MTM + (size_t)6 * kFragBytes;           // Gamma_C (D floats)
+  static constexpr size_t RFAC = GAM + sizeof(float) * D;               // EXACT: per-token factors of k, then q
+  static constexpr size_t BYTES = (RFAC + (EXACT ? 2 * C * sizeof(float) : 0) + kWorkspaceAlign - 1) /
+                                  kWorkspaceAlign * kWorkspaceAlign;
+  __device__ __forceinline__ static size_t khat(int rt, int kb) { return KHAT + (size_t)(NKB * rt + kb) * AF; }
+  __device__ __forceinline__ static size_t qhat(int rt, int kb) { return QHAT + (size_t)(NKB * rt + kb) * AF; }
+  __device__ __forceinline__ static size_t pmat(int t, int kb) { return PMAT + (size_t)(2 * t + kb) * kFragBytes; }
   // M T is lower triangular: row tiles 0 and 1 have k-block 0 only.
-  __device__ __forceinline__ static int mt_frag(int rt, int kb) { return rt < 2 ? rt : 2 * rt - 2 + kb; }
+  __device__ __forceinline__ static size_t mtm(int rt, int kb) {
+    return MTM + (size_t)(rt < 2 ? rt : 2 * rt - 2 + kb) * kFragBytes;
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -541,7 +556,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     int64_t total_tokens, int64_t W, int64_t j0, const int32_t *__restrict__ base,
     char *__restrict__ recs) {
   using Cf = LocCfg<D>;
-  using Rc = Rec<D>;
+  // one rate per head with bf16 q/k: the record holds exact k and q (Rec)
+  constexpr bool EXACT = GATE == KDA_GATE_HEAD && std::is_same<TIn, __bf16>::value &&
+                         std::is_same<P, SplitBF16>::value;
+  using Rc = Rec<D, EXACT>;
   using IO = FragIO<P>;
   using Frag = typename P::Frag;
   constexpr int DK = Cf::DK, NKB = Cf::NKB, MP = Cf::MP, LP = Cf::LP, KP = Cf::KP;
@@ -742,12 +760,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     }
     const Frag ka = P::make(xa);
     const Frag qa = P::make(xq);
+    if constexpr (EXACT) {
+      // k and q as loaded (zero past the chunk), and the token's factors
+      // Gamma_r / ||k_r|| and Gamma_r / ||q_r|| (one rate per head: bp and
+      // bef are the same in every channel)
+      // (a value select per word: a select between the two uint4 objects
+      // would take their addresses and move kr, qr to scratch)
+      const uint32_t keep = ok ? 0xffffffffu : 0u;
+      const uint4 kw = kr[kb].u, qw = qr[kb].u;
+      *reinterpret_cast<uint4 *>(rec + Rc::khat(wave, kb) + 16 * lane) =
+          make_uint4(kw.x & keep, kw.y & keep, kw.z & keep, kw.w & keep);
+      *reinterpret_cast<uint4 *>(rec + Rc::qhat(wave, kb) + 16 * lane) =
+          make_uint4(qw.x & keep, qw.y & keep, qw.z & keep, qw.w & keep);
+      if (kb == 0 && g == 0) {
+        float *rf = reinterpret_cast<float *>(rec + Rc::RFAC);
+        const float gr = rv ? bp[0][0] * bef[0] : 0.f;
+        rf[16 * wave + m] = gr * inv_k;
+        rf[C + 16 * wave + m] = gr * inv_q;
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = xa[j] * bef[j];  // Gamma_r k_r
-    IO::store(rec + (size_t)(Rc::KHAT + NKB * wave + kb) * kFragBytes, lane, x);
+      for (int j = 0; j < 8; ++j) x[j] = xa[j] * bef[j];  // Gamma_r k_r
+      IO::store(rec + Rc::khat(wave, kb), lane, x);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = xq[j] * bef[j];  // Gamma_r q_r
-    IO::store(rec + (size_t)(Rc::QHAT + NKB * wave + kb) * kFragBytes, lane, x);
+      for (int j = 0; j < 8; ++j) x[j] = xq[j] * bef[j];  // Gamma_r q_r
+      IO::store(rec + Rc::qhat(wave, kb), lane, x);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = block_tiny ? 0.f : kf[j] * __builtin_amdgcn_rcpf(bp[kb][j]);
     const Frag ki = P::make(x);
@@ -923,7 +961,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
           x[i] = acc[2 * kb][i];
           x[4 + i] = acc[2 * kb + 1][i];
         }
-        IO::store(rec + (size_t)(Rc::MTM + Rc::mt_frag(wave, kb)) * kFragBytes, lane, x);
+        IO::store(rec + Rc::mtm(wave, kb), lane, x);
       }
     }
   }
@@ -964,7 +1002,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
           x[i] = acc[2 * kb][i];
           x[4 + i] = acc[2 * kb + 1][i];
         }
-        IO::store(rec + (size_t)(Rc::PMAT + 2 * t + kb) * kFragBytes, lane, x);
+        IO::store(rec + Rc::pmat(t, kb), lane, x);
       }
     }
   }
@@ -1013,23 +1051,28 @@ struct ScanBuf {
   FragRaw a[Cf::NKB];       // Khat (U waves) or Qhat (O waves), row tile rt
   FragRaw p[2];             // Ktil^T T, state tile = wave
   float4 gam;               // Gamma_C, rows of state tile = wave
+  float4 rf;                // exact records: the factors of rows 16 rt + 4 g .. + 3
   uint32_t tch;             // one word of a record two chunks ahead
 };
 
 // Loads of one record, in two groups issued in the two phases of the
 // previous chunk: the row-tile operands (group 0) and the rest (group 1).
-template <int D, typename TIn, typename P, int CT>
+template <int D, typename TIn, typename P, int CT, bool EXACT>
 __device__ __forceinline__ void load_scan_a(ScanBuf<D, TIn, CT> &B, int kk, const char *rec, int wave, int lane,
                                             int rot) {
   using Cf = ScanCfg<D, CT>;
-  using Rc = Rec<D>;
+  using Rc = Rec<D, EXACT>;
   // The workgroups of one head read the same record at the same time; each
   // starts at a different k-block (register slot kk holds k-block
   // (kk + rot) mod NKB).
   const int rt = wave & 3;
-  const int abase = wave < 4 ? Rc::KHAT : Rc::QHAT;
   const int kb = (kk + rot) % Cf::NKB;
-  FragIO<P>::load(B.a[kk], rec + (size_t)(abase + Cf::NKB * rt + kb) * kFragBytes, lane);
+  const char *f = rec + (wave < 4 ? Rc::khat(rt, kb) : Rc::qhat(rt, kb));
+  if constexpr (EXACT) {
+    B.a[kk].a = *reinterpret_cast<const uint4 *>(f + 16 * lane);  // one exact bf16 plane
+  } else {
+    FragIO<P>::load(B.a[kk], f, lane);
+  }
 }
 
 // V of a chunk (U waves), issued with the first row-tile load of the
@@ -1064,24 +1107,26 @@ __device__ __forceinline__ void load_scan_v(ScanBuf<D, TIn, CT> &B, const TIn *v
   }
 }
 
-template <int D, typename TIn, typename P, int CT>
+template <int D, typename TIn, typename P, int CT, bool EXACT>
 __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn, CT> &B, const char *rec, int wave, int lane) {
   using Cf = ScanCfg<D, CT>;
-  using Rc = Rec<D>;
+  using Rc = Rec<D, EXACT>;
   using IO = FragIO<P>;
   // M T is loaded by the O waves only (a wave-uniform branch).
   const int rt = wave & 3, g = lane >> 4;
   if (wave >= 4) {
     // (row tiles 0 and 1 use only their k-block 0 block)
-    IO::load(B.mt[0], rec + (size_t)(Rc::MTM + Rc::mt_frag(rt, 0)) * kFragBytes, lane);
-    if (rt >= 2) IO::load(B.mt[1], rec + (size_t)(Rc::MTM + Rc::mt_frag(rt, 1)) * kFragBytes, lane);
+    IO::load(B.mt[0], rec + Rc::mtm(rt, 0), lane);
+    if (rt >= 2) IO::load(B.mt[1], rec + Rc::mtm(rt, 1), lane);
   }
   const int t = wave < Cf::NTILE ? wave : Cf::NTILE - 1;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) IO::load(B.p[kb], rec + (size_t)(Rc::PMAT + 2 * t + kb) * kFragBytes, lane);
+  for (int kb = 0; kb < 2; ++kb) IO::load(B.p[kb], rec + Rc::pmat(t, kb), lane);
   // rows 16 t + 4 g .. + 3, the lane's row group (a vector load: a scalar
   // load here would be waited for at the next barrier, with the LDS stores)
   B.gam = *reinterpret_cast<const float4 *>(rec + Rc::GAM + sizeof(float) * (16 * t + 4 * g));
+  if constexpr (EXACT)  // factors of k (U waves) or q (O waves) for rows 16 rt + 4 g .. + 3
+    B.rf = *reinterpret_cast<const float4 *>(rec + Rc::RFAC + sizeof(float) * ((wave < 4 ? 0 : C) + 16 * rt + 4 * g));
 }
 
 // Two waves per SIMD: the two register sets of record fragments take about
@@ -1090,13 +1135,13 @@ __device__ __forceinline__ void load_scan_b(ScanBuf<D, TIn, CT> &B, const char *
 // products, so a head's record is streamed to half as many CUs (batches with
 // more workgroups than CUs); with CT = 1 a head's chain spreads over twice
 // as many CUs (small batches).
-template <int D, typename TIn, typename P, int CT>
+template <int D, typename TIn, typename P, int CT, bool EXACT>
 __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_state_kernel(
     const TIn *__restrict__ v, const int32_t *__restrict__ cu, int32_t seq_len, int N, int H,
     int64_t total_tokens, int64_t W, int64_t j0, const int32_t *__restrict__ base,
     const char *__restrict__ recs, const float *S0, float *carry, float *__restrict__ o, float *S_T) {
   using Cf = ScanCfg<D, CT>;
-  using Rc = Rec<D>;
+  using Rc = Rec<D, EXACT>;
   using IO = FragIO<P>;
   using Buf = ScanBuf<D, TIn, CT>;
   constexpr int VW = Cf::VW, G = Cf::G, NKB = Cf::NKB, NTILE = Cf::NTILE, NTH = Cf::NTH;
@@ -1175,7 +1220,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 
   Buf bufA, bufB;
   auto prefetch_b = [&](int64_t cc, Buf &B) __attribute__((always_inline)) {
-    load_scan_b<D, TIn, P>(B, rec_of(cc), wave, lane);
+    load_scan_b<D, TIn, P, CT, EXACT>(B, rec_of(cc), wave, lane);
   };
   auto prefetch_v = [&](int64_t cc, Buf &B) __attribute__((always_inline)) {
     if (uwave) {
@@ -1264,19 +1309,32 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {  // register slot kk holds k-block (kk + cg) mod NKB
 #pragma unroll
-      for (int t = 0; t < CT; ++t) P::mma(acc[kk & 1][t], IO::frag(U.a[kk]), Bs[t][kk]);
+      for (int t = 0; t < CT; ++t) {
+        if constexpr (EXACT) {  // exact bf16 k or q: its lo part is zero
+          const auto a = __builtin_bit_cast(bf16x8, U.a[kk].a);
+          acc[kk & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Bs[t][kk].hi, acc[kk & 1][t], 0, 0, 0);
+          acc[kk & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Bs[t][kk].lo, acc[kk & 1][t], 0, 0, 0);
+        } else {
+          P::mma(acc[kk & 1][t], IO::frag(U.a[kk]), Bs[t][kk]);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
-      load_scan_a<D, TIn, P>(Nx, kk, rn, wave, lane, cg);
+      load_scan_a<D, TIn, P, CT, EXACT>(Nx, kk, rn, wave, lane, cg);
       if (kk == 0) prefetch_v(cn, Nx);
       __builtin_amdgcn_sched_barrier(0);
     }
     Nx.tch = touch(cn + 1 < cend ? cn + 1 : cn);
     if (!uwave) store_o();  // the previous chunk's o, while the U waves form U
     f32x4 ov[CT];
+    // (exact records: rows scaled by Gamma_r / ||k_r|| or Gamma_r / ||q_r||)
+    const float rfac[4] = {U.rf.x, U.rf.y, U.rf.z, U.rf.w};
 #pragma unroll
     for (int t = 0; t < CT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ov[t][i] = acc[0][t][i] + acc[1][t][i];
+      for (int i = 0; i < 4; ++i) {
+        ov[t][i] = acc[0][t][i] + acc[1][t][i];
+        if constexpr (EXACT) ov[t][i] *= rfac[i];
+      }
     if (uwave) {
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
@@ -1327,7 +1385,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
 
   if (cbeg < cend) {
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) load_scan_a<D, TIn, P>(bufA, kk, rec_of(cbeg), wave, lane, cg);
+    for (int kk = 0; kk < NKB; ++kk) load_scan_a<D, TIn, P, CT, EXACT>(bufA, kk, rec_of(cbeg), wave, lane, cg);
     prefetch_v(cbeg, bufA);
     prefetch_b(cbeg, bufA);
     bufA.tch = touch(cbeg);
@@ -1376,6 +1434,9 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   // (all of them with one stripe).  (Measured: two tiles win for two dense
   // 4k sequences, 21.0 vs 18.4 M tokens/s; one tile for the eight-sequence
   // varlen batch in 512 MiB stripes, 19.2 vs 17.0.)
+  // the record layout the chunk-local kernel writes for this gate and dtype
+  constexpr bool kExact = GATE == KDA_GATE_HEAD && std::is_same<TIn, __bf16>::value &&
+                          std::is_same<P, SplitBF16>::value;
   const int64_t pairs8 = ((int64_t)N * H + 7) / 8 * 8;
   int64_t busy = N;
   if (plan.stripes > 1 && plan.chunks > 0) {
@@ -1401,11 +1462,11 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
     }
     if (phases & kPhaseState) {
       if (wide) {
-        hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P, D >= 32 ? 2 : 1>), dim3((unsigned)sblocks),
+        hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P, D >= 32 ? 2 : 1, kExact>), dim3((unsigned)sblocks),
                            dim3(ScanCfg<D>::NTH), 0, stream, vp, cu, s.seq_len, N, H, s.total_tokens, W, j0, base,
                            recs, S0, carry, o, S_T);
       } else {
-        hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P, 1>), dim3((unsigned)sblocks), dim3(ScanCfg<D>::NTH), 0,
+        hipLaunchKernelGGL((chunk_state_kernel<D, TIn, P, 1, kExact>), dim3((unsigned)sblocks), dim3(ScanCfg<D>::NTH), 0,
                            stream, vp, cu, s.seq_len, N, H, s.total_tokens, W, j0, base, recs, S0, carry, o, S_T);
       }
       e = hipGetLastError();

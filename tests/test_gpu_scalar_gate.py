@@ -3,7 +3,11 @@ the fp64 scalar-gate oracle (oracle/scalar_gate.py).
 
 alpha holds one rate per (token, head); the kernels are the KDA kernels with
 the rate broadcast to every key channel, so besides the oracle they must
-reproduce the per-channel path fed that broadcast exactly.  Tolerances as for
+reproduce the per-channel path fed that broadcast: exactly for fp32 q/k/v and
+for decode; for the bf16 prefill the scalar path keeps k and q exact in its
+chunk records (Khat = Gamma k with one Gamma per token) where the
+per-channel path carries Khat and Qhat as bf16 hi/lo pairs, so the two agree
+to within that rounding (rel-L2 5e-5).  Tolerances against the oracle as for
 KDA: rel-L2 1e-5 (fp32 q/k/v), 2e-3 (bf16), separately for o and S_T; the
 oracle consumes the exact tensors the GPU consumed.
 """
@@ -53,17 +57,22 @@ def test_scalar_gate_decay_regimes(decay, dtype):
     _check(o, ST, ro, rST, TOL[dtype], f"decay {decay}")
 
 
-def test_scalar_gate_equals_per_channel_broadcast():
-    """The per-head rate broadcast to every key channel through the KDA path
-    gives the same bits."""
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_scalar_gate_equals_per_channel_broadcast(dtype):
+    """The per-head rate broadcast to every key channel through the KDA path:
+    the same bits for fp32 q/k/v and for decode; within the per-channel
+    path's hi/lo rounding of Khat and Qhat for the bf16 prefill."""
     dev = device()
-    d = inputs.prefill_inputs([0, 1, 65, 200], 3, 128, torch.bfloat16, "medium", 0.3, seed=22,
+    d = inputs.prefill_inputs([0, 1, 65, 200], 3, 128, dtype, "medium", 0.3, seed=22,
                               device=dev, gate="head")
     wide = d["alpha"][:, :, None].expand(d["q"].shape).contiguous()
     args = (d["q"], d["k"], d["v"])
     o1, S1 = kda.prefill(*args, d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
     o2, S2 = kda.prefill(*args, wide, d["beta"], d["S0"], d["cu_seqlens"])
-    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    if dtype == torch.float32:
+        assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    else:
+        assert rel_l2(np64(o1), np64(o2)) < 5e-5 and rel_l2(np64(S1), np64(S2)) < 5e-5
     for t in range(3):
         S_a, S_b = d["S0"].clone(), d["S0"].clone()
         x = lambda key: d[key][t:t + 4].contiguous()
