@@ -130,8 +130,19 @@ def record_bytes_per_token(d):
     return rec / 64.0
 
 
+def exact_record_bytes_per_token(d):
+    """Record of the scalar-gate form with bf16 q/k: k and q as single bf16
+    fragments (1 KiB each: 4 row tiles x d/32 k-blocks), Ktil^T T (d/16 x 2
+    fragments of 2 KiB), the six M T fragments, Gamma_C (d floats) and the two
+    per-token factors (2 x 64 floats), 256-byte aligned."""
+    nkb = max(d, 32) // 32
+    raw = 2 * 4 * nkb * 1024 + (d // 16) * 2 * 2048 + 6 * 2048 + 4 * d + 2 * 64 * 4
+    return (-(-raw // 256) * 256) / 64.0
+
+
 def kernel_bytes(d, gate="channel"):
-    rb = record_bytes_per_token(d)
+    # (the scalar-gate form keeps exact k and q in its records: bf16 inputs)
+    rb = exact_record_bytes_per_token(d) if gate == "head" else record_bytes_per_token(d)
     return {"chunk_local_kernel": 512 + ALPHA_BYTES[gate] + 4 + rb, "chunk_state_kernel": rb + 256 + 512}
 
 

@@ -30,6 +30,10 @@ def test_kernel_bytes_follow_the_record_size():
     kb = bench.kernel_bytes(128)
     assert kb["chunk_local_kernel"] == 512 + 512 + 4 + rb
     assert kb["chunk_state_kernel"] == rb + 256 + 512
+    # scalar gate: k and q exact (1 KiB fragments) plus two per-token factors:
+    # 16 + 16 + 32 + 12 KiB + 512 + 512 B = 78,848 B per chunk
+    assert bench.exact_record_bytes_per_token(128) == 78848 / 64
+    assert bench.kernel_bytes(128, "head")["chunk_state_kernel"] == 78848 / 64 + 256 + 512
 
 
 def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):
