@@ -24,7 +24,7 @@ import pytest
 import torch
 
 from gated_delta_rule_76_amd import inputs, kda
-from oracle import kda_recurrent, rel_l2
+from oracle import gdn_recurrent, kda_recurrent, rel_l2
 from tests.gpu_util import device, np64, parity, seeded_sample
 from tests.oracle_pool import per_head
 
@@ -203,10 +203,12 @@ def test_prefill_varlen_8seq_workload():
     _check(o, ST, ro, rST, 2e-3, "varlen_8seq", cu)
 
 
-def test_two_phase_calls_equal_prefill():
+@pytest.mark.parametrize("gate", ["channel", "head"])
+def test_two_phase_calls_equal_prefill(gate):
     """kda_prefill_chunk_local then kda_prefill_state_pass == kda_prefill."""
     dev = device()
-    d = inputs.prefill_inputs([0, 100, 37], 2, 128, torch.bfloat16, "strong", 0.1, seed=13, device=dev)
+    d = inputs.prefill_inputs([0, 100, 37], 2, 128, torch.bfloat16, "strong", 0.1, seed=13, device=dev,
+                              gate=gate)
     args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
     ref_o, ref_S = kda.prefill(*args)
     call = kda.PrefillCall(*args)
@@ -219,11 +221,12 @@ def _table_bytes(N):
     return -(-4 * (N + 1) // 256) * 256
 
 
-# (lengths, dense batch?, heads, head size, dtype, S0)
-STRIPE_CASES = [([300, 300], True, 3, 64, torch.bfloat16, 0.3),
-                ([0, 100, 37, 500, 0, 64, 1, 129], False, 2, 128, torch.bfloat16, 0.1),
-                ([0, 0, 250], False, 2, 32, torch.float32, None),
-                ([200], False, 4, 16, torch.float32, 0.5)]
+# (lengths, dense batch?, heads, head size, dtype, S0, gate)
+STRIPE_CASES = [([300, 300], True, 3, 64, torch.bfloat16, 0.3, "channel"),
+                ([0, 100, 37, 500, 0, 64, 1, 129], False, 2, 128, torch.bfloat16, 0.1, "channel"),
+                ([0, 0, 250], False, 2, 32, torch.float32, None, "channel"),
+                ([200], False, 4, 16, torch.float32, 0.5, "channel"),
+                ([90, 0, 400, 7], False, 3, 128, torch.bfloat16, 0.2, "head")]
 
 
 @pytest.mark.parametrize("case", range(len(STRIPE_CASES)))
@@ -232,14 +235,15 @@ def test_striped_workspace_equals_one_stripe(case):
     stripe edges inside and between sequences, empty sequences) give the
     one-stripe results bit for bit: with S_T, without S_T (the state is handed
     over in the carry area after the records), and in place (S_T = S0)."""
-    lens, dense, H, D, dtype, s0 = STRIPE_CASES[case]
+    lens, dense, H, D, dtype, s0, gate = STRIPE_CASES[case]
     dev = device()
-    d = inputs.prefill_inputs(lens, H, D, dtype, "medium", s0, seed=60 + case, device=dev)
+    d = inputs.prefill_inputs(lens, H, D, dtype, "medium", s0, seed=60 + case, device=dev, gate=gate)
     N = len(lens)
     q, k, v, a, b = (d[x] for x in ("q", "k", "v", "alpha", "beta"))
     cu = d["cu_seqlens"]
     if dense:
-        q, k, v, a = (t.reshape(N, lens[0], H, D) for t in (q, k, v, a))
+        q, k, v = (t.reshape(N, lens[0], H, D) for t in (q, k, v))
+        a = a.reshape((N, lens[0]) + tuple(a.shape[1:]))
         b, cu = b.reshape(N, lens[0], H), None
     S0 = None if d["S0"] is None else d["S0"]
     ref_o, ref_S = kda.prefill(q, k, v, a, b, S0, cu)
@@ -292,9 +296,11 @@ def test_prefill_long_1m_workload():
     assert torch.equal(o2, o) and torch.equal(S2, ST)
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-def test_wide_state_pass_equals_per_sequence(D, dtype):
+@pytest.mark.parametrize("D,dtype,gate", [(32, torch.float32, "channel"), (64, torch.float32, "channel"),
+                                          (128, torch.float32, "channel"), (32, torch.bfloat16, "channel"),
+                                          (64, torch.bfloat16, "channel"), (128, torch.bfloat16, "channel"),
+                                          (128, torch.bfloat16, "head")])
+def test_wide_state_pass_equals_per_sequence(D, dtype, gate):
     """A batch with more state-pass workgroups than the chip has CUs (six
     sequences x 24 heads) takes the state pass with two 16-column tiles per
     workgroup; each sequence run alone takes one tile per workgroup.  The two
@@ -304,7 +310,7 @@ def test_wide_state_pass_equals_per_sequence(D, dtype):
     batch must match the oracle."""
     dev = device()
     lens, H = [130, 0, 64, 1, 200, 77], 24
-    d = inputs.prefill_inputs(lens, H, D, dtype, "medium", 0.3, seed=D, device=dev)
+    d = inputs.prefill_inputs(lens, H, D, dtype, "medium", 0.3, seed=D, device=dev, gate=gate)
     o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
     cu = [0]
     for n in lens:
@@ -321,6 +327,7 @@ def test_wide_state_pass_equals_per_sequence(D, dtype):
                 assert rel_l2(np64(oi), np64(o[sl])) < 1e-6, f"sequence {i}: o differs"
             assert rel_l2(np64(Si[0]), np64(ST[i])) < 1e-6, f"sequence {i}: S_T differs"
     cu_np = np.asarray(d["cu_seqlens"].cpu())
-    ro, rST = per_head(kda_recurrent, *(np64(d[x]) for x in ("q", "k", "v", "alpha", "beta")),
+    ref = kda_recurrent if gate == "channel" else gdn_recurrent
+    ro, rST = per_head(ref, *(np64(d[x]) for x in ("q", "k", "v", "alpha", "beta")),
                        S0=np64(d["S0"]), cu_seqlens=cu_np)
-    _check(o, ST, ro, rST, TOL[dtype], f"wide state pass D={D}", cu_np)
+    _check(o, ST, ro, rST, TOL[dtype], f"wide state pass D={D} {gate}", cu_np)
