@@ -35,8 +35,10 @@
 //                       A and M on the matrix cores, T by a blocked
 //                       triangular inverse, Ktil^T T and M T on the matrix
 //                       cores; writes the chunk's record (Khat, Qhat,
-//                       Ktil^T T, M T, Gamma_C as operand fragments).
-//   chunk_state_kernel  one workgroup per (sequence, head, 16 value
+//                       Ktil^T T, M T, Gamma_C as operand fragments; with
+//                       one rate per head and bf16 q/k, exact k and q and
+//                       their per-token factors instead of Khat and Qhat).
+//   chunk_state_kernel  one workgroup per (sequence, head, 16 or 32 value
 //                       columns), sequential over the sequence's chunks in
 //                       the stripe: the state slice stays in registers (fp32)
 //                       across chunks and is handed to the next stripe
@@ -1427,6 +1429,9 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   const int64_t W = plan.W;
   const TIn *qp = static_cast<const TIn *>(q), *kp = static_cast<const TIn *>(k),
             *vp = static_cast<const TIn *>(v);
+  // the record layout the chunk-local kernel writes for this gate and dtype
+  constexpr bool kExact = GATE == KDA_GATE_HEAD && std::is_same<TIn, __bf16>::value &&
+                          std::is_same<P, SplitBF16>::value;
   // Two 16-column tiles per state-pass workgroup once a stripe keeps more
   // one-tile workgroups busy than the chip has CUs (each CU then streams a
   // record for 32 value columns instead of 16); one tile otherwise.  A
@@ -1434,9 +1439,6 @@ hipError_t launch_prefill_t(const kda_shape_t &s, const void *q, const void *k, 
   // (all of them with one stripe).  (Measured: two tiles win for two dense
   // 4k sequences, 21.0 vs 18.4 M tokens/s; one tile for the eight-sequence
   // varlen batch in 512 MiB stripes, 19.2 vs 17.0.)
-  // the record layout the chunk-local kernel writes for this gate and dtype
-  constexpr bool kExact = GATE == KDA_GATE_HEAD && std::is_same<TIn, __bf16>::value &&
-                          std::is_same<P, SplitBF16>::value;
   const int64_t pairs8 = ((int64_t)N * H + 7) / 8 * 8;
   int64_t busy = N;
   if (plan.stripes > 1 && plan.chunks > 0) {
