@@ -48,7 +48,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 N_SETS = 5                     # input sets rotated between timed calls
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_prefill_4k.json")
 KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_prefill.hip")
-DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_decode_b256.json")
+DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_decode_b%d.json")  # % batch
 DECODE_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_decode.hip")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_prefill_4k.json")
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
@@ -76,6 +76,9 @@ def _parse():
     p.add_argument("--no-variants", action="store_true",
                    help="skip the scalar-gate, pre-activation, verify and backward measurements")
     p.add_argument("--decode-batch", type=int, default=256)
+    p.add_argument("--decode-large-batch", type=int, default=1024,
+                   help="with the variants, also time the decode at this batch (2 GiB of state at "
+                        "1024, eight times the Infinity Cache; 0 skips it)")
     p.add_argument("--bounded-workspace-mib", type=int, default=0,
                    help="also time the prefill with a workspace of this many MiB (in stripes when "
                         "less than the recommended size)")
@@ -651,7 +654,8 @@ def prefill_summary(pf, gate, workload=None):
 def decode_summary(dc, gate, form="final"):
     gbs = dc["B"] * dc["H"] * decode_bytes(gate) / (dc["ms_per_step"] * 1e-3) / 1e9
     # (the counter summary covers the per-channel decode kernel on activated inputs)
-    traffic = (_traffic("decode_kernel", "decode_b%d" % dc["B"], DECODE_TRAFFIC_SUMMARY, DECODE_SOURCE)
+    traffic = (_traffic("decode_kernel", "decode_b%d" % dc["B"], DECODE_TRAFFIC_SUMMARY % dc["B"],
+                        DECODE_SOURCE)
                if gate == "channel" and form == "final" else None)
     kind = ("KDA" if gate == "channel" else "scalar-gate") + (" pre-activation" if form == "preact" else "")
     return {"metric": "%s decode steps/s (B=%d, H=32, d=128)" % (kind, dc["B"]),
@@ -724,6 +728,9 @@ def main():
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         out["decode"] = decode_summary(bench_decode(args.decode_batch, dev), "channel")
+        if not args.no_variants and args.decode_large_batch:
+            print(f"[bench] decode at B={args.decode_large_batch}", file=sys.stderr, flush=True)
+            out["decode_large"] = decode_summary(bench_decode(args.decode_large_batch, dev), "channel")
     if not args.no_variants:
         # The scalar-gate (Gated DeltaNet) form on the same shapes.
         print("[bench] scalar gate", file=sys.stderr, flush=True)

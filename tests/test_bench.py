@@ -7,6 +7,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -53,14 +55,17 @@ def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch)
     assert bench._traffic("chunk_state_kernel", "prefill_4k") is None
 
 
-def test_decode_traffic_matches_its_algorithmic_bytes():
-    # the committed decode summary was taken on the committed decode source;
-    # its counters read within 1% of the algorithmic bytes of a B=256 step
-    t = bench._traffic("decode_kernel", "decode_b256", bench.DECODE_TRAFFIC_SUMMARY, bench.DECODE_SOURCE)
+@pytest.mark.parametrize("B", [256, 1024])
+def test_decode_traffic_matches_its_algorithmic_bytes(B):
+    # each committed decode summary was taken on the committed decode source;
+    # its counters read within 1% of the algorithmic bytes of one step at B
+    t = bench._traffic("decode_kernel", "decode_b%d" % B, bench.DECODE_TRAFFIC_SUMMARY % B, bench.DECODE_SOURCE)
     assert t is not None
-    algorithmic = 256 * 32 * bench.decode_bytes("channel")
+    algorithmic = B * 32 * bench.decode_bytes("channel")
     assert abs(t / algorithmic - 1) < 0.01
-    assert bench._traffic("decode_kernel", "decode_b1024", bench.DECODE_TRAFFIC_SUMMARY,
+    # a summary answers only for its own batch
+    other = 1024 if B == 256 else 256
+    assert bench._traffic("decode_kernel", "decode_b%d" % other, bench.DECODE_TRAFFIC_SUMMARY % B,
                           bench.DECODE_SOURCE) is None
 
 
