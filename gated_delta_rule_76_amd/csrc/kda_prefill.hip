@@ -371,16 +371,6 @@ struct FragIO<F32> {
   }
 };
 
-// hi*b + lo*b for an operand b that is exact in bf16 (v in bf16): the lo part
-// of b is zero, so the hi*lo term is skipped.
-__device__ __forceinline__ void mma_exact_b(f32x4 &acc, const SplitBF16::Frag &a, const SplitBF16::Frag &b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
-}
-__device__ __forceinline__ void mma_exact_b(f32x4 &acc, const F32::Frag &a, const F32::Frag &b) {
-  F32::mma(acc, a, b);
-}
-
 // Byte offsets inside one record.
 //
 // EXACT (one decay rate per head, bf16 q/k, split-bf16 operands): Khat_r =
