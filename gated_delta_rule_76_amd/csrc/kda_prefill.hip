@@ -31,7 +31,7 @@
 //   schedule_kernel     varlen packing: chunk counts per sequence -> table
 //                       of first-chunk indices (exclusive scan).
 //   chunk_local_kernel  one workgroup per (chunk of the stripe, head), fully
-//                       parallel:
+//                       parallel (the stripe's last chunks first):
 //                       A and M on the matrix cores, T by a blocked
 //                       triangular inverse, Ktil^T T and M T on the matrix
 //                       cores; writes the chunk's record (Khat, Qhat,
@@ -570,9 +570,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
   float *s_Yw = s_M + C * LP + 256 * wave;
-  // Work item: head h, packed chunk c = j0 + j of the stripe.
+  // Work item: head h, packed chunk c = j0 + j of the stripe.  Workgroups
+  // start in block order, so the stripe's chunks are taken last to first:
+  // the records written last, which the XCD's L2 still holds when the state
+  // pass starts, are those of the first chunks it reads (4k workload: state
+  // pass 141 vs 144-147 us).
   const int h = (int)(blockIdx.x % (unsigned)H);
-  const int64_t j = (int64_t)(blockIdx.x / (unsigned)H);
+  const int64_t j = (int64_t)(gridDim.x / (unsigned)H) - 1 - (int64_t)(blockIdx.x / (unsigned)H);
   const int64_t c = j0 + j;
   if (total_tokens <= 0) return;
   int n;
