@@ -49,6 +49,14 @@ kda_status_t check_prefill_shape(const kda_shape_t *s, bool varlen) {
     return KDA_ERR_UNSUPPORTED;
   // The state pass addresses one chunk's rows of v and o with 32-bit offsets.
   if ((int64_t)kda::kChunk * s->num_heads * s->d_v * 4 >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+  // Workspace byte counts (records, checkpoints, partial rows: at most a few
+  // KiB per token, head and 16 value columns) are 64-bit: (tokens + 64 N)
+  // H d_v/16 stays below 2^40.  (Written with divisions, so that the check
+  // itself cannot overflow.)
+  const int64_t groups = (int64_t)s->num_heads * (s->d_v < 16 ? 1 : s->d_v / 16);
+  const int64_t limit = ((int64_t)1 << 40) / groups;
+  if (s->total_tokens >= limit || (int64_t)s->num_seqs * kda::kChunk >= limit - s->total_tokens)
+    return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 

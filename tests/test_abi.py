@@ -88,6 +88,15 @@ def test_workspace_size_rejects(L):
     assert L.kda_prefill_workspace_size(None, ctypes.byref(out)) == INVALID
     assert L.kda_prefill_workspace_size(ctypes.byref(shape()), None) == INVALID
     assert L.kda_prefill_workspace_size(ctypes.byref(shape(d=48)), ctypes.byref(out)) == UNSUPPORTED
+    # (total_tokens + 64 N) H d/16 must stay below 2^40 (workspace byte counts
+    # are 64-bit): 2^32 tokens at H = 32, d = 128
+    lim = 1 << 32
+    assert L.kda_prefill_workspace_size(ctypes.byref(shape(N=1, T=0, H=32, d=128, total=lim - 128)),
+                                        ctypes.byref(out)) == OK
+    for big in (shape(N=1, T=0, H=32, d=128, total=lim - 64), shape(N=1, T=0, H=32, d=128, total=1 << 62),
+                shape(N=(1 << 31) - 1, T=0, H=32, d=128, total=0)):
+        assert L.kda_prefill_workspace_size(ctypes.byref(big), ctypes.byref(out)) == UNSUPPORTED
+        assert L.kda_backward_workspace_size(ctypes.byref(big), ctypes.byref(out)) == UNSUPPORTED
 
 
 def test_prefill_validation(L):
