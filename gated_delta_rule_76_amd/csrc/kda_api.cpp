@@ -222,6 +222,15 @@ kda_status_t kda_prefill_noalloc(const kda_shape_t *shape, const void *q, const 
                                        reinterpret_cast<const void *>(kda::kWorkspaceAlign),
                                        (size_t)KDA_NOALLOC_WORKSPACE_BYTES, true, true, true, false, &plan);
   if (st != KDA_OK || shape->num_seqs == 0) return st;
+  // The static workspace is the current device's: a stream of another
+  // device would run the kernels there with this device's address.
+  if (stream != nullptr) {
+    int cur = -1;
+    hipDevice_t sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return KDA_ERR_LAUNCH;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess || sdev != cur)
+      return KDA_ERR_INVALID_ARGUMENT;
+  }
   void *ws = nullptr;
   if (scratch_on_current_device(&ws) != hipSuccess) return KDA_ERR_LAUNCH;
   hipError_t e = kda::launch_prefill(*shape, q, k, v, alpha, beta, cu_seqlens, S0, o, S_T, ws, plan,

@@ -9,6 +9,7 @@ not on a GPU, the call raises.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -143,6 +144,22 @@ def _require_shape(name, t, shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _same_device(dev, **tensors):
+    """Every tensor of one call must be on one GPU: the kernels run on that
+    GPU's stream and would follow the other pointers into another GPU's
+    memory."""
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev} (every tensor of a call on one GPU)")
+
+
+def _on(dev):
+    """The call's GPU as the current device while the library runs (the
+    no-allocation entry point takes its static workspace on the current
+    device)."""
+    return torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()
+
+
 def make_shape(num_seqs, seq_len, total_tokens, num_heads, d, dtype, gate=KDA_GATE_CHANNEL,
                input_form=KDA_INPUT_FINAL):
     return KdaShape(int(num_seqs), int(seq_len), int(total_tokens), int(num_heads), int(d), int(d),
@@ -234,12 +251,15 @@ class PrefillCall:
                         else torch.empty((N, H, D, D), dtype=torch.float32, device=dev))
             _require_gpu("final_state", self.S_T, torch.float32)
             _require_shape("final_state", self.S_T, (N, H, D, D))
+        _same_device(dev, k=k, v=v, alpha=alpha, beta=beta, cu_seqlens=cu_seqlens, initial_state=initial_state,
+                     out=self.o, final_state=self.S_T)
         if workspace is None and allocate_workspace:
             need = (workspace_bytes if workspace_bytes is not None
                     else prefill_workspace_size(N, total, H, D, q.dtype))
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         if workspace is not None:
             _require_gpu("workspace", workspace)
+        _same_device(dev, workspace=workspace)
         self.workspace = workspace
         self.device = dev
         self._t = (q, k, v, alpha, beta, cu_seqlens, initial_state)
@@ -252,34 +272,38 @@ class PrefillCall:
     def run(self):
         q, k, v, alpha, beta, cu, S0 = self._t
         ws, nb = self._ws()
-        _check(lib().kda_prefill(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                 _ptr(beta), _ptr(cu), _ptr(S0), _ptr(self.o), _ptr(self.S_T), ws, nb,
-                                 _stream(self.device)), "kda_prefill")
+        with _on(self.device):
+            _check(lib().kda_prefill(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                     _ptr(beta), _ptr(cu), _ptr(S0), _ptr(self.o), _ptr(self.S_T), ws, nb,
+                                     _stream(self.device)), "kda_prefill")
         return self.o, self.S_T
 
     def run_noalloc(self):
         """kda_prefill_noalloc: the same call with the library's static
         workspace (no workspace tensor is used or needed)."""
         q, k, v, alpha, beta, cu, S0 = self._t
-        _check(lib().kda_prefill_noalloc(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                         _ptr(beta), _ptr(cu), _ptr(S0), _ptr(self.o), _ptr(self.S_T),
-                                         _stream(self.device)), "kda_prefill_noalloc")
+        with _on(self.device):
+            _check(lib().kda_prefill_noalloc(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                             _ptr(beta), _ptr(cu), _ptr(S0), _ptr(self.o), _ptr(self.S_T),
+                                             _stream(self.device)), "kda_prefill_noalloc")
         return self.o, self.S_T
 
     def chunk_local(self):
         q, k, _, alpha, beta, cu, _ = self._t
         ws, nb = self._ws()
-        _check(lib().kda_prefill_chunk_local(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(alpha),
-                                             _ptr(beta), _ptr(cu), ws, nb, _stream(self.device)),
-               "kda_prefill_chunk_local")
+        with _on(self.device):
+            _check(lib().kda_prefill_chunk_local(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(alpha),
+                                                 _ptr(beta), _ptr(cu), ws, nb, _stream(self.device)),
+                   "kda_prefill_chunk_local")
 
     def state_pass(self):
         q, k, v, alpha, _, cu, S0 = self._t
         ws, nb = self._ws()
-        _check(lib().kda_prefill_state_pass(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v),
-                                            _ptr(alpha), _ptr(cu), _ptr(S0), _ptr(self.o),
-                                            _ptr(self.S_T), ws, nb, _stream(self.device)),
-               "kda_prefill_state_pass")
+        with _on(self.device):
+            _check(lib().kda_prefill_state_pass(ctypes.byref(self.shape), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(alpha), _ptr(cu), _ptr(S0), _ptr(self.o),
+                                                _ptr(self.S_T), ws, nb, _stream(self.device)),
+                   "kda_prefill_state_pass")
         return self.o, self.S_T
 
 
@@ -342,9 +366,11 @@ def decode_step(q, k, v, alpha, beta, state, out=None, preact=False):
     o = out if out is not None else torch.empty((N, H, D), dtype=torch.float32, device=q.device)
     _require_gpu("out", o, torch.float32)
     _require_shape("out", o, (N, H, D))
+    _same_device(q.device, k=k, v=v, alpha=alpha, beta=beta, state=state, out=o)
     shape = make_shape(N, 1, N, H, D, q.dtype, gate, KDA_INPUT_PREACT if preact else KDA_INPUT_FINAL)
-    st = lib().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                               _ptr(state), _ptr(o), _stream(q.device))
+    with _on(q.device):
+        st = lib().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                   _ptr(state), _ptr(o), _stream(q.device))
     _check(st, "kda_decode_step")
     return o
 
@@ -385,10 +411,12 @@ def decode_tokens(q, k, v, alpha, beta, state, keep_states=False, preact=False, 
         _require_gpu("states", hist, torch.float32)
         if tuple(hist.shape) != (N, K, H, D, D):
             raise ValueError(f"states must be {(N, K, H, D, D)}")
+    _same_device(q.device, k=k, v=v, alpha=alpha, beta=beta, state=state, out=o, states=hist)
     shape = make_shape(N, K, N * K, H, D, q.dtype, gate, KDA_INPUT_PREACT if preact else KDA_INPUT_FINAL)
-    _check(lib().kda_decode_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                   _ptr(beta), _ptr(state), _ptr(o), _ptr(hist), _stream(q.device)),
-           "kda_decode_tokens")
+    with _on(q.device):
+        _check(lib().kda_decode_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                       _ptr(beta), _ptr(state), _ptr(o), _ptr(hist), _stream(q.device)),
+               "kda_decode_tokens")
     return (o, hist) if keep_states else o
 
 
@@ -403,9 +431,11 @@ def state_commit(state, states, accepted):
     N, K, H, D, _ = states.shape
     if tuple(state.shape) != (N, H, D, D) or tuple(accepted.shape) != (N,):
         raise ValueError("state, states and accepted disagree in shape")
+    _same_device(state.device, states=states, accepted=accepted)
     shape = make_shape(N, K, N * K, H, D, torch.float32)
-    _check(lib().kda_state_commit(ctypes.byref(shape), _ptr(state), _ptr(states), _ptr(accepted),
-                                  _stream(state.device)), "kda_state_commit")
+    with _on(state.device):
+        _check(lib().kda_state_commit(ctypes.byref(shape), _ptr(state), _ptr(states), _ptr(accepted),
+                                      _stream(state.device)), "kda_state_commit")
     return state
 
 
@@ -471,9 +501,12 @@ def backward(q, k, v, alpha, beta, dO, initial_state=None, dS_T=None, cu_seqlens
         nbytes = int(need.value) if workspace_bytes is None else int(workspace_bytes)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _require_gpu("workspace", workspace)
-    _check(lib().kda_backward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                              _ptr(cu_seqlens), _ptr(initial_state), _ptr(dO), _ptr(dS_T), _ptr(dq),
-                              _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(dbeta), _ptr(dS0), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(dev)),
-           "kda_backward")
+    _same_device(dev, k=k, v=v, alpha=alpha, beta=beta, dO=dO, cu_seqlens=cu_seqlens,
+                 initial_state=initial_state, dS_T=dS_T, workspace=workspace)
+    with _on(dev):
+        _check(lib().kda_backward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(cu_seqlens), _ptr(initial_state), _ptr(dO), _ptr(dS_T), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(dbeta), _ptr(dS0), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(dev)),
+               "kda_backward")
     return dq, dk, dv, dalpha, dbeta, dS0

@@ -224,7 +224,10 @@ kda_status_t kda_prefill_state_pass(const kda_shape_t *shape,
  *    Otherwise KDA_ERR_WORKSPACE_TOO_SMALL, before any HIP call.
  *  - The call allocates nothing: no hipMalloc, no allocating library call.
  *    Its first call on a device looks up the array's address there
- *    (hipGetSymbolAddress) and caches it.
+ *    (hipGetSymbolAddress) and caches it.  The array used is the current
+ *    device's, so a non-NULL stream must belong to the current device
+ *    (hipStreamGetDevice); otherwise KDA_ERR_INVALID_ARGUMENT, nothing
+ *    enqueued.
  *  - Every call on one GPU uses that GPU's one array, whose contents on
  *    entry do not matter.  Calls that overlap in time on the same GPU (two
  *    streams, or two host threads) race on it and give wrong results; order

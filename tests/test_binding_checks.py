@@ -74,3 +74,17 @@ def test_decode_tokens_rejects_wrong_history(host_only):
     with pytest.raises(ValueError, match="states must be"):
         kda.decode_tokens(q, k, v, torch.rand(N, K, H, D), torch.rand(N, K, H), S, keep_states=True,
                           states=torch.empty(N, K - 1, H, D, D))
+
+
+def test_tensors_of_one_call_must_share_a_device(host_only):
+    # (the meta device stands in for a second GPU: nothing is launched)
+    q, k, v, a, b = _prefill_inputs()
+    with pytest.raises(ValueError, match="beta is on meta"):
+        kda.prefill(q, k, v, a, b.to("meta"))
+    with pytest.raises(ValueError, match="out is on meta"):
+        kda.prefill(q, k, v, a, b, out=torch.empty(70, 2, 16, device="meta"))
+    N, H, D = 4, 2, 16
+    q, k, v = (torch.randn(N, H, D) for _ in range(3))
+    S = torch.zeros(N, H, D, D, device="meta")
+    with pytest.raises(ValueError, match="state is on meta"):
+        kda.decode_step(q, k, v, torch.rand(N, H, D), torch.rand(N, H), S)
