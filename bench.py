@@ -268,6 +268,36 @@ def bench_decode(B, dev, gate="channel", form="final"):
     return {"B": B, "H": H, "D": D, "steps": n, "ms_per_step": ms, "state_rmw_gbs": rmw_gbs}
 
 
+def bench_decode_context(B, dev, steps=1000):
+    """The per-token cost does not grow with the tokens already seen: one
+    state advanced by 10 + ``steps`` consecutive decode steps (cycling
+    through the workload's 100 input sets), the first and the last 100 of the
+    ``steps`` each timed by one event pair."""
+    from gated_delta_rule_76_amd import inputs, kda
+    spec = inputs.WORKLOADS["decode_b256"]
+    H, D, n = spec["H"], spec["D"], spec["steps"]
+    d = inputs.decode_inputs(B, H, D, n, torch.bfloat16, spec["decay"], spec["s_std"], seed=0, device=dev)
+    S = d["S"].clone()
+    o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    step = lambda s: kda.decode_step(d["q"][s % n], d["k"][s % n], d["v"][s % n], d["alpha"][s % n],
+                                     d["beta"][s % n], S, out=o)
+    e = [_events() for _ in range(2)]
+    warm = 10  # (untimed: the state's first reads are not cached yet)
+    for s in range(warm + steps):
+        if s == warm:
+            e[0][0].record()
+        if s == warm + 100:
+            e[0][1].record()
+        if s == warm + steps - 100:
+            e[1][0].record()
+        step(s)
+    e[1][1].record()
+    torch.cuda.synchronize()
+    first, last = (a.elapsed_time(b) / 100 for a, b in e)
+    return {"B": B, "steps": steps, "first_100_ms_per_step": first, "last_100_ms_per_step": last,
+            "last_over_first": last / first}
+
+
 def bench_verify(B, K, dev, steps=50):
     """Speculative verification of K tokens per sequence (the next token and
     K - 1 drafts): kda_decode_tokens with the state history, then
@@ -728,6 +758,8 @@ def main():
     if not args.no_decode:
         print("[bench] decode", file=sys.stderr, flush=True)
         out["decode"] = decode_summary(bench_decode(args.decode_batch, dev), "channel")
+        if not args.no_variants:
+            out["decode"]["context_growth"] = bench_decode_context(args.decode_batch, dev)
         if not args.no_variants and args.decode_large_batch:
             print(f"[bench] decode at B={args.decode_large_batch}", file=sys.stderr, flush=True)
             out["decode_large"] = decode_summary(bench_decode(args.decode_large_batch, dev), "channel")
