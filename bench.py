@@ -227,8 +227,13 @@ def bench_prefill(name, steps, warmup, dev, gate="channel", form="final"):
     cl = np.array([a.elapsed_time(b) for a, b, _ in evs])
     sp = np.array([b.elapsed_time(c) for _, b, c in evs])
     per_call = cl + sp
+    # Each phase's average over the calls, leaving out calls that took more
+    # than three times the median (a stall of the device or the host between
+    # the events, not kernel time; their count is reported).
+    keep = per_call <= 3.0 * np.median(per_call)
     return {"total_tokens": total, "H": H, "D": D, "ms": ms, "wall_s": wall, "lengths": lens,
-            "phases_ms": {"chunk_local": float(cl.mean()), "state_pass": float(sp.mean())},
+            "phases_ms": {"chunk_local": float(cl[keep].mean()), "state_pass": float(sp[keep].mean())},
+            "stalled_calls": int((~keep).sum()),
             "call_ms": {"median": float(np.median(per_call)), "p10": float(np.percentile(per_call, 10)),
                         "p90": float(np.percentile(per_call, 90))}}
 
@@ -750,6 +755,7 @@ def main():
         "layer_roofline": ps["layer_roofline"],
         "mfma": ps["mfma"],
         "call_ms": pf["call_ms"],
+        "stalled_calls": pf["stalled_calls"],
     }
     if args.bounded_workspace_mib:
         print(f"[bench] prefill with a {args.bounded_workspace_mib} MiB workspace", file=sys.stderr, flush=True)
@@ -770,6 +776,7 @@ def main():
         sg = {"prefill": prefill_summary(pv, "head")}
         sg["prefill"]["metric"] = "scalar-gate prefill tokens/s/layer (H=32, d=128)"
         sg["prefill"]["call_ms"] = pv["call_ms"]
+        sg["prefill"]["stalled_calls"] = pv["stalled_calls"]
         if not args.no_decode:
             sg["decode"] = decode_summary(bench_decode(args.decode_batch, dev, gate="head"), "head")
         out["scalar_gate"] = sg
@@ -780,6 +787,7 @@ def main():
         pa = {"prefill": prefill_summary(pp, "channel")}
         pa["prefill"]["metric"] = "KDA prefill from pre-activations, tokens/s/layer (H=32, d=128)"
         pa["prefill"]["call_ms"] = pp["call_ms"]
+        pa["prefill"]["stalled_calls"] = pp["stalled_calls"]
         if not args.no_decode:
             pa["decode"] = decode_summary(bench_decode(args.decode_batch, dev, form="preact"), "channel",
                                           "preact")
