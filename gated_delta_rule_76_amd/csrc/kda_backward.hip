@@ -72,6 +72,9 @@ struct BwdCfg {
   static constexpr int RPT = D / LPC;                 // rows per thread
   static constexpr int NW = NT / 64;
   static constexpr int NRED = bwd_row_sums(D, GATE == KDA_GATE_HEAD);  // row sums per token
+  static constexpr int NREDP = (NRED + 3) / 4 * 4;                     // LDS row: 16-byte groups
+  // lanes of each of the first four waves that add the row sums (pairs)
+  static constexpr int RLW = ((NREDP / 2 + 3) / 4 + 1) / 2 * 2;
   static constexpr int EB = GATE == KDA_GATE_HEAD ? 2 * D : 3 * D;     // index of dbeta
   static constexpr int CK = bwd_block(D, sizeof(TIn) == 4);
   static constexpr int DA = GATE == KDA_GATE_HEAD ? 1 : D;  // rates per token
@@ -84,6 +87,7 @@ struct BwdCfg {
   static constexpr int PK = (NK + NT - 1) / NT;  // chunks per thread
   static constexpr int PA = (NA + NT - 1) / NT;
   static_assert(VW == 16 && RPT >= 1 && D % LPC == 0 && NV <= NT && NO <= NT, "layout");
+  static_assert(NW >= 4 && NW % 2 == 0 && RLW <= 64 && 4 * RLW >= NREDP / 2, "row-sum lanes");
 };
 
 // Sum over the 16 lanes of a DPP row, every lane receiving the total
@@ -116,12 +120,41 @@ __device__ __forceinline__ float column_sum(float x) {
   if constexpr (LPC == 64) x = xor32_sum(x);
   return x;
 }
+// column_sum of x and of y together.  The first lane swap leaves x's partial
+// sums in half of each column's lanes and y's in the other half, so the rest
+// of the reduction runs once for both; the last swap hands every lane both.
+template <int LPC>
+__device__ __forceinline__ void column_sum2(float &x, float &y) {
+  if constexpr (LPC == 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const float u = row16_allsum(xor16_sum(__uint_as_float(r[0]) + __uint_as_float(r[1])));  // lanes < 32: x
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(u), false, false);
+    x = __uint_as_float(b[0]);
+    y = __uint_as_float(b[1]);
+  } else if constexpr (LPC == 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const float u = row16_allsum(__uint_as_float(r[0]) + __uint_as_float(r[1]));  // rows 0, 2: x
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
+    x = __uint_as_float(b[0]);
+    y = __uint_as_float(b[1]);
+  } else {
+    x = row16_allsum(x);
+    y = row16_allsum(y);
+  }
+}
 template <int LPC>
 __device__ __forceinline__ float across_columns(float x) {
   if constexpr (LPC == 16) x = xor16_sum(x);
   if constexpr (LPC <= 32) x = xor32_sum(x);
   return x;
 }
+
+// Wait until every global load and store this wave issued has completed
+// (s_waitcnt vmcnt(0)).  Placed where the next block's prefetch has had a
+// whole phase of LDS-only work to arrive: the compiler cannot count the loads
+// and stores issued under per-thread conditions, so without it it waits for
+// everything right after the prefetch, at the first reuse of a register.
+__device__ __forceinline__ void wait_global_ops() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // One block's inputs in LDS.
 template <int D, typename TIn, int GATE>
@@ -155,7 +188,8 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
   constexpr int NT = Cf::NT, LPC = Cf::LPC;
 
   __shared__ float s_ring[CK][NT][RPT];  // S_{t-1} of the block's tokens, per thread
-  __shared__ float s_red[2][NW][NRED];            // per-wave row sums, double-buffered
+  constexpr int NREDP = Cf::NREDP;
+  __shared__ __attribute__((aligned(16))) float s_red[2][NW][NREDP];  // per-wave row sums, double-buffered
   __shared__ __attribute__((aligned(16))) BlockIn<D, TIn, GATE> s_in;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -315,6 +349,7 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
 #pragma unroll
     for (int j = 0; j < CK; ++j)
       if (j < nt) fwd_step(j);
+    wait_global_ops();  // the next block's inputs
     if (b + 1 < nblk) {
       __syncthreads();  // every wave is done with block b
       stash(R);
@@ -337,6 +372,7 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) ckn[i] = cp[i];
   }
+  wait_global_ops();  // (once: so that no load is pending at the loop head)
   for (int64_t b = nblk - 1; b >= 0; --b) {
     const int64_t tb = b * CK;
     const int nt = (int)(len - tb < CK ? len - tb : CK);
@@ -361,6 +397,7 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       for (int i = 0; i < RPT; ++i) s_ring[j][tid][i] = s[i];
       fwd_step(j);
     }
+    wait_global_ops();  // the block before: inputs and checkpoint
 #pragma unroll
     for (int j = CK - 1; j >= 0; --j) {
       if (j >= nt) continue;
@@ -377,19 +414,19 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
         xk += X[i] * kf[i];
         gk += G[i] * kf[i];
       }
-      xk = column_sum<LPC>(xk);
-      gk = column_sum<LPC>(gk);
+      column_sum2<LPC>(xk, gk);
       const float bt = s_in.b[j];
       const float w = to_f32(s_in.v[j][c]) - xk;
-      dv[th * D + col] = bt * gk;  // (the column's lanes store the same value)
+      const float bw = bt * w, bg = bt * gk;
+      dv[th * D + col] = bg;  // (the column's lanes store the same value)
       float dkp[RPT], dqp[RPT], dap[RPT];
       float da_all = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float st = X[i] + bt * kf[i] * w;  // S_t
-        dkp[i] = bt * (G[i] * w - X[i] * gk);
+        const float st = X[i] + kf[i] * bw;  // S_t
+        dkp[i] = G[i] * bw - X[i] * bg;
         dqp[i] = st * dOc;
-        const float e = G[i] - bt * kf[i] * gk;
+        const float e = G[i] - kf[i] * bg;
         dap[i] = e * sp[i];
         da_all += dap[i];
         G[i] = rate(j, i) * e;
@@ -421,14 +458,23 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
       __syncthreads();
       // The slice's partial row sums of this token, in one contiguous row.
       float *prow = part + ((int64_t)sl * pc.rows * H + (row0 + tb + j) * H + h) * NRED;
+      // Two threads per group of four consecutive sums, each adding half of
+      // the waves' rows with 16-byte reads, then one lane exchange; the
+      // threads sit in the first four waves, one per SIMD.
+      if (wave < 4 && lane < Cf::RLW) {
+        const int i = wave * Cf::RLW + lane;
+        const int g = i >> 1, p = i & 1;  // (the pair of a group is two adjacent lanes)
+        if (g < NREDP / 4) {
+          const f32x4 *src = reinterpret_cast<const f32x4 *>(&s_red[par][p * (NW / 2)][4 * g]);
+          f32x4 acc = src[0];
 #pragma unroll
-      for (int u0 = 0; u0 < NRED; u0 += NT) {
-        const int e = u0 + tid;
-        if (e < NRED) {
-          float u = 0.f;
+          for (int w2 = 1; w2 < NW / 2; ++w2) acc += src[w2 * (NREDP / 4)];
 #pragma unroll
-          for (int w2 = 0; w2 < NW; ++w2) u += s_red[par][w2][e];
-          prow[e] = u;
+          for (int m = 0; m < 4; ++m)
+            acc[m] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[m]), 0xB1, 0xf, 0xf, false));
+          const int e = 4 * g + 2 * p;  // this thread stores sums e and e + 1
+          if (e < NRED) prow[e] = p ? acc[2] : acc[0];
+          if (e + 1 < NRED) prow[e + 1] = p ? acc[3] : acc[1];
         }
       }
       par ^= 1;
