@@ -51,6 +51,9 @@ KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_prefi
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_decode_b%d.json")  # % batch
 DECODE_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_decode.hip")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_prefill_4k.json")
+BACKWARD_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_backward_4k.json")
+BACKWARD_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_backward.hip")
+VERIFY_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_b%d_k%d.json")  # % (batch, tokens)
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
 # Useful matrix work of the chunked form per token and head at d = 128, C = 64:
 # the decayed Gram blocks, the triangular transform and the state products
@@ -87,6 +90,9 @@ def _parse():
                         "less than the recommended size)")
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
+    p.add_argument("--only", choices=["backward", "verify"],
+                   help="run only this leg (after --calibrate-copy, if given) and print its summary; "
+                        "for hardware counter runs of one kernel family")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a plain elementwise float64 copy of 256 MiB (a kernel of "
                         "known size for scaling hardware byte counters)")
@@ -379,11 +385,17 @@ def bench_backward(name, dev, steps=10, ws_bytes=None):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     gbs = T * H * backward_bytes() / (ms * 1e-3) / 1e9
+    # counter bytes of one call (both kernels), for the recommended workspace only
+    traffic = None
+    if ws_bytes == kda.backward_workspace_size(len(lens), T, H, D):
+        parts = [_traffic(kn, name, BACKWARD_TRAFFIC_SUMMARY, BACKWARD_SOURCE)
+                 for kn in ("bwd_kernel", "bwd_reduce_kernel")]
+        traffic = None if None in parts else sum(parts)
     return {"metric": "KDA backward tokens/s/layer (%s)" % name, "value": T / (ms * 1e-3),
             "unit": "tokens/s/layer", "ms_per_step": ms, "workspace_bytes": int(ws.numel()),
             "roofline": {"bound": "hbm", "kernel": "bwd_kernel + bwd_reduce_kernel", "achieved": gbs,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                         "bytes_per_token_head": backward_bytes()}}
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": traffic, "bytes_per_token_head": backward_bytes()}}
 
 
 def verify_summary(vf):
@@ -395,7 +407,9 @@ def verify_summary(vf):
             "tokens_per_s": B * K / (vf["verify_ms"] * 1e-3),
             "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": None, "bytes_per_seq_head": verify_bytes(K)},
+                         "traffic": _traffic("decode_tokens_kernel", "verify_b%d_k%d" % (B, K),
+                                             VERIFY_TRAFFIC_SUMMARY % (B, K), DECODE_SOURCE),
+                         "bytes_per_seq_head": verify_bytes(K)},
             "commit": {"sequences_committed": vf["committed_seqs"],
                        "achieved_gbs": vf["committed_seqs"] * H * 2 * 128 * 128 * 4 / (vf["commit_ms"] * 1e-3) / 1e9}}
 
@@ -728,6 +742,14 @@ def main():
             torch.add(src, 0.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.only == "backward":
+        print("[bench] backward only", file=sys.stderr, flush=True)
+        print(json.dumps({"backward": bench_backward("prefill_4k", dev)}), flush=True)
+        return
+    if args.only == "verify":
+        print("[bench] speculative verify only", file=sys.stderr, flush=True)
+        print(json.dumps({"verify": verify_summary(bench_verify(args.decode_batch, 2, dev))}), flush=True)
+        return
     print(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
     pf = bench_prefill(args.workload, args.steps, args.warmup, dev)

@@ -18,6 +18,14 @@ runs):
     python -m gated_delta_rule_76_amd.counters F.csv W.csv --target decode \\
         --workload decode_b256 > profiles/traffic_decode_b256.json
 
+The backward and the speculative verification leg alone (bench.py --only
+backward / --only verify, each with --calibrate-copy):
+
+    python -m gated_delta_rule_76_amd.counters F.csv W.csv --target backward \\
+        --workload prefill_4k > profiles/traffic_backward_4k.json
+    python -m gated_delta_rule_76_amd.counters F.csv W.csv --target decode \\
+        --workload verify_b256_k2 > profiles/traffic_verify_b256_k2.json
+
 FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB).  Each is scaled by
 the factor that maps the same counter of a plain elementwise float64 copy
 of 256 MiB (the --calibrate-copy kernel, which reads and writes exactly
@@ -55,6 +63,7 @@ COPY_BYTES = 256 << 20
 TARGETS = {
     "prefill": ("kda_prefill.hip", ("chunk_local_kernel", "chunk_state_kernel")),
     "decode": ("kda_decode.hip", ("decode_kernel", "decode_tokens_kernel", "commit_kernel")),
+    "backward": ("kda_backward.hip", ("bwd_kernel", "bwd_reduce_kernel")),
 }
 
 

@@ -338,8 +338,9 @@ kda_status_t kda_backward(const kda_shape_t *shape, const void *q, const void *k
       (cu_seqlens && !aligned4(cu_seqlens)))
     return KDA_ERR_INVALID_ARGUMENT;
   if (s.num_seqs == 0) return s.total_tokens > 0 ? KDA_ERR_INVALID_ARGUMENT : KDA_OK;
-  // One workgroup per (sequence, head, 16 value columns).
-  if ((int64_t)s.num_seqs * s.num_heads * (s.d_v < 16 ? 1 : s.d_v / 16) >= ((int64_t)1 << 31))
+  // One workgroup per (sequence, head, 16 value columns), the pairs rounded
+  // up to a multiple of 8.
+  if (((int64_t)s.num_seqs * s.num_heads + 7) / 8 * 8 * (s.d_v < 16 ? 1 : s.d_v / 16) >= ((int64_t)1 << 31))
     return KDA_ERR_UNSUPPORTED;
   if (workspace == nullptr) return KDA_ERR_WORKSPACE_TOO_SMALL;
   const kda::BwdLayout L = kda::backward_plan(s, varlen, workspace_bytes);

@@ -195,8 +195,15 @@ __global__ __launch_bounds__((BwdCfg<D, TIn, GATE>::NT)) void bwd_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid / LPC, rg = tid % LPC;  // column of the slice, row group
   const int r0 = rg * RPT;
-  const int sl = blockIdx.x % SL;
-  const int nh = blockIdx.x / SL;
+  // blockIdx -> work: consecutive workgroups are dealt round-robin to the 8
+  // XCDs, so the SL column slices of one (sequence, head) get block indices
+  // congruent mod 8.  They share an XCD and its L2, and the rows of k, q and
+  // alpha that every slice reads come from HBM once for all of them.  (The
+  // grid covers the (sequence, head) pairs rounded up to a multiple of 8.)
+  const int id = blockIdx.x;
+  const int sl = (id >> 3) % SL;
+  const int nh = ((id >> 3) / SL) * 8 + (id & 7);
+  if (nh >= N * H) return;
   const int n = nh / H, h = nh % H;
   const int col = sl * VW + c;
   int64_t start, len;
@@ -596,7 +603,7 @@ hipError_t launch_bwd_t(const kda_shape_t &s, const BwdArgs &a, const BwdLayout 
   float *part = reinterpret_cast<float *>(ws + L.part_off);
   float *pstate = reinterpret_cast<float *>(ws + L.pstate_off);
   float *carry = reinterpret_cast<float *>(ws + L.carry_off);
-  const int64_t blocks = (int64_t)s.num_seqs * s.num_heads * Cf::SL;
+  const int64_t blocks = ((int64_t)s.num_seqs * s.num_heads + 7) / 8 * 8 * Cf::SL;
   const int64_t state = (int64_t)s.num_seqs * s.num_heads * D * D;
   const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
             *v = static_cast<const TIn *>(a.v);
