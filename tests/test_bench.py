@@ -69,6 +69,26 @@ def test_decode_traffic_matches_its_algorithmic_bytes(B):
                           bench.DECODE_SOURCE) is None
 
 
+def test_verify_traffic_matches_its_algorithmic_bytes():
+    # speculative verification (B=256, two tokens, state history): the counters
+    # of the verify kernel read within 1% of the state read once, two states
+    # written and the tokens' inputs and outputs
+    t = bench._traffic("decode_tokens_kernel", "verify_b256_k2", bench.VERIFY_TRAFFIC_SUMMARY % (256, 2),
+                       bench.DECODE_SOURCE)
+    assert t is not None
+    assert abs(t / (256 * 32 * bench.verify_bytes(2)) - 1) < 0.01
+
+
+def test_backward_traffic_is_summarised_for_both_kernels():
+    # the backward summary covers both of its kernels on the committed source;
+    # its bytes exceed the layer's algorithmic 3,848 per token and head (the
+    # checkpoints and the per-slice partial rows make a round trip through HBM)
+    parts = [bench._traffic(k, "prefill_4k", bench.BACKWARD_TRAFFIC_SUMMARY, bench.BACKWARD_SOURCE)
+             for k in ("bwd_kernel", "bwd_reduce_kernel")]
+    assert None not in parts
+    assert sum(parts) > 4096 * 32 * bench.backward_bytes()
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
