@@ -54,6 +54,7 @@ MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_prefill_4k.json")
 BACKWARD_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_backward_4k.json")
 BACKWARD_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_backward.hip")
 VERIFY_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_b%d_k%d.json")  # % (batch, tokens)
+VERIFY_RECOMPUTE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_recompute_b%d_k%d.json")
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
 # Useful matrix work of the chunked form per token and head at d = 128, C = 64:
 # the decayed Gram blocks, the triangular transform and the state products
@@ -90,7 +91,7 @@ def _parse():
                         "less than the recommended size)")
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
-    p.add_argument("--only", choices=["backward", "verify"],
+    p.add_argument("--only", choices=["backward", "verify", "verify_recompute"],
                    help="run only this leg (after --calibrate-copy, if given) and print its summary; "
                         "for hardware counter runs of one kernel family")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -354,6 +355,70 @@ def bench_verify(B, K, dev, steps=50):
     n_acc = int((accepted > 0).sum())
     return {"B": B, "K": K, "H": H, "step_ms": pair, "verify_ms": vt, "commit_ms": ct,
             "committed_seqs": n_acc}
+
+
+def bench_verify_recompute(B, K, dev, steps=50):
+    """Speculative verification with rollback by recomputation: kda_verify_tokens
+    (outputs only, no state written), then kda_accept_tokens of the same
+    seeded accepted counts as bench_verify.  One event pair around ``steps``
+    back-to-back rounds, then around the verifies alone and the accepts alone."""
+    from gated_delta_rule_76_amd import inputs, kda
+    spec = inputs.WORKLOADS["decode_b256"]
+    H, D = spec["H"], spec["D"]
+    sets = []
+    for i in range(N_SETS):
+        d = inputs.decode_inputs(B * K, H, D, 1, torch.bfloat16, spec["decay"], spec["s_std"], seed=i,
+                                 device=dev)
+        sets.append({key: d[key][0].reshape((B, K) + tuple(d[key].shape[2:])).contiguous()
+                     for key in ("q", "k", "v", "alpha", "beta")})
+    S = inputs.state(B, H, D, spec["s_std"], seed=0, device=dev)
+    o = torch.empty((B, K, H, D), dtype=torch.float32, device=dev)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(0)
+    accepted = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev)
+    ver = lambda t: kda.verify_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, out=o)
+    acc = lambda t: kda.accept_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, accepted)
+    for i in range(5):
+        ver(sets[i % N_SETS])
+        acc(sets[i % N_SETS])
+    torch.cuda.synchronize()
+
+    def timed(body):
+        e0, e1 = _events()
+        e0.record()
+        for i in range(steps):
+            body(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    pair = timed(lambda i: (ver(sets[i % N_SETS]), acc(sets[i % N_SETS])))
+    vt = timed(lambda i: ver(sets[i % N_SETS]))
+    at = timed(lambda i: acc(sets[i % N_SETS]))
+    n_acc = int((accepted > 0).sum())
+    state = D * D * 4
+    tok = K * (768 + 512 + 4 + 512)
+    # bytes: verify reads each state once plus the tokens' inputs and outputs;
+    # an accepting sequence's state is read and written once more, with the
+    # inputs of its tokens (all k counted)
+    v_bytes = B * H * (state + tok)
+    a_bytes = n_acc * H * (2 * state + K * (768 + 512 + 4))
+    gbs = (v_bytes + a_bytes) / (pair * 1e-3) / 1e9
+    return {"metric": "speculative verify steps/s, rollback by recomputation (B=%d, %d tokens per "
+                      "sequence, H=32, d=128)" % (B, K),
+            "value": 1e3 / pair, "unit": "steps/s", "step_ms": pair, "verify_ms": vt, "accept_ms": at,
+            "tokens_per_s": B * K / (pair * 1e-3), "sequences_accepting": n_acc,
+            "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel (verify + accept)",
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": _round_traffic(B, K), "bytes_per_step": v_bytes + a_bytes}}
+
+
+def _round_traffic(B, K):
+    """Counter bytes of one verify + accept round: the summary averages the
+    multi-token kernel's dispatches, verify and accept in equal numbers."""
+    t = _traffic("decode_tokens_kernel", "verify_recompute_b%d_k%d" % (B, K),
+                 VERIFY_RECOMPUTE_TRAFFIC_SUMMARY % (B, K), DECODE_SOURCE)
+    return None if t is None else 2 * t
 
 
 def bench_backward(name, dev, steps=10, ws_bytes=None):
@@ -750,6 +815,10 @@ def main():
         print("[bench] speculative verify only", file=sys.stderr, flush=True)
         print(json.dumps({"verify": verify_summary(bench_verify(args.decode_batch, 2, dev))}), flush=True)
         return
+    if args.only == "verify_recompute":
+        print("[bench] speculative verify by recomputation only", file=sys.stderr, flush=True)
+        print(json.dumps({"verify_recompute": bench_verify_recompute(args.decode_batch, 2, dev)}), flush=True)
+        return
     print(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
     pf = bench_prefill(args.workload, args.steps, args.warmup, dev)
@@ -817,6 +886,7 @@ def main():
         if not args.no_decode:
             print("[bench] speculative verify", file=sys.stderr, flush=True)
             out["verify"] = verify_summary(bench_verify(args.decode_batch, 2, dev))
+            out["verify_recompute"] = bench_verify_recompute(args.decode_batch, 2, dev)
         print("[bench] backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(args.workload if args.workload == "prefill_4k" else "prefill_4k", dev)
         if args.bounded_backward_mib:

@@ -297,6 +297,26 @@ kda_status_t kda_state_commit(const kda_shape_t *shape, float *S, const float *S
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status_t kda_verify_tokens(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta, const float *S, float *o, void *stream) {
+  kda_status_t st = check_decode_call(shape, false, q, k, v, alpha, beta, S, o);
+  if (st != KDA_OK || shape->num_seqs == 0) return st;
+  hipError_t e = kda::launch_verify_tokens(*shape, q, k, v, alpha, beta, S, o, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_accept_tokens(const kda_shape_t *shape, const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta, float *S, const int32_t *accepted,
+                               void *stream) {
+  // (no outputs: S stands in for o in the shared checks)
+  kda_status_t st = check_decode_call(shape, false, q, k, v, alpha, beta, S, S);
+  if (st != KDA_OK || shape->num_seqs == 0) return st;
+  if (accepted == nullptr || !aligned4(accepted)) return KDA_ERR_INVALID_ARGUMENT;
+  hipError_t e = kda::launch_accept_tokens(*shape, q, k, v, alpha, beta, S, accepted,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 kda_status_t kda_decode_step(const kda_shape_t *shape, const void *q, const void *k, const void *v,
                              const float *alpha, const float *beta, float *S, float *o,
                              void *stream) {

@@ -243,11 +243,20 @@ __device__ __forceinline__ void load_token_in(TokenIn<D, TIn> &x, const TIn *__r
   x.b = beta[th];
 }
 
-template <int D, typename TIn, int GATE, int FORM, bool HIST, bool NTL>
+// What a multi-token call does with the state and the outputs.
+enum TokMode : int {
+  kTokAdvance = 0,  // o for every token; S advanced in place by all of them
+  kTokHistory = 1,  // o for every token; the state after each token to hist; S unchanged
+  kTokVerify = 2,   // o for every token; S unchanged, nothing else written
+  kTokAccept = 3,   // no o; S advanced in place by the first accepted[n] tokens
+};
+
+template <int D, typename TIn, int GATE, int FORM, int MODE, bool NTL>
 __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ S,
-    float *__restrict__ o, float *__restrict__ hist, int ntok, int H) {
+    float *__restrict__ o, float *__restrict__ hist, const int32_t *__restrict__ accepted, int ntok, int H) {
+  constexpr bool HIST = MODE == kTokHistory;
   using Cfg = DecodeCfg<D>;
   constexpr int TPR = Cfg::TPR, RPP = Cfg::RPP, PASSES = Cfg::PASSES, NW = Cfg::NW;
   constexpr bool kPre = FORM == KDA_INPUT_PREACT;
@@ -264,6 +273,14 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
   const int cq = tid % TPR;
   const int r0 = tid / TPR;
   const int cj = tid < D ? tid : 0;
+  // tokens to run: all ntok, or the sequence's accepted count (clamped to
+  // [0, ntok]; a sequence with none keeps its state untouched)
+  int nt = ntok;
+  if constexpr (MODE == kTokAccept) {
+    const int j = accepted[n];
+    nt = j < 0 ? 0 : (j > ntok ? ntok : j);
+    if (nt == 0) return;
+  }
 
   TokenIn<D, TIn> cur, nxt;
   load_token_in<D, TIn, GATE>(cur, q, k, v, alpha, beta, n * ntok * H + h, r0, cj);
@@ -280,10 +297,10 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
     }
   }
 
-  for (int t = 0; t < ntok; ++t) {
+  for (int t = 0; t < nt; ++t) {
     const int64_t th = (n * ntok + t) * H + h;  // token row * H + head
     // The next token's inputs (the last token reloads its own: no branch).
-    const int tn = t + 1 < ntok ? t + 1 : t;
+    const int tn = t + 1 < nt ? t + 1 : t;
     load_token_in<D, TIn, GATE>(nxt, q, k, v, alpha, beta, (n * ntok + tn) * H + h, r0, cj);
 
     float a[PASSES], kk[PASSES], qq[PASSES];
@@ -365,7 +382,7 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
       }
       const float wv = bt * (vj - xs);
       s_w[tid] = kPre ? wv * ik : wv;
-      o[th * D + tid] = ys + qk * wv;
+      if constexpr (MODE != kTokAccept) o[th * D + tid] = ys + qk * wv;
     }
     __syncthreads();
     const float w0 = s_w[cq * 4 + 0], w1 = s_w[cq * 4 + 1], w2 = s_w[cq * 4 + 2], w3 = s_w[cq * 4 + 3];
@@ -386,7 +403,7 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
     }
     cur = nxt;
   }
-  if constexpr (!HIST) {
+  if constexpr (MODE == kTokAdvance || MODE == kTokAccept) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const f32x4 nv = {s[p].x, s[p].y, s[p].z, s[p].w};
@@ -484,9 +501,11 @@ hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, con
   });
 }
 
-hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
-                                const float *alpha, const float *beta, float *S, float *o, float *hist,
-                                hipStream_t stream) {
+namespace {
+
+hipError_t launch_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v, const float *alpha,
+                         const float *beta, float *S, float *o, float *hist, const int32_t *accepted, int mode,
+                         hipStream_t stream) {
   return dispatch(s, [&](auto d, auto t, auto g, auto f) {
     constexpr int D = decltype(d)::value;
     using TIn = typename decltype(t)::type;
@@ -498,23 +517,50 @@ hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void 
     // every state written) pass 1 GiB it is read with non-temporal loads too
     // (two tokens with history at B=256, 1.5 GiB: 336 -> 299 us per call).
     const int64_t state_bytes = blocks * (int64_t)(D * D) * (int64_t)sizeof(float);
-    const int64_t writes = hist != nullptr ? (int64_t)s.seq_len : 1;
+    const int64_t writes = mode == kTokHistory ? (int64_t)s.seq_len : (mode == kTokVerify ? 0 : 1);
     const bool ntl = state_bytes * (1 + writes) > kStreamStateBytes;
-    auto go = [&](auto hist_c, auto ntl_c) {
-      constexpr bool HI = decltype(hist_c)::value, NL = decltype(ntl_c)::value;
-      hipLaunchKernelGGL((decode_tokens_kernel<D, TIn, G, F, HI, NL>), dim3((unsigned)blocks),
-                         dim3(DecodeCfg<D>::NT), 0, stream, qp, kp, vp, alpha, beta, S, o, hist, s.seq_len,
-                         s.num_heads);
+    auto go = [&](auto mode_c, auto ntl_c) {
+      constexpr int MO = decltype(mode_c)::value;
+      constexpr bool NL = decltype(ntl_c)::value;
+      hipLaunchKernelGGL((decode_tokens_kernel<D, TIn, G, F, MO, NL>), dim3((unsigned)blocks),
+                         dim3(DecodeCfg<D>::NT), 0, stream, qp, kp, vp, alpha, beta, S, o, hist, accepted,
+                         s.seq_len, s.num_heads);
     };
-    if (hist != nullptr) {
-      if (ntl) go(std::true_type{}, std::true_type{});
-      else go(std::true_type{}, std::false_type{});
-    } else {
-      if (ntl) go(std::false_type{}, std::true_type{});
-      else go(std::false_type{}, std::false_type{});
+    auto go_mode = [&](auto mode_c) {
+      if (ntl) go(mode_c, std::true_type{});
+      else go(mode_c, std::false_type{});
+    };
+    switch (mode) {
+      case kTokAdvance: go_mode(Int<kTokAdvance>{}); break;
+      case kTokHistory: go_mode(Int<kTokHistory>{}); break;
+      case kTokVerify: go_mode(Int<kTokVerify>{}); break;
+      case kTokAccept: go_mode(Int<kTokAccept>{}); break;
+      default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   });
+}
+
+}  // namespace
+
+hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, float *S, float *o, float *hist,
+                                hipStream_t stream) {
+  return launch_tokens(s, q, k, v, alpha, beta, S, o, hist, nullptr, hist != nullptr ? kTokHistory : kTokAdvance,
+                       stream);
+}
+
+hipError_t launch_verify_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, const float *S, float *o,
+                                hipStream_t stream) {
+  // (the kernel never writes S in this mode)
+  return launch_tokens(s, q, k, v, alpha, beta, const_cast<float *>(S), o, nullptr, nullptr, kTokVerify, stream);
+}
+
+hipError_t launch_accept_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, float *S, const int32_t *accepted,
+                                hipStream_t stream) {
+  return launch_tokens(s, q, k, v, alpha, beta, S, nullptr, nullptr, accepted, kTokAccept, stream);
 }
 
 hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, const int32_t *accepted,

@@ -113,6 +113,17 @@ hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void 
 hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, const int32_t *accepted,
                          hipStream_t stream);
 
+// s.seq_len tokens per sequence from S, outputs only (S is not written).
+hipError_t launch_verify_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, const float *S, float *o,
+                                hipStream_t stream);
+
+// S advanced in place by the first accepted[n] (clamped to [0, s.seq_len])
+// of each sequence's s.seq_len tokens; no outputs.
+hipError_t launch_accept_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, float *S, const int32_t *accepted,
+                                hipStream_t stream);
+
 // Backward pass.  Workspace: state checkpoints every bwd_block tokens per
 // (sequence, head) -- d_k x d_v floats per slot -- then the per-slice
 // partial row sums over the d_v / 16 column slices, [slices][rows][H]

@@ -98,6 +98,10 @@ def lib():
     L.kda_decode_tokens.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_state_commit.restype = ctypes.c_int
     L.kda_state_commit.argtypes = [shp, vp, vp, vp, vp]
+    L.kda_verify_tokens.restype = ctypes.c_int
+    L.kda_verify_tokens.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_accept_tokens.restype = ctypes.c_int
+    L.kda_accept_tokens.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_backward_workspace_size.restype = ctypes.c_int
     L.kda_backward_workspace_size.argtypes = [shp, ctypes.POINTER(sz)]
     L.kda_backward.restype = ctypes.c_int
@@ -418,6 +422,61 @@ def decode_tokens(q, k, v, alpha, beta, state, keep_states=False, preact=False, 
                                        _ptr(beta), _ptr(state), _ptr(o), _ptr(hist), _stream(q.device)),
                "kda_decode_tokens")
     return (o, hist) if keep_states else o
+
+
+def _token_round(q, k, v, alpha, beta, state, preact):
+    """Checks shared by verify_tokens and accept_tokens; returns (N, K, H, D,
+    shape struct)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_gpu(name, t)
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float32 or bfloat16")
+    _require_gpu("alpha", alpha, torch.float32)
+    _require_gpu("beta", beta, torch.float32)
+    _require_gpu("state", state, torch.float32)
+    if q.dim() != 4:
+        raise ValueError("multi-token decode inputs are [N, k, H, D]")
+    N, K, H, D = q.shape
+    gate = _gate_of(alpha, q)
+    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("beta", beta, q.shape[:-1]),
+                         ("state", state, (N, H, D, D))):
+        if tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
+    shape = make_shape(N, K, N * K, H, D, q.dtype, gate, KDA_INPUT_PREACT if preact else KDA_INPUT_FINAL)
+    return N, K, H, D, shape
+
+
+def verify_tokens(q, k, v, alpha, beta, state, preact=False, out=None):
+    """Outputs of k drafted tokens per sequence from the live states, which
+    are left as they are (verification with rollback by recomputation: pair
+    with ``accept_tokens``).  Inputs as for ``decode_tokens``; returns o
+    [N, k, H, D] fp32."""
+    N, K, H, D, shape = _token_round(q, k, v, alpha, beta, state, preact)
+    o = out if out is not None else torch.empty((N, K, H, D), dtype=torch.float32, device=q.device)
+    _require_gpu("out", o, torch.float32)
+    _require_shape("out", o, (N, K, H, D))
+    _same_device(q.device, k=k, v=v, alpha=alpha, beta=beta, state=state, out=o)
+    with _on(q.device):
+        _check(lib().kda_verify_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                       _ptr(beta), _ptr(state), _ptr(o), _stream(q.device)),
+               "kda_verify_tokens")
+    return o
+
+
+def accept_tokens(q, k, v, alpha, beta, state, accepted, preact=False):
+    """Advance state[n] in place by the first accepted[n] of the k tokens
+    (clamped to [0, k]) that ``verify_tokens`` checked; accepted: int32 [N]
+    on the GPU.  Returns ``state``."""
+    N, K, H, D, shape = _token_round(q, k, v, alpha, beta, state, preact)
+    _require_gpu("accepted", accepted, torch.int32)
+    if tuple(accepted.shape) != (N,):
+        raise ValueError(f"accepted has shape {tuple(accepted.shape)}, expected {(N,)}")
+    _same_device(q.device, k=k, v=v, alpha=alpha, beta=beta, state=state, accepted=accepted)
+    with _on(q.device):
+        _check(lib().kda_accept_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                       _ptr(beta), _ptr(state), _ptr(accepted), _stream(q.device)),
+               "kda_accept_tokens")
+    return state
 
 
 def state_commit(state, states, accepted):

@@ -294,6 +294,35 @@ kda_status_t kda_decode_tokens(const kda_shape_t *shape,
 kda_status_t kda_state_commit(const kda_shape_t *shape, float *S, const float *S_hist,
                               const int32_t *accepted, void *stream);
 
+/* Speculative verification with rollback by recomputation instead of a
+ * state history (the same passage as kda_decode_tokens).  kda_verify_tokens
+ * gives the outputs of k tokens per sequence from the live state and writes
+ * nothing else; kda_accept_tokens then advances the live state by the first
+ * accepted[n] of those tokens (clamped to [0, k]; 0 leaves S[n] untouched),
+ * running them again.  Per (sequence, head) a verify round reads the state
+ * once and an accepting sequence reads and writes it once more, where
+ * kda_decode_tokens with S_hist writes k states and kda_state_commit copies
+ * one: no history buffer, and fewer state bytes per round.  Both give the
+ * outputs and states that kda_decode_tokens (with S_hist) and
+ * kda_state_commit give, bit for bit.
+ *   shape, q, k, v, alpha, beta   as for kda_decode_tokens (the same token
+ *                 rows for both calls of a round)
+ *   S             [N][H][d_k][d_v] fp32 live states (read only in
+ *                 kda_verify_tokens, updated in kda_accept_tokens)
+ *   o             [N * k][H][d_v] fp32 output for every token (verify)
+ *   accepted      [N] int32 device array (accept), 4-byte aligned
+ * Gate kind and input form as for the other calls; a shape, pointer or
+ * alignment the checks of kda_decode_tokens reject is rejected the same
+ * way. */
+kda_status_t kda_verify_tokens(const kda_shape_t *shape,
+                               const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta,
+                               const float *S, float *o, void *stream);
+kda_status_t kda_accept_tokens(const kda_shape_t *shape,
+                               const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta,
+                               float *S, const int32_t *accepted, void *stream);
+
 /* Backward pass (training): gradients of L with respect to q, k, v, alpha,
  * beta and the initial states, given dL/do for every token (dO) and dL/dS_T
  * for every final state (dS_T, or NULL for zero).  It differentiates the

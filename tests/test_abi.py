@@ -49,11 +49,11 @@ def decode(L, s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, o=FAKE):
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["kda_abi_version", "kda_backward", "kda_backward_workspace_size",
-                                    "kda_decode_step", "kda_decode_tokens", "kda_prefill",
-                                    "kda_prefill_chunk_local", "kda_prefill_noalloc",
+    assert declared_functions() == ["kda_abi_version", "kda_accept_tokens", "kda_backward",
+                                    "kda_backward_workspace_size", "kda_decode_step", "kda_decode_tokens",
+                                    "kda_prefill", "kda_prefill_chunk_local", "kda_prefill_noalloc",
                                     "kda_prefill_state_pass", "kda_prefill_workspace_size",
-                                    "kda_state_commit", "kda_status_string"]
+                                    "kda_state_commit", "kda_status_string", "kda_verify_tokens"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -218,6 +218,33 @@ def test_decode_tokens_and_commit_validation(L):
     assert com(sh(), acc=None) == INVALID
     assert com(sh(), acc=FAKE + 2) == INVALID
     assert com(sh(), hist=FAKE + 4) == INVALID
+
+
+def test_verify_and_accept_validation(L):
+    # the recompute-rollback pair checks the same shape, pointers and
+    # alignment as kda_decode_tokens (no GPU: every call here is rejected or
+    # has nothing to launch)
+    def ver(s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, o=FAKE):
+        return L.kda_verify_tokens(ctypes.byref(s) if s is not None else None, q, k, v, a, b, S, o, None)
+
+    def acc(s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, accepted=FAKE):
+        return L.kda_accept_tokens(ctypes.byref(s) if s is not None else None, q, k, v, a, b, S, accepted,
+                                   None)
+    sh = lambda N=4, K=3, total=None, d=128, gate=0, form=0: kda.KdaShape(
+        N, K, N * K if total is None else total, 2, d, d, 1, gate, form)
+    for call, fields in ((ver, ("q", "k", "v", "a", "b", "S", "o")),
+                         (acc, ("q", "k", "v", "a", "b", "S", "accepted"))):
+        assert call(None) == INVALID
+        assert call(sh(K=0)) == INVALID                # at least one token per sequence
+        assert call(sh(total=11)) == INVALID           # total must be N * k
+        assert call(sh(d=96)) == UNSUPPORTED
+        assert call(sh(gate=2)) == INVALID
+        assert call(sh(form=2)) == INVALID
+        assert call(sh(N=0, total=0)) == OK            # nothing to do, nothing launched
+        for field in fields:
+            assert call(sh(), **{field: None}) == INVALID, field
+            assert call(sh(), **{field: FAKE + 2}) == INVALID, field
+        assert call(sh(gate=1), a=FAKE + 2) == INVALID
 
 
 def test_backward_validation_and_workspace(L):

@@ -79,6 +79,24 @@ def test_verify_traffic_matches_its_algorithmic_bytes():
     assert abs(t / (256 * 32 * bench.verify_bytes(2)) - 1) < 0.01
 
 
+def test_verify_by_recomputation_traffic_matches_its_algorithmic_bytes():
+    # a round of verify_tokens + accept_tokens (B=256, two tokens, the seeded
+    # accepted counts of the bench: 182 accepting sequences) moves within 1%
+    # of its algorithmic bytes, and fewer than the history round (verify with
+    # the history, then commit)
+    B, K, H, acc = 256, 2, 32, 182
+    t = bench._round_traffic(B, K)
+    assert t is not None
+    state, tok = 128 * 128 * 4, K * (768 + 512 + 4 + 512)
+    algorithmic = B * H * (state + tok) + acc * H * (2 * state + K * (768 + 512 + 4))
+    assert abs(t / algorithmic - 1) < 0.01
+    hist = (bench._traffic("decode_tokens_kernel", "verify_b256_k2", bench.VERIFY_TRAFFIC_SUMMARY % (B, K),
+                           bench.DECODE_SOURCE)
+            + bench._traffic("commit_kernel", "verify_b256_k2", bench.VERIFY_TRAFFIC_SUMMARY % (B, K),
+                             bench.DECODE_SOURCE))
+    assert t < 0.6 * hist
+
+
 def test_backward_traffic_is_summarised_for_both_kernels():
     # the backward summary covers both of its kernels on the committed source;
     # its bytes exceed the layer's algorithmic 3,848 per token and head (the

@@ -133,3 +133,100 @@ def test_verify_workload_b256_two_tokens():
     ro, rst = _oracle(sel)
     assert rel_l2(np64(o[n_idx, :, h_idx]), ro[:, :, 0]) < 2e-3
     assert rel_l2(np64(hist[n_idx, :, h_idx]), rst[:, :, 0]) < 2e-3
+
+
+def _round(t, S, accepted, preact=False):
+    """One verification round with rollback by recomputation: verify_tokens
+    (S untouched), then accept_tokens; returns (o, the advanced state)."""
+    S = S.clone()
+    S_before = S.clone()
+    o = kda.verify_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, preact=preact)
+    assert torch.equal(S, S_before)                                  # verify writes no state
+    kda.accept_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, accepted, preact=preact)
+    return o, S
+
+
+@pytest.mark.parametrize("K", [1, 2, 4, 7])
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_verify_and_accept_equal_history_and_commit(K, D, dtype):
+    """Rollback by recomputation gives, bit for bit, the outputs of
+    decode_tokens with the history and the states of state_commit, for every
+    accepted count (none, some, all, past k, negative), and both match the
+    oracle."""
+    dev = device()
+    N = 6
+    t = _inputs(N, K, 2, D, dtype, seed=60 + K * D, dev=dev)
+    accepted = torch.tensor([0, 1, K, K + 5, -2, min(2, K)], dtype=torch.int32, device=dev)
+    o, S = _round(t, t["S"], accepted)
+    S_h = t["S"].clone()
+    o_h, hist = kda.decode_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S_h, keep_states=True)
+    kda.state_commit(S_h, hist, accepted)
+    assert torch.equal(o, o_h) and torch.equal(S, S_h)
+    assert torch.equal(S[0], t["S"][0]) and torch.equal(S[4], t["S"][4])   # nothing accepted
+    ro, rst = _oracle(t)
+    want = sp.commit(np64(t["S"]), rst, accepted.cpu().numpy())
+    assert rel_l2(np64(o), ro) < 1e-5 and rel_l2(np64(S), want) < 1e-5
+
+
+@pytest.mark.parametrize("gate", ["channel", "head"])
+@pytest.mark.parametrize("form", ["final", "preact"])
+def test_verify_and_accept_gate_and_form(gate, form):
+    dev = device()
+    N, K = 4, 3
+    t = _inputs(N, K, 2, 64, torch.bfloat16, seed=61, dev=dev, gate=gate, form=form)
+    accepted = torch.tensor([3, 0, 1, 2], dtype=torch.int32, device=dev)
+    o, S = _round(t, t["S"], accepted, preact=form == "preact")
+    ro, rst = _oracle(t, form)
+    want = sp.commit(np64(t["S"]), rst, accepted.cpu().numpy())
+    assert rel_l2(np64(o), ro) < 1e-5 and rel_l2(np64(S), want) < 1e-5
+
+
+def test_accept_rounds_chain():
+    """Three rounds in a row on one live state (each round's drafts depend on
+    nothing else here): after them the state equals running the accepted
+    tokens of every round one after another."""
+    dev = device()
+    N, K, H, D = 5, 3, 2, 128
+    S = _inputs(N, K, H, D, torch.bfloat16, seed=70, dev=dev)["S"].clone()
+    S_ref = S.clone()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(70)
+    for r in range(3):
+        t = _inputs(N, K, H, D, torch.bfloat16, seed=71 + r, dev=dev)
+        accepted = torch.randint(0, K + 1, (N,), generator=g, dtype=torch.int32).to(dev)
+        _, S = _round(t, S, accepted)
+        # the reference: each sequence advanced by its accepted tokens alone
+        for n in range(N):
+            j = int(accepted[n])
+            if j > 0:
+                head = {key: t[key][n:n + 1, :j].contiguous() for key in ("q", "k", "v", "alpha", "beta")}
+                Sn = S_ref[n:n + 1].clone()
+                kda.decode_tokens(head["q"], head["k"], head["v"], head["alpha"], head["beta"], Sn)
+                S_ref[n] = Sn[0]
+    assert torch.equal(S, S_ref)
+
+
+def test_verify_and_accept_workload_b256_two_tokens():
+    """B=256, H=32, d=128, bf16, two tokens per sequence: the round by
+    recomputation equals the history and commit round bit for bit, and a
+    seeded sample of 256 (sequence, head) pairs matches the oracle."""
+    dev = device()
+    B, H, D, K = 256, 32, 128, 2
+    t = _inputs(B, K, H, D, torch.bfloat16, seed=0, dev=dev, decay="strong")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(0)
+    accepted = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev)
+    o, S = _round(t, t["S"], accepted)
+    S_h = t["S"].clone()
+    o_h, hist = kda.decode_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S_h, keep_states=True)
+    kda.state_commit(S_h, hist, accepted)
+    assert torch.equal(o, o_h) and torch.equal(S, S_h)
+    pick = seeded_sample(B * H, 256, seed=7)
+    n_idx, h_idx = pick // H, pick % H
+    sel = {key: t[key][n_idx, :, h_idx][:, :, None] for key in ("q", "k", "v", "alpha", "beta")}
+    sel["S"] = t["S"][n_idx, h_idx][:, None]
+    ro, rst = _oracle(sel)
+    want = sp.commit(np64(sel["S"]), rst, accepted.cpu().numpy()[n_idx])
+    assert rel_l2(np64(o[n_idx, :, h_idx]), ro[:, :, 0]) < 2e-3
+    assert rel_l2(np64(S[n_idx, h_idx]), want[:, 0]) < 2e-3
