@@ -31,7 +31,7 @@ KDA_GATE_CHANNEL = 0
 KDA_GATE_HEAD = 1
 KDA_INPUT_FINAL = 0
 KDA_INPUT_PREACT = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 NOALLOC_WORKSPACE_BYTES = 128 << 20   # KDA_NOALLOC_WORKSPACE_BYTES
 CHUNK = 64
 

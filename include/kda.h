@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 #define KDA_CHUNK 64 /* prefill chunk length (tokens); not a semantic parameter */
 
 typedef enum kda_status {
