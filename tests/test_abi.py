@@ -62,7 +62,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.kda_abi_version() == 4
+    assert L.kda_abi_version() == 5
     names = [L.kda_status_string(i).decode() for i in range(5)]
     assert names == ["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
                      "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_LAUNCH"]
