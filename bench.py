@@ -55,6 +55,7 @@ BACKWARD_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_backward_4k.j
 BACKWARD_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_backward.hip")
 VERIFY_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_b%d_k%d.json")  # % (batch, tokens)
 VERIFY_RECOMPUTE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_recompute_b%d_k%d.json")
+VERIFY_FUSED_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_fused_b%d_k%d.json")
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
 # Useful matrix work of the chunked form per token and head at d = 128, C = 64:
 # the decayed Gram blocks, the triangular transform and the state products
@@ -91,7 +92,7 @@ def _parse():
                         "less than the recommended size)")
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
-    p.add_argument("--only", choices=["backward", "verify", "verify_recompute"],
+    p.add_argument("--only", choices=["backward", "verify", "verify_recompute", "verify_fused"],
                    help="run only this leg (after --calibrate-copy, if given) and print its summary; "
                         "for hardware counter runs of one kernel family")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -411,6 +412,57 @@ def bench_verify_recompute(B, K, dev, steps=50):
             "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel (verify + accept)",
                          "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": _round_traffic(B, K), "bytes_per_step": v_bytes + a_bytes}}
+
+
+def bench_verify_fused(B, K, dev, steps=50):
+    """Verification rounds in one pass over the state each: every call
+    accepts the previous round's seeded accepted counts (the same counts as
+    bench_verify) and verifies the next round's tokens (kda_accept_verify_tokens).
+    One event pair around ``steps`` back-to-back rounds."""
+    from gated_delta_rule_76_amd import inputs, kda
+    spec = inputs.WORKLOADS["decode_b256"]
+    H, D = spec["H"], spec["D"]
+    sets = []
+    for i in range(N_SETS):
+        d = inputs.decode_inputs(B * K, H, D, 1, torch.bfloat16, spec["decay"], spec["s_std"], seed=i,
+                                 device=dev)
+        sets.append({key: d[key][0].reshape((B, K) + tuple(d[key].shape[2:])).contiguous()
+                     for key in ("q", "k", "v", "alpha", "beta")})
+    S = inputs.state(B, H, D, spec["s_std"], seed=0, device=dev)
+    o = torch.empty((B, K, H, D), dtype=torch.float32, device=dev)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(0)
+    accepted = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev)
+    keys = ("q", "k", "v", "alpha", "beta")
+
+    def rnd(i):
+        p, t = sets[(i + N_SETS - 1) % N_SETS], sets[i % N_SETS]
+        kda.accept_verify_tokens(tuple(p[key] for key in keys), accepted, *(t[key] for key in keys), S, out=o)
+    for i in range(5):
+        rnd(i)
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for i in range(steps):
+        rnd(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n_acc = int((accepted > 0).sum())
+    state = D * D * 4
+    # the state read once and, for an accepting sequence, written once; the
+    # accepted tokens' inputs (all k counted) and this round's inputs and outputs
+    nbytes = B * H * (state + K * (768 + 512 + 4 + 512)) + n_acc * H * (state + K * (768 + 512 + 4))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    t = _traffic("decode_tokens_kernel", "verify_fused_b%d_k%d" % (B, K), VERIFY_FUSED_TRAFFIC_SUMMARY % (B, K),
+                 DECODE_SOURCE)
+    return {"metric": "speculative verify steps/s, accept and verify in one pass (B=%d, %d tokens per "
+                      "sequence, H=32, d=128)" % (B, K),
+            "value": 1e3 / ms, "unit": "steps/s", "step_ms": ms, "tokens_per_s": B * K / (ms * 1e-3),
+            "sequences_accepting": n_acc,
+            "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel (accept + verify)", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": t,
+                         "bytes_per_step": nbytes}}
 
 
 def _round_traffic(B, K):
@@ -815,6 +867,10 @@ def main():
         print("[bench] speculative verify only", file=sys.stderr, flush=True)
         print(json.dumps({"verify": verify_summary(bench_verify(args.decode_batch, 2, dev))}), flush=True)
         return
+    if args.only == "verify_fused":
+        print("[bench] speculative verify, accept and verify in one pass, only", file=sys.stderr, flush=True)
+        print(json.dumps({"verify_fused": bench_verify_fused(args.decode_batch, 2, dev)}), flush=True)
+        return
     if args.only == "verify_recompute":
         print("[bench] speculative verify by recomputation only", file=sys.stderr, flush=True)
         print(json.dumps({"verify_recompute": bench_verify_recompute(args.decode_batch, 2, dev)}), flush=True)
@@ -887,6 +943,7 @@ def main():
             print("[bench] speculative verify", file=sys.stderr, flush=True)
             out["verify"] = verify_summary(bench_verify(args.decode_batch, 2, dev))
             out["verify_recompute"] = bench_verify_recompute(args.decode_batch, 2, dev)
+            out["verify_fused"] = bench_verify_fused(args.decode_batch, 2, dev)
         print("[bench] backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(args.workload if args.workload == "prefill_4k" else "prefill_4k", dev)
         if args.bounded_backward_mib:

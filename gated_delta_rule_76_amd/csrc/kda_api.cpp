@@ -317,6 +317,21 @@ kda_status_t kda_accept_tokens(const kda_shape_t *shape, const void *q, const vo
   return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+kda_status_t kda_accept_verify_tokens(const kda_shape_t *shape, const void *q0, const void *k0, const void *v0,
+                                      const float *alpha0, const float *beta0, const int32_t *accepted,
+                                      const void *q, const void *k, const void *v, const float *alpha,
+                                      const float *beta, float *S, float *o, void *stream) {
+  kda_status_t st = check_decode_call(shape, false, q, k, v, alpha, beta, S, o);
+  if (st != KDA_OK || shape->num_seqs == 0) return st;
+  // the previous round's tokens: the same shape, so the same checks
+  st = check_decode_call(shape, false, q0, k0, v0, alpha0, beta0, S, o);
+  if (st != KDA_OK) return st;
+  if (accepted == nullptr || !aligned4(accepted)) return KDA_ERR_INVALID_ARGUMENT;
+  hipError_t e = kda::launch_accept_verify_tokens(*shape, q0, k0, v0, alpha0, beta0, accepted, q, k, v, alpha,
+                                                  beta, S, o, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 kda_status_t kda_decode_step(const kda_shape_t *shape, const void *q, const void *k, const void *v,
                              const float *alpha, const float *beta, float *S, float *o,
                              void *stream) {

@@ -249,13 +249,22 @@ enum TokMode : int {
   kTokHistory = 1,  // o for every token; the state after each token to hist; S unchanged
   kTokVerify = 2,   // o for every token; S unchanged, nothing else written
   kTokAccept = 3,   // no o; S advanced in place by the first accepted[n] tokens
+  kTokAcceptVerify = 4,  // S advanced by the first accepted[n] tokens of the previous round
+                         // (prev), then o for every token of this one; S holds the former
+};
+
+// One multi-token call: token rows n*ntok .. n*ntok + ntok - 1 of a source
+// belong to sequence n.
+template <typename TIn>
+struct TokSrc {
+  const TIn *q, *k, *v;
+  const float *alpha, *beta;
 };
 
 template <int D, typename TIn, int GATE, int FORM, int MODE, bool NTL>
 __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
-    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-    const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ S,
-    float *__restrict__ o, float *__restrict__ hist, const int32_t *__restrict__ accepted, int ntok, int H) {
+    const TokSrc<TIn> in, const TokSrc<TIn> prev, float *__restrict__ S, float *__restrict__ o,
+    float *__restrict__ hist, const int32_t *__restrict__ accepted, int ntok, int H) {
   constexpr bool HIST = MODE == kTokHistory;
   using Cfg = DecodeCfg<D>;
   constexpr int TPR = Cfg::TPR, RPP = Cfg::RPP, PASSES = Cfg::PASSES, NW = Cfg::NW;
@@ -273,17 +282,23 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
   const int cq = tid % TPR;
   const int r0 = tid / TPR;
   const int cj = tid < D ? tid : 0;
-  // tokens to run: all ntok, or the sequence's accepted count (clamped to
-  // [0, ntok]; a sequence with none keeps its state untouched)
-  int nt = ntok;
-  if constexpr (MODE == kTokAccept) {
+  // accepted tokens to run first (accept modes): the sequence's count,
+  // clamped to [0, ntok]; with none the state is not written
+  int na = 0;
+  if constexpr (MODE == kTokAccept || MODE == kTokAcceptVerify) {
     const int j = accepted[n];
-    nt = j < 0 ? 0 : (j > ntok ? ntok : j);
-    if (nt == 0) return;
+    na = j < 0 ? 0 : (j > ntok ? ntok : j);
+    if constexpr (MODE == kTokAccept) {
+      if (na == 0) return;
+    }
   }
+  // the source of the first tokens run: the accepted ones, or the call's
+  const TokSrc<TIn> first = (MODE == kTokAccept || (MODE == kTokAcceptVerify && na > 0)) ? prev : in;
 
+  // The first token's inputs are loaded before the state, so no load waits
+  // on another after the state arrives.
   TokenIn<D, TIn> cur, nxt;
-  load_token_in<D, TIn, GATE>(cur, q, k, v, alpha, beta, n * ntok * H + h, r0, cj);
+  load_token_in<D, TIn, GATE>(cur, first.q, first.k, first.v, first.alpha, first.beta, n * ntok * H + h, r0, cj);
   float *Sp = S + nh * (int64_t)(D * D) + cq * 4;
   float4 s[PASSES];
 #pragma unroll
@@ -296,119 +311,139 @@ __global__ __launch_bounds__(DecodeCfg<D>::NT) void decode_tokens_kernel(
       s[p] = *reinterpret_cast<const float4 *>(src);
     }
   }
-
-  for (int t = 0; t < nt; ++t) {
-    const int64_t th = (n * ntok + t) * H + h;  // token row * H + head
-    // The next token's inputs (the last token reloads its own: no branch).
-    const int tn = t + 1 < nt ? t + 1 : t;
-    load_token_in<D, TIn, GATE>(nxt, q, k, v, alpha, beta, (n * ntok + tn) * H + h, r0, cj);
-
-    float a[PASSES], kk[PASSES], qq[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      a[p] = kPre ? decay_from_preact(cur.a[p]) : cur.a[p];
-      kk[p] = to_f32(cur.k[p]);
-      qq[p] = to_f32(cur.q[p]);
-    }
-    const float bt = kPre ? strength_from_preact(cur.b) : cur.b;
-    const float vj = to_f32(cur.v);
-
-    float qk_part = 0.f, kn_part = 0.f, qn_part = 0.f;
-    if (cq == 0) {
-#pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        qk_part += qq[p] * kk[p];
-        if constexpr (kPre) {
-          kn_part += kk[p] * kk[p];
-          qn_part += qq[p] * qq[p];
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      qk_part += __shfl_xor(qk_part, off);
-      if constexpr (kPre) {
-        kn_part += __shfl_xor(kn_part, off);
-        qn_part += __shfl_xor(qn_part, off);
-      }
-    }
-    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const float ka = a[p] * kk[p], qa = a[p] * qq[p];
-      x[0] += ka * s[p].x; x[1] += ka * s[p].y; x[2] += ka * s[p].z; x[3] += ka * s[p].w;
-      y[0] += qa * s[p].x; y[1] += qa * s[p].y; y[2] += qa * s[p].z; y[3] += qa * s[p].w;
-    }
-#pragma unroll
-    for (int off = TPR; off < 64; off <<= 1) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] += __shfl_xor(x[j], off);
-        y[j] += __shfl_xor(y[j], off);
-      }
-    }
-    if (lane < TPR) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s_red[wave][0][cq * 4 + j] = x[j];
-        s_red[wave][1][cq * 4 + j] = y[j];
-      }
-    }
-    if (lane == 0) {
-      s_qk[wave][0] = qk_part;
-      s_qk[wave][1] = kn_part;
-      s_qk[wave][2] = qn_part;
-    }
-    __syncthreads();
-    if (tid < D) {
-      float xs = 0.f, ys = 0.f, qk = 0.f, kn = 0.f, qn = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        xs += s_red[w][0][tid];
-        ys += s_red[w][1][tid];
-        qk += s_qk[w][0];
-        if constexpr (kPre) {
-          kn += s_qk[w][1];
-          qn += s_qk[w][2];
-        }
-      }
-      float ik = 1.f, iq = 1.f;
-      if constexpr (kPre) {
-        ik = inv_norm(kn);
-        iq = inv_norm(qn);
-        xs *= ik;
-        ys *= iq;
-        qk *= ik * iq;
-      }
-      const float wv = bt * (vj - xs);
-      s_w[tid] = kPre ? wv * ik : wv;
-      if constexpr (MODE != kTokAccept) o[th * D + tid] = ys + qk * wv;
-    }
-    __syncthreads();
-    const float w0 = s_w[cq * 4 + 0], w1 = s_w[cq * 4 + 1], w2 = s_w[cq * 4 + 2], w3 = s_w[cq * 4 + 3];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      s[p].x = a[p] * s[p].x + kk[p] * w0;
-      s[p].y = a[p] * s[p].y + kk[p] * w1;
-      s[p].z = a[p] * s[p].z + kk[p] * w2;
-      s[p].w = a[p] * s[p].w + kk[p] * w3;
-    }
-    if constexpr (HIST) {
-      float *Hp = hist + th * (int64_t)(D * D) + cq * 4;
-#pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        const f32x4 nv = {s[p].x, s[p].y, s[p].z, s[p].w};
-        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(Hp + (int64_t)(r0 + p * RPP) * D));
-      }
-    }
-    cur = nxt;
-  }
-  if constexpr (MODE == kTokAdvance || MODE == kTokAccept) {
+  auto store_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const f32x4 nv = {s[p].x, s[p].y, s[p].z, s[p].w};
       __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(Sp + (int64_t)(r0 + p * RPP) * D));
     }
+  };
+
+  // count tokens of src from the state in registers, cur holding the first
+  // one's inputs; WO: write their outputs
+  auto run = [&](const TokSrc<TIn> &src, int count, auto wo) __attribute__((always_inline)) {
+    constexpr bool WO = decltype(wo)::value;
+    for (int t = 0; t < count; ++t) {
+      const int64_t th = (n * ntok + t) * H + h;  // token row * H + head
+      // The next token's inputs (the last token reloads its own: no branch).
+      const int tn = t + 1 < count ? t + 1 : t;
+      load_token_in<D, TIn, GATE>(nxt, src.q, src.k, src.v, src.alpha, src.beta, (n * ntok + tn) * H + h, r0, cj);
+
+      float a[PASSES], kk[PASSES], qq[PASSES];
+  #pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        a[p] = kPre ? decay_from_preact(cur.a[p]) : cur.a[p];
+        kk[p] = to_f32(cur.k[p]);
+        qq[p] = to_f32(cur.q[p]);
+      }
+      const float bt = kPre ? strength_from_preact(cur.b) : cur.b;
+      const float vj = to_f32(cur.v);
+
+      float qk_part = 0.f, kn_part = 0.f, qn_part = 0.f;
+      if (cq == 0) {
+  #pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          qk_part += qq[p] * kk[p];
+          if constexpr (kPre) {
+            kn_part += kk[p] * kk[p];
+            qn_part += qq[p] * qq[p];
+          }
+        }
+      }
+  #pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        qk_part += __shfl_xor(qk_part, off);
+        if constexpr (kPre) {
+          kn_part += __shfl_xor(kn_part, off);
+          qn_part += __shfl_xor(qn_part, off);
+        }
+      }
+      float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const float ka = a[p] * kk[p], qa = a[p] * qq[p];
+        x[0] += ka * s[p].x; x[1] += ka * s[p].y; x[2] += ka * s[p].z; x[3] += ka * s[p].w;
+        y[0] += qa * s[p].x; y[1] += qa * s[p].y; y[2] += qa * s[p].z; y[3] += qa * s[p].w;
+      }
+  #pragma unroll
+      for (int off = TPR; off < 64; off <<= 1) {
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] += __shfl_xor(x[j], off);
+          y[j] += __shfl_xor(y[j], off);
+        }
+      }
+      if (lane < TPR) {
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s_red[wave][0][cq * 4 + j] = x[j];
+          s_red[wave][1][cq * 4 + j] = y[j];
+        }
+      }
+      if (lane == 0) {
+        s_qk[wave][0] = qk_part;
+        s_qk[wave][1] = kn_part;
+        s_qk[wave][2] = qn_part;
+      }
+      __syncthreads();
+      if (tid < D) {
+        float xs = 0.f, ys = 0.f, qk = 0.f, kn = 0.f, qn = 0.f;
+  #pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          xs += s_red[w][0][tid];
+          ys += s_red[w][1][tid];
+          qk += s_qk[w][0];
+          if constexpr (kPre) {
+            kn += s_qk[w][1];
+            qn += s_qk[w][2];
+          }
+        }
+        float ik = 1.f, iq = 1.f;
+        if constexpr (kPre) {
+          ik = inv_norm(kn);
+          iq = inv_norm(qn);
+          xs *= ik;
+          ys *= iq;
+          qk *= ik * iq;
+        }
+        const float wv = bt * (vj - xs);
+        s_w[tid] = kPre ? wv * ik : wv;
+        if constexpr (WO) o[th * D + tid] = ys + qk * wv;
+      }
+      __syncthreads();
+      const float w0 = s_w[cq * 4 + 0], w1 = s_w[cq * 4 + 1], w2 = s_w[cq * 4 + 2], w3 = s_w[cq * 4 + 3];
+  #pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        s[p].x = a[p] * s[p].x + kk[p] * w0;
+        s[p].y = a[p] * s[p].y + kk[p] * w1;
+        s[p].z = a[p] * s[p].z + kk[p] * w2;
+        s[p].w = a[p] * s[p].w + kk[p] * w3;
+      }
+      if constexpr (HIST) {
+        float *Hp = hist + th * (int64_t)(D * D) + cq * 4;
+  #pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          const f32x4 nv = {s[p].x, s[p].y, s[p].z, s[p].w};
+          __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(Hp + (int64_t)(r0 + p * RPP) * D));
+        }
+      }
+      cur = nxt;
+    }
+  };
+
+  if constexpr (MODE == kTokAccept) {
+    run(prev, na, std::false_type{});
+    store_state();
+  } else if constexpr (MODE == kTokAcceptVerify) {
+    if (na > 0) {
+      run(prev, na, std::false_type{});
+      store_state();
+      load_token_in<D, TIn, GATE>(cur, in.q, in.k, in.v, in.alpha, in.beta, n * ntok * H + h, r0, cj);
+    }
+    run(in, ntok, std::true_type{});
+  } else {
+    run(in, ntok, std::true_type{});
+    if constexpr (MODE == kTokAdvance) store_state();
   }
 }
 
@@ -503,16 +538,24 @@ hipError_t launch_decode(const kda_shape_t &s, const void *q, const void *k, con
 
 namespace {
 
-hipError_t launch_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v, const float *alpha,
-                         const float *beta, float *S, float *o, float *hist, const int32_t *accepted, int mode,
-                         hipStream_t stream) {
+// Token sources: the call's tokens (q, k, v, alpha, beta), and the previous
+// round's for kTokAcceptVerify (q0 .. beta0; the accept mode runs the call's).
+struct TokPtrs {
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+};
+
+hipError_t launch_tokens(const kda_shape_t &s, const TokPtrs &cur, const TokPtrs &prev, float *S, float *o,
+                         float *hist, const int32_t *accepted, int mode, hipStream_t stream) {
   return dispatch(s, [&](auto d, auto t, auto g, auto f) {
     constexpr int D = decltype(d)::value;
     using TIn = typename decltype(t)::type;
     constexpr int G = decltype(g)::value, F = decltype(f)::value;
     const int64_t blocks = (int64_t)s.num_seqs * s.num_heads;
-    const TIn *qp = static_cast<const TIn *>(q), *kp = static_cast<const TIn *>(k),
-              *vp = static_cast<const TIn *>(v);
+    const TokSrc<TIn> in{static_cast<const TIn *>(cur.q), static_cast<const TIn *>(cur.k),
+                         static_cast<const TIn *>(cur.v), cur.alpha, cur.beta};
+    const TokSrc<TIn> pv{static_cast<const TIn *>(prev.q), static_cast<const TIn *>(prev.k),
+                         static_cast<const TIn *>(prev.v), prev.alpha, prev.beta};
     // The state is read once; once the bytes the call moves (that read plus
     // every state written) pass 1 GiB it is read with non-temporal loads too
     // (two tokens with history at B=256, 1.5 GiB: 336 -> 299 us per call).
@@ -523,8 +566,8 @@ hipError_t launch_tokens(const kda_shape_t &s, const void *q, const void *k, con
       constexpr int MO = decltype(mode_c)::value;
       constexpr bool NL = decltype(ntl_c)::value;
       hipLaunchKernelGGL((decode_tokens_kernel<D, TIn, G, F, MO, NL>), dim3((unsigned)blocks),
-                         dim3(DecodeCfg<D>::NT), 0, stream, qp, kp, vp, alpha, beta, S, o, hist, accepted,
-                         s.seq_len, s.num_heads);
+                         dim3(DecodeCfg<D>::NT), 0, stream, in, pv, S, o, hist, accepted, s.seq_len,
+                         s.num_heads);
     };
     auto go_mode = [&](auto mode_c) {
       if (ntl) go(mode_c, std::true_type{});
@@ -535,6 +578,7 @@ hipError_t launch_tokens(const kda_shape_t &s, const void *q, const void *k, con
       case kTokHistory: go_mode(Int<kTokHistory>{}); break;
       case kTokVerify: go_mode(Int<kTokVerify>{}); break;
       case kTokAccept: go_mode(Int<kTokAccept>{}); break;
+      case kTokAcceptVerify: go_mode(Int<kTokAcceptVerify>{}); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -546,21 +590,31 @@ hipError_t launch_tokens(const kda_shape_t &s, const void *q, const void *k, con
 hipError_t launch_decode_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
                                 const float *alpha, const float *beta, float *S, float *o, float *hist,
                                 hipStream_t stream) {
-  return launch_tokens(s, q, k, v, alpha, beta, S, o, hist, nullptr, hist != nullptr ? kTokHistory : kTokAdvance,
-                       stream);
+  const TokPtrs in{q, k, v, alpha, beta};
+  return launch_tokens(s, in, in, S, o, hist, nullptr, hist != nullptr ? kTokHistory : kTokAdvance, stream);
 }
 
 hipError_t launch_verify_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
                                 const float *alpha, const float *beta, const float *S, float *o,
                                 hipStream_t stream) {
   // (the kernel never writes S in this mode)
-  return launch_tokens(s, q, k, v, alpha, beta, const_cast<float *>(S), o, nullptr, nullptr, kTokVerify, stream);
+  const TokPtrs in{q, k, v, alpha, beta};
+  return launch_tokens(s, in, in, const_cast<float *>(S), o, nullptr, nullptr, kTokVerify, stream);
 }
 
 hipError_t launch_accept_tokens(const kda_shape_t &s, const void *q, const void *k, const void *v,
                                 const float *alpha, const float *beta, float *S, const int32_t *accepted,
                                 hipStream_t stream) {
-  return launch_tokens(s, q, k, v, alpha, beta, S, nullptr, nullptr, accepted, kTokAccept, stream);
+  const TokPtrs in{q, k, v, alpha, beta};
+  return launch_tokens(s, in, in, S, nullptr, nullptr, accepted, kTokAccept, stream);
+}
+
+hipError_t launch_accept_verify_tokens(const kda_shape_t &s, const void *q0, const void *k0, const void *v0,
+                                       const float *alpha0, const float *beta0, const int32_t *accepted,
+                                       const void *q, const void *k, const void *v, const float *alpha,
+                                       const float *beta, float *S, float *o, hipStream_t stream) {
+  const TokPtrs prev{q0, k0, v0, alpha0, beta0}, in{q, k, v, alpha, beta};
+  return launch_tokens(s, in, prev, S, o, nullptr, accepted, kTokAcceptVerify, stream);
 }
 
 hipError_t launch_commit(const kda_shape_t &s, float *S, const float *hist, const int32_t *accepted,

@@ -124,6 +124,14 @@ hipError_t launch_accept_tokens(const kda_shape_t &s, const void *q, const void 
                                 const float *alpha, const float *beta, float *S, const int32_t *accepted,
                                 hipStream_t stream);
 
+// S advanced in place by the first accepted[n] of the previous round's
+// tokens (q0 .. beta0), then the outputs of this round's tokens from it (S
+// keeps the former).
+hipError_t launch_accept_verify_tokens(const kda_shape_t &s, const void *q0, const void *k0, const void *v0,
+                                       const float *alpha0, const float *beta0, const int32_t *accepted,
+                                       const void *q, const void *k, const void *v, const float *alpha,
+                                       const float *beta, float *S, float *o, hipStream_t stream);
+
 // Backward pass.  Workspace: state checkpoints every bwd_block tokens per
 // (sequence, head) -- d_k x d_v floats per slot -- then the per-slice
 // partial row sums over the d_v / 16 column slices, [slices][rows][H]

@@ -102,6 +102,8 @@ def lib():
     L.kda_verify_tokens.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_accept_tokens.restype = ctypes.c_int
     L.kda_accept_tokens.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_accept_verify_tokens.restype = ctypes.c_int
+    L.kda_accept_verify_tokens.argtypes = [shp] + [vp] * 14
     L.kda_backward_workspace_size.restype = ctypes.c_int
     L.kda_backward_workspace_size.argtypes = [shp, ctypes.POINTER(sz)]
     L.kda_backward.restype = ctypes.c_int
@@ -477,6 +479,33 @@ def accept_tokens(q, k, v, alpha, beta, state, accepted, preact=False):
                                        _ptr(beta), _ptr(state), _ptr(accepted), _stream(q.device)),
                "kda_accept_tokens")
     return state
+
+
+def accept_verify_tokens(prev, accepted, q, k, v, alpha, beta, state, preact=False, out=None):
+    """One verification round in one pass over the state: ``state`` advanced
+    in place by the first accepted[n] tokens of the previous round, ``prev`` =
+    (q, k, v, alpha, beta) of that round, then the outputs of this round's
+    tokens from it (equal to accept_tokens(*prev, state, accepted) then
+    verify_tokens(q, k, v, alpha, beta, state)).  Returns o [N, k, H, D]."""
+    q0, k0, v0, alpha0, beta0 = prev
+    N, K, H, D, shape = _token_round(q, k, v, alpha, beta, state, preact)
+    N0, K0, H0, D0, shape0 = _token_round(q0, k0, v0, alpha0, beta0, state, preact)
+    if (N0, K0, H0, D0) != (N, K, H, D) or q0.dtype != q.dtype or shape0.gate != shape.gate:
+        raise ValueError("the previous round's tokens must have this round's shape, dtype and gate kind")
+    _require_gpu("accepted", accepted, torch.int32)
+    if tuple(accepted.shape) != (N,):
+        raise ValueError(f"accepted has shape {tuple(accepted.shape)}, expected {(N,)}")
+    o = out if out is not None else torch.empty((N, K, H, D), dtype=torch.float32, device=q.device)
+    _require_gpu("out", o, torch.float32)
+    _require_shape("out", o, (N, K, H, D))
+    _same_device(q.device, k=k, v=v, alpha=alpha, beta=beta, state=state, out=o, q0=q0, k0=k0, v0=v0,
+                 alpha0=alpha0, beta0=beta0, accepted=accepted)
+    with _on(q.device):
+        _check(lib().kda_accept_verify_tokens(ctypes.byref(shape), _ptr(q0), _ptr(k0), _ptr(v0), _ptr(alpha0),
+                                              _ptr(beta0), _ptr(accepted), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
+                                              _stream(q.device)), "kda_accept_verify_tokens")
+    return o
 
 
 def state_commit(state, states, accepted):

@@ -323,6 +323,27 @@ kda_status_t kda_accept_tokens(const kda_shape_t *shape,
                                const float *alpha, const float *beta,
                                float *S, const int32_t *accepted, void *stream);
 
+/* One round of the loop above in one pass over the state: S[n] advanced by
+ * the first accepted[n] tokens of the previous round (q0 .. beta0, what
+ * kda_accept_tokens would run), then the outputs of this round's tokens (q ..
+ * beta, what kda_verify_tokens would give) from the advanced state, which S
+ * keeps.  Equal, bit for bit, to kda_accept_tokens then kda_verify_tokens;
+ * per (sequence, head) the state is read once and written once when
+ * accepted[n] > 0.  Both rounds have the shape's k tokens per sequence.
+ *   shape           as for kda_verify_tokens
+ *   q0, k0, v0, alpha0, beta0, accepted   the previous round (as for
+ *                   kda_accept_tokens)
+ *   q, k, v, alpha, beta, o               this round (as for
+ *                   kda_verify_tokens)
+ *   S               [N][H][d_k][d_v] fp32 live states, updated */
+kda_status_t kda_accept_verify_tokens(const kda_shape_t *shape,
+                                      const void *q0, const void *k0, const void *v0,
+                                      const float *alpha0, const float *beta0,
+                                      const int32_t *accepted,
+                                      const void *q, const void *k, const void *v,
+                                      const float *alpha, const float *beta,
+                                      float *S, float *o, void *stream);
+
 /* Backward pass (training): gradients of L with respect to q, k, v, alpha,
  * beta and the initial states, given dL/do for every token (dO) and dL/dS_T
  * for every final state (dS_T, or NULL for zero).  It differentiates the

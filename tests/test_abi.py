@@ -49,7 +49,8 @@ def decode(L, s, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, S=FAKE, o=FAKE):
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["kda_abi_version", "kda_accept_tokens", "kda_backward",
+    assert declared_functions() == ["kda_abi_version", "kda_accept_tokens", "kda_accept_verify_tokens",
+                                    "kda_backward",
                                     "kda_backward_workspace_size", "kda_decode_step", "kda_decode_tokens",
                                     "kda_prefill", "kda_prefill_chunk_local", "kda_prefill_noalloc",
                                     "kda_prefill_state_pass", "kda_prefill_workspace_size",
@@ -245,6 +246,27 @@ def test_verify_and_accept_validation(L):
             assert call(sh(), **{field: None}) == INVALID, field
             assert call(sh(), **{field: FAKE + 2}) == INVALID, field
         assert call(sh(gate=1), a=FAKE + 2) == INVALID
+
+
+def test_accept_verify_validation(L):
+    # the fused round checks both rounds' tokens like kda_decode_tokens, and
+    # the accepted counts (every call here is rejected or launches nothing)
+    names = ("q0", "k0", "v0", "a0", "b0", "acc", "q", "k", "v", "a", "b", "S", "o")
+
+    def av(s, **kw):
+        args = [kw.get(n, FAKE) for n in names]
+        return L.kda_accept_verify_tokens(ctypes.byref(s) if s is not None else None, *args, None)
+    sh = lambda N=4, K=3, total=None, d=128, gate=0: kda.KdaShape(N, K, N * K if total is None else total,
+                                                                  2, d, d, 1, gate, 0)
+    assert av(None) == INVALID
+    assert av(sh(K=0)) == INVALID
+    assert av(sh(total=11)) == INVALID
+    assert av(sh(d=96)) == UNSUPPORTED
+    assert av(sh(N=0, total=0)) == OK
+    for field in names:
+        assert av(sh(), **{field: None}) == INVALID, field
+        assert av(sh(), **{field: FAKE + 2}) == INVALID, field
+    assert av(sh(gate=1), a0=FAKE + 2) == INVALID
 
 
 def test_backward_validation_and_workspace(L):

@@ -97,6 +97,19 @@ def test_verify_by_recomputation_traffic_matches_its_algorithmic_bytes():
     assert t < 0.6 * hist
 
 
+def test_fused_round_traffic_matches_its_algorithmic_bytes():
+    # accept + verify in one pass: the state read once and written once for
+    # an accepting sequence (182 of 256 in the bench's seeded counts)
+    B, K, H, acc = 256, 2, 32, 182
+    t = bench._traffic("decode_tokens_kernel", "verify_fused_b%d_k%d" % (B, K),
+                       bench.VERIFY_FUSED_TRAFFIC_SUMMARY % (B, K), bench.DECODE_SOURCE)
+    assert t is not None
+    state = 128 * 128 * 4
+    algorithmic = B * H * (state + K * (768 + 512 + 4 + 512)) + acc * H * (state + K * (768 + 512 + 4))
+    assert abs(t / algorithmic - 1) < 0.01
+    assert t < 0.8 * bench._round_traffic(B, K)
+
+
 def test_backward_traffic_is_summarised_for_both_kernels():
     # the backward summary covers both of its kernels on the committed source;
     # its bytes exceed the layer's algorithmic 3,848 per token and head (the

@@ -230,3 +230,69 @@ def test_verify_and_accept_workload_b256_two_tokens():
     want = sp.commit(np64(sel["S"]), rst, accepted.cpu().numpy()[n_idx])
     assert rel_l2(np64(o[n_idx, :, h_idx]), ro[:, :, 0]) < 2e-3
     assert rel_l2(np64(S[n_idx, h_idx]), want[:, 0]) < 2e-3
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_accept_verify_equals_accept_then_verify(K, D, dtype):
+    """The fused round (accept the previous round's tokens, then verify this
+    round's) gives the outputs and states of accept_tokens then verify_tokens,
+    bit for bit, for every accepted count, and the oracle's."""
+    dev = device()
+    N = 6
+    t0 = _inputs(N, K, 2, D, dtype, seed=80 + K * D, dev=dev)
+    t1 = _inputs(N, K, 2, D, dtype, seed=81 + K * D, dev=dev)
+    accepted = torch.tensor([0, 1, K, K + 5, -2, min(2, K)], dtype=torch.int32, device=dev)
+    prev = tuple(t0[key] for key in ("q", "k", "v", "alpha", "beta"))
+    S_a = t0["S"].clone()
+    kda.accept_tokens(*prev, S_a, accepted)
+    o_a = kda.verify_tokens(t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], S_a)
+    S_f = t0["S"].clone()
+    o_f = kda.accept_verify_tokens(prev, accepted, t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], S_f)
+    assert torch.equal(o_f, o_a) and torch.equal(S_f, S_a)
+    # the oracle: the accepted tokens from S, then this round from there
+    _, rst0 = _oracle(t0)
+    S_ref = sp.commit(np64(t0["S"]), rst0, accepted.cpu().numpy())
+    t1_ref = dict(t1)
+    t1_ref["S"] = torch.from_numpy(S_ref)
+    ro, _ = _oracle(t1_ref)
+    assert rel_l2(np64(S_f), S_ref) < 1e-5 and rel_l2(np64(o_f), ro) < 1e-5
+
+
+@pytest.mark.parametrize("gate", ["channel", "head"])
+@pytest.mark.parametrize("form", ["final", "preact"])
+def test_accept_verify_gate_and_form(gate, form):
+    dev = device()
+    N, K = 4, 3
+    t0 = _inputs(N, K, 2, 64, torch.bfloat16, seed=82, dev=dev, gate=gate, form=form)
+    t1 = _inputs(N, K, 2, 64, torch.bfloat16, seed=83, dev=dev, gate=gate, form=form)
+    accepted = torch.tensor([3, 0, 1, 2], dtype=torch.int32, device=dev)
+    prev = tuple(t0[key] for key in ("q", "k", "v", "alpha", "beta"))
+    pre = form == "preact"
+    S_a = t0["S"].clone()
+    kda.accept_tokens(*prev, S_a, accepted, preact=pre)
+    o_a = kda.verify_tokens(t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], S_a, preact=pre)
+    S_f = t0["S"].clone()
+    o_f = kda.accept_verify_tokens(prev, accepted, t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], S_f,
+                                   preact=pre)
+    assert torch.equal(o_f, o_a) and torch.equal(S_f, S_a)
+
+
+def test_accept_verify_workload_b256_two_tokens():
+    """B=256, H=32, d=128, bf16, two tokens per sequence: the fused round
+    equals accept then verify bit for bit."""
+    dev = device()
+    B, H, D, K = 256, 32, 128, 2
+    t0 = _inputs(B, K, H, D, torch.bfloat16, seed=0, dev=dev, decay="strong")
+    t1 = _inputs(B, K, H, D, torch.bfloat16, seed=1, dev=dev, decay="strong")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(0)
+    accepted = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev)
+    prev = tuple(t0[key] for key in ("q", "k", "v", "alpha", "beta"))
+    S_a = t0["S"].clone()
+    kda.accept_tokens(*prev, S_a, accepted)
+    o_a = kda.verify_tokens(t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], S_a)
+    S_f = t0["S"].clone()
+    o_f = kda.accept_verify_tokens(prev, accepted, t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], S_f)
+    assert torch.equal(o_f, o_a) and torch.equal(S_f, S_a)
