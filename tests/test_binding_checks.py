@@ -88,3 +88,39 @@ def test_tensors_of_one_call_must_share_a_device(host_only):
     S = torch.zeros(N, H, D, D, device="meta")
     with pytest.raises(ValueError, match="state is on meta"):
         kda.decode_step(q, k, v, torch.rand(N, H, D), torch.rand(N, H), S)
+
+
+def _round_inputs(N=3, K=2, H=2, D=16, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    q, k, v = (torch.randn(N, K, H, D, generator=g) for _ in range(3))
+    return q, k, v, torch.rand(N, K, H, D, generator=g), torch.rand(N, K, H, generator=g)
+
+
+def test_verify_tokens_rejects_short_out(host_only):
+    q, k, v, a, b = _round_inputs()
+    with pytest.raises(ValueError, match="out has shape"):
+        kda.verify_tokens(q, k, v, a, b, torch.zeros(3, 2, 16, 16), out=torch.empty(3, 2, 2, 8))
+
+
+def test_accept_tokens_rejects_wrong_counts(host_only):
+    q, k, v, a, b = _round_inputs()
+    S = torch.zeros(3, 2, 16, 16)
+    with pytest.raises(ValueError, match="accepted has shape"):
+        kda.accept_tokens(q, k, v, a, b, S, torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="state has shape"):
+        kda.accept_tokens(q, k, v, a, b, torch.zeros(3, 2, 16, 8), torch.zeros(3, dtype=torch.int32))
+
+
+def test_accept_verify_rejects_mismatched_rounds(host_only):
+    prev = _round_inputs(seed=1)
+    q, k, v, a, b = _round_inputs(seed=2)
+    S = torch.zeros(3, 2, 16, 16)
+    acc = torch.zeros(3, dtype=torch.int32)
+    # the previous round with more tokens per sequence than this one
+    longer = _round_inputs(K=3, seed=3)
+    with pytest.raises(ValueError, match="previous round"):
+        kda.accept_verify_tokens(longer, acc, q, k, v, a, b, S)
+    with pytest.raises(ValueError, match="out has shape"):
+        kda.accept_verify_tokens(prev, acc, q, k, v, a, b, S, out=torch.empty(3, 2, 2, 15))
+    with pytest.raises(ValueError, match="accepted has shape"):
+        kda.accept_verify_tokens(prev, torch.zeros(2, dtype=torch.int32), q, k, v, a, b, S)
