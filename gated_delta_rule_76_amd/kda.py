@@ -508,6 +508,38 @@ def accept_verify_tokens(prev, accepted, q, k, v, alpha, beta, state, preact=Fal
     return o
 
 
+class AcceptVerifyCall:
+    """A validated ``accept_verify_tokens`` round bound to its tensors, for
+    loops that issue it many times: the checks and the pointer marshalling run
+    once, ``run()`` makes only the C call (on the current stream of the
+    tensors' device)."""
+
+    def __init__(self, prev, accepted, q, k, v, alpha, beta, state, preact=False, out=None):
+        q0, k0, v0, alpha0, beta0 = prev
+        N, K, H, D, shape = _token_round(q, k, v, alpha, beta, state, preact)
+        N0, K0, H0, D0, shape0 = _token_round(q0, k0, v0, alpha0, beta0, state, preact)
+        if (N0, K0, H0, D0) != (N, K, H, D) or q0.dtype != q.dtype or shape0.gate != shape.gate:
+            raise ValueError("the previous round's tokens must have this round's shape, dtype and gate kind")
+        _require_gpu("accepted", accepted, torch.int32)
+        if tuple(accepted.shape) != (N,):
+            raise ValueError(f"accepted has shape {tuple(accepted.shape)}, expected {(N,)}")
+        self.o = out if out is not None else torch.empty((N, K, H, D), dtype=torch.float32, device=q.device)
+        _require_gpu("out", self.o, torch.float32)
+        _require_shape("out", self.o, (N, K, H, D))
+        _same_device(q.device, k=k, v=v, alpha=alpha, beta=beta, state=state, out=self.o, q0=q0, k0=k0, v0=v0,
+                     alpha0=alpha0, beta0=beta0, accepted=accepted)
+        self.shape = shape
+        self.device = q.device
+        self._keep = (q0, k0, v0, alpha0, beta0, accepted, q, k, v, alpha, beta, state)  # keep them alive
+        self._args = [_ptr(t) for t in self._keep] + [_ptr(self.o)]
+
+    def run(self):
+        with _on(self.device):
+            _check(lib().kda_accept_verify_tokens(ctypes.byref(self.shape), *self._args, _stream(self.device)),
+                   "kda_accept_verify_tokens")
+        return self.o
+
+
 def state_commit(state, states, accepted):
     """state[n] <- states[n, accepted[n] - 1] for accepted[n] >= 1 (capped at
     k); accepted[n] <= 0 keeps state[n].  accepted: int32 [N] on the GPU."""

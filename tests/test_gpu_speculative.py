@@ -296,3 +296,19 @@ def test_accept_verify_workload_b256_two_tokens():
     S_f = t0["S"].clone()
     o_f = kda.accept_verify_tokens(prev, accepted, t1["q"], t1["k"], t1["v"], t1["alpha"], t1["beta"], S_f)
     assert torch.equal(o_f, o_a) and torch.equal(S_f, S_a)
+
+
+def test_prepared_round_equals_the_call():
+    """AcceptVerifyCall (checks once, then only the C call) gives what
+    accept_verify_tokens gives."""
+    dev = device()
+    N, K = 5, 2
+    t0 = _inputs(N, K, 2, 128, torch.bfloat16, seed=90, dev=dev)
+    t1 = _inputs(N, K, 2, 128, torch.bfloat16, seed=91, dev=dev)
+    accepted = torch.tensor([2, 0, 1, 2, 1], dtype=torch.int32, device=dev)
+    prev = tuple(t0[key] for key in ("q", "k", "v", "alpha", "beta"))
+    cur = tuple(t1[key] for key in ("q", "k", "v", "alpha", "beta"))
+    S1, S2 = t0["S"].clone(), t0["S"].clone()
+    o1 = kda.accept_verify_tokens(prev, accepted, *cur, S1)
+    o2 = kda.AcceptVerifyCall(prev, accepted, *cur, S2).run()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
