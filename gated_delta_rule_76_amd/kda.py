@@ -487,25 +487,7 @@ def accept_verify_tokens(prev, accepted, q, k, v, alpha, beta, state, preact=Fal
     (q, k, v, alpha, beta) of that round, then the outputs of this round's
     tokens from it (equal to accept_tokens(*prev, state, accepted) then
     verify_tokens(q, k, v, alpha, beta, state)).  Returns o [N, k, H, D]."""
-    q0, k0, v0, alpha0, beta0 = prev
-    N, K, H, D, shape = _token_round(q, k, v, alpha, beta, state, preact)
-    N0, K0, H0, D0, shape0 = _token_round(q0, k0, v0, alpha0, beta0, state, preact)
-    if (N0, K0, H0, D0) != (N, K, H, D) or q0.dtype != q.dtype or shape0.gate != shape.gate:
-        raise ValueError("the previous round's tokens must have this round's shape, dtype and gate kind")
-    _require_gpu("accepted", accepted, torch.int32)
-    if tuple(accepted.shape) != (N,):
-        raise ValueError(f"accepted has shape {tuple(accepted.shape)}, expected {(N,)}")
-    o = out if out is not None else torch.empty((N, K, H, D), dtype=torch.float32, device=q.device)
-    _require_gpu("out", o, torch.float32)
-    _require_shape("out", o, (N, K, H, D))
-    _same_device(q.device, k=k, v=v, alpha=alpha, beta=beta, state=state, out=o, q0=q0, k0=k0, v0=v0,
-                 alpha0=alpha0, beta0=beta0, accepted=accepted)
-    with _on(q.device):
-        _check(lib().kda_accept_verify_tokens(ctypes.byref(shape), _ptr(q0), _ptr(k0), _ptr(v0), _ptr(alpha0),
-                                              _ptr(beta0), _ptr(accepted), _ptr(q), _ptr(k), _ptr(v),
-                                              _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
-                                              _stream(q.device)), "kda_accept_verify_tokens")
-    return o
+    return AcceptVerifyCall(prev, accepted, q, k, v, alpha, beta, state, preact=preact, out=out).run()
 
 
 class AcceptVerifyCall:
