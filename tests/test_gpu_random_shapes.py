@@ -8,7 +8,9 @@ checks prefill (o and S_T, rel-L2 over each whole tensor and over every
 multi-token verification (outputs, per-token states, live state untouched)
 against the oracle on the same inputs, with the tolerances of the dedicated
 tests: 2e-3 (bf16 prefill), 1e-5 (fp32 prefill, verification), 2e-5
-(backward).
+(backward); the verification cases also check rollback by recomputation
+(verify, accept, and both in one pass) against the history round bit for
+bit.
 """
 
 import random
@@ -81,9 +83,27 @@ def _verify_case(rng, dev, D, H, dtype, decay, seed):
     flat = lambda t: np64(t).reshape((-1,) + tuple(t.shape[2:]))
     ro, rst = speculative.decode_tokens(*(flat(tok[n]) for n in ("q", "k", "v", "alpha", "beta")), np64(S0), K)
     what = f"verify B={B} K={K}"
+    # the rollback by recomputation against the history round, bit for bit
+    # (accepted counts from the case's own seed, so the other cases keep their draws)
+    acc = torch.from_numpy(np.random.RandomState(seed).randint(-1, K + 2, size=B).astype(np.int32)).to(dev)
+    S_c = S0.clone()
+    kda.state_commit(S_c, hist, acc)
+    S_r = S0.clone()
+    o_r = kda.verify_tokens(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], S_r)
+    same_verify = torch.equal(o_r, o) and torch.equal(S_r, S0)
+    kda.accept_tokens(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], S_r, acc)
+    # one pass: accept these tokens, then verify them again from the advanced state
+    cur = tuple(tok[n] for n in ("q", "k", "v", "alpha", "beta"))
+    S_f = S0.clone()
+    o_f = kda.accept_verify_tokens(cur, acc, *cur, S_f)
+    o_2 = kda.verify_tokens(*cur, S_r)
     return [(what + " o", rel_l2(np64(o).reshape(ro.shape), ro), 1e-5),
             (what + " states", rel_l2(np64(hist).reshape(rst.shape), rst), 1e-5),
-            (what + " live state changed", float(not torch.equal(S, S0)), 0.5)]
+            (what + " live state changed", float(not torch.equal(S, S0)), 0.5),
+            (what + " verify_tokens differs from the history round", float(not same_verify), 0.5),
+            (what + " accept_tokens differs from the commit", float(not torch.equal(S_r, S_c)), 0.5),
+            (what + " accept_verify_tokens differs", float(not (torch.equal(S_f, S_r) and torch.equal(o_f, o_2))),
+             0.5)]
 
 
 def test_random_shapes_match_the_oracle():
