@@ -51,6 +51,13 @@ KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_prefi
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_decode_b%d.json")  # % batch
 DECODE_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_decode.hip")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "mfma_prefill_4k.json")
+# the counter summaries of the prefill's variants on the same workload: the
+# scalar gate and the pre-activation inputs (workload name + suffix)
+VARIANT_SUFFIX = {("channel", "final"): "", ("head", "final"): "_head", ("channel", "preact"): "_preact"}
+
+
+def _variant_path(path, suffix):
+    return path[:-len(".json")] + suffix + ".json" if suffix else path
 BACKWARD_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_backward_4k.json")
 BACKWARD_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_backward.hip")
 VERIFY_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_b%d_k%d.json")  # % (batch, tokens)
@@ -92,7 +99,8 @@ def _parse():
                         "less than the recommended size)")
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
-    p.add_argument("--only", choices=["backward", "verify", "verify_recompute", "verify_fused"],
+    p.add_argument("--only", choices=["backward", "verify", "verify_recompute", "verify_fused", "prefill_head",
+                                      "prefill_preact"],
                    help="run only this leg (after --calibrate-copy, if given) and print its summary; "
                         "for hardware counter runs of one kernel family")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -751,23 +759,23 @@ def _traffic(kernel, workload, summary=None, source=None):
     return k["fetch_bytes"] + k["write_bytes"]
 
 
-def _mfma_issued(workload):
+def _mfma_issued(workload, suffix=""):
     """Issued matrix-core flops per prefill call from the committed counter
-    summary, per kernel, or None when it is missing or was taken on other
-    kernel source."""
+    summary (of the variant ``suffix`` names), per kernel, or None when it is
+    missing or was taken on other kernel source."""
     try:
-        with open(MFMA_SUMMARY) as f:
+        with open(_variant_path(MFMA_SUMMARY, suffix)) as f:
             t = json.load(f)
         with open(KERNEL_SOURCE, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != sha or t.get("workload") != workload:
+    if t.get("source_sha256") != sha or t.get("workload") != workload + suffix:
         return None
     return {k: v["issued_flop"] for k, v in t.get("kernels", {}).items()}
 
 
-def prefill_summary(pf, gate, workload=None):
+def prefill_summary(pf, gate, workload=None, form="final"):
     """Rate, the dominant kernel's roofline and the matrix-core figures of
     one bench_prefill result.
 
@@ -789,7 +797,8 @@ def prefill_summary(pf, gate, workload=None):
     alg = th * lb / (times[dom] * 1e-3) / 1e9
     layer_gbs = th * lb / (pf["ms"] * 1e-3) / 1e9
     value = pf["total_tokens"] / (pf["ms"] * 1e-3)
-    issued = _mfma_issued(workload) if workload is not None and gate == "channel" else None
+    suffix = VARIANT_SUFFIX.get((gate, form))
+    issued = _mfma_issued(workload, suffix) if workload is not None and suffix is not None else None
     hbm_ceiling = HBM_PEAK_GBS * 1e9 / (lb * pf["H"])
     mf = {"peak_tflops": MFMA_PEAK_TFLOPS, "useful_flop_per_token_head": USEFUL_FLOP_PER_TOKEN_HEAD,
           "useful_tflops": th * USEFUL_FLOP_PER_TOKEN_HEAD / (pf["ms"] * 1e-3) / 1e12,
@@ -802,7 +811,7 @@ def prefill_summary(pf, gate, workload=None):
         mf["issued_flop_per_token_head"] = per_call / th
         mf["issued_tflops"] = per_call / (pf["ms"] * 1e-3) / 1e12
         mf["issued_frac"] = mf["issued_tflops"] / MFMA_PEAK_TFLOPS
-        mf["counters"] = os.path.relpath(MFMA_SUMMARY, ROOT)
+        mf["counters"] = os.path.relpath(_variant_path(MFMA_SUMMARY, suffix), ROOT)
         ceiling = min(hbm_ceiling, MFMA_PEAK_TFLOPS * 1e12 / (per_call / th * pf["H"]))
     mf["ceiling_tokens_per_s"] = ceiling
     mf["frac_of_ceiling"] = value / ceiling
@@ -869,6 +878,12 @@ def main():
         print("[bench] speculative verify only", file=sys.stderr, flush=True)
         print(json.dumps({"verify": verify_summary(bench_verify(args.decode_batch, 2, dev))}), flush=True)
         return
+    if args.only in ("prefill_head", "prefill_preact"):
+        gate, form = ("head", "final") if args.only == "prefill_head" else ("channel", "preact")
+        print(f"[bench] {args.only} only", file=sys.stderr, flush=True)
+        pv = bench_prefill(args.workload, args.steps, args.warmup, dev, gate=gate, form=form)
+        print(json.dumps({args.only: prefill_summary(pv, gate, args.workload, form)}), flush=True)
+        return
     if args.only == "verify_fused":
         print("[bench] speculative verify, accept and verify in one pass, only", file=sys.stderr, flush=True)
         print(json.dumps({"verify_fused": bench_verify_fused(args.decode_batch, 2, dev)}), flush=True)
@@ -922,7 +937,9 @@ def main():
         # The scalar-gate (Gated DeltaNet) form on the same shapes.
         print("[bench] scalar gate", file=sys.stderr, flush=True)
         pv = bench_prefill(args.workload, args.steps, args.warmup, dev, gate="head")
-        sg = {"prefill": prefill_summary(pv, "head")}
+        sg = {"prefill": prefill_summary(pv, "head", args.workload)}
+        sg["prefill"]["roofline"]["traffic"] = _traffic(sg["prefill"]["roofline"]["kernel"], args.workload + "_head",
+                                                        _variant_path(TRAFFIC_SUMMARY, "_head"))
         sg["prefill"]["metric"] = "scalar-gate prefill tokens/s/layer (H=32, d=128)"
         sg["prefill"]["call_ms"] = pv["call_ms"]
         sg["prefill"]["stalled_calls"] = pv["stalled_calls"]
@@ -933,7 +950,10 @@ def main():
         # stage); the bytes moved are the same as for activated inputs.
         print("[bench] pre-activation inputs", file=sys.stderr, flush=True)
         pp = bench_prefill(args.workload, args.steps, args.warmup, dev, form="preact")
-        pa = {"prefill": prefill_summary(pp, "channel")}
+        pa = {"prefill": prefill_summary(pp, "channel", args.workload, "preact")}
+        pa["prefill"]["roofline"]["traffic"] = _traffic(pa["prefill"]["roofline"]["kernel"],
+                                                        args.workload + "_preact",
+                                                        _variant_path(TRAFFIC_SUMMARY, "_preact"))
         pa["prefill"]["metric"] = "KDA prefill from pre-activations, tokens/s/layer (H=32, d=128)"
         pa["prefill"]["call_ms"] = pp["call_ms"]
         pa["prefill"]["stalled_calls"] = pp["stalled_calls"]

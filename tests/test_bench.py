@@ -110,6 +110,19 @@ def test_fused_round_traffic_matches_its_algorithmic_bytes():
     assert t < 0.8 * bench._round_traffic(B, K)
 
 
+@pytest.mark.parametrize("suffix", ["_head", "_preact"])
+def test_prefill_variants_have_their_own_counter_summaries(suffix):
+    # the scalar-gate and pre-activation prefills are profiled on their own
+    # runs (bench.py --only prefill_head / prefill_preact): each summary
+    # answers for its variant only, on the committed prefill source
+    issued = bench._mfma_issued("prefill_4k", suffix)
+    assert issued is not None and issued["chunk_state_kernel"] > 0 and issued["chunk_local_kernel"] > 0
+    t = bench._traffic("chunk_state_kernel", "prefill_4k" + suffix,
+                       bench._variant_path(bench.TRAFFIC_SUMMARY, suffix))
+    assert t is not None
+    assert bench._traffic("chunk_state_kernel", "prefill_4k", bench._variant_path(bench.TRAFFIC_SUMMARY, suffix)) is None
+
+
 def test_backward_traffic_is_summarised_for_both_kernels():
     # the backward summary covers both of its kernels on the committed source;
     # its bytes exceed the layer's algorithmic 3,848 per token and head (the
