@@ -39,7 +39,8 @@ inline int64_t max_chunks(const kda_shape_t &s) {
   return s.total_tokens / kChunk + (int64_t)s.num_seqs;
 }
 
-// Prefill workspace: [chunk table: (N+1) int32, padded to 256 B]
+// Prefill workspace: [chunk table: (N+1) int32, then the sequences by
+//                     descending chunk count: N int32; padded to 256 B]
 //                    [records: W H, slot h W + c - j0]
 //                    [carry: N H d_k d_v floats, only if needed]
 // The chunks of the batch are numbered in packed order (sequence after
@@ -56,7 +57,7 @@ inline int64_t max_chunks(const kda_shape_t &s) {
 //                     need)
 //   minimum size      table + H records (+ the carry area if S_T is NULL)
 inline size_t schedule_bytes(const kda_shape_t &s) {
-  return align_up(sizeof(int32_t) * (size_t)(s.num_seqs + 1), kWorkspaceAlign);
+  return align_up(sizeof(int32_t) * (size_t)(2 * s.num_seqs + 1), kWorkspaceAlign);
 }
 inline size_t prefill_workspace_bytes(const kda_shape_t &s) {
   return schedule_bytes(s) + (size_t)max_chunks(s) * (size_t)s.num_heads * record_bytes(s.d_k);

@@ -240,11 +240,17 @@ __device__ __forceinline__ int64_t load_token(int64_t t0, int r, int valid, int6
 
 // ---------------------------------------------------------------------------
 // Varlen schedule: base[n] = number of chunks of sequences < n, base[N] =
-// total chunks.  One workgroup; a block-wide scan per 1024 sequences.
+// total chunks.  One workgroup; a block-wide scan per 1024 sequences.  Then
+// order[0..N) = the sequences by descending chunk count (ties by index): the
+// state pass deals its workgroups out in that order, so the longest chains
+// start first and the short ones fill in behind them (longest-first list
+// scheduling of the sequential per-sequence passes).  Batches of more than
+// 1024 sequences keep the packed order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ cu, int N,
                                                         int32_t seq_len, int32_t *__restrict__ base) {
   __shared__ int32_t s_scan[1024];
+  __shared__ int32_t s_cnt[1024];
   const int tid = threadIdx.x;
   int32_t carry = 0;
   for (int start = 0; start < N; start += 1024) {
@@ -255,6 +261,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
       seq_range(cu, seq_len, n, s0, len);
       cnt = (int32_t)((len + C - 1) / C);
     }
+    s_cnt[tid] = cnt;
     s_scan[tid] = cnt;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -268,6 +275,21 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
     __syncthreads();
   }
   if (tid == 0) base[N] = carry;
+  int32_t *order = base + N + 1;
+  if (N <= 1024) {
+    // (s_cnt holds every sequence's count: one pass of the loop above)
+    if (tid < N) {
+      const int32_t mine = s_cnt[tid];
+      int rank = 0;
+      for (int m = 0; m < N; ++m) {
+        const int32_t c = s_cnt[m];
+        rank += (c > mine) || (c == mine && m < tid);
+      }
+      order[rank] = tid;
+    }
+  } else {
+    for (int n = tid; n < N; n += 1024) order[n] = n;
+  }
 }
 
 // A dense batch (no cu_seqlens) needs no table: every sequence has
@@ -1159,7 +1181,10 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   const int64_t pair = (int64_t)(within / G) * 8 + xcd;
   const int cg = within % G;
   if (pair >= (int64_t)N * H) return;
-  const int n = (int)(pair / H), h = (int)(pair % H);
+  // varlen: the sequences in the schedule's longest-first order
+  const int n = cu != nullptr ? base[N + 1 + (int)(pair / H)] : (int)(pair / H);
+  const int h = (int)(pair % H);
+  const int64_t nh = (int64_t)n * H + h;  // the (sequence, head) whose state this is
   const int col0 = VW * cg;
 
   // The sequence's packed chunks in this stripe, [lo, hi).  A sequence with
@@ -1180,7 +1205,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
     for (int e = tid; e < VW * (DK - D); e += NTH) Sop.store(e / (DK - D), D + e % (DK - D), 0.f);
   }
   f32x4 sreg[CT];
-  const float *S0p = sin ? sin + (size_t)pair * D * D : nullptr;
+  const float *S0p = sin ? sin + (size_t)nh * D * D : nullptr;
 #pragma unroll
   for (int t = 0; t < CT; ++t) {
     sreg[t] = zero4();
@@ -1401,7 +1426,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NTH) __attribute__((amdgpu_waves_per_eu
   // The state after this stripe: the final state, or the carry into the
   // next stripe.
   if (sout != nullptr && wave < NTILE) {
-    float *STp = sout + (size_t)pair * D * D;
+    float *STp = sout + (size_t)nh * D * D;
 #pragma unroll
     for (int t = 0; t < CT; ++t)
 #pragma unroll

@@ -131,7 +131,9 @@ int kda_abi_version(void);
 const char *kda_status_string(kda_status_t status);
 
 /* Recommended bytes of device workspace for kda_prefill of `shape` (written
- * to *bytes): a chunk table of N+1 int32 (padded to 256 B), then one record
+ * to *bytes): a chunk table of 2N+1 int32 (each sequence's first chunk, the
+ * total, and the sequences in the order the state pass takes them; padded to
+ * 256 B), then one record
  * of chunk operands (108.5 KiB at d = 128) per head and per 64-token chunk,
  * for an upper bound on the batch's chunks, floor(total_tokens/64) + N.  It
  * depends on N, H, d and total_tokens only.  With it every chunk of the batch

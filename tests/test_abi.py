@@ -73,7 +73,7 @@ def test_version_and_status_strings(L):
 @pytest.mark.parametrize("N,T,H,d", [(1, 64, 2, 16), (1, 4096, 32, 128), (8, 0, 32, 128), (3, 65, 4, 64)])
 def test_workspace_size_formula(N, T, H, d):
     need = kda.prefill_workspace_size(N, N * T, H, d)
-    sched = ((4 * (N + 1) + 255) // 256) * 256
+    sched = ((4 * (2 * N + 1) + 255) // 256) * 256      # chunk table + longest-first order
     chunks = (N * T) // 64 + N
     nkb = max(d, 32) // 32
     frags = 4 * nkb * 2 + (d // 16) * 2 + 6           # Khat, Qhat, Ktil^T T, M T

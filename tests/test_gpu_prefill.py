@@ -218,7 +218,7 @@ def test_two_phase_calls_equal_prefill(gate):
 
 
 def _table_bytes(N):
-    return -(-4 * (N + 1) // 256) * 256
+    return -(-4 * (2 * N + 1) // 256) * 256
 
 
 # (lengths, dense batch?, heads, head size, dtype, S0, gate)
