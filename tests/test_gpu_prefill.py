@@ -98,6 +98,24 @@ def test_prefill_varlen_ragged_and_empty(dtype):
     assert torch.equal(ST[0], d["S0"][0]) and torch.equal(ST[6], d["S0"][6])   # empty sequences
 
 
+@pytest.mark.parametrize("N", [300, 1100])
+def test_prefill_many_short_sequences(N):
+    """Hundreds and more than 1,024 sequences (the chunk table's scan runs in
+    blocks of 1,024, and the state pass takes the sequences longest first up to
+    1,024 of them, in packed order above): lengths 0..150, some empty; every
+    output and final state against the oracle."""
+    dev = device()
+    rng = np.random.RandomState(N)
+    lens = [int(x) for x in rng.randint(0, 151, size=N)]
+    lens[3] = 0
+    d = inputs.prefill_inputs(lens, 2, 16, torch.float32, "medium", 0.3, seed=N, device=dev)
+    o, ST = kda.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"])
+    cu = np.asarray(d["cu_seqlens"].cpu())
+    ro, rST = _oracle(d, cu=cu, S0=np64(d["S0"]))
+    _check(o, ST, ro, rST, TOL[torch.float32], f"{N} short sequences", cu)
+    assert torch.equal(ST[3], d["S0"][3])
+
+
 @pytest.mark.parametrize("D", [32, 128])
 def test_prefill_dense_batch_layout(D):
     dev = device()
