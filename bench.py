@@ -422,6 +422,42 @@ def bench_verify_recompute(B, K, dev, steps=50):
                          "traffic": _round_traffic(B, K), "bytes_per_step": v_bytes + a_bytes}}
 
 
+def bench_decode_tokens(B, K, dev, steps=50):
+    """Multi-token decode: K tokens per sequence per call, the state read and
+    written once per call (kda_decode_tokens without a history), B=256; one
+    event pair around ``steps`` back-to-back calls.  Against single-token
+    decode the state traffic per token drops K-fold."""
+    from gated_delta_rule_76_amd import inputs, kda
+    spec = inputs.WORKLOADS["decode_b256"]
+    H, D = spec["H"], spec["D"]
+    sets = []
+    for i in range(N_SETS):
+        d = inputs.decode_inputs(B * K, H, D, 1, torch.bfloat16, spec["decay"], spec["s_std"], seed=i,
+                                 device=dev)
+        sets.append({key: d[key][0].reshape((B, K) + tuple(d[key].shape[2:])).contiguous()
+                     for key in ("q", "k", "v", "alpha", "beta")})
+    S = inputs.state(B, H, D, spec["s_std"], seed=0, device=dev)
+    o = torch.empty((B, K, H, D), dtype=torch.float32, device=dev)
+    run = lambda t: kda.decode_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, out=o)
+    for i in range(5):
+        run(sets[i % N_SETS])
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for i in range(steps):
+        run(sets[i % N_SETS])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = B * H * (2 * D * D * 4 + K * (768 + 512 + 4 + 512))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "multi-token decode tokens/s (B=%d, %d tokens per sequence per call, H=32, d=128)" % (B, K),
+            "value": B * K / (ms * 1e-3), "unit": "tokens/s", "call_ms": ms,
+            "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel (advance)", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "bytes_per_call": nbytes}}
+
+
 def bench_verify_fused(B, K, dev, steps=50):
     """Verification rounds in one pass over the state each: every call
     accepts the previous round's seeded accepted counts (the same counts as
@@ -966,6 +1002,7 @@ def main():
             out["verify"] = verify_summary(bench_verify(args.decode_batch, 2, dev))
             out["verify_recompute"] = bench_verify_recompute(args.decode_batch, 2, dev)
             out["verify_fused"] = bench_verify_fused(args.decode_batch, 2, dev)
+            out["decode_tokens_k4"] = bench_decode_tokens(args.decode_batch, 4, dev)
         print("[bench] backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(args.workload if args.workload == "prefill_4k" else "prefill_4k", dev)
         if args.bounded_backward_mib:
