@@ -63,6 +63,7 @@ BACKWARD_SOURCE = os.path.join(ROOT, "gated_delta_rule_76_amd", "csrc", "kda_bac
 VERIFY_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_b%d_k%d.json")  # % (batch, tokens)
 VERIFY_RECOMPUTE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_recompute_b%d_k%d.json")
 VERIFY_FUSED_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_verify_fused_b%d_k%d.json")
+DECODE_TOKENS_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_decode_tokens_b%d_k%d.json")
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
 # Useful matrix work of the chunked form per token and head at d = 128, C = 64:
 # the decayed Gram blocks, the triangular transform and the state products
@@ -100,7 +101,7 @@ def _parse():
     p.add_argument("--oracle-rates", action="store_true",
                    help="only time the fp64 CPU oracle on every workload (no GPU)")
     p.add_argument("--only", choices=["backward", "verify", "verify_recompute", "verify_fused", "prefill_head",
-                                      "prefill_preact"],
+                                      "prefill_preact", "decode_tokens"],
                    help="run only this leg (after --calibrate-copy, if given) and print its summary; "
                         "for hardware counter runs of one kernel family")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -451,10 +452,12 @@ def bench_decode_tokens(B, K, dev, steps=50):
     ms = e0.elapsed_time(e1) / steps
     nbytes = B * H * (2 * D * D * 4 + K * (768 + 512 + 4 + 512))
     gbs = nbytes / (ms * 1e-3) / 1e9
+    t = _traffic("decode_tokens_kernel", "decode_tokens_b%d_k%d" % (B, K), DECODE_TOKENS_TRAFFIC_SUMMARY % (B, K),
+                 DECODE_SOURCE)
     return {"metric": "multi-token decode tokens/s (B=%d, %d tokens per sequence per call, H=32, d=128)" % (B, K),
             "value": B * K / (ms * 1e-3), "unit": "tokens/s", "call_ms": ms,
             "roofline": {"bound": "hbm", "kernel": "decode_tokens_kernel (advance)", "achieved": gbs,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": t,
                          "bytes_per_call": nbytes}}
 
 
@@ -923,6 +926,10 @@ def main():
     if args.only == "verify_fused":
         print("[bench] speculative verify, accept and verify in one pass, only", file=sys.stderr, flush=True)
         print(json.dumps({"verify_fused": bench_verify_fused(args.decode_batch, 2, dev)}), flush=True)
+        return
+    if args.only == "decode_tokens":
+        print("[bench] multi-token decode only", file=sys.stderr, flush=True)
+        print(json.dumps({"decode_tokens_k4": bench_decode_tokens(args.decode_batch, 4, dev)}), flush=True)
         return
     if args.only == "verify_recompute":
         print("[bench] speculative verify by recomputation only", file=sys.stderr, flush=True)

@@ -26,6 +26,11 @@ backward / --only verify, each with --calibrate-copy):
     python -m gated_delta_rule_76_amd.counters F.csv W.csv --target decode \\
         --workload verify_b256_k2 > profiles/traffic_verify_b256_k2.json
 
+The multi-token decode leg (bench.py --only decode_tokens --calibrate-copy):
+
+    python -m gated_delta_rule_76_amd.counters F.csv W.csv --target decode \\
+        --workload decode_tokens_b256_k4 > profiles/traffic_decode_tokens_b256_k4.json
+
 FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB).  Each is scaled by
 the factor that maps the same counter of a plain elementwise float64 copy
 of 256 MiB (the --calibrate-copy kernel, which reads and writes exactly

@@ -79,6 +79,16 @@ def test_verify_traffic_matches_its_algorithmic_bytes():
     assert abs(t / (256 * 32 * bench.verify_bytes(2)) - 1) < 0.01
 
 
+def test_multi_token_decode_traffic_matches_its_algorithmic_bytes():
+    # four tokens per sequence per call at B=256: the state read and written
+    # once, the four tokens' inputs read and outputs written, within 1%
+    B, K, H = 256, 4, 32
+    t = bench._traffic("decode_tokens_kernel", "decode_tokens_b%d_k%d" % (B, K),
+                       bench.DECODE_TOKENS_TRAFFIC_SUMMARY % (B, K), bench.DECODE_SOURCE)
+    assert t is not None
+    assert abs(t / (B * H * (2 * 128 * 128 * 4 + K * (768 + 512 + 4 + 512))) - 1) < 0.01
+
+
 def test_verify_by_recomputation_traffic_matches_its_algorithmic_bytes():
     # a round of verify_tokens + accept_tokens (B=256, two tokens, the seeded
     # accepted counts of the bench: 182 accepting sequences) moves within 1%
