@@ -135,6 +135,25 @@ def test_verify_workload_b256_two_tokens():
     assert rel_l2(np64(hist[n_idx, :, h_idx]), rst[:, :, 0]) < 2e-3
 
 
+def test_tokens_in_place_workload_b256_four_tokens():
+    """B=256, H=32, d=128, bf16, four tokens per sequence per call with the
+    state advanced in place (the multi-token decode that bench.py times):
+    every output and the final state of a seeded sample of 256
+    (sequence, head) pairs."""
+    dev = device()
+    B, H, D, K = 256, 32, 128, 4
+    t = _inputs(B, K, H, D, torch.bfloat16, seed=3, dev=dev, decay="strong")
+    S = t["S"].clone()
+    o = kda.decode_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S)
+    pick = seeded_sample(B * H, 256, seed=11)
+    n_idx, h_idx = pick // H, pick % H
+    sel = {key: t[key][n_idx, :, h_idx][:, :, None] for key in ("q", "k", "v", "alpha", "beta")}
+    sel["S"] = t["S"][n_idx, h_idx][:, None]
+    ro, rst = _oracle(sel)
+    assert rel_l2(np64(o[n_idx, :, h_idx]), ro[:, :, 0]) < 2e-3
+    assert rel_l2(np64(S[n_idx, h_idx]), rst[:, -1, 0]) < 2e-3
+
+
 def _round(t, S, accepted, preact=False):
     """One verification round with rollback by recomputation: verify_tokens
     (S untouched), then accept_tokens; returns (o, the advanced state)."""
